@@ -1,0 +1,130 @@
+"""The oracle: TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.
+
+A plain, slow, double-precision CPU implementation of band + global sparse
+attention (``lfattn_oracle.c``, loaded here through ctypes) and a numpy
+brute-force mask form of it (``brute.py``).  Only the test suite, the smoke
+check and the benchmark's CPU baseline leg may import this package; the GPU
+library never does, and the two share no code.
+
+The definition it implements, and the passages it follows, are stated in the
+header of ``lfattn_oracle.c``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lfattn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+               "-pthread", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i32p = ctypes.POINTER(ctypes.c_int)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        lib.lfo_allowed_set.restype = ctypes.c_int64
+        lib.lfo_allowed_set.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p,
+                                        ctypes.c_int, ctypes.c_int, i32p]
+        lib.lfo_count_pairs.restype = ctypes.c_int64
+        lib.lfo_count_pairs.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        i32p, i32p, ctypes.c_int]
+        lib.lfo_attention.restype = ctypes.c_int
+        lib.lfo_attention.argtypes = [f32p, f32p, f32p, f64p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p,
+                                      ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64,
+                                      ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _i32(a):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+
+
+def allowed_set(n: int, window: int, dilation: int, glob, i: int) -> np.ndarray:
+    """Sorted key positions row i scores (one head)."""
+    lib = _load()
+    g, gp = _i32(list(glob))
+    keys = np.empty(n + len(g) + 1, dtype=np.int32)
+    cnt = lib.lfo_allowed_set(n, window, dilation, gp, len(g), i,
+                              keys.ctypes.data_as(ctypes.POINTER(ctypes.c_int)))
+    if cnt < 0:
+        raise ValueError("oracle: invalid arguments (code %d)" % cnt)
+    return keys[:cnt].copy()
+
+
+def count_pairs(B: int, H: int, n: int, window: int, dilation=None, glob=()) -> int:
+    """Total scored pairs over B x H x n rows, by explicit set construction."""
+    lib = _load()
+    g, gp = _i32(list(glob))
+    d, dp = _i32(dilation)
+    cnt = lib.lfo_count_pairs(B, H, n, window, dp, gp, len(g))
+    if cnt < 0:
+        raise ValueError("oracle: invalid arguments (code %d)" % cnt)
+    return int(cnt)
+
+
+def attention(q, k, v, window: int, dilation=None, glob=(), scale: float = 0.0,
+              rows=None, nthreads: int | None = None) -> np.ndarray:
+    """Oracle attention output in float64.
+
+    q, k, v: float32 arrays [B, H, N, D] (bf16 data already widened).
+    rows: None for every row (returns [B, H, N, D]) or flat indices
+    (b*H + h)*N + i (returns [len(rows), D]).
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    B, H, N, D = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    g, gp = _i32(list(glob))
+    d, dp = _i32(dilation)
+    if d is not None:
+        assert len(d) == H
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    if rows is None:
+        n_rows = B * H * N
+        rp = None
+        out = np.empty((B, H, N, D), dtype=np.float64)
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n_rows = len(r)
+        rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        out = np.empty((n_rows, D), dtype=np.float64)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    st = lib.lfo_attention(q.ctypes.data_as(f32p), k.ctypes.data_as(f32p), v.ctypes.data_as(f32p),
+                           out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                           B, H, N, D, window, dp, gp, len(g), float(scale), rp, n_rows,
+                           int(nthreads))
+    if st != 0:
+        raise ValueError("oracle: attention failed (code %d)" % st)
+    return out

@@ -1,0 +1,275 @@
+/*
+ * lfattn oracle: TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.
+ *
+ * A plain, slow, double-precision CPU implementation of the forward pass of
+ * band + global sparse self-attention.  It exists only to check the GPU
+ * library.  Only the test suite, the smoke check and the benchmark's CPU
+ * baseline leg may load or call it; the GPU library never links or loads it,
+ * and it shares no code, header, table or constant with that library.
+ *
+ * What is computed, for one (batch b, head h, query row i), all in double:
+ *
+ *   S_i = { 0, 1, ..., N-1 }                                   if i is global
+ *   S_i = { i + d*k : -hw <= k <= hw, 0 <= i + d*k < N }  u  G  otherwise
+ *   z_j = scale * sum_c Q[i,c] * K[j,c]                          for j in S_i
+ *   O_i = sum_{j in S_i} exp(z_j - max z) V_j / sum_{j in S_i} exp(z_j - max z)
+ *
+ * with hw = floor(window / 2), d = the head's dilation and G the set of global
+ * token positions.  Sources:
+ *   - attention itself, softmax(Q K^T / sqrt(d_k)) V: "Unlimiformer:
+ *     Long-Range Transformers with Unlimited Length Input", section 2.3, Eq. (1);
+ *     the default scale is 1/sqrt(D) from that equation.
+ *   - subtracting max z before exp: same section, footnote 3 (softmax does not
+ *     change when one constant is added to all of its inputs).
+ *   - the band: Ultralytics glossary "Longformer", section on how the attention
+ *     works, sliding-window bullet (256 neighbours on each side), and the
+ *     mask-counting sample in that section, whose predicate is
+ *     |pos_i - pos_j| <= window // 2 (inclusive, floor).
+ *   - dilation: same section, dilated sliding-window bullet (attended positions
+ *     are spaced out so a head sees further at the same cost).  The page gives
+ *     no formula; the reading used here keeps the 2*hw+1 offsets and spaces
+ *     them d apart: keys i + d*k.
+ *   - global tokens: same section, global-attention bullet (chosen tokens attend
+ *     to every position and every position attends to them); the sample sets
+ *     row 0 and column 0 of the boolean mask, so a global key that is already
+ *     inside a row's band is counted once (set union).
+ *   - memory tokens: "GMAT: Global Memory Augmentation for Transformers",
+ *     section "Global Memory": M memory tokens are prefixed; they attend to all
+ *     M+L positions, and main tokens attend to all memory tokens plus a sparse
+ *     pattern over the main sequence.  With a band as the sparse pattern this is
+ *     exactly the set above with G = {0, ..., M-1}.
+ *
+ * Inputs are float (fp32 data, or bf16 data already widened to fp32 exactly);
+ * every product and sum is formed in double.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define LFO_OK 0
+#define LFO_EINVAL (-1)
+#define LFO_ENOMEM (-2)
+
+/* Band half-width: the page's sample compares |i - j| with window // 2. */
+static int64_t half_width(int window) { return (int64_t)window / 2; }
+
+static int is_global(const int* glob, int n_glob, int i) {
+  for (int t = 0; t < n_glob; ++t)
+    if (glob[t] == i) return 1;
+  return 0;
+}
+
+static int cmp_int(const void* a, const void* b) {
+  int x = *(const int*)a, y = *(const int*)b;
+  return (x > y) - (x < y);
+}
+
+static int check_globals(int N, const int* glob, int n_glob) {
+  if (n_glob < 0 || (n_glob > 0 && glob == NULL)) return 0;
+  for (int t = 0; t < n_glob; ++t)
+    if (glob[t] < 0 || glob[t] >= N) return 0;
+  return 1;
+}
+
+/*
+ * The allowed key set S_i of query row i, written to keys[] in increasing
+ * order without repeats (capacity: N + n_glob ints).  Returns |S_i|, or
+ * LFO_EINVAL on bad arguments.  Sources: the Longformer glossary page's
+ * sliding-window, dilated-window and global-attention bullets and its mask
+ * sample; the GMAT page's "Global Memory" section (see the file header).
+ */
+int64_t lfo_allowed_set(int N, int window, int dilation, const int* glob,
+                        int n_glob, int i, int* keys) {
+  if (N <= 0 || window < 0 || dilation < 1 || i < 0 || i >= N || keys == NULL)
+    return LFO_EINVAL;
+  if (!check_globals(N, glob, n_glob)) return LFO_EINVAL;
+
+  if (is_global(glob, n_glob, i)) {
+    /* A global row attends to every position. */
+    for (int j = 0; j < N; ++j) keys[j] = j;
+    return N;
+  }
+
+  const int64_t hw = half_width(window);
+  const int64_t d = dilation;
+  int64_t n = 0;
+  /* Only offsets k with 0 <= i + d*k < N can contribute; the loop visits
+   * exactly those inside [-hw, hw] and checks the range again. */
+  int64_t k_lo = -((int64_t)i / d);
+  int64_t k_hi = ((int64_t)(N - 1) - i) / d;
+  if (k_lo < -hw) k_lo = -hw;
+  if (k_hi > hw) k_hi = hw;
+  for (int64_t k = k_lo; k <= k_hi; ++k) {
+    int64_t j = (int64_t)i + d * k;
+    if (j >= 0 && j < N) keys[n++] = (int)j;
+  }
+  /* Every row also attends to every global token. */
+  for (int t = 0; t < n_glob; ++t) keys[n++] = glob[t];
+
+  /* Set union: sort, then drop repeats. */
+  qsort(keys, (size_t)n, sizeof(int), cmp_int);
+  int64_t u = 0;
+  for (int64_t t = 0; t < n; ++t)
+    if (u == 0 || keys[u - 1] != keys[t]) keys[u++] = keys[t];
+  return u;
+}
+
+/*
+ * Total number of scored (query, key) pairs, summed over B batches, H heads
+ * and N rows, by building every S_i explicitly.  dilation: H entries, or NULL
+ * for all 1.  This is the quantity the Longformer glossary page counts with
+ * mask.sum() in its sample.  Returns the count, or LFO_EINVAL / LFO_ENOMEM.
+ */
+int64_t lfo_count_pairs(int B, int H, int N, int window, const int* dilation,
+                        const int* glob, int n_glob) {
+  if (B <= 0 || H <= 0 || N <= 0 || window < 0) return LFO_EINVAL;
+  if (!check_globals(N, glob, n_glob)) return LFO_EINVAL;
+  int* keys = (int*)malloc(sizeof(int) * ((size_t)N + (size_t)n_glob + 1));
+  if (!keys) return LFO_ENOMEM;
+  int64_t total = 0;
+  for (int h = 0; h < H; ++h) {
+    int d = dilation ? dilation[h] : 1;
+    if (d < 1) { free(keys); return LFO_EINVAL; }
+    int64_t per_head = 0;
+    for (int i = 0; i < N; ++i) {
+      int64_t n = lfo_allowed_set(N, window, d, glob, n_glob, i, keys);
+      if (n < 0) { free(keys); return n; }
+      per_head += n;
+    }
+    total += per_head * B; /* the pattern does not depend on the batch */
+  }
+  free(keys);
+  return total;
+}
+
+/* ---- attention values ---------------------------------------------------- */
+
+typedef struct {
+  const float *Q, *K, *V;
+  double* O;
+  int B, H, N, D, window, n_glob;
+  const int* dilation;
+  const int* glob;
+  double scale;
+  const int64_t* rows; /* flattened (b*H + h)*N + i, or NULL for all rows */
+  int64_t n_rows;
+  int64_t first, last; /* this worker's share of the row list */
+  int status;
+} lfo_job;
+
+/*
+ * One query row: Eq. (1) of the Unlimiformer page restricted to S_i, with the
+ * max subtracted first (footnote 3 of that section).  Two passes over S_i:
+ * scores and their maximum, then weights, their sum and the weighted sum of V.
+ */
+static int one_row(const lfo_job* jb, int64_t flat, int* keys, double* z,
+                   double* acc, double* out) {
+  const int N = jb->N, D = jb->D;
+  const int64_t bh = flat / N;
+  const int i = (int)(flat % N);
+  const int h = (int)(bh % jb->H);
+  const int d = jb->dilation ? jb->dilation[h] : 1;
+  const float* q = jb->Q + (size_t)flat * D;
+  const float* Kbh = jb->K + (size_t)bh * N * D;
+  const float* Vbh = jb->V + (size_t)bh * N * D;
+
+  int64_t n = lfo_allowed_set(N, jb->window, d, jb->glob, jb->n_glob, i, keys);
+  if (n <= 0) return LFO_EINVAL; /* never empty: k = 0 gives j = i */
+
+  double zmax = -INFINITY;
+  for (int64_t t = 0; t < n; ++t) {
+    const float* kr = Kbh + (size_t)keys[t] * D;
+    double s = 0.0;
+    for (int c = 0; c < D; ++c) s += (double)q[c] * (double)kr[c];
+    z[t] = jb->scale * s;
+    if (z[t] > zmax) zmax = z[t];
+  }
+  double den = 0.0;
+  for (int c = 0; c < D; ++c) acc[c] = 0.0;
+  for (int64_t t = 0; t < n; ++t) {
+    double e = exp(z[t] - zmax);
+    den += e;
+    const float* vr = Vbh + (size_t)keys[t] * D;
+    for (int c = 0; c < D; ++c) acc[c] += e * (double)vr[c];
+  }
+  for (int c = 0; c < D; ++c) out[c] = acc[c] / den;
+  return LFO_OK;
+}
+
+static void* worker(void* arg) {
+  lfo_job* jb = (lfo_job*)arg;
+  const int N = jb->N, D = jb->D;
+  int* keys = (int*)malloc(sizeof(int) * ((size_t)N + (size_t)jb->n_glob + 1));
+  double* z = (double*)malloc(sizeof(double) * ((size_t)N + (size_t)jb->n_glob + 1));
+  double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!keys || !z || !acc) {
+    jb->status = LFO_ENOMEM;
+  } else {
+    for (int64_t r = jb->first; r < jb->last; ++r) {
+      int64_t flat = jb->rows ? jb->rows[r] : r;
+      int st = one_row(jb, flat, keys, z, acc, jb->O + (size_t)r * D);
+      if (st != LFO_OK) { jb->status = st; break; }
+    }
+  }
+  free(keys); free(z); free(acc);
+  return NULL;
+}
+
+/*
+ * Attention output for a list of rows.  Q, K, V: [B, H, N, D] row-major
+ * floats.  rows: flattened indices (b*H + h)*N + i, n_rows of them, or NULL
+ * with n_rows = B*H*N for every row.  O: n_rows x D doubles, in the order of
+ * rows.  scale <= 0 selects 1/sqrt(D).  nthreads >= 1 workers split the row
+ * list into contiguous ranges.  Returns LFO_OK or a negative error.
+ */
+int lfo_attention(const float* Q, const float* K, const float* V, double* O,
+                  int B, int H, int N, int D, int window, const int* dilation,
+                  const int* glob, int n_glob, double scale,
+                  const int64_t* rows, int64_t n_rows, int nthreads) {
+  if (!Q || !K || !V || !O || B <= 0 || H <= 0 || N <= 0 || D <= 0 ||
+      window < 0 || n_rows < 0)
+    return LFO_EINVAL;
+  if (!check_globals(N, glob, n_glob)) return LFO_EINVAL;
+  if (dilation)
+    for (int h = 0; h < H; ++h)
+      if (dilation[h] < 1) return LFO_EINVAL;
+  const int64_t total = (int64_t)B * H * N;
+  if (!rows && n_rows != total) return LFO_EINVAL;
+  if (rows)
+    for (int64_t r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= total) return LFO_EINVAL;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  if (nthreads < 1) nthreads = 1;
+  if (n_rows == 0) return LFO_OK;
+  if ((int64_t)nthreads > n_rows) nthreads = (int)n_rows;
+
+  lfo_job* jobs = (lfo_job*)calloc((size_t)nthreads, sizeof(lfo_job));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !tids) { free(jobs); free(tids); return LFO_ENOMEM; }
+  for (int t = 0; t < nthreads; ++t) {
+    lfo_job* jb = &jobs[t];
+    jb->Q = Q; jb->K = K; jb->V = V; jb->O = O;
+    jb->B = B; jb->H = H; jb->N = N; jb->D = D; jb->window = window;
+    jb->dilation = dilation; jb->glob = glob; jb->n_glob = n_glob;
+    jb->scale = scale; jb->rows = rows; jb->n_rows = n_rows;
+    jb->first = n_rows * t / nthreads;
+    jb->last = n_rows * (t + 1) / nthreads;
+    jb->status = LFO_OK;
+  }
+  char* created = (char*)calloc((size_t)nthreads, 1);
+  if (!created) { free(jobs); free(tids); return LFO_ENOMEM; }
+  for (int t = 1; t < nthreads; ++t)
+    created[t] = (char)(pthread_create(&tids[t], NULL, worker, &jobs[t]) == 0);
+  worker(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) {
+    if (created[t]) pthread_join(tids[t], NULL);
+    else worker(&jobs[t]); /* no thread could be started: do its share here */
+  }
+  int st = LFO_OK;
+  for (int t = 0; t < nthreads; ++t)
+    if (jobs[t].status != LFO_OK) st = jobs[t].status;
+  free(jobs); free(tids); free(created);
+  return st;
+}
