@@ -1,0 +1,152 @@
+"""Benchmark: scored pairs per second of the band + global attention forward.
+
+One step is one lfattn_forward (global-row kernel + band kernel) over the
+Longformer-base workload (B 1, H 12, N 4096, D 64, bf16, window 512, global
+tokens 0..31) with inputs already resident in device memory.  Prints one JSON
+line.  Options: --gpus (only 1 is supported: the path runs on one GPU),
+--steps, --warmup, --workload (another of the named workloads), --no-cpu.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention scored-pairs/sec and % of bf16 MFMA peak, N=4096 Longformer-base shape"
+# MI355X published dense peaks: bf16 MFMA 2.5 PFLOP/s, fp32 MFMA 157.3 TFLOP/s;
+# HBM3E 8 TB/s.
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="longformer_base_n4096")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return p.parse_args()
+
+
+def cpu_baseline(inp, wl, pairs_per_head_total):
+    """The oracle as it stands, on this host's cores, over the whole workload
+    (repeated until at least 3 s have passed; one pass is about 1 s)."""
+    import oracle
+    threads = os.cpu_count() or 1
+    args = (inp.q, inp.k, inp.v, wl.window, list(inp.dilation), list(inp.glob))
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention(*args, nthreads=threads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= 3.0:
+            break
+    return {"value": pairs_per_head_total * passes / el, "unit": "pairs/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole {wl.name} workload (all {wl.B * wl.H * wl.N} rows), "
+                      f"{passes} pass(es) in {el:.2f} s, double precision, {threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding is described in DESIGN.md, not run).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_sparse_band_amd import lfattn as L
+    from long_context_sparse_band_amd import workloads as W
+
+    wl = W.BY_NAME[args.workload]
+    inp = W.generate(wl)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(a).to(dev).to(tdt).contiguous() for a in (inp.q, inp.k, inp.v))
+    o = torch.empty_like(q)
+    dtype = L.LFATTN_BF16 if wl.dtype == "bf16" else L.LFATTN_F32
+    h = L.lfattn_create(wl.B, wl.H, wl.N, wl.D, dtype, wl.window, list(inp.dilation),
+                        list(inp.glob))
+    pairs = L.lfattn_scored_pairs(h)
+    n_g = len(inp.glob)
+    glob_pairs = wl.B * wl.H * n_g * wl.N           # global rows: all N keys
+    band_pairs = pairs - glob_pairs                 # band kernel: every other row
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        L.lfattn_forward(h, q, k, v, o, stream)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` forwards between two events on the stream.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        L.lfattn_forward(h, q, k, v, o, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # Per-kernel durations: the same forwards with the library's events around
+    # each kernel (a second pass, so the first timing is undisturbed).
+    L.lfattn_set_timing(h, True)
+    for _ in range(args.steps):
+        L.lfattn_forward(h, q, k, v, o, stream)
+    band_ms, glob_ms, n = L.lfattn_read_timing(h)
+    L.lfattn_set_timing(h, False)
+    L.lfattn_destroy(h)
+    band_ms /= max(n, 1)
+    glob_ms /= max(n, 1)
+
+    flops_per_pair = 4 * wl.D                       # 2D for Q.K, 2D for P.V
+    band_tflops = band_pairs * flops_per_pair / (band_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    value = pairs / (ms * 1e-3)
+    elem = 2 if wl.dtype == "bf16" else 4
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "scored pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded i.i.d. Gaussian Q, K, V)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
+                   "window": wl.window, "dilation": list(inp.dilation)[:1] if len(set(inp.dilation)) == 1 else list(inp.dilation),
+                   "n_global": n_g, "scored_pairs": pairs, "parallelism": "single GPU"},
+        "whole_forward_tflops": pairs * flops_per_pair / (ms * 1e-3) / 1e12,
+        "whole_forward_mfma_frac": pairs * flops_per_pair / (ms * 1e-3) / 1e12 / peak,
+        "kernels_ms": {"band": band_ms, "global_rows": glob_ms},
+        "roofline": {
+            "kernel": "band_kernel",
+            "bound": "mfma",
+            "achieved": band_tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": band_tflops / peak,
+            "traffic": None,
+            "algorithmic_flops_per_launch": band_pairs * flops_per_pair,
+            "ideal_bytes_per_launch": 4 * wl.B * wl.H * wl.N * wl.D * elem,
+        },
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(inp, wl, pairs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+/*
+ * lfattn: band + global sparse self-attention, forward pass, on AMD MI355X
+ * (gfx950).  C ABI.
+ *
+ * Operation (per batch b, head h, query row i; Q, K, V, O are [B, H, N, D]):
+ *
+ *   S_i = { 0, ..., N-1 }                                        if i in G
+ *   S_i = { i + d_h*k : -hw <= k <= hw, 0 <= i + d_h*k < N }  u  G  otherwise
+ *   O_i = sum_{j in S_i} softmax_j(scale * Q_i . K_j) V_j
+ *
+ * with hw = floor(window / 2), d_h the dilation of head h and G the set of
+ * global token positions.  This is attention as in Eq. (1) of "Unlimiformer:
+ * Long-Range Transformers with Unlimited Length Input" (section 2.3)
+ * restricted to the Longformer pattern of the Ultralytics glossary page
+ * "Longformer" (section on how the attention works: the sliding-window,
+ * dilated-window and global-attention bullets, and the mask sample there,
+ * which uses |i - j| <= window // 2 and sets a global token's whole row and
+ * column).  GMAT's memory tokens ("GMAT: Global Memory Augmentation for
+ * Transformers", section "Global Memory") are the case G = {0, ..., M-1} with
+ * the main sequence after them.  The page gives no formula for dilation; this
+ * library reads it as "the same 2*hw+1 offsets, spaced d_h apart".  A global
+ * key that already lies in a row's band is scored once (set union).
+ *
+ * Layouts.  Q, K, V, O: contiguous [B, H, N, D] arrays in device memory, D
+ * fastest, 16-byte aligned, element type set at create (float, or bfloat16
+ * stored as 16-bit words).  Accumulation is always fp32; bf16 outputs are
+ * rounded to nearest even.
+ *
+ * Ownership.  Q, K, V, O belong to the caller.  Q, K, V are only read; O is
+ * fully overwritten and must not overlap Q, K or V.  The host arrays passed to
+ * lfattn_create (dilation, global_idx) are copied; the caller may free them on
+ * return.  The handle owns its device tables and workspace and frees them in
+ * lfattn_destroy.
+ *
+ * Execution.  lfattn_forward allocates nothing and does not wait on the host:
+ * it enqueues its kernels on the given HIP stream and returns.  Device-side
+ * errors surface at the caller's next synchronisation, as for any HIP call.
+ * A handle keeps per-call workspace, so one handle must not be used by two
+ * forwards that may run at the same time (e.g. on two streams); create one
+ * handle per stream instead.  All calls on a handle must be made with the
+ * device that was current at lfattn_create.
+ *
+ * Errors.  Every entry point returns a status synchronously.  Arguments are
+ * checked before any HIP call is made, so invalid arguments never touch the
+ * device.
+ */
+#ifndef LFATTN_H
+#define LFATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lfattn_ctx* lfattn_t;
+
+typedef enum {
+  LFATTN_OK = 0,
+  LFATTN_EINVAL = 1,      /* bad argument: null/misaligned pointer, size, window,
+                             dilation, global index outside [0, N), overlap */
+  LFATTN_EUNSUPPORTED = 2, /* valid but not implemented: D not 64 or 128 */
+  LFATTN_ENOMEM = 3,      /* device or host allocation failed */
+  LFATTN_EHIP = 4         /* a HIP runtime call or kernel launch failed */
+} lfattn_status;
+
+typedef enum { LFATTN_F32 = 0, LFATTN_BF16 = 1 } lfattn_dtype;
+
+/*
+ * Create a handle for one problem shape and pattern.
+ *   out        receives the handle (set to NULL on failure).
+ *   B, H, N    batch, heads, sequence length (each >= 1).
+ *   D          head dimension: 64 or 128.
+ *   dtype      element type of Q, K, V and O.
+ *   window     >= 0; half-width hw = window / 2 (floor), as in the Longformer
+ *              page's sample (window 512 means 256 on each side, inclusive).
+ *   dilation   H host ints >= 1, or NULL for all 1 (dilated-window bullet).
+ *   global_idx n_global host ints in [0, N), any order, repeats allowed (a
+ *              position listed twice is global once); NULL if n_global == 0.
+ *   scale      softmax scale; <= 0 selects 1/sqrt(D) (Eq. (1) of the
+ *              Unlimiformer page).  NaN or infinity is EINVAL.
+ * Allocates the handle's device tables and workspace on the current device
+ * (the only host-to-device copies the library makes happen here).
+ */
+lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dtype dtype,
+                            int window, const int* dilation, const int* global_idx,
+                            int n_global, float scale);
+
+/*
+ * Enqueue one forward pass on `stream` (NULL: the null stream).
+ * Q, K, V: device pointers to [B, H, N, D] inputs; O: device pointer to the
+ * [B, H, N, D] output.  Returns EINVAL for a null or misaligned pointer or an
+ * O that overlaps an input, EHIP if a launch fails.
+ */
+lfattn_status lfattn_forward(lfattn_t ctx, const void* Q, const void* K, const void* V,
+                             void* O, hipStream_t stream);
+
+/* Release the handle and its device memory (waits for the device first).
+ * NULL is accepted and ignored. */
+lfattn_status lfattn_destroy(lfattn_t ctx);
+
+/* Static English text for a status code. */
+const char* lfattn_status_string(lfattn_status status);
+
+/*
+ * Number of (query, key) pairs one forward scores, summed over B, H and N:
+ * sum_i |S_i|, the count the Longformer page's sample takes with mask.sum().
+ */
+lfattn_status lfattn_scored_pairs(lfattn_t ctx, long long* pairs);
+
+/*
+ * The canonical global list the handle uses: sorted, without repeats.
+ * Writes min(n, capacity) positions to out (may be NULL when capacity is 0)
+ * and the full count n to *n_out.
+ */
+lfattn_status lfattn_global_list(lfattn_t ctx, int* out, int capacity, int* n_out);
+
+/*
+ * Per-kernel timing with HIP events, for measurement.  While enabled, each
+ * forward also records events around its kernels on the forward's stream (at
+ * most 4096 forwards are recorded; later ones are not).  lfattn_read_timing
+ * waits for the recorded events and returns the summed milliseconds of the
+ * band kernel and of the global-row kernel and the number of forwards
+ * recorded, then clears the record.  Enabling or disabling also clears it.
+ */
+lfattn_status lfattn_set_timing(lfattn_t ctx, int enable);
+lfattn_status lfattn_read_timing(lfattn_t ctx, double* band_ms, double* global_ms,
+                                 int* n_forwards);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LFATTN_H */

@@ -1,0 +1,343 @@
+// C-ABI entry points of liblfattn (declared in include/lfattn.h): argument
+// checks, the canonical global list, the band work table, workspace, and the
+// kernel launches.
+#include "lfattn.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "lfattn_internal.h"
+
+using lfattn::BandWork;
+using lfattn::kBandRows;
+using lfattn::kTileKeys;
+using lfattn::kWaveRows;
+
+namespace {
+
+constexpr int kMaxTimedForwards = 4096;
+constexpr int kXcds = 8;           // MI355X: workgroups go round-robin over 8 XCDs
+constexpr int kMaxChunks = 16;     // key chunks per global row set (merge cost)
+constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
+constexpr long long kMaxN = 1LL << 29;
+
+}  // namespace
+
+struct lfattn_ctx {
+  int B = 0, H = 0, N = 0, D = 0, dtype = 0, window = 0, hw = 0;
+  float scale = 0.0f;
+  std::vector<int> dil;
+  std::vector<int> glob;  // sorted, unique
+  long long pairs = 0;
+  int device = 0;
+
+  BandWork* d_work = nullptr;
+  int n_band_wg = 0;
+  int* d_dil = nullptr;
+  int* d_glob = nullptr;
+  unsigned char* d_isglob = nullptr;
+
+  float* d_part = nullptr;
+  unsigned* d_counters = nullptr;
+  int g_waves = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
+
+  bool timing = false;
+  int n_timed = 0;
+  std::vector<hipEvent_t> ev;  // 3 per timed forward
+};
+
+namespace {
+
+template <typename T>
+lfattn_status dev_alloc(T** p, size_t count) {
+  *p = nullptr;
+  if (count == 0) return LFATTN_OK;
+  if (hipMalloc((void**)p, count * sizeof(T)) != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return LFATTN_ENOMEM;
+  }
+  return LFATTN_OK;
+}
+
+void free_ctx(lfattn_ctx* c) {
+  if (!c) return;
+  (void)hipFree(c->d_work);
+  (void)hipFree(c->d_dil);
+  (void)hipFree(c->d_glob);
+  (void)hipFree(c->d_isglob);
+  (void)hipFree(c->d_part);
+  (void)hipFree(c->d_counters);
+  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  delete c;
+}
+
+// Scored pairs of one head with dilation d: every row's band (keys i + d*k,
+// |k| <= hw, inside [0, N)), plus the global keys outside that band; global
+// rows score all N keys.
+long long head_pairs(int N, long long hw, int d, const std::vector<int>& glob,
+                     const std::vector<unsigned char>& isg) {
+  long long total = 0;
+  for (long long i = 0; i < N; ++i) {
+    if (isg[i]) {
+      total += N;
+      continue;
+    }
+    long long left = std::min(i / d, hw), right = std::min((N - 1 - i) / d, hw);
+    long long n = 1 + left + right;
+    for (int g : glob) {
+      long long off = g - i;
+      bool in_band = off % d == 0 && off / d <= hw && off / d >= -hw;
+      if (!in_band) ++n;
+    }
+    total += n;
+  }
+  return total;
+}
+
+bool overlaps(const void* a, const void* b, size_t bytes) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bytes && y < x + bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lfattn_status_string(lfattn_status s) {
+  switch (s) {
+    case LFATTN_OK: return "ok";
+    case LFATTN_EINVAL: return "invalid argument";
+    case LFATTN_EUNSUPPORTED: return "unsupported configuration";
+    case LFATTN_ENOMEM: return "out of memory";
+    case LFATTN_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dtype dtype,
+                            int window, const int* dilation, const int* global_idx,
+                            int n_global, float scale) {
+  // ---- argument checks: no HIP call before all of them pass ----
+  if (!out) return LFATTN_EINVAL;
+  *out = nullptr;
+  if (B < 1 || H < 1 || N < 1 || D < 1 || window < 0 || n_global < 0) return LFATTN_EINVAL;
+  if (dtype != LFATTN_F32 && dtype != LFATTN_BF16) return LFATTN_EINVAL;
+  if (n_global > 0 && !global_idx) return LFATTN_EINVAL;
+  if (std::isnan(scale) || std::isinf(scale)) return LFATTN_EINVAL;
+  if (dilation)
+    for (int h = 0; h < H; ++h)
+      if (dilation[h] < 1) return LFATTN_EINVAL;
+  for (int t = 0; t < n_global; ++t)
+    if (global_idx[t] < 0 || global_idx[t] >= N) return LFATTN_EINVAL;
+  if (D != 64 && D != 128) return LFATTN_EUNSUPPORTED;
+  if ((long long)N >= kMaxN || (long long)B * H > (1LL << 24)) return LFATTN_EUNSUPPORTED;
+
+  lfattn_ctx* c = new (std::nothrow) lfattn_ctx;
+  if (!c) return LFATTN_ENOMEM;
+  c->B = B; c->H = H; c->N = N; c->D = D; c->dtype = (int)dtype; c->window = window;
+  c->hw = (int)std::min<long long>(window / 2, N);  // a wider half-width changes nothing
+  c->scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+  c->dil.assign(H, 1);
+  if (dilation) c->dil.assign(dilation, dilation + H);
+  // Canonical global list: sorted, repeats removed (a position listed twice is
+  // global once, as setting a mask row or column twice changes nothing).
+  c->glob.assign(global_idx, global_idx + n_global);
+  std::sort(c->glob.begin(), c->glob.end());
+  c->glob.erase(std::unique(c->glob.begin(), c->glob.end()), c->glob.end());
+  std::vector<unsigned char> isg(N, 0);
+  for (int g : c->glob) isg[g] = 1;
+
+  // Scored pairs, per distinct dilation value.
+  {
+    std::vector<int> ds = c->dil;
+    std::sort(ds.begin(), ds.end());
+    ds.erase(std::unique(ds.begin(), ds.end()), ds.end());
+    long long total = 0;
+    for (int d : ds) {
+      long long per = head_pairs(N, window / 2, d, c->glob, isg);
+      total += per * (long long)std::count(c->dil.begin(), c->dil.end(), d);
+    }
+    c->pairs = total * B;
+  }
+
+  // Band work: one item per 128 rows of each (b, h, residue r) subsequence,
+  // laid out so that the items the hardware sends to one XCD (blockIdx
+  // congruent mod 8) are consecutive query blocks of the same head, which
+  // share their band's K and V rows in that XCD's L2.
+  std::vector<BandWork> items;
+  for (int bh = 0; bh < B * H; ++bh) {
+    const int d = c->dil[bh % H];
+    for (int r = 0; r < d && r < N; ++r) {
+      const int Lr = (N - r + d - 1) / d;
+      for (int t0 = 0; t0 < Lr; t0 += kBandRows) items.push_back(BandWork{bh, r, t0, 0});
+    }
+  }
+  const int n_items = (int)items.size();
+  std::vector<BandWork> table(n_items);
+  {
+    int next = 0;
+    for (int x = 0; x < kXcds; ++x)
+      for (int bid = x; bid < n_items; bid += kXcds) table[bid] = items[next++];
+  }
+  c->n_band_wg = n_items;
+
+  // Global rows: sets of up to 128 rows (waves of 32), key chunks per set.
+  const int n_g = (int)c->glob.size();
+  if (n_g > 0) {
+    c->g_waves = n_g <= 32 ? 1 : (n_g <= 64 ? 2 : 4);
+    const int rows_per_set = c->g_waves * kWaveRows;
+    c->n_sets = (n_g + rows_per_set - 1) / rows_per_set;
+    const long long bhs = (long long)B * H * c->n_sets;
+    const int max_chunks = (N + kTileKeys - 1) / kTileKeys;
+    int chunks = (int)std::min<long long>(kMaxChunks, (kGlobTarget + bhs - 1) / bhs);
+    chunks = std::max(1, std::min(chunks, max_chunks));
+    int per = (N + chunks - 1) / chunks;
+    per = (per + kTileKeys - 1) / kTileKeys * kTileKeys;
+    c->chunk_keys = per;
+    c->n_chunks = (N + per - 1) / per;
+    c->n_glob_wg = (int)(bhs * c->n_chunks);
+  }
+
+  // ---- device state ----
+  lfattn_status st = LFATTN_OK;
+  if (hipGetDevice(&c->device) != hipSuccess) { free_ctx(c); return LFATTN_EHIP; }
+  if ((st = dev_alloc(&c->d_work, table.size())) != LFATTN_OK ||
+      (st = dev_alloc(&c->d_dil, (size_t)H)) != LFATTN_OK ||
+      (st = dev_alloc(&c->d_isglob, (size_t)N)) != LFATTN_OK ||
+      (st = dev_alloc(&c->d_glob, (size_t)std::max(n_g, 1))) != LFATTN_OK) {
+    free_ctx(c);
+    return st;
+  }
+  if (n_g > 0) {
+    const size_t rec = (size_t)D + 4;
+    const size_t n_part = (size_t)B * H * c->n_sets * c->n_chunks * c->g_waves * kWaveRows * rec;
+    if ((st = dev_alloc(&c->d_part, n_part)) != LFATTN_OK ||
+        (st = dev_alloc(&c->d_counters, (size_t)B * H * c->n_sets)) != LFATTN_OK) {
+      free_ctx(c);
+      return st;
+    }
+  }
+  bool ok = hipMemcpy(c->d_work, table.data(), table.size() * sizeof(BandWork),
+                      hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(c->d_dil, c->dil.data(), H * sizeof(int), hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(c->d_isglob, isg.data(), N, hipMemcpyHostToDevice) == hipSuccess;
+  if (n_g > 0) {
+    ok = ok && hipMemcpy(c->d_glob, c->glob.data(), n_g * sizeof(int), hipMemcpyHostToDevice) == hipSuccess;
+    ok = ok && hipMemset(c->d_counters, 0, (size_t)B * H * c->n_sets * sizeof(unsigned)) == hipSuccess;
+  }
+  if (!ok) {
+    (void)hipGetLastError();
+    free_ctx(c);
+    return LFATTN_EHIP;
+  }
+  *out = c;
+  return LFATTN_OK;
+}
+
+lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const void* V, void* O,
+                             hipStream_t stream) {
+  if (!c || !Q || !K || !V || !O) return LFATTN_EINVAL;
+  const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u;
+  if (mis) return LFATTN_EINVAL;
+  const size_t bytes = (size_t)c->B * c->H * c->N * c->D * (c->dtype == LFATTN_BF16 ? 2 : 4);
+  if (overlaps(O, Q, bytes) || overlaps(O, K, bytes) || overlaps(O, V, bytes)) return LFATTN_EINVAL;
+
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != c->device) return LFATTN_EINVAL;
+
+  const float sl2 = c->scale * 1.4426950408889634f;
+  const bool timed = c->timing && c->n_timed < kMaxTimedForwards;
+  hipEvent_t* ev = timed ? &c->ev[3 * c->n_timed] : nullptr;
+  if (timed && hipEventRecord(ev[0], stream) != hipSuccess) return LFATTN_EHIP;
+
+  const int n_g = (int)c->glob.size();
+  if (n_g > 0) {
+    lfattn::GlobArgs g;
+    g.Q = Q; g.K = K; g.V = V; g.O = O;
+    g.glob = c->d_glob; g.part = c->d_part; g.counters = c->d_counters;
+    g.H = c->H; g.N = c->N; g.n_glob = n_g;
+    g.n_sets = c->n_sets; g.n_chunks = c->n_chunks; g.chunk_keys = c->chunk_keys;
+    g.sl2 = sl2;
+    if (lfattn::launch_glob(c->dtype, c->D, c->g_waves, g, c->n_glob_wg, stream) != hipSuccess)
+      return LFATTN_EHIP;
+  }
+  if (timed && hipEventRecord(ev[1], stream) != hipSuccess) return LFATTN_EHIP;
+
+  lfattn::BandArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O;
+  a.work = c->d_work; a.dil = c->d_dil; a.glob = c->d_glob; a.is_glob = c->d_isglob;
+  a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
+  if (lfattn::launch_band(c->dtype, c->D, a, c->n_band_wg, stream) != hipSuccess)
+    return LFATTN_EHIP;
+
+  if (timed) {
+    if (hipEventRecord(ev[2], stream) != hipSuccess) return LFATTN_EHIP;
+    ++c->n_timed;
+  }
+  return LFATTN_OK;
+}
+
+lfattn_status lfattn_destroy(lfattn_t c) {
+  if (!c) return LFATTN_OK;
+  (void)hipDeviceSynchronize();
+  free_ctx(c);
+  return LFATTN_OK;
+}
+
+lfattn_status lfattn_scored_pairs(lfattn_t c, long long* pairs) {
+  if (!c || !pairs) return LFATTN_EINVAL;
+  *pairs = c->pairs;
+  return LFATTN_OK;
+}
+
+lfattn_status lfattn_global_list(lfattn_t c, int* out, int capacity, int* n_out) {
+  if (!c || !n_out || capacity < 0 || (capacity > 0 && !out)) return LFATTN_EINVAL;
+  const int n = (int)c->glob.size();
+  for (int t = 0; t < n && t < capacity; ++t) out[t] = c->glob[t];
+  *n_out = n;
+  return LFATTN_OK;
+}
+
+lfattn_status lfattn_set_timing(lfattn_t c, int enable) {
+  if (!c) return LFATTN_EINVAL;
+  if (enable && c->ev.empty()) {
+    c->ev.resize(3 * kMaxTimedForwards, nullptr);
+    for (auto& e : c->ev)
+      if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipGetLastError();
+        for (auto& x : c->ev)
+          if (x) (void)hipEventDestroy(x);
+        c->ev.clear();
+        return LFATTN_EHIP;
+      }
+  }
+  c->timing = enable != 0;
+  c->n_timed = 0;
+  return LFATTN_OK;
+}
+
+lfattn_status lfattn_read_timing(lfattn_t c, double* band_ms, double* global_ms, int* n_forwards) {
+  if (!c || !band_ms || !global_ms || !n_forwards) return LFATTN_EINVAL;
+  double b = 0.0, g = 0.0;
+  if (c->n_timed > 0 && hipEventSynchronize(c->ev[3 * (c->n_timed - 1) + 2]) != hipSuccess)
+    return LFATTN_EHIP;
+  for (int t = 0; t < c->n_timed; ++t) {
+    float x = 0.0f, y = 0.0f;
+    if (hipEventElapsedTime(&x, c->ev[3 * t], c->ev[3 * t + 1]) != hipSuccess ||
+        hipEventElapsedTime(&y, c->ev[3 * t + 1], c->ev[3 * t + 2]) != hipSuccess)
+      return LFATTN_EHIP;
+    g += x;
+    b += y;
+  }
+  *band_ms = b;
+  *global_ms = g;
+  *n_forwards = c->n_timed;
+  c->n_timed = 0;
+  return LFATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Internal declarations shared by the kernels and the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lfattn {
+
+// Keys per tile staged in LDS, and query rows per wavefront (one 32x32 MFMA
+// block of queries).
+constexpr int kTileKeys = 64;
+constexpr int kWaveRows = 32;
+// Waves per band workgroup; a band workgroup covers kBandWaves * 32 query rows.
+constexpr int kBandWaves = 4;
+constexpr int kBandRows = kBandWaves * kWaveRows;
+
+// One band workgroup's work: batch-head bh, dilation residue r, and the first
+// position t0 (in the residue's subsequence r, r+d, r+2d, ...) of its rows.
+struct BandWork {
+  int bh;
+  int r;
+  int t0;
+  int pad;
+};
+
+struct BandArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  const BandWork* work;        // one entry per workgroup
+  const int* dil;              // [H] dilation per head
+  const int* glob;             // [n_glob] sorted global positions
+  const unsigned char* is_glob;  // [N] 1 where the position is global
+  int H, N, hw, n_glob;
+  float sl2;                   // softmax scale times log2(e)
+};
+
+struct GlobArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  const int* glob;             // [n_glob] sorted global positions
+  float* part;                 // partial (m, l, acc[D]) records
+  unsigned* counters;          // [B*H*n_sets] arrival counters, zero between calls
+  int H, N, n_glob;
+  int n_sets;                  // sets of up to waves*32 global rows per head
+  int n_chunks;                // key chunks per (bh, set)
+  int chunk_keys;              // keys per chunk, a multiple of kTileKeys
+  float sl2;
+};
+
+// Launchers (defined next to the kernels).  dtype: 0 fp32, 1 bf16.
+hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s);
+hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s);
+
+}  // namespace lfattn

@@ -1,0 +1,650 @@
+// HIP kernels for band + global sparse attention on gfx950 (MI355X).
+//
+// Band kernel: one workgroup of 4 wavefronts takes 128 consecutive query rows
+// of one (batch, head, dilation residue) and walks the key tiles of their band
+// (64 keys each, staged in LDS), then the tiles of gathered global keys.  Each
+// wavefront owns 32 query rows and computes, per tile,
+//   S^T = K_tile Q^T          (v_mfma_f32_32x32x16_bf16, or _32x32x2f32)
+//   online softmax on S^T     (running max and sum per query row)
+//   O^T += V_tile^T P^T       (same MFMA shape, fp32 accumulators)
+// Scores are kept transposed (keys down the MFMA rows, queries across lanes)
+// so that one lane holds 16 keys of a single query: the row maximum is a
+// per-lane reduction plus one exchange between lane l and lane l+32, and the
+// exponentiated scores already sit in the lane layout of the next MFMA's B
+// operand.
+//
+// Global-row kernel: the rows of global tokens attend to all N keys.  Each
+// workgroup scores a chunk of keys for up to 128 global rows and writes a
+// partial (max, sum, unnormalised output); the last workgroup to finish a
+// (batch, head, row set) merges the partials and writes those output rows.
+//
+// The math is Eq. (1) of the Unlimiformer page (section 2.3) over the
+// Longformer pattern (Ultralytics glossary "Longformer", section on how the
+// attention works); the running maximum relies on softmax ignoring a constant
+// added to all its inputs (Unlimiformer section 2.3, footnote 3).
+#include "lfattn_internal.h"
+
+namespace lfattn {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int TK = kTileKeys;
+// Running maximum before any key is seen: finite, so that exp2(m - m_new) is
+// 0 rather than NaN.
+constexpr float kNegInit = -1.0e30f;
+// The running maximum is only moved when a tile's maximum exceeds it by more
+// than this (log2 units); weights then stay below 2^8, far inside fp32 and
+// bf16 range, and most tiles skip rescaling the accumulators.
+constexpr float kSlack = 8.0f;
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Key of accumulator register i (0..15) of a 32x32 MFMA result block, for the
+// lane half hi = lane / 32: row 8*(i/4) + 4*hi + i%4 of the block.
+__device__ __forceinline__ int block_row(int i, int hi) { return 8 * (i >> 2) + 4 * hi + (i & 3); }
+
+// Position of key kk (0..63) inside a V^T row in LDS.  Within each group of 16
+// keys, keys 16s + 8a + 4b + c (a, b in {0,1}, c in 0..3) go to slot
+// 16s + 8b + 4a + c, so that the 8 keys one lane feeds to a 32x32x16 MFMA
+// k-step (registers 8*(ks%2) .. +7 of its score block) are contiguous.
+__device__ __forceinline__ int vt_slot(int kk) {
+  return (kk & ~15) | (((kk >> 2) & 1) << 3) | (((kk >> 3) & 1) << 2) | (kk & 3);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles and the cooperative loaders.
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int D>
+struct Tile;
+
+// bf16: K row-major [key][d] (16-byte row padding), V transposed [d][slot].
+template <int D>
+struct Tile<true, D> {
+  static constexpr int KP = D + 8;
+  static constexpr int VP = TK + 8;
+  unsigned short k[TK * KP];
+  unsigned short vt[D * VP];
+};
+
+// fp32: K and V both row-major [key][d]; the pitches spread the MFMA operand
+// reads over the LDS banks.
+template <int D>
+struct Tile<false, D> {
+  static constexpr int KP = D + 4;
+  static constexpr int VP = D + 8;
+  float k[TK * KP];
+  float v[TK * VP];
+};
+
+template <bool BF16, int D, int NT>
+struct Loader;
+
+template <int D, int NT>
+struct Loader<true, D, NT> {
+  static constexpr int C8 = D / 8;                  // 16-byte chunks per row
+  static constexpr int NK = TK * C8 / NT;           // K chunks per thread
+  static constexpr int NV = (TK / 2) * C8 / NT;     // V key-pair chunks per thread
+  static_assert(NK >= 1 && NV >= 1, "tile too small for the workgroup");
+  uint4 k[NK];
+  uint4 v[2 * NV];
+
+  // row_of(kk) gives the sequence position of tile key kk, or -1.
+  template <typename RowOf>
+  __device__ __forceinline__ void fetch(const unsigned short* Kp, const unsigned short* Vp,
+                                        RowOf row_of, int tid) {
+#pragma unroll
+    for (int e = 0; e < NK; ++e) {
+      const int c = tid + NT * e;
+      const int kk = c / C8, c8 = c % C8;
+      const int row = row_of(kk);
+      k[e] = row >= 0 ? *(const uint4*)(Kp + (size_t)row * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int c = tid + NT * e;
+      const int p = c % (TK / 2), c8 = c / (TK / 2);
+      const int r0 = row_of(2 * p), r1 = row_of(2 * p + 1);
+      v[2 * e] = r0 >= 0 ? *(const uint4*)(Vp + (size_t)r0 * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+      v[2 * e + 1] = r1 >= 0 ? *(const uint4*)(Vp + (size_t)r1 * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void store(Tile<true, D>& t, int tid) const {
+#pragma unroll
+    for (int e = 0; e < NK; ++e) {
+      const int c = tid + NT * e;
+      const int kk = c / C8, c8 = c % C8;
+      *(uint4*)&t.k[kk * Tile<true, D>::KP + c8 * 8] = k[e];
+    }
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int c = tid + NT * e;
+      const int p = c % (TK / 2), c8 = c / (TK / 2);
+      const int slot = vt_slot(2 * p);  // even; key 2p+1 lands in slot + 1
+      const unsigned* a = (const unsigned*)&v[2 * e];
+      const unsigned* b = (const unsigned*)&v[2 * e + 1];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // d = c8*8 + 2w (low halves) and c8*8 + 2w + 1 (high halves).
+        const unsigned lo = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
+        const unsigned hi = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);
+        *(unsigned*)&t.vt[(c8 * 8 + 2 * w) * Tile<true, D>::VP + slot] = lo;
+        *(unsigned*)&t.vt[(c8 * 8 + 2 * w + 1) * Tile<true, D>::VP + slot] = hi;
+      }
+    }
+  }
+};
+
+template <int D, int NT>
+struct Loader<false, D, NT> {
+  static constexpr int C4 = D / 4;           // 16-byte chunks per row
+  static constexpr int NC = TK * C4 / NT;    // chunks per thread, each of K and V
+  static_assert(NC >= 1, "tile too small for the workgroup");
+  float4 k[NC];
+  float4 v[NC];
+
+  template <typename RowOf>
+  __device__ __forceinline__ void fetch(const float* Kp, const float* Vp, RowOf row_of, int tid) {
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+      const int c = tid + NT * e;
+      const int kk = c / C4, c4 = c % C4;
+      const int row = row_of(kk);
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      k[e] = row >= 0 ? *(const float4*)(Kp + (size_t)row * D + c4 * 4) : z;
+      v[e] = row >= 0 ? *(const float4*)(Vp + (size_t)row * D + c4 * 4) : z;
+    }
+  }
+
+  __device__ __forceinline__ void store(Tile<false, D>& t, int tid) const {
+#pragma unroll
+    for (int e = 0; e < NC; ++e) {
+      const int c = tid + NT * e;
+      const int kk = c / C4, c4 = c % C4;
+      *(float4*)&t.k[kk * Tile<false, D>::KP + c4 * 4] = k[e];
+      *(float4*)&t.v[kk * Tile<false, D>::VP + c4 * 4] = v[e];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Per-wavefront attention state for 32 query rows, and one tile step.
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int D>
+struct WaveAttn;
+
+template <int D>
+struct WaveAttn<true, D> {
+  bf16x8 q[D / 16];     // B operand of S^T = K Q^T: Q[row][16*ks + 8*hi + 0..7]
+  f32x16 acc[D / 32];   // O^T blocks: d = 32*blk + block_row(i, hi), query = lane % 32
+  float m, l;
+
+  __device__ __forceinline__ void load_q(const unsigned short* Qp, int row, int hi) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      if (row >= 0) {
+        q[ks] = *(const bf16x8*)(Qp + (size_t)row * D + 16 * ks + 8 * hi);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[ks][j] = (__bf16)0.0f;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
+    m = kNegInit;
+    l = 0.0f;
+  }
+
+  __device__ __forceinline__ void scores(const Tile<true, D>& t, int lane, f32x16 (&s)[2]) const {
+    const int hi = lane >> 5, r = lane & 31;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = *(const bf16x8*)&t.k[(32 * kb + r) * Tile<true, D>::KP + 16 * ks + 8 * hi];
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[ks], s[kb], 0, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void accumulate(const Tile<true, D>& t, int lane, const f32x16 (&p)[2]) {
+    const int hi = lane >> 5, r = lane & 31;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[ks][j] = (__bf16)p[ks >> 1][8 * (ks & 1) + j];
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = *(const bf16x8*)&t.vt[(32 * b + r) * Tile<true, D>::VP + 16 * ks + 8 * hi];
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc[b], 0, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store_row(unsigned short* Op, int row, int hi, float inv) const {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 o;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c] = (__bf16)(acc[b][4 * g + c] * inv);
+        *(bf16x4*)(Op + (size_t)row * D + 32 * b + 8 * g + 4 * hi) = o;
+      }
+    }
+  }
+};
+
+template <int D>
+struct WaveAttn<false, D> {
+  // B operand of the fp32 MFMA k-steps: step t pairs d = t (hi = 0) with
+  // d = t + D/2 (hi = 1); any fixed pairing of d values is a valid split.
+  float q[D / 2];
+  f32x16 acc[D / 32];
+  float m, l;
+
+  __device__ __forceinline__ void load_q(const float* Qp, int row, int hi) {
+#pragma unroll
+    for (int t4 = 0; t4 < D / 8; ++t4) {
+      float4 x = row >= 0 ? *(const float4*)(Qp + (size_t)row * D + (D / 2) * hi + 4 * t4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      q[4 * t4] = x.x; q[4 * t4 + 1] = x.y; q[4 * t4 + 2] = x.z; q[4 * t4 + 3] = x.w;
+    }
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
+    m = kNegInit;
+    l = 0.0f;
+  }
+
+  __device__ __forceinline__ void scores(const Tile<false, D>& t, int lane, f32x16 (&s)[2]) const {
+    const int hi = lane >> 5, r = lane & 31;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+#pragma unroll
+      for (int t4 = 0; t4 < D / 8; ++t4) {
+        const float4 a = *(const float4*)&t.k[(32 * kb + r) * Tile<false, D>::KP + (D / 2) * hi + 4 * t4];
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, q[4 * t4], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, q[4 * t4 + 1], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, q[4 * t4 + 2], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, q[4 * t4 + 3], s[kb], 0, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void accumulate(const Tile<false, D>& t, int lane, const f32x16 (&p)[2]) {
+    const int hi = lane >> 5, r = lane & 31;
+    // k-step (kb, i) pairs key 32*kb + block_row(i, 0) (hi = 0) with
+    // 32*kb + block_row(i, 1) (hi = 1): exactly the keys whose weights the two
+    // lane halves hold in register i of score block kb.
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float a = t.v[(32 * kb + block_row(i, hi)) * Tile<false, D>::VP + 32 * b + r];
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[kb][i], acc[b], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store_row(float* Op, int row, int hi, float inv) const {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 o = make_float4(acc[b][4 * g] * inv, acc[b][4 * g + 1] * inv,
+                               acc[b][4 * g + 2] * inv, acc[b][4 * g + 3] * inv);
+        *(float4*)(Op + (size_t)row * D + 32 * b + 8 * g + 4 * hi) = o;
+      }
+    }
+  }
+};
+
+// Online softmax over one tile of transposed scores s (raw, -inf where the
+// pair is not scored), then the P.V accumulation.  m is kept in log2 units
+// of the scaled scores.
+template <bool BF16, int D, typename Tl>
+__device__ __forceinline__ void softmax_accumulate(WaveAttn<BF16, D>& st, const Tl& tile,
+                                                   int lane, f32x16 (&s)[2], float sl2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+  mx = pair_max(mx) * sl2;
+  if (__any(mx > st.m + kSlack)) {
+    const float mn = fmaxf(st.m, mx);
+    const float alpha = fast_exp2(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.acc[b][i] *= alpha;
+    st.m = mn;
+  }
+  float ls = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(s[kb][i], sl2, -st.m));
+      s[kb][i] = p;
+      ls += p;
+    }
+  st.l += ls;
+  st.accumulate(tile, lane, s);
+}
+
+template <bool BF16>
+struct ElemT;
+template <>
+struct ElemT<true> { typedef unsigned short type; };
+template <>
+struct ElemT<false> { typedef float type; };
+
+// ---------------------------------------------------------------------------
+// Band kernel.
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
+  typedef typename ElemT<BF16>::type E;
+  constexpr int NT = kBandWaves * 64;
+  __shared__ Tile<BF16, D> tile;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
+  const BandWork w = a.work[blockIdx.x];
+  const int h = w.bh % a.H;
+  const int d = a.dil[h];
+  const int r = w.r, t0 = w.t0, hw = a.hw, N = a.N;
+  const int Lr = (N - r + d - 1) / d;  // length of the residue's subsequence
+  const size_t base = (size_t)w.bh * N * D;
+  const E* Qp = (const E*)a.Q + base;
+  const E* Kp = (const E*)a.K + base;
+  const E* Vp = (const E*)a.V + base;
+
+  // This wave's query rows: subsequence positions ua .. ub (ub < Lr).
+  const int ua = t0 + kWaveRows * wave;
+  const int ub = min(ua + kWaveRows - 1, Lr - 1);
+  const bool wave_live = ua < Lr;
+  const int u = ua + (lane & 31);
+  const int qrow = u < Lr ? r + d * u : -1;
+
+  WaveAttn<BF16, D> st;
+  st.load_q(Qp, qrow, hi);
+
+  // Key range of the workgroup's band, in subsequence positions.
+  const int s_lo = max(0, t0 - hw);
+  const int s_hi = min(Lr - 1, t0 + kBandRows - 1 + hw);
+  const int n_band = (s_hi - s_lo) / TK + 1;
+  const int n_glob_tiles = (a.n_glob + TK - 1) / TK;
+  const int n_tiles = n_band + n_glob_tiles;
+
+  auto row_of_tile = [&](int tt) {
+    return [=](int kk) -> int {
+      if (tt < n_band) {
+        const int s = s_lo + TK * tt + kk;
+        return s <= s_hi ? r + d * s : -1;
+      }
+      const int slot = TK * (tt - n_band) + kk;
+      return slot < a.n_glob ? a.glob[slot] : -1;
+    };
+  };
+
+  Loader<BF16, D, NT> ld;
+  ld.fetch(Kp, Vp, row_of_tile(0), tid);
+
+  for (int tt = 0; tt < n_tiles; ++tt) {
+    ld.store(tile, tid);
+    __syncthreads();
+    if (tt + 1 < n_tiles) ld.fetch(Kp, Vp, row_of_tile(tt + 1), tid);
+
+    if (wave_live) {
+      f32x16 s[2];
+      if (tt < n_band) {
+        const int s0 = s_lo + TK * tt;
+        const int kb_ = min(s0 + TK - 1, s_hi);  // last real key of the tile
+        const bool any = s0 <= ub + hw && kb_ >= ua - hw;
+        if (any) {
+          const bool full = (kb_ == s0 + TK - 1) && (s0 + TK - 1 - ua <= hw) && (ub - s0 <= hw);
+          st.scores(tile, lane, s);
+          if (!full) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int sk = s0 + 32 * kb + block_row(i, hi);
+                const int dd = sk - u;
+                if (sk > s_hi || dd > hw || dd < -hw) s[kb][i] = -INFINITY;
+              }
+          }
+          softmax_accumulate(st, tile, lane, s, a.sl2);
+        }
+      } else {
+        // Global keys, minus those already inside this row's band.
+        const int g0 = TK * (tt - n_band);
+        bool keep[2][16];
+        bool any = false;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int slot = g0 + 32 * kb + block_row(i, hi);
+            bool k = false;
+            if (slot < a.n_glob && u < Lr) {
+              const int g = a.glob[slot];
+              const int off = g - r;
+              const bool same_class = off >= 0 && off % d == 0;
+              const int dd = same_class ? off / d - u : 0;
+              k = !(same_class && dd <= hw && dd >= -hw);
+            }
+            keep[kb][i] = k;
+            any |= k;
+          }
+        if (__any(any)) {
+          st.scores(tile, lane, s);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (!keep[kb][i]) s[kb][i] = -INFINITY;
+          softmax_accumulate(st, tile, lane, s, a.sl2);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (wave_live) {
+    const float lt = pair_sum(st.l);
+    if (qrow >= 0 && !a.is_glob[qrow]) st.store_row((E*)a.O + base, qrow, hi, 1.0f / lt);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Global-row kernel: partials over key chunks, merged by the last arrival.
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int D, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
+  typedef typename ElemT<BF16>::type E;
+  constexpr int NT = WAVES * 64;
+  constexpr int ROWS = WAVES * kWaveRows;   // global rows per set
+  constexpr int REC = D + 4;                // partial record: m, l, 2 pad, acc[D]
+  __shared__ Tile<BF16, D> tile;
+  __shared__ int last;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
+  const int chunk = blockIdx.x % a.n_chunks;
+  const int bhs = blockIdx.x / a.n_chunks;
+  const int bh = bhs / a.n_sets, set = bhs % a.n_sets;
+  const int N = a.N;
+  const size_t base = (size_t)bh * N * D;
+  const E* Qp = (const E*)a.Q + base;
+  const E* Kp = (const E*)a.K + base;
+  const E* Vp = (const E*)a.V + base;
+
+  const int gfirst = set * ROWS + kWaveRows * wave;  // first global slot of this wave
+  const bool wave_live = gfirst < a.n_glob;
+  const int gslot = gfirst + (lane & 31);
+  const int qrow = gslot < a.n_glob ? a.glob[gslot] : -1;
+
+  WaveAttn<BF16, D> st;
+  st.load_q(Qp, qrow, hi);
+
+  const int c0 = chunk * a.chunk_keys;
+  const int c1 = min(N, c0 + a.chunk_keys);
+  const int n_tiles = (c1 - c0 + TK - 1) / TK;
+  auto row_of_tile = [&](int tt) {
+    return [=](int kk) -> int {
+      const int j = c0 + TK * tt + kk;
+      return j < c1 ? j : -1;
+    };
+  };
+
+  Loader<BF16, D, NT> ld;
+  ld.fetch(Kp, Vp, row_of_tile(0), tid);
+  for (int tt = 0; tt < n_tiles; ++tt) {
+    ld.store(tile, tid);
+    __syncthreads();
+    if (tt + 1 < n_tiles) ld.fetch(Kp, Vp, row_of_tile(tt + 1), tid);
+    if (wave_live) {
+      f32x16 s[2];
+      st.scores(tile, lane, s);
+      const int j0 = c0 + TK * tt;
+      if (j0 + TK > c1) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (j0 + 32 * kb + block_row(i, hi) >= c1) s[kb][i] = -INFINITY;
+      }
+      softmax_accumulate(st, tile, lane, s, a.sl2);
+    }
+    __syncthreads();
+  }
+
+  // Partial record of this wave's 32 rows for this chunk.
+  float* part = a.part + ((size_t)bhs * a.n_chunks + chunk) * ROWS * REC;
+  if (wave_live) {
+    const float lt = pair_sum(st.l);
+    float* rec = part + (size_t)(kWaveRows * wave + (lane & 31)) * REC;
+    if (hi == 0) {
+      rec[0] = st.m;
+      rec[1] = lt;
+    }
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(float4*)(rec + 4 + 32 * b + 8 * g + 4 * hi) =
+            make_float4(st.acc[b][4 * g], st.acc[b][4 * g + 1], st.acc[b][4 * g + 2],
+                        st.acc[b][4 * g + 3]);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(&a.counters[bhs], 1u) == (unsigned)(a.n_chunks - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+
+  // Last arrival: merge every chunk's partial for this set and write O.
+  const float* part0 = a.part + (size_t)bhs * a.n_chunks * ROWS * REC;
+  E* Op = (E*)a.O + base;
+  for (int x = tid; x < ROWS * (D / 4); x += NT) {
+    const int rr = x / (D / 4), dq = x % (D / 4);
+    const int slot = set * ROWS + rr;
+    if (slot >= a.n_glob) continue;
+    float m = kNegInit, l = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < a.n_chunks; ++c) {
+      const float* rec = part0 + ((size_t)c * ROWS + rr) * REC;
+      const float mc = rec[0], lc = rec[1];
+      const float4 ac = *(const float4*)(rec + 4 + 4 * dq);
+      const float mn = fmaxf(m, mc);
+      const float s1 = fast_exp2(m - mn), s2 = fast_exp2(mc - mn);
+      l = l * s1 + lc * s2;
+      acc.x = acc.x * s1 + ac.x * s2;
+      acc.y = acc.y * s1 + ac.y * s2;
+      acc.z = acc.z * s1 + ac.z * s2;
+      acc.w = acc.w * s1 + ac.w * s2;
+      m = mn;
+    }
+    const float inv = 1.0f / l;
+    const int row = a.glob[slot];
+    if constexpr (BF16) {
+      bf16x4 o;
+      o[0] = (__bf16)(acc.x * inv); o[1] = (__bf16)(acc.y * inv);
+      o[2] = (__bf16)(acc.z * inv); o[3] = (__bf16)(acc.w * inv);
+      *(bf16x4*)(Op + (size_t)row * D + 4 * dq) = o;
+    } else {
+      *(float4*)(Op + (size_t)row * D + 4 * dq) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+  }
+  if (tid == 0) atomicExch(&a.counters[bhs], 0u);
+}
+
+}  // namespace
+
+hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s) {
+  if (n_wg <= 0) return hipSuccess;
+  dim3 grid(n_wg), block(kBandWaves * 64);
+  if (dtype == 1 && D == 64) hipLaunchKernelGGL((band_kernel<true, 64>), grid, block, 0, s, a);
+  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((band_kernel<true, 128>), grid, block, 0, s, a);
+  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((band_kernel<false, 64>), grid, block, 0, s, a);
+  else if (dtype == 0 && D == 128) hipLaunchKernelGGL((band_kernel<false, 128>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+static hipError_t launch_glob_t(int waves, const GlobArgs& a, int n_wg, hipStream_t s) {
+  dim3 grid(n_wg);
+  if (waves == 1) hipLaunchKernelGGL((glob_kernel<BF16, D, 1>), grid, dim3(64), 0, s, a);
+  else if (waves == 2) hipLaunchKernelGGL((glob_kernel<BF16, D, 2>), grid, dim3(128), 0, s, a);
+  else if (waves == 4) hipLaunchKernelGGL((glob_kernel<BF16, D, 4>), grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s) {
+  if (n_wg <= 0) return hipSuccess;
+  if (dtype == 1 && D == 64) return launch_glob_t<true, 64>(waves, a, n_wg, s);
+  if (dtype == 1 && D == 128) return launch_glob_t<true, 128>(waves, a, n_wg, s);
+  if (dtype == 0 && D == 64) return launch_glob_t<false, 64>(waves, a, n_wg, s);
+  if (dtype == 0 && D == 128) return launch_glob_t<false, 128>(waves, a, n_wg, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lfattn

@@ -1,0 +1,183 @@
+"""Thin ctypes binding of liblfattn (include/lfattn.h), same names as the C ABI.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of liblfattn.so.  PyTorch appears only to hand over device pointers
+and the current HIP stream.  If the library is missing, loading it raises;
+there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblfattn.so")
+
+LFATTN_OK = 0
+LFATTN_EINVAL = 1
+LFATTN_EUNSUPPORTED = 2
+LFATTN_ENOMEM = 3
+LFATTN_EHIP = 4
+
+LFATTN_F32 = 0
+LFATTN_BF16 = 1
+
+# Every entry point include/lfattn.h declares.
+EXPORTS = ("lfattn_create", "lfattn_forward", "lfattn_destroy", "lfattn_status_string",
+           "lfattn_scored_pairs", "lfattn_global_list", "lfattn_set_timing",
+           "lfattn_read_timing")
+
+_lib = None
+
+
+class LfattnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lfattn_status_string(status)} (status {status})")
+
+
+def load():
+    """Open liblfattn.so and declare the C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    i32p = ctypes.POINTER(ctypes.c_int)
+    lib.lfattn_create.restype = ctypes.c_int
+    lib.lfattn_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p,
+                                  ctypes.c_int, ctypes.c_float]
+    lib.lfattn_forward.restype = ctypes.c_int
+    lib.lfattn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.lfattn_destroy.restype = ctypes.c_int
+    lib.lfattn_destroy.argtypes = [vp]
+    lib.lfattn_status_string.restype = ctypes.c_char_p
+    lib.lfattn_status_string.argtypes = [ctypes.c_int]
+    lib.lfattn_scored_pairs.restype = ctypes.c_int
+    lib.lfattn_scored_pairs.argtypes = [vp, ctypes.POINTER(ctypes.c_longlong)]
+    lib.lfattn_global_list.restype = ctypes.c_int
+    lib.lfattn_global_list.argtypes = [vp, i32p, ctypes.c_int, i32p]
+    lib.lfattn_set_timing.restype = ctypes.c_int
+    lib.lfattn_set_timing.argtypes = [vp, ctypes.c_int]
+    lib.lfattn_read_timing.restype = ctypes.c_int
+    lib.lfattn_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double), i32p]
+    _lib = lib
+    return lib
+
+
+def lfattn_status_string(status: int) -> str:
+    return load().lfattn_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != LFATTN_OK:
+        raise LfattnError(status, what)
+
+
+def _int_array(values):
+    if values is None:
+        return None
+    vals = [int(x) for x in values]
+    return (ctypes.c_int * max(1, len(vals)))(*vals)
+
+
+def lfattn_create(B: int, H: int, N: int, D: int, dtype: int, window: int,
+                  dilation=None, global_idx=(), scale: float = 0.0) -> int:
+    """Returns the handle (an integer address).  dtype: LFATTN_F32 or LFATTN_BF16."""
+    lib = load()
+    handle = ctypes.c_void_p()
+    g = list(global_idx) if global_idx is not None else []
+    st = lib.lfattn_create(ctypes.byref(handle), B, H, N, D, dtype, window,
+                           _int_array(dilation), _int_array(g) if g else None, len(g),
+                           float(scale))
+    _check(st, "lfattn_create")
+    return handle.value
+
+
+def _ptr(x) -> int:
+    return x if isinstance(x, int) else x.data_ptr()
+
+
+def lfattn_forward(handle: int, Q, K, V, O, stream=None) -> None:
+    """Enqueue one forward.  Q, K, V, O: device tensors (or raw addresses);
+    stream: a HIP stream handle (int), a torch stream, or None for torch's
+    current stream on the current device."""
+    lib = load()
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(lib.lfattn_forward(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), stream),
+           "lfattn_forward")
+
+
+def lfattn_destroy(handle: int) -> None:
+    _check(load().lfattn_destroy(handle), "lfattn_destroy")
+
+
+def lfattn_scored_pairs(handle: int) -> int:
+    n = ctypes.c_longlong()
+    _check(load().lfattn_scored_pairs(handle, ctypes.byref(n)), "lfattn_scored_pairs")
+    return int(n.value)
+
+
+def lfattn_global_list(handle: int) -> list:
+    lib = load()
+    n = ctypes.c_int()
+    _check(lib.lfattn_global_list(handle, None, 0, ctypes.byref(n)), "lfattn_global_list")
+    buf = (ctypes.c_int * max(1, n.value))()
+    _check(lib.lfattn_global_list(handle, buf, n.value, ctypes.byref(n)), "lfattn_global_list")
+    return list(buf[: n.value])
+
+
+def lfattn_set_timing(handle: int, enable: bool) -> None:
+    _check(load().lfattn_set_timing(handle, 1 if enable else 0), "lfattn_set_timing")
+
+
+def lfattn_read_timing(handle: int):
+    """(band_ms_total, global_ms_total, n_forwards) since timing was enabled/read."""
+    b, g, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    _check(load().lfattn_read_timing(handle, ctypes.byref(b), ctypes.byref(g), ctypes.byref(n)),
+           "lfattn_read_timing")
+    return b.value, g.value, n.value
+
+
+class LFAttention:
+    """Owns one handle: create on construction, destroy on close()."""
+
+    def __init__(self, B, H, N, D, dtype, window, dilation=None, global_idx=(), scale=0.0):
+        self.shape = (B, H, N, D)
+        self.dtype = dtype
+        self.handle = lfattn_create(B, H, N, D, dtype, window, dilation, global_idx, scale)
+
+    def forward(self, Q, K, V, O, stream=None):
+        lfattn_forward(self.handle, Q, K, V, O, stream)
+        return O
+
+    @property
+    def scored_pairs(self) -> int:
+        return lfattn_scored_pairs(self.handle)
+
+    def close(self):
+        if self.handle:
+            lfattn_destroy(self.handle)
+            self.handle = 0
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,327 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Small shapes are compared on every output element; the five full-size
+workloads, in the launch configuration the benchmark times, on sampled rows
+(every global row kind, sequence ends, tile and block boundaries, random rows)
+plus properties that hold at any size.  The allowed key sets are recovered
+bit-exactly from the production kernels (mask readout).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_sparse_band_amd import lfattn as L
+from long_context_sparse_band_amd import workloads as W
+from gpu_util import compare, run, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+
+
+# (B, H, N, D, dtype, window, dilation, globals, seed)
+SMALL = [
+    (1, 1, 1, 64, "f32", 0, None, [], 1),
+    (1, 1, 1, 64, "bf16", 512, None, [0], 2),
+    (1, 2, 37, 64, "bf16", 8, None, [], 3),
+    (1, 1, 64, 64, "f32", 0, None, [], 4),
+    (2, 2, 200, 64, "bf16", 40, [1, 3], [5, 100, 199], 5),
+    (1, 3, 333, 128, "bf16", 100, [1, 2, 5], [0, 17, 300], 6),
+    (1, 2, 300, 64, "f32", 1000, None, [], 7),
+    (1, 1, 1024, 64, "f32", 512, None, [0], 8),
+    (1, 4, 700, 64, "bf16", 128, [1, 2, 3, 4], list(range(0, 700, 7)), 9),
+    (1, 2, 500, 128, "f32", 64, [2, 1], list(range(150)), 10),
+    (1, 2, 257, 64, "bf16", 513, [1, 1], [256], 11),
+    (1, 1, 130, 64, "bf16", 64, [200], [], 12),
+    (2, 2, 1000, 128, "bf16", 256, None, [999], 13),
+    (1, 2, 129, 128, "f32", 2, [1, 64], [64, 128], 14),
+    (1, 1, 2050, 64, "bf16", 512, None, list(range(32)), 15),
+    (1, 2, 4099, 64, "bf16", 300, [3, 1], [4098, 1, 2048], 16),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dH%dN%dD%d_%s_w%d_s%d" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], c[8]))
+def test_small_cases_every_element(case):
+    B, H, N, D, dt, window, dil, glob, seed = case
+    inp = W.small_case(B, H, N, D, dt, window, dilation=dil, glob=glob, seed=seed)
+    say(f"small case {case}")
+    got, pairs = run(inp)
+    want = oracle.attention(inp.q, inp.k, inp.v, window, list(inp.dilation), list(inp.glob))
+    compare(got, want, dt, str(case))
+    assert pairs == oracle.count_pairs(B, H, N, window, list(inp.dilation), list(inp.glob))
+
+
+def test_random_sweep_every_element():
+    rng = np.random.default_rng(123)
+    for t in range(24):
+        N = int(rng.integers(1, 600))
+        D = int(rng.choice([64, 128]))
+        H = int(rng.integers(1, 4))
+        dt = str(rng.choice(["f32", "bf16"]))
+        window = int(rng.integers(0, 2 * N + 3))
+        dil = [int(x) for x in rng.integers(1, 6, size=H)]
+        n_g = int(rng.integers(0, min(N, 40) + 1))
+        glob = rng.choice(N, size=n_g, replace=False).tolist() if n_g else []
+        inp = W.small_case(1, H, N, D, dt, window, dilation=dil, glob=glob, seed=1000 + t)
+        say(f"sweep {t}: H{H} N{N} D{D} {dt} w{window} dil{dil} n_g{n_g}")
+        got, _ = run(inp)
+        want = oracle.attention(inp.q, inp.k, inp.v, window, dil, list(inp.glob))
+        compare(got, want, dt, f"sweep {t}")
+
+
+def test_explicit_scale():
+    inp = W.small_case(1, 2, 300, 64, "f32", 64, glob=[7], seed=31)
+    say("explicit scale 0.05")
+    got, _ = run(inp, scale=0.05)
+    want = oracle.attention(inp.q, inp.k, inp.v, 64, None, [7], scale=0.05)
+    compare(got, want, "f32", "scale")
+
+
+def test_duplicate_unsorted_globals_are_one_set():
+    inp = W.small_case(1, 2, 400, 64, "bf16", 50, glob=[3, 77, 399], seed=32)
+    say("duplicate/unsorted global list")
+    got_a, pa = run(inp, glob=[399, 3, 77, 3, 399, 77, 77])
+    got_b, pb = run(inp, glob=[3, 77, 399])
+    assert np.array_equal(got_a, got_b) and pa == pb
+    h = L.lfattn_create(1, 2, 400, 64, L.LFATTN_BF16, 50, None, [399, 3, 77, 3])
+    try:
+        assert L.lfattn_global_list(h) == [3, 77, 399]
+    finally:
+        L.lfattn_destroy(h)
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads on sampled rows.
+# --------------------------------------------------------------------------
+
+def _sample_rows(inp, per_head=24, seed=0):
+    wl = inp.wl
+    rng = np.random.default_rng(seed)
+    glob = inp.glob.tolist()
+    rows = []
+    for b in range(wl.B):
+        for h in range(wl.H):
+            base = (b * wl.H + h) * wl.N
+            pick = {0, 1, wl.N - 1, wl.N - 2, 127, 128, 255, 256, wl.N // 2}
+            pick.update(int(x) for x in rng.integers(0, wl.N, size=per_head))
+            if glob:
+                pick.update(int(g) for g in rng.choice(glob, size=min(3, len(glob)), replace=False))
+                g = int(rng.choice(glob))
+                pick.update({g - 1, g + 1, g + 300, g - 300})
+            rows.extend(base + i for i in sorted(pick) if 0 <= i < wl.N)
+    return np.array(sorted(set(rows)), dtype=np.int64)
+
+
+@pytest.mark.parametrize("wl", W.WORKLOADS, ids=lambda w: w.name)
+def test_workload_full_size(wl):
+    import torch
+    say(f"workload {wl.name}: generating inputs")
+    inp = W.generate(wl)
+    q, k, v = to_device(inp)
+    o = torch.empty_like(q)
+    dtype = L.LFATTN_BF16 if wl.dtype == "bf16" else L.LFATTN_F32
+    say(f"workload {wl.name}: forward")
+    h = L.lfattn_create(wl.B, wl.H, wl.N, wl.D, dtype, wl.window, list(inp.dilation),
+                        list(inp.glob))
+    try:
+        L.lfattn_forward(h, q, k, v, o)
+        torch.cuda.synchronize()
+        pairs = L.lfattn_scored_pairs(h)
+    finally:
+        L.lfattn_destroy(h)
+    flat = o.view(-1, wl.D)
+    assert bool(torch.isfinite(flat.float()).all())
+    # Every output is a convex combination of value rows.
+    assert float(flat.float().abs().max()) <= float(v.float().abs().max()) * (1 + 2 ** -7)
+    rows = np.arange(wl.B * wl.H * wl.N) if wl.N <= 1024 else _sample_rows(inp)
+    got = flat[torch.from_numpy(rows).to(flat.device)].float().cpu().numpy().astype(np.float64)
+    del q, k, v, o, flat
+    say(f"workload {wl.name}: oracle on {len(rows)} rows")
+    want = oracle.attention(inp.q, inp.k, inp.v, wl.window, list(inp.dilation), list(inp.glob),
+                            rows=rows)
+    compare(got, want, wl.dtype, wl.name)
+    if wl.N <= 16448:
+        assert pairs == oracle.count_pairs(wl.B, wl.H, wl.N, wl.window, list(inp.dilation),
+                                           list(inp.glob))
+
+
+# --------------------------------------------------------------------------
+# Mask readout: recover each row's allowed key set from the production
+# kernels.  Q = K = 0 makes every scored pair weigh 1/|S_i|; V holds one-hot
+# rows for a chunk of D keys, so O[i, c] != 0 exactly when key c0 + c is in
+# S_i, and a key scored twice would show as a doubled entry.
+# --------------------------------------------------------------------------
+
+def _readout(B, H, N, D, dt, window, dil, glob, chunks=None):
+    import torch
+    dtype = L.LFATTN_BF16 if dt == "bf16" else L.LFATTN_F32
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    q = torch.zeros((B, H, N, D), dtype=tdt, device="cuda:0")
+    v = torch.zeros_like(q)
+    o = torch.empty_like(q)
+    h = L.lfattn_create(B, H, N, D, dtype, window, dil, glob)
+    codes, counts = [], []
+    try:
+        starts = range(0, N, D) if chunks is None else chunks
+        for c0 in starts:
+            v.zero_()
+            n = min(D, N - c0)
+            v[:, :, c0:c0 + n, :n] = torch.eye(n, dtype=tdt, device=v.device)
+            L.lfattn_forward(h, q, q, v, o)
+            torch.cuda.synchronize()
+            of = o.float()
+            nz = of > 0
+            # Every nonzero weight of a row is the same 1/|S_i|: no key twice.
+            rowmax = of.amax(dim=3, keepdim=True)
+            assert bool(((of == rowmax) | ~nz).all()), f"unequal weights in chunk {c0}"
+            idx = torch.nonzero(nz)
+            bh = idx[:, 0] * H + idx[:, 1]
+            codes.append(((bh * N + idx[:, 2]) * N + (c0 + idx[:, 3])).cpu().numpy())
+            if dt == "f32":  # 1/O is |S_i| exactly in fp32
+                counts.append((idx.cpu().numpy(), torch.round(1.0 / of[nz]).long().cpu().numpy()))
+    finally:
+        L.lfattn_destroy(h)
+    return np.sort(np.concatenate(codes)), counts
+
+
+def _oracle_codes(B, H, N, window, dil, glob, chunk_ranges=None):
+    out = []
+    d_list = dil or [1] * H
+    cache = {}
+    for h in range(H):
+        d = d_list[h]
+        if d not in cache:
+            rows = []
+            for i in range(N):
+                keys = oracle.allowed_set(N, window, d, glob, i).astype(np.int64)
+                if chunk_ranges is not None:
+                    keep = np.zeros(len(keys), dtype=bool)
+                    for a, b in chunk_ranges:
+                        keep |= (keys >= a) & (keys < b)
+                    keys = keys[keep]
+                rows.append(i * N + keys)
+            cache[d] = np.concatenate(rows)
+        for b in range(B):
+            out.append((b * H + h) * N * N + cache[d])
+    return np.sort(np.concatenate(out))
+
+
+READOUT = [
+    # name, B, H, N, D, dtype, window, dilation, globals, chunks (None: all)
+    ("single_head_f32", 1, 1, 1024, 64, "f32", 512, None, [0], None),
+    ("longformer_base_bf16", 1, 12, 4096, 64, "bf16", 512, None, list(range(32)), None),
+    ("dilated_charlm_bf16", 2, 8, 8192, 64, "bf16", 512, [1, 1, 1, 1, 1, 1, 2, 2], [], None),
+    ("dilated_with_globals_f32", 1, 3, 1500, 64, "f32", 200, [1, 2, 3], [0, 5, 700, 1499], None),
+    ("gmat_memory_bf16_2heads", 1, 2, 16448, 64, "bf16", 256, None, list(range(64)), None),
+    ("ragged_d128_bf16", 1, 2, 3001, 128, "bf16", 1024, [1, 2], [3000, 1500, 7], None),
+]
+
+
+@pytest.mark.parametrize("case", READOUT, ids=lambda c: c[0])
+def test_mask_readout_bit_exact(case):
+    name, B, H, N, D, dt, window, dil, glob, chunks = case
+    say(f"mask readout {name}")
+    pairs, counts = _readout(B, H, N, D, dt, window, dil, glob, chunks)
+    want = _oracle_codes(B, H, N, window, dil, glob)
+    assert len(pairs) == len(want), f"{name}: {len(pairs)} pairs scored, oracle {len(want)}"
+    assert np.array_equal(pairs, want), name
+    assert len(want) == oracle.count_pairs(B, H, N, window, dil, glob)
+    for idx, cnt in counts:  # fp32: 1/O recovers |S_i| exactly
+        for (b, h, i, c), n in zip(idx[:500], cnt[:500]):
+            d = (dil or [1] * H)[h]
+            assert n == len(oracle.allowed_set(N, window, d, glob, int(i)))
+
+
+def test_mask_readout_long_stress_chunks():
+    """Full N = 65536, D = 128, window 1024 and the seeded 64 globals, on the
+    key chunks that hold the globals, the sequence ends and random chunks."""
+    wl = W.LONG_STRESS
+    glob = W.generate(W.Workload("g", B=1, H=1, N=wl.N, D=8, dtype="f32", window=0,
+                                 dilation=(1,), n_random_glob=64, seed=wl.seed)).glob.tolist()
+    rng = np.random.default_rng(5)
+    starts = sorted({0, wl.N - wl.D} | {g // wl.D * wl.D for g in glob[:8]} |
+                    {int(x) * wl.D for x in rng.integers(0, wl.N // wl.D, size=6)})
+    say(f"mask readout long stress, {len(starts)} chunks")
+    pairs, _ = _readout(1, 1, wl.N, wl.D, "bf16", wl.window, None, glob, starts)
+    ranges = [(s, s + wl.D) for s in starts]
+    want = _oracle_codes(1, 1, wl.N, wl.window, None, glob, ranges)
+    assert np.array_equal(pairs, want)
+
+
+# --------------------------------------------------------------------------
+# Execution properties.
+# --------------------------------------------------------------------------
+
+def test_deterministic_and_repeatable():
+    import torch
+    inp = W.small_case(1, 4, 3000, 64, "bf16", 512, glob=list(range(40)), seed=41)
+    q, k, v = to_device(inp)
+    h = L.lfattn_create(1, 4, 3000, 64, L.LFATTN_BF16, 512, None, list(inp.glob))
+    try:
+        outs = []
+        say("determinism: 6 forwards")
+        for _ in range(6):
+            o = torch.empty_like(q)
+            L.lfattn_forward(h, q, k, v, o)
+            outs.append(o)
+        torch.cuda.synchronize()
+        for o in outs[1:]:
+            assert torch.equal(o, outs[0])
+    finally:
+        L.lfattn_destroy(h)
+
+
+def test_non_default_stream():
+    import torch
+    inp = W.small_case(1, 2, 1000, 64, "bf16", 128, glob=[0, 500], seed=42)
+    say("forward on a second stream")
+    ref, _ = run(inp)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got, _ = run(inp, stream=s)
+    assert np.array_equal(got, ref)
+
+
+def test_forward_rejects_bad_pointers():
+    import torch
+    h = L.lfattn_create(1, 1, 128, 64, L.LFATTN_BF16, 16, None, [])
+    try:
+        # Every pointer below stays inside x, so nothing could run out of
+        # bounds even if a check were missing.
+        x = torch.zeros(3 * 128 * 64 + 64, dtype=torch.bfloat16, device="cuda:0")
+        base = x.data_ptr()
+        with pytest.raises(L.LfattnError) as e:
+            L.lfattn_forward(h, base + 2, base, base, base + 2 * 128 * 64 * 2)
+        assert e.value.status == L.LFATTN_EINVAL
+        with pytest.raises(L.LfattnError) as e:  # O overlaps Q
+            L.lfattn_forward(h, base, base, base, base + 64)
+        assert e.value.status == L.LFATTN_EINVAL
+        with pytest.raises(L.LfattnError):
+            L.lfattn_forward(h, 0, base, base, base)
+    finally:
+        L.lfattn_destroy(h)
+
+
+def test_timing_records_both_kernels():
+    import torch
+    inp = W.small_case(1, 2, 2048, 64, "bf16", 512, glob=[0, 1, 2], seed=43)
+    q, k, v = to_device(inp)
+    o = torch.empty_like(q)
+    h = L.lfattn_create(1, 2, 2048, 64, L.LFATTN_BF16, 512, None, [0, 1, 2])
+    try:
+        L.lfattn_set_timing(h, True)
+        for _ in range(5):
+            L.lfattn_forward(h, q, k, v, o)
+        band, glob_ms, n = L.lfattn_read_timing(h)
+        assert n == 5 and band > 0 and glob_ms > 0
+        L.lfattn_set_timing(h, False)
+    finally:
+        L.lfattn_destroy(h)
