@@ -58,8 +58,8 @@ def cpu_baseline(inp, wl, pairs_per_head_total):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(sharding is described in DESIGN.md, not run).", file=sys.stderr)
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
