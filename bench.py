@@ -126,7 +126,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded i.i.d. Gaussian Q, K, V)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
-                   "window": wl.window, "dilation": list(inp.dilation)[:1] if len(set(inp.dilation)) == 1 else list(inp.dilation),
+                   "window": wl.window, "dilation": [int(x) for x in inp.dilation],
                    "n_global": n_g, "scored_pairs": pairs, "parallelism": "single GPU"},
         "whole_forward_tflops": pairs * flops_per_pair / (ms * 1e-3) / 1e12,
         "whole_forward_mfma_frac": pairs * flops_per_pair / (ms * 1e-3) / 1e12 / peak,

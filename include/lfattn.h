@@ -120,7 +120,7 @@ lfattn_status lfattn_global_list(lfattn_t ctx, int* out, int capacity, int* n_ou
  * forward also records events around its kernels on the forward's stream (at
  * most 4096 forwards are recorded; later ones are not).  lfattn_read_timing
  * waits for the recorded events and returns the summed milliseconds of the
- * band kernel and of the global-row kernel and the number of forwards
+ * band kernel and of the global-row kernels (partials and merge) and the number of forwards
  * recorded, then clears the record.  Enabling or disabling also clears it.
  */
 lfattn_status lfattn_set_timing(lfattn_t ctx, int enable);

@@ -41,12 +41,11 @@ struct lfattn_ctx {
   unsigned char* d_isglob = nullptr;
 
   float* d_part = nullptr;
-  unsigned* d_counters = nullptr;
   int g_waves = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
 
   bool timing = false;
   int n_timed = 0;
-  std::vector<hipEvent_t> ev;  // 3 per timed forward
+  std::vector<hipEvent_t> ev;  // 4 per timed forward
 };
 
 namespace {
@@ -70,7 +69,6 @@ void free_ctx(lfattn_ctx* c) {
   (void)hipFree(c->d_glob);
   (void)hipFree(c->d_isglob);
   (void)hipFree(c->d_part);
-  (void)hipFree(c->d_counters);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
   delete c;
 }
@@ -215,8 +213,7 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   if (n_g > 0) {
     const size_t rec = (size_t)D + 4;
     const size_t n_part = (size_t)B * H * c->n_sets * c->n_chunks * c->g_waves * kWaveRows * rec;
-    if ((st = dev_alloc(&c->d_part, n_part)) != LFATTN_OK ||
-        (st = dev_alloc(&c->d_counters, (size_t)B * H * c->n_sets)) != LFATTN_OK) {
+    if ((st = dev_alloc(&c->d_part, n_part)) != LFATTN_OK) {
       free_ctx(c);
       return st;
     }
@@ -227,7 +224,6 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   ok = ok && hipMemcpy(c->d_isglob, isg.data(), N, hipMemcpyHostToDevice) == hipSuccess;
   if (n_g > 0) {
     ok = ok && hipMemcpy(c->d_glob, c->glob.data(), n_g * sizeof(int), hipMemcpyHostToDevice) == hipSuccess;
-    ok = ok && hipMemset(c->d_counters, 0, (size_t)B * H * c->n_sets * sizeof(unsigned)) == hipSuccess;
   }
   if (!ok) {
     (void)hipGetLastError();
@@ -251,15 +247,18 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
 
   const float sl2 = c->scale * 1.4426950408889634f;
   const bool timed = c->timing && c->n_timed < kMaxTimedForwards;
-  hipEvent_t* ev = timed ? &c->ev[3 * c->n_timed] : nullptr;
+  hipEvent_t* ev = timed ? &c->ev[4 * c->n_timed] : nullptr;
   if (timed && hipEventRecord(ev[0], stream) != hipSuccess) return LFATTN_EHIP;
 
+  // Global rows: partials first, then the band kernel, then the merge (which
+  // reads the partials after the kernel boundary made them visible).
   const int n_g = (int)c->glob.size();
+  lfattn::GlobArgs g;
   if (n_g > 0) {
-    lfattn::GlobArgs g;
     g.Q = Q; g.K = K; g.V = V; g.O = O;
-    g.glob = c->d_glob; g.part = c->d_part; g.counters = c->d_counters;
-    g.H = c->H; g.N = c->N; g.n_glob = n_g;
+    g.glob = c->d_glob; g.part = c->d_part;
+    g.H = c->H; g.N = c->N; g.n_glob = n_g; g.n_bh = c->B * c->H;
+    g.rows_per_set = c->g_waves * kWaveRows;
     g.n_sets = c->n_sets; g.n_chunks = c->n_chunks; g.chunk_keys = c->chunk_keys;
     g.sl2 = sl2;
     if (lfattn::launch_glob(c->dtype, c->D, c->g_waves, g, c->n_glob_wg, stream) != hipSuccess)
@@ -273,9 +272,13 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
   a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
   if (lfattn::launch_band(c->dtype, c->D, a, c->n_band_wg, stream) != hipSuccess)
     return LFATTN_EHIP;
+  if (timed && hipEventRecord(ev[2], stream) != hipSuccess) return LFATTN_EHIP;
+
+  if (n_g > 0 && lfattn::launch_glob_merge(c->dtype, c->D, g, stream) != hipSuccess)
+    return LFATTN_EHIP;
 
   if (timed) {
-    if (hipEventRecord(ev[2], stream) != hipSuccess) return LFATTN_EHIP;
+    if (hipEventRecord(ev[3], stream) != hipSuccess) return LFATTN_EHIP;
     ++c->n_timed;
   }
   return LFATTN_OK;
@@ -305,7 +308,7 @@ lfattn_status lfattn_global_list(lfattn_t c, int* out, int capacity, int* n_out)
 lfattn_status lfattn_set_timing(lfattn_t c, int enable) {
   if (!c) return LFATTN_EINVAL;
   if (enable && c->ev.empty()) {
-    c->ev.resize(3 * kMaxTimedForwards, nullptr);
+    c->ev.resize(4 * kMaxTimedForwards, nullptr);
     for (auto& e : c->ev)
       if (hipEventCreate(&e) != hipSuccess) {
         (void)hipGetLastError();
@@ -323,14 +326,16 @@ lfattn_status lfattn_set_timing(lfattn_t c, int enable) {
 lfattn_status lfattn_read_timing(lfattn_t c, double* band_ms, double* global_ms, int* n_forwards) {
   if (!c || !band_ms || !global_ms || !n_forwards) return LFATTN_EINVAL;
   double b = 0.0, g = 0.0;
-  if (c->n_timed > 0 && hipEventSynchronize(c->ev[3 * (c->n_timed - 1) + 2]) != hipSuccess)
+  if (c->n_timed > 0 && hipEventSynchronize(c->ev[4 * (c->n_timed - 1) + 3]) != hipSuccess)
     return LFATTN_EHIP;
   for (int t = 0; t < c->n_timed; ++t) {
-    float x = 0.0f, y = 0.0f;
-    if (hipEventElapsedTime(&x, c->ev[3 * t], c->ev[3 * t + 1]) != hipSuccess ||
-        hipEventElapsedTime(&y, c->ev[3 * t + 1], c->ev[3 * t + 2]) != hipSuccess)
+    float x = 0.0f, y = 0.0f, z = 0.0f;
+    hipEvent_t* e = &c->ev[4 * t];
+    if (hipEventElapsedTime(&x, e[0], e[1]) != hipSuccess ||
+        hipEventElapsedTime(&y, e[1], e[2]) != hipSuccess ||
+        hipEventElapsedTime(&z, e[2], e[3]) != hipSuccess)
       return LFATTN_EHIP;
-    g += x;
+    g += x + z;
     b += y;
   }
   *band_ms = b;

@@ -42,9 +42,10 @@ struct GlobArgs {
   const void* V;
   void* O;
   const int* glob;             // [n_glob] sorted global positions
-  float* part;                 // partial (m, l, acc[D]) records
-  unsigned* counters;          // [B*H*n_sets] arrival counters, zero between calls
+  float* part;                 // partial (m, l, 2 pad, acc[D]) records
   int H, N, n_glob;
+  int n_bh;                    // B * H
+  int rows_per_set;            // waves * 32
   int n_sets;                  // sets of up to waves*32 global rows per head
   int n_chunks;                // key chunks per (bh, set)
   int chunk_keys;              // keys per chunk, a multiple of kTileKeys
@@ -53,6 +54,8 @@ struct GlobArgs {
 
 // Launchers (defined next to the kernels).  dtype: 0 fp32, 1 bf16.
 hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s);
+hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s);
 hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s);
+hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s);
 
 }  // namespace lfattn

@@ -13,10 +13,11 @@
 // exponentiated scores already sit in the lane layout of the next MFMA's B
 // operand.
 //
-// Global-row kernel: the rows of global tokens attend to all N keys.  Each
-// workgroup scores a chunk of keys for up to 128 global rows and writes a
-// partial (max, sum, unnormalised output); the last workgroup to finish a
-// (batch, head, row set) merges the partials and writes those output rows.
+// Global-row kernels: the rows of global tokens attend to all N keys.  Each
+// workgroup of the partial kernel scores a chunk of keys for up to 128 global
+// rows and writes a partial (max, sum, unnormalised output); the merge kernel,
+// launched after the band kernel on the same stream, combines the chunks of
+// every global row and writes those output rows.
 //
 // The math is Eq. (1) of the Unlimiformer page (section 2.3) over the
 // Longformer pattern (Ultralytics glossary "Longformer", section on how the
@@ -379,6 +380,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   typedef typename ElemT<BF16>::type E;
   constexpr int NT = kBandWaves * 64;
   __shared__ Tile<BF16, D> tile;
+  __shared__ __attribute__((aligned(16))) int gsub[TK];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
@@ -420,11 +422,33 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
     };
   };
 
+  // Keys a row may score inside a band tile form the interval [lo, hi] of
+  // subsequence positions.  Rows past the end of the subsequence get an empty
+  // interval.
+  int lo = max(u - hw, 0), hi_key = min(u + hw, s_hi);
+  if (u >= Lr || hi_key < lo) {
+    lo = 0x3fffffff;
+    hi_key = lo;
+  }
+  const unsigned rng = (unsigned)(hi_key - lo);
+  constexpr int kNotInClass = 0x40000000;
+
   Loader<BF16, D, NT> ld;
   ld.fetch(Kp, Vp, row_of_tile(0), tid);
 
   for (int tt = 0; tt < n_tiles; ++tt) {
     ld.store(tile, tid);
+    if (tt >= n_band && tid < TK) {
+      // Position of each global key in this residue's subsequence, or a value
+      // no row's band reaches when the key belongs to another residue class.
+      const int slot = TK * (tt - n_band) + tid;
+      int sp = kNotInClass;
+      if (slot < a.n_glob) {
+        const int off = a.glob[slot] - r;
+        if (off >= 0 && off % d == 0) sp = off / d;
+      }
+      gsub[tid] = sp;
+    }
     __syncthreads();
     if (tt + 1 < n_tiles) ld.fetch(Kp, Vp, row_of_tile(tt + 1), tid);
 
@@ -438,37 +462,37 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
           const bool full = (kb_ == s0 + TK - 1) && (s0 + TK - 1 - ua <= hw) && (ub - s0 <= hw);
           st.scores(tile, lane, s);
           if (!full) {
+            const int base = s0 + 4 * hi - lo;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
-                const int sk = s0 + 32 * kb + block_row(i, hi);
-                const int dd = sk - u;
-                if (sk > s_hi || dd > hw || dd < -hw) s[kb][i] = -INFINITY;
+                const unsigned x = (unsigned)(base + 32 * kb + block_row(i, 0));
+                s[kb][i] = x > rng ? -INFINITY : s[kb][i];
               }
           }
           softmax_accumulate(st, tile, lane, s, a.sl2);
         }
       } else {
         // Global keys, minus those already inside this row's band.
-        const int g0 = TK * (tt - n_band);
-        bool keep[2][16];
+        const int nvalid = min(TK, a.n_glob - TK * (tt - n_band));
+        const unsigned span = 2u * (unsigned)hw;
         bool any = false;
+        unsigned keep = 0;  // bit 16*kb + i
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int slot = g0 + 32 * kb + block_row(i, hi);
-            bool k = false;
-            if (slot < a.n_glob && u < Lr) {
-              const int g = a.glob[slot];
-              const int off = g - r;
-              const bool same_class = off >= 0 && off % d == 0;
-              const int dd = same_class ? off / d - u : 0;
-              k = !(same_class && dd <= hw && dd >= -hw);
+          for (int g = 0; g < 4; ++g) {
+            const int kk0 = 32 * kb + 8 * g + 4 * hi;
+            const int4 sp = *(const int4*)&gsub[kk0];
+            const int spv[4] = {sp.x, sp.y, sp.z, sp.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const bool k = (kk0 + c < nvalid) && u < Lr &&
+                             (unsigned)(spv[c] - u + hw) > span;
+              keep |= (unsigned)k << (16 * kb + 4 * g + c);
+              any |= k;
             }
-            keep[kb][i] = k;
-            any |= k;
           }
         if (__any(any)) {
           st.scores(tile, lane, s);
@@ -476,7 +500,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (!keep[kb][i]) s[kb][i] = -INFINITY;
+              s[kb][i] = ((keep >> (16 * kb + i)) & 1u) ? s[kb][i] : -INFINITY;
           softmax_accumulate(st, tile, lane, s, a.sl2);
         }
       }
@@ -491,7 +515,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Global-row kernel: partials over key chunks, merged by the last arrival.
+// Global-row partial kernel: one (batch-head, row set, key chunk) per workgroup.
 // ---------------------------------------------------------------------------
 
 template <bool BF16, int D, int WAVES>
@@ -501,7 +525,6 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
   constexpr int ROWS = WAVES * kWaveRows;   // global rows per set
   constexpr int REC = D + 4;                // partial record: m, l, 2 pad, acc[D]
   __shared__ Tile<BF16, D> tile;
-  __shared__ int last;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
@@ -571,58 +594,58 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
             make_float4(st.acc[b][4 * g], st.acc[b][4 * g + 1], st.acc[b][4 * g + 2],
                         st.acc[b][4 * g + 3]);
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = atomicAdd(&a.counters[bhs], 1u) == (unsigned)(a.n_chunks - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+}
 
-  // Last arrival: merge every chunk's partial for this set and write O.
-  const float* part0 = a.part + (size_t)bhs * a.n_chunks * ROWS * REC;
-  E* Op = (E*)a.O + base;
-  for (int x = tid; x < ROWS * (D / 4); x += NT) {
-    const int rr = x / (D / 4), dq = x % (D / 4);
-    const int slot = set * ROWS + rr;
-    if (slot >= a.n_glob) continue;
-    float m = kNegInit, l = 0.0f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c = 0; c < a.n_chunks; ++c) {
-      const float* rec = part0 + ((size_t)c * ROWS + rr) * REC;
-      const float mc = rec[0], lc = rec[1];
-      const float4 ac = *(const float4*)(rec + 4 + 4 * dq);
-      const float mn = fmaxf(m, mc);
-      const float s1 = fast_exp2(m - mn), s2 = fast_exp2(mc - mn);
-      l = l * s1 + lc * s2;
-      acc.x = acc.x * s1 + ac.x * s2;
-      acc.y = acc.y * s1 + ac.y * s2;
-      acc.z = acc.z * s1 + ac.z * s2;
-      acc.w = acc.w * s1 + ac.w * s2;
-      m = mn;
-    }
-    const float inv = 1.0f / l;
-    const int row = a.glob[slot];
-    if constexpr (BF16) {
-      bf16x4 o;
-      o[0] = (__bf16)(acc.x * inv); o[1] = (__bf16)(acc.y * inv);
-      o[2] = (__bf16)(acc.z * inv); o[3] = (__bf16)(acc.w * inv);
-      *(bf16x4*)(Op + (size_t)row * D + 4 * dq) = o;
-    } else {
-      *(float4*)(Op + (size_t)row * D + 4 * dq) =
-          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
+// Merge of the global-row partials: one thread per (global row, 4 columns).
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
+  typedef typename ElemT<BF16>::type E;
+  constexpr int REC = D + 4;
+  const int rows = a.rows_per_set;
+  const long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)a.n_bh * a.n_glob * (D / 4);
+  if (x >= total) return;
+  const int dq = (int)(x % (D / 4));
+  const long long rs = x / (D / 4);
+  const int slot = (int)(rs % a.n_glob);
+  const int bh = (int)(rs / a.n_glob);
+  const int set = slot / rows, rr = slot % rows;
+  const float* part0 =
+      a.part + ((size_t)(bh * a.n_sets + set) * a.n_chunks * rows + rr) * REC;
+  float m = kNegInit, l = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = 0; c < a.n_chunks; ++c) {
+    const float* rec = part0 + (size_t)c * rows * REC;
+    const float mc = rec[0], lc = rec[1];
+    const float4 ac = *(const float4*)(rec + 4 + 4 * dq);
+    const float mn = fmaxf(m, mc);
+    const float s1 = fast_exp2(m - mn), s2 = fast_exp2(mc - mn);
+    l = l * s1 + lc * s2;
+    acc.x = acc.x * s1 + ac.x * s2;
+    acc.y = acc.y * s1 + ac.y * s2;
+    acc.z = acc.z * s1 + ac.z * s2;
+    acc.w = acc.w * s1 + ac.w * s2;
+    m = mn;
   }
-  if (tid == 0) atomicExch(&a.counters[bhs], 0u);
+  const float inv = 1.0f / l;
+  E* Op = (E*)a.O + (size_t)bh * a.N * D + (size_t)a.glob[slot] * D + 4 * dq;
+  if constexpr (BF16) {
+    bf16x4 o;
+    o[0] = (__bf16)(acc.x * inv); o[1] = (__bf16)(acc.y * inv);
+    o[2] = (__bf16)(acc.z * inv); o[3] = (__bf16)(acc.w * inv);
+    *(bf16x4*)Op = o;
+  } else {
+    *(float4*)Op = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s) {
   if (n_wg <= 0) return hipSuccess;
+  if (dtype == 1) return launch_band_bf16(D, a, n_wg, s);
   dim3 grid(n_wg), block(kBandWaves * 64);
-  if (dtype == 1 && D == 64) hipLaunchKernelGGL((band_kernel<true, 64>), grid, block, 0, s, a);
-  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((band_kernel<true, 128>), grid, block, 0, s, a);
-  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((band_kernel<false, 64>), grid, block, 0, s, a);
+  if (dtype == 0 && D == 64) hipLaunchKernelGGL((band_kernel<false, 64>), grid, block, 0, s, a);
   else if (dtype == 0 && D == 128) hipLaunchKernelGGL((band_kernel<false, 128>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
@@ -645,6 +668,18 @@ hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg,
   if (dtype == 0 && D == 64) return launch_glob_t<false, 64>(waves, a, n_wg, s);
   if (dtype == 0 && D == 128) return launch_glob_t<false, 128>(waves, a, n_wg, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s) {
+  const long long total = (long long)a.n_bh * a.n_glob * (D / 4);
+  if (total <= 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (dtype == 1 && D == 64) hipLaunchKernelGGL((glob_merge_kernel<true, 64>), grid, block, 0, s, a);
+  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((glob_merge_kernel<true, 128>), grid, block, 0, s, a);
+  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((glob_merge_kernel<false, 64>), grid, block, 0, s, a);
+  else if (dtype == 0 && D == 128) hipLaunchKernelGGL((glob_merge_kernel<false, 128>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace lfattn
