@@ -59,7 +59,8 @@ typedef enum {
   LFATTN_OK = 0,
   LFATTN_EINVAL = 1,      /* bad argument: null/misaligned pointer, size, window,
                              dilation, global index outside [0, N), overlap */
-  LFATTN_EUNSUPPORTED = 2, /* valid but not implemented: D not 64 or 128 */
+  LFATTN_EUNSUPPORTED = 2, /* valid but not implemented: D not 64 or 128, N >= 2^29,
+                             or more than 512 distinct global positions with bf16 */
   LFATTN_ENOMEM = 3,      /* device or host allocation failed */
   LFATTN_EHIP = 4         /* a HIP runtime call or kernel launch failed */
 } lfattn_status;
@@ -77,6 +78,7 @@ typedef enum { LFATTN_F32 = 0, LFATTN_BF16 = 1 } lfattn_dtype;
  *   dilation   H host ints >= 1, or NULL for all 1 (dilated-window bullet).
  *   global_idx n_global host ints in [0, N), any order, repeats allowed (a
  *              position listed twice is global once); NULL if n_global == 0.
+ *              bf16 handles take at most 512 distinct positions.
  *   scale      softmax scale; <= 0 selects 1/sqrt(D) (Eq. (1) of the
  *              Unlimiformer page).  NaN or infinity is EINVAL.
  * Allocates the handle's device tables and workspace on the current device

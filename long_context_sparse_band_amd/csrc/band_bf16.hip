@@ -1,30 +1,37 @@
 // bf16 band kernel for gfx950 (MI355X).
 //
-// One workgroup (4 wavefronts) takes 128*QB consecutive query rows of one
-// (batch, head, dilation residue) and walks the 64-key tiles of their band,
-// then the tiles of gathered global keys.  Each wavefront owns 32*QB rows
-// (QB blocks of 32, one 32x32 MFMA column block each).
+// A workgroup of 4 wavefronts takes 128 consecutive query rows of one (batch,
+// head, dilation residue) and walks the 64-key tiles of their band, then the
+// tiles of gathered global keys.  Each wavefront owns QB blocks of 32 rows
+// (one 32x32 MFMA column block each).  With KS = 2 the workgroup's tile list
+// is split in two halves: wavefronts 0,1 take query blocks 0,1 over the first
+// half and wavefronts 2,3 the same query blocks over the second half; the two
+// partial softmax states of a row are merged through LDS at the end.  This
+// keeps twice as many wavefronts busy on short sequences.
 //
-// Memory path: K and V tiles go global -> LDS with direct loads
-// (global_load_lds_dwordx4) into a ring of NS stages, NS-1 tiles ahead of the
-// one being computed; nothing is staged in registers.  Rows are 16-byte-chunk
-// swizzled so that the MFMA operand reads of 16 consecutive rows hit distinct
-// LDS banks.  V stays row-major: the A operand of O^T += V^T P^T is read with
-// ds_read_b64_tr_b16, whose lane transpose delivers the 8 keys of one value
-// column that a lane feeds to a 32x32x16 k-step.
+// Memory path: the K and V tiles of a step go global -> LDS with direct loads
+// (global_load_lds_dwordx4) into a ring of NS stages; nothing is staged in
+// registers.  Rows are 16-byte-chunk swizzled so that the MFMA operand reads
+// of 16 consecutive rows hit distinct LDS banks.  V stays row-major: the A
+// operand of O^T += V^T P^T is read with ds_read_b64_tr_b16, whose lane
+// transpose delivers the 8 keys of one value column that a lane feeds to a
+// 32x32x16 k-step.  The global positions (and their place in the residue's
+// subsequence) are staged in LDS once, so issuing a global tile never waits
+// on a plain global load.
 //
 // Per tile and wavefront: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on
-// the MFMA rows, queries across lanes, so a lane holds 16 keys of one query);
-// weights exp2(s*scale*log2e - m) against the running maximum m; P rounded to
-// bf16 is already the B operand of the P.V MFMA, and its row sum is taken with
-// v_dot2_f32_bf16 on the packed pairs (the same rounded weights as the
-// numerator).  The maximum is not computed in the common case: a tile whose
-// weights sum past 2^8 on any lane (which includes the first tile, where m
-// starts at -1e30, and any overflow to infinity) is redone against its true
-// maximum, rescaling the accumulators.  That is exact because softmax ignores
-// a constant added to all its inputs (Unlimiformer, section 2.3, footnote 3).
-// 32-key halves of a tile that no row of the wave may score are skipped
-// (no MFMA, no exp); only tiles cut by a band edge evaluate the band predicate.
+// the MFMA rows, queries across lanes, so a lane holds 16 keys of one query;
+// each K read serves the QB query blocks); weights exp2(s*scale*log2e - m)
+// against the running maximum m; P rounded to bf16 is already the B operand
+// of the P.V MFMA, and its row sum is taken with v_dot2_f32_bf16 on the packed
+// pairs (the same rounded weights as the numerator).  The maximum is not
+// computed in the common case: a tile whose weights sum past 2^8 on any lane
+// (including the first tile, where m starts at -1e30, and any overflow) is
+// redone against its true maximum, rescaling the accumulators.  That is exact
+// because softmax ignores a constant added to all its inputs (Unlimiformer,
+// section 2.3, footnote 3).  32-key halves of a tile that no row of the wave
+// may score are skipped; only halves cut by a band edge evaluate the band
+// predicate.
 //
 // The math is Eq. (1) of the Unlimiformer page (section 2.3) over the pattern
 // of the Ultralytics glossary page "Longformer" (section on how the attention
@@ -67,6 +74,22 @@ __device__ __forceinline__ float pair_max(float x) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ds_read_b64_tr_b16 issued as inline assembly.  The compiler's builtin for it
+// is treated as possibly aliasing the in-flight direct-to-LDS loads and gets a
+// full vmcnt(0) wait in front of it, which would drain the load ring; the
+// ring's own waits already order these reads.  The result must not be used
+// before lgkm_wait() has been passed the same registers.
+__device__ __forceinline__ s16x4 ds_read_tr16(unsigned lds_addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr));
+  return r;
+}
+__device__ __forceinline__ void lgkm_wait(s16x4& a0, s16x4& a1, s16x4& a2, s16x4& a3,
+                                          s16x4& a4, s16x4& a5, s16x4& a6, s16x4& a7) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7));
+}
+
 // Key of register i (0..15) of a 32x32 MFMA result block for lane half hi.
 __device__ __forceinline__ constexpr int block_row(int i, int hi) {
   return 8 * (i >> 2) + 4 * hi + (i & 3);
@@ -80,26 +103,39 @@ struct Geo {
   static constexpr int RPI = 1024 / RB;     // rows one wave-wide direct load fills
   static constexpr int NI = TK / RPI / 4;   // direct loads per wave per matrix and tile
   static constexpr int MAT = TK * RB;       // bytes of one K (or V) tile
-  // Physical chunk of logical chunk c in row `row` (an involution).
+  // Physical chunk of logical chunk c in row `row` (an involution).  Only the
+  // low row bits enter, so rows 32 apart (the two halves of a tile) and the
+  // 16-row k-steps of the transposed reads share one lane pattern.
   static __device__ __forceinline__ int swz(int row, int c) {
     if constexpr (D == 64) return c ^ ((row >> 1) & 7);
     else return c ^ (row & 15);
   }
 };
 
-template <int D, int NS>
+constexpr int kGlobCap = kMaxGlobalBf16;  // global positions staged in LDS
+
+template <int D, int KS, int NS>
 struct Smem {
-  unsigned char st[NS][2 * Geo<D>::MAT];
-  int gsub[NS][TK];
+  unsigned char st[NS][KS][2 * Geo<D>::MAT];
+  int gpos[kGlobCap];
+  int gsp[kGlobCap];
 };
 
-template <int D, int QB, int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void band_bf16_kernel(BandArgs a) {
+template <int D, int QB, int KS, int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void band_bf16_kernel(BandArgs a) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(16))) Smem<D, NS> sm;
+  constexpr int RW = 32 * QB;        // rows per wave
+  constexpr int QBLKS = 4 / KS;      // query blocks per workgroup
+  constexpr int BM = RW * QBLKS;     // rows per workgroup
+  constexpr int L = KS * 2 * G::NI;  // direct loads per wave per step
+  static_assert(BM == 128, "a workgroup covers 128 rows");
+  __shared__ __attribute__((aligned(16))) Smem<D, KS, NS> sm;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int qblk = wave % QBLKS, kh = wave / QBLKS;
   const BandWork w = a.work[blockIdx.x];
   const int h = w.bh % a.H;
   const int d = a.dil[h];
@@ -109,19 +145,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const unsigned short* Qp = (const unsigned short*)a.Q + base;
   const unsigned short* Kp = (const unsigned short*)a.K + base;
   const unsigned short* Vp = (const unsigned short*)a.V + base;
-  constexpr int BM = 128 * QB;
+  const int n_glob = a.n_glob;
+
+  // Global positions, and where each sits in this residue's subsequence (or a
+  // value no band reaches), staged once.
+  for (int x = tid; x < n_glob; x += 256) {
+    const int g = a.glob[x];
+    const int off = g - r;
+    sm.gpos[x] = g;
+    sm.gsp[x] = (off >= 0 && off % d == 0) ? off / d : kNotInClass;
+  }
 
   // Rows of this wave: subsequence positions ua .. ub.
-  const int ua = t0 + 32 * QB * wave;
-  const int ub = min(ua + 32 * QB - 1, Lr - 1);
+  const int ua = t0 + RW * qblk;
+  const int ub = min(ua + RW - 1, Lr - 1);
   const bool live = ua < Lr;
+  const int s_lo = max(0, t0 - hw);
+  const int s_hi = min(Lr - 1, t0 + BM - 1 + hw);
 
   // Q operand (B of S^T = K Q^T): Q[row][16ks + 8hi + 0..7].
   bf16x8 q[QB][D / 16];
   int u[QB], lo[QB];
   unsigned rng[QB];
-  const int s_lo = max(0, t0 - hw);
-  const int s_hi = min(Lr - 1, t0 + BM - 1 + hw);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     u[qb] = ua + 32 * qb + l32;
@@ -151,62 +196,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   const int n_band = (s_hi - s_lo) / TK + 1;
-  const int n_gt = (a.n_glob + TK - 1) / TK;
-  const int n_tiles = n_band + n_gt;
+  const int n_tiles = n_band + (n_glob + TK - 1) / TK;
+  const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles kh*n_steps + j
 
-  // Issue the direct loads of tile j into stage sidx.
+  __syncthreads();  // staged global positions visible
+
+  // Issue the direct loads of step j into stage sidx: exactly L per wave, so
+  // the ring's vmcnt arithmetic holds (tiles past the end load a real row).
   auto issue = [&](int j, int sidx) {
-    LDS_AS unsigned char* st = (LDS_AS unsigned char*)sm.st[sidx];
-    const bool band = j < n_band;
-    const int s0 = s_lo + TK * j, g0 = TK * (j - n_band);
 #pragma unroll
-    for (int e = 0; e < G::NI; ++e) {
-      const int qd = wave + 4 * e;
-      const int row = G::RPI * qd + lane / G::CPR;
-      const int c = G::swz(row, lane % G::CPR);
-      int grow;
-      if (band) {
-        const int s = min(s0 + row, s_hi);  // rows past the band end repeat a real row
-        grow = r + d * s;
-      } else {
-        const int slot = min(g0 + row, a.n_glob - 1);
-        grow = a.glob[slot];
+    for (int hh = 0; hh < KS; ++hh) {
+      const int tj = hh * n_steps + j;
+      LDS_AS unsigned char* st = (LDS_AS unsigned char*)sm.st[sidx][hh];
+#pragma unroll
+      for (int e = 0; e < G::NI; ++e) {
+        const int qd = wave + 4 * e;
+        const int row = G::RPI * qd + lane / G::CPR;
+        const int c = G::swz(row, lane % G::CPR);
+        int grow;
+        if (tj < n_band) grow = r + d * min(s_lo + TK * tj + row, s_hi);
+        else if (tj < n_tiles) grow = sm.gpos[min(TK * (tj - n_band) + row, n_glob - 1)];
+        else grow = r;
+        const size_t off = (size_t)grow * D + 8 * c;
+        __builtin_amdgcn_global_load_lds((const void*)(Kp + off), (LDS_AS void*)(st + 1024 * qd), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(Vp + off), (LDS_AS void*)(st + G::MAT + 1024 * qd), 16, 0, 0);
       }
-      const size_t off = (size_t)grow * D + 8 * c;
-      __builtin_amdgcn_global_load_lds((const void*)(Kp + off), (LDS_AS void*)(st + 1024 * qd), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(Vp + off), (LDS_AS void*)(st + G::MAT + 1024 * qd), 16, 0, 0);
-    }
-    if (!band && tid < TK) {
-      // Subsequence position of each global key in this residue class (or a
-      // value no band reaches).
-      const int slot = g0 + tid;
-      int sp = kNotInClass;
-      if (slot < a.n_glob) {
-        const int off = a.glob[slot] - r;
-        if (off >= 0 && off % d == 0) sp = off / d;
-      }
-      sm.gsub[sidx][tid] = sp;
     }
   };
 
-  // Prologue: tiles 0 .. NS-2.
+  // Per-lane LDS byte offsets of the MFMA operands inside a tile; the k-step
+  // and the 32-key half enter as immediate offsets.
+  unsigned koff[D / 16];
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (j < n_tiles) issue(j, j);
-
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * G::RB + 16 * G::swz(l32, 2 * ks + hi);
+  const int g16 = lane >> 4, t16 = lane & 15;
+  unsigned voff[D / 32][2];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) {
+    const int dcol = 32 * b + 16 * (g16 & 1) + 4 * (t16 & 3);
+    const int c = dcol >> 3, half = (dcol >> 2) & 1;
+    const int row0 = 4 * (g16 >> 1) + (t16 >> 2), row1 = row0 + 8;
+    voff[b][0] = G::MAT + row0 * G::RB + 16 * G::swz(row0, c) + 8 * half;
+    voff[b][1] = G::MAT + row1 * G::RB + 16 * G::swz(row1, c) + 8 * half;
+  }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int t = 0; t < n_tiles; ++t) {
-    // Wait for this wave's loads of tile t (the loads of up to NS-2 later
-    // tiles may stay in flight), then for every wave's.
-    if (t + NS - 2 < n_tiles) wait_vm_lgkm0<2 * G::NI * (NS - 2)>();
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_steps) issue(j, j);
+
+  for (int j = 0; j < n_steps; ++j) {
+    // Wait for this wave's loads of step j (those of up to NS-2 later steps
+    // may stay in flight), then for every wave's.
+    if (j + NS - 2 < n_steps) wait_vm_lgkm0<L * (NS - 2)>();
     else wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
-    if (t + NS - 1 < n_tiles) issue(t + NS - 1, (t + NS - 1) % NS);
+    if (j + NS - 1 < n_steps) issue(j + NS - 1, (j + NS - 1) % NS);
 
-    if (!live) continue;
-    const int sidx = t % NS;
-    const LDS_AS unsigned char* st = (const LDS_AS unsigned char*)sm.st[sidx];
+    const int t = kh * n_steps + j;
+    if (!live || t >= n_tiles) continue;
+    const LDS_AS unsigned char* st = (const LDS_AS unsigned char*)sm.st[j % NS][kh];
+    const unsigned sbase = (unsigned)(uintptr_t)st;
     const bool band = t < n_band;
 
     // Which 32-key halves of the tile any row of this wave scores, and which
@@ -223,7 +273,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     } else {
       const int g0 = TK * (t - n_band);
-      const int nvalid = min(TK, a.n_glob - g0);
+      const int nvalid = min(TK, n_glob - g0);
       const unsigned span = 2u * (unsigned)hw;
       bool any[2] = {false, false};
 #pragma unroll
@@ -234,12 +284,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int kk0 = 32 * kb + 8 * g4 + 4 * hi;
-            const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsub[sidx][kk0];
-            const int spv[4] = {sp[0], sp[1], sp[2], sp[3]};
+            const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsp[min(g0 + kk0, kGlobCap - 4)];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const bool k = (kk0 + c < nvalid) && u[qb] < Lr &&
-                             (unsigned)(spv[c] - u[qb] + hw) > span;
+                             (unsigned)(sp[c] - u[qb] + hw) > span;
               bits |= (unsigned)k << (4 * g4 + c);
             }
           }
@@ -254,126 +303,168 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (!act[0] && !act[1]) continue;
 
-    // S^T = K Q^T for the active halves (each K read serves all QB blocks).
-    f32x16 S[QB][2];
+    // Each active 32-key half goes through scores, weights and P.V in turn.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (!act[kb]) continue;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) S[qb][kb] = f32x16{};
-      const int kk = 32 * kb + l32;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 kv = *(const LDS_AS bf16x8*)(st + kk * G::RB + 16 * G::swz(kk, 2 * ks + hi));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          S[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, q[qb][ks], S[qb][kb], 0, 0, 0);
-      }
-    }
 
-    // Masks.
+      // S^T = K Q^T for this half (each K read serves all QB query blocks),
+      // then the band or global mask.
+      f32x16 S[QB];
+      {
+        bf16x8 kv[D / 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!act[kb] || !edge[kb]) continue;
+        for (int ks = 0; ks < D / 16; ++ks)
+          kv[ks] = *(const LDS_AS bf16x8*)(st + koff[ks] + 32 * kb * G::RB);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if (band) {
-          const int basek = s_lo + TK * t + 32 * kb + 4 * hi - lo[qb];
+        for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const unsigned x = (unsigned)(basek + block_row(i, 0));
-            S[qb][kb][i] = x > rng[qb] ? -INFINITY : S[qb][kb][i];
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks], q[qb][ks], S[qb], 0, 0, 0);
+      }
+      if (edge[kb]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          if (band) {
+            const int basek = s_lo + TK * t + 32 * kb + 4 * hi - lo[qb];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const unsigned x = (unsigned)(basek + block_row(i, 0));
+              S[qb][i] = x > rng[qb] ? -INFINITY : S[qb][i];
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              S[qb][i] = ((keep[qb][kb] >> i) & 1u) ? S[qb][i] : -INFINITY;
           }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            S[qb][kb][i] = ((keep[qb][kb] >> i) & 1u) ? S[qb][kb][i] : -INFINITY;
         }
       }
-    }
 
-    // Weights, packed to bf16 (the B operand of P.V), and their row sums.
-    unsigned P[QB][2][8];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      auto weights = [&](float mq) {
+      // Weights, packed to bf16 (the B operand of P.V), and their row sums.
+      unsigned P[QB][8];
+      float ls[QB];
+      auto weights = [&](int qb, float mq) {
         float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (!act[kb]) continue;
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            f32x2 pf;
-            pf[0] = fast_exp2(fmaf(S[qb][kb][i], a.sl2, -mq));
-            pf[1] = fast_exp2(fmaf(S[qb][kb][i + 1], a.sl2, -mq));
-            const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
-            P[qb][kb][i / 2] = __builtin_bit_cast(unsigned, pb);
-            if (i & 2) s1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s1, false);
-            else s0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s0, false);
-          }
+        for (int i = 0; i < 16; i += 2) {
+          f32x2 pf;
+          pf[0] = fast_exp2(fmaf(S[qb][i], a.sl2, -mq));
+          pf[1] = fast_exp2(fmaf(S[qb][i + 1], a.sl2, -mq));
+          const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+          P[qb][i / 2] = __builtin_bit_cast(unsigned, pb);
+          if (i & 2) s1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s1, false);
+          else s0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s0, false);
         }
-        return s0 + s1;
+        ls[qb] = s0 + s1;
       };
-      float ls = weights(m[qb]);
-      if (__any(!(ls <= kSumLimit))) {
-        // Move the running maximum to this tile's maximum and redo it.
-        float mx = -INFINITY;
+      bool redo = false;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (!act[kb]) continue;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][kb][i]);
-        }
-        const float mn = fmaxf(m[qb], pair_max(mx) * a.sl2);
-        const float alpha = fast_exp2(m[qb] - mn);
-        l[qb] *= alpha;
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[qb][b][i] *= alpha;
-        m[qb] = mn;
-        ls = weights(mn);
+      for (int qb = 0; qb < QB; ++qb) {
+        weights(qb, m[qb]);
+        redo |= !(ls[qb] <= kSumLimit);
       }
-      l[qb] += ls;
-    }
-
-    // O^T += V^T P^T.  V^T operand for k-step ks (keys 16ks..16ks+15) and
-    // column block b, read transposed: lane L gets keys 16ks + 4*(L/32) + j
-    // (j < 4) and 16ks + 8 + 4*(L/32) + (j-4) (j >= 4) of column 32b + L%32,
-    // the same key order as the P^T registers 8*(ks%2) .. +7.
-    const int g16 = lane >> 4, t16 = lane & 15;
+      if (__builtin_expect(__any(redo), 0)) {
+        // Move each running maximum up to this half's maximum and redo it.
+        // (The empty volatile statement keeps this rare path a real branch:
+        // executed unconditionally it would double the exps of every tile.)
+        asm volatile("" ::: "memory");
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!act[kb]) continue;
+        for (int qb = 0; qb < QB; ++qb) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
+          const float mn = fmaxf(m[qb], pair_max(mx) * a.sl2);
+          const float alpha = fast_exp2(m[qb] - mn);
+          l[qb] *= alpha;
+#pragma unroll
+          for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[qb][b][i] *= alpha;
+          m[qb] = mn;
+          weights(qb, mn);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb];
+
+      // O^T += V^T P^T.  V^T operand for k-step ks (keys 16ks..16ks+15) and
+      // column block b, read transposed: lane L gets keys 16ks + 4*(L/32) + j
+      // (j < 4) and 16ks + 8 + 4*(L/32) + (j-4) (j >= 4) of column 32b + L%32,
+      // the same key order as the P^T registers 8*(ks%2) .. +7.
+      constexpr int NB = D / 32;
+      s16x4 vr[2][4][2];  // [k2][b][row0/row1]; b < NB used
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr)
+            vr[k2][b][rr] = ds_read_tr16(sbase + voff[b][rr] + (16 * (2 * kb + k2)) * G::RB);
+      if constexpr (NB == 2) {
+        lgkm_wait(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1],
+                  vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1]);
+      } else {
+        lgkm_wait(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1],
+                  vr[0][2][0], vr[0][2][1], vr[0][3][0], vr[0][3][1]);
+        lgkm_wait(vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1],
+                  vr[1][2][0], vr[1][2][1], vr[1][3][0], vr[1][3][1]);
+      }
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const int ks = 2 * kb + k2;
-        const int row0 = 16 * ks + 4 * (g16 >> 1) + (t16 >> 2);
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const int dcol = 32 * b + 16 * (g16 & 1) + 4 * (t16 & 3);
-          const int c = dcol >> 3, half = (dcol >> 2) & 1;
-          const LDS_AS unsigned char* vb = st + G::MAT;
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (LDS_AS s16x4*)(vb + row0 * G::RB + 16 * G::swz(row0, c) + 8 * half));
-          const int row1 = row0 + 8;
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (LDS_AS s16x4*)(vb + row1 * G::RB + 16 * G::swz(row1, c) + 8 * half));
+        for (int b = 0; b < NB; ++b) {
           const bf16x8 va = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+              bf16x8, __builtin_shufflevector(vr[k2][b][0], vr[k2][b][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            const unsigned* pp = &P[qb][kb][4 * k2];
-            const uint4 pu = make_uint4(pp[0], pp[1], pp[2], pp[3]);
-            const bf16x8 pbv = __builtin_bit_cast(bf16x8, pu);
-            acc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbv, acc[qb][b], 0, 0, 0);
+            const uint4 pu = make_uint4(P[qb][4 * k2], P[qb][4 * k2 + 1], P[qb][4 * k2 + 2],
+                                        P[qb][4 * k2 + 3]);
+            acc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                va, __builtin_bit_cast(bf16x8, pu), acc[qb][b], 0, 0, 0);
           }
         }
       }
     }
   }
 
-  if (!live) return;
+  if constexpr (KS == 2) {
+    // Merge the second key half's state into the first through LDS (the
+    // stage buffers are free: every load was waited for in the last step).
+    constexpr int PER = QB * (2 + D / 2);
+    static_assert((size_t)2 * 64 * PER * 4 <= sizeof(sm.st), "merge area");
+    __syncthreads();
+    float* mine = (float*)&sm.st[0][0][0] + ((size_t)qblk * 64 + lane) * PER;
+    if (kh == 1 && live) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        mine[qb * (2 + D / 2)] = m[qb];
+        mine[qb * (2 + D / 2) + 1] = l[qb];
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mine[qb * (2 + D / 2) + 2 + 16 * b + i] = acc[qb][b][i];
+      }
+    }
+    __syncthreads();
+    if (kh == 1 || !live) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m1 = mine[qb * (2 + D / 2)], l1 = mine[qb * (2 + D / 2) + 1];
+      const float mn = fmaxf(m[qb], m1);
+      const float a0 = fast_exp2(m[qb] - mn), a1 = fast_exp2(m1 - mn);
+      l[qb] = l[qb] * a0 + l1 * a1;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[qb][b][i] = acc[qb][b][i] * a0 + mine[qb * (2 + D / 2) + 2 + 16 * b + i] * a1;
+    }
+  } else {
+    if (!live) return;
+  }
+
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = pair_sum(l[qb]);
@@ -396,13 +487,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-int band_bf16_rows_per_wg(int D) { return D == 64 ? 128 : 128; }
+int band_bf16_global_cap() { return kGlobCap; }
 
 hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s) {
   if (n_wg <= 0) return hipSuccess;
+  if (a.n_glob > kGlobCap) return hipErrorInvalidValue;
   dim3 grid(n_wg), block(256);
-  if (D == 64) hipLaunchKernelGGL((band_bf16_kernel<64, 1, 3>), grid, block, 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((band_bf16_kernel<128, 1, 2>), grid, block, 0, s, a);
+  if (D == 64) hipLaunchKernelGGL((band_bf16_kernel<64, 2, 2, 2>), grid, block, 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((band_bf16_kernel<128, 1, 1, 2>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -146,6 +146,10 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   c->glob.assign(global_idx, global_idx + n_global);
   std::sort(c->glob.begin(), c->glob.end());
   c->glob.erase(std::unique(c->glob.begin(), c->glob.end()), c->glob.end());
+  if (dtype == LFATTN_BF16 && (int)c->glob.size() > lfattn::kMaxGlobalBf16) {
+    delete c;
+    return LFATTN_EUNSUPPORTED;
+  }
   std::vector<unsigned char> isg(N, 0);
   for (int g : c->glob) isg[g] = 1;
 

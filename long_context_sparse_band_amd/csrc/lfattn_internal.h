@@ -13,6 +13,8 @@ constexpr int kWaveRows = 32;
 // Waves per band workgroup; a band workgroup covers kBandWaves * 32 query rows.
 constexpr int kBandWaves = 4;
 constexpr int kBandRows = kBandWaves * kWaveRows;
+// The bf16 band kernel stages the global positions in LDS; this many at most.
+constexpr int kMaxGlobalBf16 = 512;
 
 // One band workgroup's work: batch-head bh, dilation residue r, and the first
 // position t0 (in the residue's subsequence r, r+d, r+2d, ...) of its rows.
