@@ -121,6 +121,213 @@ struct Smem {
   int gsp[kGlobCap];
 };
 
+// Kinds of a 32-key half of a tile for one wavefront.
+constexpr int kOff = 0;   // no row of the wave scores it
+constexpr int kFull = 1;  // every row scores every key
+constexpr int kEdge = 2;  // cut by a band edge: per-pair band predicate
+constexpr int kGlob = 3;  // gathered global keys: per-pair keep bits
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgValu = 0x2, kSgMfma = 0x8, kSgDsRead = 0x100, kSgTrans = 0x400;
+
+// One 16-byte direct global -> LDS load: lane i's 16 bytes land at LDS byte
+// address lds + 16*i.  Written as inline assembly so that the compiler does
+// not treat every later LDS read as depending on it (which made it drain all
+// outstanding loads before the transposed reads); the ring's explicit waits
+// order the accesses.
+__device__ __forceinline__ void dma16(const void* gaddr, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(gaddr)
+               : "memory", "m0");
+}
+
+// Per-wavefront state: queries, accumulators, softmax state, band intervals,
+// and the per-lane LDS offsets of the MFMA operands inside a tile.
+template <int D, int QB>
+struct Wave {
+  bf16x8 q[QB][D / 16];   // B operand of S^T = K Q^T: Q[row][16ks + 8hi + 0..7]
+  f32x16 acc[QB][D / 32]; // O^T: d = 32b + block_row(i, hi), query = lane % 32
+  float m[QB], l[QB];
+  int lo[QB];             // band keys of a row: subsequence positions lo .. lo + rng
+  unsigned rng[QB];
+  int u[QB];              // subsequence position of the lane's row (>= Lr: none)
+  int Lr;                 // length of the residue's subsequence
+  int hw;                 // band half-width
+  unsigned gsp;           // LDS address of the staged subsequence positions of G
+  unsigned koff[D / 16];  // K operand, k-step ks (the half adds 32 rows)
+  unsigned voff[D / 32][2];  // V^T operand, column block b, rows +0 / +8
+  float sl2;
+  int hi;
+};
+
+// S^T for one half (kb): MFMAs on the K rows 32kb .. 32kb+31 of the tile.
+template <int D, int QB, int KB>
+__device__ __forceinline__ void half_scores(const Wave<D, QB>& w, unsigned sbase, f32x16 (&S)[QB]) {
+  using G = Geo<D>;
+  bf16x8 kv[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    kv[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(sbase + w.koff[ks] + 32 * KB * G::RB);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks], w.q[qb][ks], S[qb], 0, 0, 0);
+}
+
+// Mask of one half.  kEdge: the band predicate, key in [lo, lo + rng].
+// kGlob (gathered global keys g0 + kk): keep a key unless the row has no
+// valid slot there or the key already lies in the row's band (its position
+// in the residue's subsequence is within hw of the row's).  kTail: keep keys
+// below the end `s0` of a key range.
+constexpr int kTail = 4;
+template <int D, int QB, int KB, int KIND>
+__device__ __forceinline__ void half_mask(const Wave<D, QB>& w, int s0, f32x16 (&S)[QB],
+                                          int nvalid = 0) {
+  if constexpr (KIND == kEdge) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int basek = s0 + 32 * KB + 4 * w.hi - w.lo[qb];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const unsigned x = (unsigned)(basek + block_row(i, 0));
+        S[qb][i] = x > w.rng[qb] ? -INFINITY : S[qb][i];
+      }
+    }
+  } else if constexpr (KIND == kGlob) {
+    const unsigned span = 2u * (unsigned)w.hw;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int kk0 = 32 * KB + 8 * g4 + 4 * w.hi;
+      const i32x4 sp = *(const LDS_AS i32x4*)(uintptr_t)(w.gsp + 4 * (s0 + kk0));
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const bool keep = (kk0 + c < nvalid) && w.u[qb] < w.Lr &&
+                            (unsigned)(sp[c] - w.u[qb] + w.hw) > span;
+          S[qb][4 * g4 + c] = keep ? S[qb][4 * g4 + c] : -INFINITY;
+        }
+    }
+  } else if constexpr (KIND == kTail) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        S[qb][i] = 32 * KB + block_row(i, w.hi) < s0 ? S[qb][i] : -INFINITY;
+  }
+}
+
+// Weights of one half, packed to bf16 pairs, with their per-lane sums.
+template <int D, int QB>
+__device__ __forceinline__ void half_weights(const Wave<D, QB>& w, const f32x16 (&S)[QB],
+                                             unsigned (&P)[QB][8], float (&ls)[QB]) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      f32x2 pf;
+      pf[0] = fast_exp2(fmaf(S[qb][i], w.sl2, -w.m[qb]));
+      pf[1] = fast_exp2(fmaf(S[qb][i + 1], w.sl2, -w.m[qb]));
+      const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+      P[qb][i / 2] = __builtin_bit_cast(unsigned, pb);
+      if (i & 2) s1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s1, false);
+      else s0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s0, false);
+    }
+    ls[qb] = s0 + s1;
+  }
+}
+
+// Accept a half's weights, or (rarely) move the running maxima up to the
+// half's maximum, rescale the accumulators and redo the weights.
+template <int D, int QB>
+__device__ __forceinline__ void half_accept(Wave<D, QB>& w, const f32x16 (&S)[QB],
+                                            unsigned (&P)[QB][8], float (&ls)[QB]) {
+  bool redo = false;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) redo |= !(ls[qb] <= kSumLimit);
+  if (__builtin_expect(__any(redo), 0)) {
+    asm volatile("" ::: "memory");  // keep this a real branch
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
+      const float mn = fmaxf(w.m[qb], pair_max(mx) * w.sl2);
+      const float alpha = fast_exp2(w.m[qb] - mn);
+      w.l[qb] *= alpha;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.acc[qb][b][i] *= alpha;
+      w.m[qb] = mn;
+    }
+    half_weights(w, S, P, ls);
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) w.l[qb] += ls[qb];
+}
+
+// O^T += V^T P^T for one half.  V^T operand for k-step ks (keys
+// 16ks..16ks+15) and column block b, read transposed: lane L gets keys
+// 16ks + 4*(L/32) + j (j < 4) and 16ks + 8 + 4*(L/32) + (j-4) (j >= 4) of
+// column 32b + L%32, the key order of the P^T registers 8*(ks%2) .. +7.
+template <int D, int QB, int KB>
+__device__ __forceinline__ void half_pv(Wave<D, QB>& w, unsigned sbase, const unsigned (&P)[QB][8]) {
+  using G = Geo<D>;
+  constexpr int NB = D / 32;
+  bf16x8 va[2][NB];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const unsigned roff = (16 * (2 * KB + k2)) * G::RB;
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS s16x4*)(uintptr_t)(sbase + w.voff[b][0] + roff));
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS s16x4*)(uintptr_t)(sbase + w.voff[b][1] + roff));
+      va[k2][b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const uint4 pu = make_uint4(P[qb][4 * k2], P[qb][4 * k2 + 1], P[qb][4 * k2 + 2],
+                                    P[qb][4 * k2 + 3]);
+        w.acc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            va[k2][b], __builtin_bit_cast(bf16x8, pu), w.acc[qb][b], 0, 0, 0);
+      }
+}
+
+// One tile for one wavefront, halves of kinds K0 and K1, one half after the
+// other: scores, mask, weights, (rare) rescale, P.V.
+template <int D, int QB, int KB, int KIND>
+__device__ __forceinline__ void half(Wave<D, QB>& w, unsigned sbase, int s0, int nvalid) {
+  f32x16 S[QB];
+  unsigned P[QB][8];
+  float ls[QB];
+  half_scores<D, QB, KB>(w, sbase, S);
+  half_mask<D, QB, KB, KIND>(w, s0, S, nvalid);
+  half_weights(w, S, P, ls);
+  half_accept(w, S, P, ls);
+  half_pv<D, QB, KB>(w, sbase, P);
+}
+
+// s0: first key position of the tile (kEdge), first slot of G (kGlob), or
+// number of valid keys (kTail); nvalid: valid slots (kGlob).
+template <int D, int QB, int K0, int K1>
+__device__ __forceinline__ void tile(Wave<D, QB>& w, unsigned sbase, int s0, int nvalid = 0) {
+  if constexpr (K0 != kOff) half<D, QB, 0, K0>(w, sbase, s0, nvalid);
+  if constexpr (K1 != kOff) half<D, QB, 1, K1>(w, sbase, s0, nvalid);
+}
+
 template <int D, int QB, int KS, int NS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void band_bf16_kernel(BandArgs a) {
@@ -485,9 +692,135 @@ void band_bf16_kernel(BandArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Global-row partials (bf16): the rows of global tokens score every key.  One
+// wavefront per workgroup takes QB blocks of 32 global rows of one (batch,
+// head) and one chunk of keys, streams the chunk's 64-key tiles through its
+// own LDS ring with the same tile code as the band kernel (no band mask; the
+// ragged last tile uses keep bits), and writes a partial record (m, l, acc)
+// per row.  glob_merge_kernel combines the chunks after the band kernel.
+// ---------------------------------------------------------------------------
+template <int D, int QB, int NS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void glob_bf16_kernel(GlobArgs a) {
+  using G = Geo<D>;
+  constexpr int ROWS = 32 * QB;
+  constexpr int LPT = TK / G::RPI;  // direct loads per matrix per tile (one wave)
+  constexpr int L = 2 * LPT;
+  constexpr int REC = D + 4;
+  __shared__ __attribute__((aligned(16))) unsigned char st[NS][2 * G::MAT];
+
+  const int lane = threadIdx.x, hi = lane >> 5, l32 = lane & 31;
+  const int chunk = blockIdx.x % a.n_chunks;
+  const int bhs = blockIdx.x / a.n_chunks;
+  const int bh = bhs / a.n_sets, set = bhs % a.n_sets;
+  const int N = a.N;
+  const size_t base = (size_t)bh * N * D;
+  const unsigned short* Qp = (const unsigned short*)a.Q + base;
+  const unsigned short* Kp = (const unsigned short*)a.K + base;
+  const unsigned short* Vp = (const unsigned short*)a.V + base;
+  const int c0 = chunk * a.chunk_keys;
+  const int c1 = min(N, c0 + a.chunk_keys);
+  const int n_t = (c1 - c0 + TK - 1) / TK;
+
+  Wave<D, QB> w;
+  w.sl2 = a.sl2;
+  w.hi = hi;
+  int slot[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    slot[qb] = set * ROWS + 32 * qb + l32;
+    const bool ok = slot[qb] < a.n_glob;
+    const size_t row = ok ? (size_t)a.glob[slot[qb]] : 0;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      w.q[qb][ks] = *(const bf16x8*)(Qp + row * D + 16 * ks + 8 * hi);
+      if (!ok) w.q[qb][ks] = bf16x8{};
+    }
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) w.acc[qb][b] = f32x16{};
+    w.m[qb] = kNegInit;
+    w.l[qb] = 0.0f;
+    w.lo[qb] = 0;
+    w.rng[qb] = 0;
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) w.koff[ks] = l32 * G::RB + 16 * G::swz(l32, 2 * ks + hi);
+  {
+    const int g16 = lane >> 4, t16 = lane & 15;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+      const int dcol = 32 * b + 16 * (g16 & 1) + 4 * (t16 & 3);
+      const int c = dcol >> 3, half = (dcol >> 2) & 1;
+      const int row0 = 4 * (g16 >> 1) + (t16 >> 2), row1 = row0 + 8;
+      w.voff[b][0] = G::MAT + row0 * G::RB + 16 * G::swz(row0, c) + 8 * half;
+      w.voff[b][1] = G::MAT + row1 * G::RB + 16 * G::swz(row1, c) + 8 * half;
+    }
+  }
+
+  // Direct loads of tile j into stage sidx (rows past the chunk repeat its
+  // last key; they are masked).
+  auto issue = [&](int j, int sidx) {
+    const unsigned sb = (unsigned)(uintptr_t)(LDS_AS void*)st[sidx];
+#pragma unroll
+    for (int qd = 0; qd < LPT; ++qd) {
+      const int row = G::RPI * qd + lane / G::CPR;
+      const int c = G::swz(row, lane % G::CPR);
+      const size_t off = (size_t)min(c0 + TK * j + row, c1 - 1) * D + 8 * c;
+      dma16(Kp + off, sb + 1024 * qd);
+      dma16(Vp + off, sb + G::MAT + 1024 * qd);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_t) issue(j, j);
+
+  for (int j = 0; j < n_t; ++j) {
+    if (j + NS - 2 < n_t) wait_vm_lgkm0<L * (NS - 2)>();
+    else wait_vm_lgkm0<0>();
+    if (j + NS - 1 < n_t) issue(j + NS - 1, (j + NS - 1) % NS);
+    const unsigned sbase = (unsigned)(uintptr_t)(LDS_AS void*)st[j % NS];
+    const int j0 = c0 + TK * j;
+    if (j0 + TK <= c1) tile<D, QB, kFull, kFull>(w, sbase, 0);
+    else tile<D, QB, kTail, kTail>(w, sbase, c1 - j0);
+  }
+
+  // Partial record of each row for this chunk.
+  float* part = a.part + ((size_t)bhs * a.n_chunks + chunk) * ROWS * REC;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = pair_sum(w.l[qb]);
+    if (slot[qb] >= a.n_glob) continue;
+    float* rec = part + (size_t)(32 * qb + l32) * REC;
+    if (hi == 0) {
+      rec[0] = w.m[qb];
+      rec[1] = lt;
+    }
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(float4*)(rec + 4 + 32 * b + 8 * g4 + 4 * hi) =
+            make_float4(w.acc[qb][b][4 * g4], w.acc[qb][b][4 * g4 + 1], w.acc[qb][b][4 * g4 + 2],
+                        w.acc[qb][b][4 * g4 + 3]);
+  }
+}
+
 }  // namespace
 
 int band_bf16_global_cap() { return kGlobCap; }
+
+int glob_bf16_rows_per_set(int) { return 32; }  // one 32x32 MFMA column block
+
+hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s) {
+  if (n_wg <= 0) return hipSuccess;
+  if (a.rows_per_set != 32) return hipErrorInvalidValue;
+  dim3 grid(n_wg), block(64);
+  if (D == 64) hipLaunchKernelGGL((glob_bf16_kernel<64, 1, 3>), grid, block, 0, s, a);
+  else if (D == 128) hipLaunchKernelGGL((glob_bf16_kernel<128, 1, 2>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s) {
   if (n_wg <= 0) return hipSuccess;

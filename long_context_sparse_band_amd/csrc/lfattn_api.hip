@@ -20,7 +20,7 @@ namespace {
 
 constexpr int kMaxTimedForwards = 4096;
 constexpr int kXcds = 8;           // MI355X: workgroups go round-robin over 8 XCDs
-constexpr int kMaxChunks = 16;     // key chunks per global row set (merge cost)
+constexpr int kMaxChunks = lfattn::kMergeBatch;  // key chunks per global row set
 constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
 constexpr long long kMaxN = 1LL << 29;
 
@@ -41,7 +41,7 @@ struct lfattn_ctx {
   unsigned char* d_isglob = nullptr;
 
   float* d_part = nullptr;
-  int g_waves = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
+  int g_waves = 0, g_rows = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
 
   bool timing = false;
   int n_timed = 0;
@@ -187,16 +187,29 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   }
   c->n_band_wg = n_items;
 
-  // Global rows: sets of up to 128 rows (waves of 32), key chunks per set.
+  // Global rows: sets of rows (a workgroup's share of the global rows) times
+  // key chunks, at most kMaxChunks chunks so that the merge reads every
+  // chunk's record in one batch.  bf16: one wavefront of 32 rows per
+  // workgroup, chunks of at least four tiles; fp32: up to four wavefronts of
+  // 32 rows.
   const int n_g = (int)c->glob.size();
   if (n_g > 0) {
-    c->g_waves = n_g <= 32 ? 1 : (n_g <= 64 ? 2 : 4);
-    const int rows_per_set = c->g_waves * kWaveRows;
+    const bool bf16 = dtype == LFATTN_BF16;
+    int rows_per_set;
+    if (bf16) {
+      rows_per_set = lfattn::glob_bf16_rows_per_set(n_g);
+      c->g_waves = 1;
+    } else {
+      c->g_waves = n_g <= 32 ? 1 : (n_g <= 64 ? 2 : 4);
+      rows_per_set = c->g_waves * kWaveRows;
+    }
+    c->g_rows = rows_per_set;
     c->n_sets = (n_g + rows_per_set - 1) / rows_per_set;
     const long long bhs = (long long)B * H * c->n_sets;
-    const int max_chunks = (N + kTileKeys - 1) / kTileKeys;
-    int chunks = (int)std::min<long long>(kMaxChunks, (kGlobTarget + bhs - 1) / bhs);
-    chunks = std::max(1, std::min(chunks, max_chunks));
+    const int tiles = (N + kTileKeys - 1) / kTileKeys;
+    const int max_chunks = std::min(kMaxChunks, bf16 ? std::max(1, tiles / 4) : tiles);
+    int chunks = (int)std::min<long long>(max_chunks, (kGlobTarget + bhs - 1) / bhs);
+    chunks = std::max(1, chunks);
     int per = (N + chunks - 1) / chunks;
     per = (per + kTileKeys - 1) / kTileKeys * kTileKeys;
     c->chunk_keys = per;
@@ -216,7 +229,7 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   }
   if (n_g > 0) {
     const size_t rec = (size_t)D + 4;
-    const size_t n_part = (size_t)B * H * c->n_sets * c->n_chunks * c->g_waves * kWaveRows * rec;
+    const size_t n_part = (size_t)B * H * c->n_sets * c->n_chunks * c->g_rows * rec;
     if ((st = dev_alloc(&c->d_part, n_part)) != LFATTN_OK) {
       free_ctx(c);
       return st;
@@ -262,7 +275,7 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
     g.Q = Q; g.K = K; g.V = V; g.O = O;
     g.glob = c->d_glob; g.part = c->d_part;
     g.H = c->H; g.N = c->N; g.n_glob = n_g; g.n_bh = c->B * c->H;
-    g.rows_per_set = c->g_waves * kWaveRows;
+    g.rows_per_set = c->g_rows;
     g.n_sets = c->n_sets; g.n_chunks = c->n_chunks; g.chunk_keys = c->chunk_keys;
     g.sl2 = sl2;
     if (lfattn::launch_glob(c->dtype, c->D, c->g_waves, g, c->n_glob_wg, stream) != hipSuccess)

@@ -15,6 +15,9 @@ constexpr int kBandWaves = 4;
 constexpr int kBandRows = kBandWaves * kWaveRows;
 // The bf16 band kernel stages the global positions in LDS; this many at most.
 constexpr int kMaxGlobalBf16 = 512;
+// Key chunks of the global rows are merged from one batch of loads; the
+// chunk count per row set is at most this.
+constexpr int kMergeBatch = 16;
 
 // One band workgroup's work: batch-head bh, dilation residue r, and the first
 // position t0 (in the residue's subsequence r, r+d, r+2d, ...) of its rows.
@@ -57,6 +60,8 @@ struct GlobArgs {
 // Launchers (defined next to the kernels).  dtype: 0 fp32, 1 bf16.
 hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s);
 hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s);
+hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s);
+int glob_bf16_rows_per_set(int n_glob);
 hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s);
 hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s);
 

@@ -597,10 +597,13 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
 }
 
 // Merge of the global-row partials: one thread per (global row, 4 columns).
+// The records of up to kMergeBatch chunks are loaded together (independent
+// loads, one memory round trip), then combined against their common maximum.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
   typedef typename ElemT<BF16>::type E;
   constexpr int REC = D + 4;
+  constexpr int U = kMergeBatch;
   const int rows = a.rows_per_set;
   const long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)a.n_bh * a.n_glob * (D / 4);
@@ -612,20 +615,43 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
   const int set = slot / rows, rr = slot % rows;
   const float* part0 =
       a.part + ((size_t)(bh * a.n_sets + set) * a.n_chunks * rows + rr) * REC;
+  const size_t cs = (size_t)rows * REC;  // stride between chunks
+  const int nc = a.n_chunks;
   float m = kNegInit, l = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const float* rec = part0 + (size_t)c * rows * REC;
-    const float mc = rec[0], lc = rec[1];
-    const float4 ac = *(const float4*)(rec + 4 + 4 * dq);
-    const float mn = fmaxf(m, mc);
-    const float s1 = fast_exp2(m - mn), s2 = fast_exp2(mc - mn);
-    l = l * s1 + lc * s2;
-    acc.x = acc.x * s1 + ac.x * s2;
-    acc.y = acc.y * s1 + ac.y * s2;
-    acc.z = acc.z * s1 + ac.z * s2;
-    acc.w = acc.w * s1 + ac.w * s2;
-    m = mn;
+  for (int c = 0; c < nc; c += U) {
+    float mm[U], ll[U];
+    float4 aa[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c + u < nc) {
+        const float* rec = part0 + (size_t)(c + u) * cs;
+        const float2 ml = *(const float2*)rec;
+        mm[u] = ml.x;
+        ll[u] = ml.y;
+        aa[u] = *(const float4*)(rec + 4 + 4 * dq);
+      } else {
+        mm[u] = kNegInit;
+        ll[u] = 0.0f;
+        aa[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mm[u]);
+    const float sc = fast_exp2(m - mx);
+    l *= sc;
+    acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wgt = fast_exp2(mm[u] - mx);
+      l += ll[u] * wgt;
+      acc.x += aa[u].x * wgt;
+      acc.y += aa[u].y * wgt;
+      acc.z += aa[u].z * wgt;
+      acc.w += aa[u].w * wgt;
+    }
+    m = mx;
   }
   const float inv = 1.0f / l;
   E* Op = (E*)a.O + (size_t)bh * a.N * D + (size_t)a.glob[slot] * D + 4 * dq;
@@ -663,6 +689,7 @@ static hipError_t launch_glob_t(int waves, const GlobArgs& a, int n_wg, hipStrea
 
 hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s) {
   if (n_wg <= 0) return hipSuccess;
+  if (dtype == 1) return launch_glob_bf16(D, a, n_wg, s);
   if (dtype == 1 && D == 64) return launch_glob_t<true, 64>(waves, a, n_wg, s);
   if (dtype == 1 && D == 128) return launch_glob_t<true, 128>(waves, a, n_wg, s);
   if (dtype == 0 && D == 64) return launch_glob_t<false, 64>(waves, a, n_wg, s);
