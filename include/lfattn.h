@@ -119,11 +119,13 @@ lfattn_status lfattn_global_list(lfattn_t ctx, int* out, int capacity, int* n_ou
 
 /*
  * Per-kernel timing with HIP events, for measurement.  While enabled, each
- * forward also records events around its kernels on the forward's stream (at
- * most 4096 forwards are recorded; later ones are not).  lfattn_read_timing
- * waits for the recorded events and returns the summed milliseconds of the
- * band kernel and of the global-row kernels (partials and merge) and the number of forwards
- * recorded, then clears the record.  Enabling or disabling also clears it.
+ * forward launches its kernels with start and stop events that take each
+ * kernel's own begin and end timestamps (at most 4096 forwards are recorded;
+ * later ones run untimed).  lfattn_read_timing waits for the recorded events
+ * and returns, summed over the recorded forwards, the milliseconds of the band
+ * kernel and of the global-row kernels (partials plus merge; 0 without global
+ * positions) and the number of forwards recorded, then clears the record.
+ * Enabling or disabling also clears it.
  */
 lfattn_status lfattn_set_timing(lfattn_t ctx, int enable);
 lfattn_status lfattn_read_timing(lfattn_t ctx, double* band_ms, double* global_ms,

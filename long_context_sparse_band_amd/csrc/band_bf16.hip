@@ -812,24 +812,22 @@ int band_bf16_global_cap() { return kGlobCap; }
 
 int glob_bf16_rows_per_set(int) { return 32; }  // one 32x32 MFMA column block
 
-hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s) {
+hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t) {
   if (n_wg <= 0) return hipSuccess;
   if (a.rows_per_set != 32) return hipErrorInvalidValue;
-  dim3 grid(n_wg), block(64);
-  if (D == 64) hipLaunchKernelGGL((glob_bf16_kernel<64, 1, 3>), grid, block, 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((glob_bf16_kernel<128, 1, 2>), grid, block, 0, s, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  const dim3 grid(n_wg), block(64);
+  if (D == 64) return launch_kernel(glob_bf16_kernel<64, 1, 3>, grid, block, s, a, t);
+  if (D == 128) return launch_kernel(glob_bf16_kernel<128, 1, 2>, grid, block, s, a, t);
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s) {
+hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t) {
   if (n_wg <= 0) return hipSuccess;
   if (a.n_glob > kGlobCap) return hipErrorInvalidValue;
-  dim3 grid(n_wg), block(256);
-  if (D == 64) hipLaunchKernelGGL((band_bf16_kernel<64, 2, 2, 2>), grid, block, 0, s, a);
-  else if (D == 128) hipLaunchKernelGGL((band_bf16_kernel<128, 1, 1, 2>), grid, block, 0, s, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  const dim3 grid(n_wg), block(256);
+  if (D == 64) return launch_kernel(band_bf16_kernel<64, 2, 2, 2>, grid, block, s, a, t);
+  if (D == 128) return launch_kernel(band_bf16_kernel<128, 1, 1, 2>, grid, block, s, a, t);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace lfattn

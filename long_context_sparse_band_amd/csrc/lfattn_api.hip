@@ -19,6 +19,9 @@ using lfattn::kWaveRows;
 namespace {
 
 constexpr int kMaxTimedForwards = 4096;
+// Timing events per forward: band start/stop, global partials start/stop,
+// merge start/stop.
+constexpr int kEvPerForward = 6;
 constexpr int kXcds = 8;           // MI355X: workgroups go round-robin over 8 XCDs
 constexpr int kMaxChunks = lfattn::kMergeBatch;  // key chunks per global row set
 constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
@@ -45,7 +48,7 @@ struct lfattn_ctx {
 
   bool timing = false;
   int n_timed = 0;
-  std::vector<hipEvent_t> ev;  // 4 per timed forward
+  std::vector<hipEvent_t> ev;  // kEvPerForward per timed forward
 };
 
 namespace {
@@ -264,8 +267,13 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
 
   const float sl2 = c->scale * 1.4426950408889634f;
   const bool timed = c->timing && c->n_timed < kMaxTimedForwards;
-  hipEvent_t* ev = timed ? &c->ev[4 * c->n_timed] : nullptr;
-  if (timed && hipEventRecord(ev[0], stream) != hipSuccess) return LFATTN_EHIP;
+  hipEvent_t* ev = timed ? &c->ev[kEvPerForward * c->n_timed] : nullptr;
+  lfattn::Timing t_band, t_part, t_merge;
+  if (timed) {
+    t_band = {ev[0], ev[1]};
+    t_part = {ev[2], ev[3]};
+    t_merge = {ev[4], ev[5]};
+  }
 
   // Global rows: partials first, then the band kernel, then the merge (which
   // reads the partials after the kernel boundary made them visible).
@@ -278,26 +286,21 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
     g.rows_per_set = c->g_rows;
     g.n_sets = c->n_sets; g.n_chunks = c->n_chunks; g.chunk_keys = c->chunk_keys;
     g.sl2 = sl2;
-    if (lfattn::launch_glob(c->dtype, c->D, c->g_waves, g, c->n_glob_wg, stream) != hipSuccess)
+    if (lfattn::launch_glob(c->dtype, c->D, c->g_waves, g, c->n_glob_wg, stream, t_part) != hipSuccess)
       return LFATTN_EHIP;
   }
-  if (timed && hipEventRecord(ev[1], stream) != hipSuccess) return LFATTN_EHIP;
 
   lfattn::BandArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O;
   a.work = c->d_work; a.dil = c->d_dil; a.glob = c->d_glob; a.is_glob = c->d_isglob;
   a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
-  if (lfattn::launch_band(c->dtype, c->D, a, c->n_band_wg, stream) != hipSuccess)
-    return LFATTN_EHIP;
-  if (timed && hipEventRecord(ev[2], stream) != hipSuccess) return LFATTN_EHIP;
-
-  if (n_g > 0 && lfattn::launch_glob_merge(c->dtype, c->D, g, stream) != hipSuccess)
+  if (lfattn::launch_band(c->dtype, c->D, a, c->n_band_wg, stream, t_band) != hipSuccess)
     return LFATTN_EHIP;
 
-  if (timed) {
-    if (hipEventRecord(ev[3], stream) != hipSuccess) return LFATTN_EHIP;
-    ++c->n_timed;
-  }
+  if (n_g > 0 && lfattn::launch_glob_merge(c->dtype, c->D, g, stream, t_merge) != hipSuccess)
+    return LFATTN_EHIP;
+
+  if (timed) ++c->n_timed;
   return LFATTN_OK;
 }
 
@@ -325,7 +328,7 @@ lfattn_status lfattn_global_list(lfattn_t c, int* out, int capacity, int* n_out)
 lfattn_status lfattn_set_timing(lfattn_t c, int enable) {
   if (!c) return LFATTN_EINVAL;
   if (enable && c->ev.empty()) {
-    c->ev.resize(4 * kMaxTimedForwards, nullptr);
+    c->ev.resize(kEvPerForward * kMaxTimedForwards, nullptr);
     for (auto& e : c->ev)
       if (hipEventCreate(&e) != hipSuccess) {
         (void)hipGetLastError();
@@ -343,17 +346,20 @@ lfattn_status lfattn_set_timing(lfattn_t c, int enable) {
 lfattn_status lfattn_read_timing(lfattn_t c, double* band_ms, double* global_ms, int* n_forwards) {
   if (!c || !band_ms || !global_ms || !n_forwards) return LFATTN_EINVAL;
   double b = 0.0, g = 0.0;
-  if (c->n_timed > 0 && hipEventSynchronize(c->ev[4 * (c->n_timed - 1) + 3]) != hipSuccess)
-    return LFATTN_EHIP;
+  const bool has_glob = !c->glob.empty();
+  if (c->n_timed > 0) {
+    hipEvent_t* last = &c->ev[kEvPerForward * (c->n_timed - 1)];
+    if (hipEventSynchronize(last[has_glob ? 5 : 1]) != hipSuccess) return LFATTN_EHIP;
+  }
   for (int t = 0; t < c->n_timed; ++t) {
+    hipEvent_t* e = &c->ev[kEvPerForward * t];
     float x = 0.0f, y = 0.0f, z = 0.0f;
-    hipEvent_t* e = &c->ev[4 * t];
-    if (hipEventElapsedTime(&x, e[0], e[1]) != hipSuccess ||
-        hipEventElapsedTime(&y, e[1], e[2]) != hipSuccess ||
-        hipEventElapsedTime(&z, e[2], e[3]) != hipSuccess)
+    if (hipEventElapsedTime(&x, e[0], e[1]) != hipSuccess) return LFATTN_EHIP;
+    if (has_glob && (hipEventElapsedTime(&y, e[2], e[3]) != hipSuccess ||
+                     hipEventElapsedTime(&z, e[4], e[5]) != hipSuccess))
       return LFATTN_EHIP;
-    g += x + z;
-    b += y;
+    b += x;
+    g += y + z;
   }
   *band_ms = b;
   *global_ms = g;

@@ -1,6 +1,7 @@
 // Internal declarations shared by the kernels and the C-ABI host code.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,12 +58,29 @@ struct GlobArgs {
   float sl2;
 };
 
+// Optional events around one launch: start and stop take the kernel's own
+// begin and end timestamps (hipExtLaunchKernel), so their elapsed time is the
+// kernel's duration without the stream's marker overhead.  Null: untimed.
+struct Timing {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename A>
+inline hipError_t launch_kernel(void (*k)(A), dim3 grid, dim3 block, hipStream_t s, const A& a,
+                                const Timing& t) {
+  void* args[] = {const_cast<A*>(&a)};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, 0, s, t.start,
+                            t.stop, 0);
+}
+
 // Launchers (defined next to the kernels).  dtype: 0 fp32, 1 bf16.
-hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s);
-hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s);
-hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s);
+hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t);
+hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t);
+hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t);
 int glob_bf16_rows_per_set(int n_glob);
-hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s);
-hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s);
+hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s,
+                       const Timing& t);
+hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s, const Timing& t);
 
 }  // namespace lfattn

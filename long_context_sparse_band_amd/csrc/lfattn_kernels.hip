@@ -667,46 +667,42 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
 
 }  // namespace
 
-hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s) {
+hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t) {
   if (n_wg <= 0) return hipSuccess;
-  if (dtype == 1) return launch_band_bf16(D, a, n_wg, s);
-  dim3 grid(n_wg), block(kBandWaves * 64);
-  if (dtype == 0 && D == 64) hipLaunchKernelGGL((band_kernel<false, 64>), grid, block, 0, s, a);
-  else if (dtype == 0 && D == 128) hipLaunchKernelGGL((band_kernel<false, 128>), grid, block, 0, s, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-template <bool BF16, int D>
-static hipError_t launch_glob_t(int waves, const GlobArgs& a, int n_wg, hipStream_t s) {
-  dim3 grid(n_wg);
-  if (waves == 1) hipLaunchKernelGGL((glob_kernel<BF16, D, 1>), grid, dim3(64), 0, s, a);
-  else if (waves == 2) hipLaunchKernelGGL((glob_kernel<BF16, D, 2>), grid, dim3(128), 0, s, a);
-  else if (waves == 4) hipLaunchKernelGGL((glob_kernel<BF16, D, 4>), grid, dim3(256), 0, s, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s) {
-  if (n_wg <= 0) return hipSuccess;
-  if (dtype == 1) return launch_glob_bf16(D, a, n_wg, s);
-  if (dtype == 1 && D == 64) return launch_glob_t<true, 64>(waves, a, n_wg, s);
-  if (dtype == 1 && D == 128) return launch_glob_t<true, 128>(waves, a, n_wg, s);
-  if (dtype == 0 && D == 64) return launch_glob_t<false, 64>(waves, a, n_wg, s);
-  if (dtype == 0 && D == 128) return launch_glob_t<false, 128>(waves, a, n_wg, s);
+  if (dtype == 1) return launch_band_bf16(D, a, n_wg, s, t);
+  const dim3 grid(n_wg), block(kBandWaves * 64);
+  if (dtype == 0 && D == 64) return launch_kernel(band_kernel<false, 64>, grid, block, s, a, t);
+  if (dtype == 0 && D == 128) return launch_kernel(band_kernel<false, 128>, grid, block, s, a, t);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s) {
+template <int D>
+static hipError_t launch_glob_f32(int waves, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t) {
+  const dim3 grid(n_wg);
+  if (waves == 1) return launch_kernel(glob_kernel<false, D, 1>, grid, dim3(64), s, a, t);
+  if (waves == 2) return launch_kernel(glob_kernel<false, D, 2>, grid, dim3(128), s, a, t);
+  if (waves == 4) return launch_kernel(glob_kernel<false, D, 4>, grid, dim3(256), s, a, t);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s,
+                       const Timing& t) {
+  if (n_wg <= 0) return hipSuccess;
+  if (dtype == 1) return launch_glob_bf16(D, a, n_wg, s, t);
+  if (dtype == 0 && D == 64) return launch_glob_f32<64>(waves, a, n_wg, s, t);
+  if (dtype == 0 && D == 128) return launch_glob_f32<128>(waves, a, n_wg, s, t);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s, const Timing& t) {
   const long long total = (long long)a.n_bh * a.n_glob * (D / 4);
   if (total <= 0) return hipSuccess;
-  dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  if (dtype == 1 && D == 64) hipLaunchKernelGGL((glob_merge_kernel<true, 64>), grid, block, 0, s, a);
-  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((glob_merge_kernel<true, 128>), grid, block, 0, s, a);
-  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((glob_merge_kernel<false, 64>), grid, block, 0, s, a);
-  else if (dtype == 0 && D == 128) hipLaunchKernelGGL((glob_merge_kernel<false, 128>), grid, block, 0, s, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (dtype == 1 && D == 64) return launch_kernel(glob_merge_kernel<true, 64>, grid, block, s, a, t);
+  if (dtype == 1 && D == 128) return launch_kernel(glob_merge_kernel<true, 128>, grid, block, s, a, t);
+  if (dtype == 0 && D == 64) return launch_kernel(glob_merge_kernel<false, 64>, grid, block, s, a, t);
+  if (dtype == 0 && D == 128) return launch_kernel(glob_merge_kernel<false, 128>, grid, block, s, a, t);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace lfattn
