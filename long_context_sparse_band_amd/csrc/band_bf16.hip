@@ -159,6 +159,7 @@ struct Wave {
   unsigned voff[D / 32][2];  // V^T operand, column block b, rows +0 / +8
   float sl2;
   int hi;
+  bool fresh;             // no half scored yet: maxima unset
 };
 
 // S^T for one half (kb): MFMAs on the K rows 32kb .. 32kb+31 of the tile.
@@ -207,8 +208,8 @@ __device__ __forceinline__ void half_mask(const Wave<D, QB>& w, int s0, f32x16 (
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const bool keep = (kk0 + c < nvalid) && w.u[qb] < w.Lr &&
-                            (unsigned)(sp[c] - w.u[qb] + w.hw) > span;
+          const bool keep = (kk0 + c < nvalid) & (w.u[qb] < w.Lr) &
+                            ((unsigned)(sp[c] - w.u[qb] + w.hw) > span);
           S[qb][4 * g4 + c] = keep ? S[qb][4 * g4 + c] : -INFINITY;
         }
     }
@@ -315,6 +316,17 @@ __device__ __forceinline__ void half(Wave<D, QB>& w, unsigned sbase, int s0, int
   float ls[QB];
   half_scores<D, QB, KB>(w, sbase, S);
   half_mask<D, QB, KB, KIND>(w, s0, S, nvalid);
+  if (w.fresh) {
+    // First half: start the running maxima at its own maxima.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
+      w.m[qb] = fmaxf(kNegInit, pair_max(mx) * w.sl2);
+    }
+    w.fresh = false;
+  }
   half_weights(w, S, P, ls);
   half_accept(w, S, P, ls);
   half_pv<D, QB, KB>(w, sbase, P);
@@ -354,13 +366,14 @@ void band_bf16_kernel(BandArgs a) {
   const unsigned short* Vp = (const unsigned short*)a.V + base;
   const int n_glob = a.n_glob;
 
-  // Global positions, and where each sits in this residue's subsequence (or a
-  // value no band reaches), staged once.
-  for (int x = tid; x < n_glob; x += 256) {
-    const int g = a.glob[x];
-    const int off = g - r;
-    sm.gpos[x] = g;
-    sm.gsp[x] = (off >= 0 && off % d == 0) ? off / d : kNotInClass;
+  // Global positions this thread stages in LDS (loaded first, so that their
+  // latency overlaps the Q loads and the first tile loads).
+  constexpr int kStageIters = (kGlobCap + 255) / 256;
+  int gv[kStageIters];
+#pragma unroll
+  for (int it = 0; it < kStageIters; ++it) {
+    const int x = tid + 256 * it;
+    gv[it] = x < n_glob ? a.glob[x] : 0;
   }
 
   // Rows of this wave: subsequence positions ua .. ub.
@@ -406,7 +419,6 @@ void band_bf16_kernel(BandArgs a) {
   const int n_tiles = n_band + (n_glob + TK - 1) / TK;
   const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles kh*n_steps + j
 
-  __syncthreads();  // staged global positions visible
 
   // Issue the direct loads of step j into stage sidx: exactly L per wave, so
   // the ring's vmcnt arithmetic holds (tiles past the end load a real row).
@@ -431,6 +443,53 @@ void band_bf16_kernel(BandArgs a) {
     }
   };
 
+  // The first stages' loads go out before the global positions are staged
+  // unless one of their tiles is a gathered global tile.
+  bool early = true;
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+#pragma unroll
+    for (int hh = 0; hh < KS; ++hh) {
+      const int tj = hh * n_steps + j;
+      early &= !(j < n_steps && tj >= n_band && tj < n_tiles);
+    }
+  if (early) {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < n_steps) issue(j, j);
+  }
+
+  // Global positions, and where each sits in this residue's subsequence (or
+  // a value no band reaches).
+#pragma unroll
+  for (int it = 0; it < kStageIters; ++it) {
+    const int x = tid + 256 * it;
+    if (x < n_glob) {
+      const int g = gv[it];
+      const int off = g - r;
+      sm.gpos[x] = g;
+      sm.gsp[x] = (off >= 0 && off % d == 0) ? off / d : kNotInClass;
+    }
+  }
+  __syncthreads();  // staged global positions visible
+
+  // Whether a global key lies in the band of one of this wave's rows.  If
+  // not, a global tile needs no per-pair dedupe test, only the count of its
+  // valid slots.
+  bool gdup = false;
+  if (live) {
+    const int lo_w = ua - hw;
+    const unsigned span_w = (unsigned)(ub - ua + 2 * hw);
+    for (int x = lane; x < n_glob; x += 64) gdup |= (unsigned)(sm.gsp[x] - lo_w) <= span_w;
+  }
+  gdup = __any(gdup);
+
+  if (!early) {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < n_steps) issue(j, j);
+  }
+
   // Per-lane LDS byte offsets of the MFMA operands inside a tile; the k-step
   // and the 32-key half enter as immediate offsets.
   unsigned koff[D / 16];
@@ -447,10 +506,10 @@ void band_bf16_kernel(BandArgs a) {
     voff[b][1] = G::MAT + row1 * G::RB + 16 * G::swz(row1, c) + 8 * half;
   }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-#pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (j < n_steps) issue(j, j);
+  // Until the wave has scored its first half, the running maxima are unset;
+  // that half starts them at its own maxima instead of going through the
+  // rescale path.
+  bool fresh = true;
 
   for (int j = 0; j < n_steps; ++j) {
     // Wait for this wave's loads of step j (those of up to NS-2 later steps
@@ -478,6 +537,19 @@ void band_bf16_kernel(BandArgs a) {
         act[kb] = k0 <= s_hi && k0 <= ub + hw && k1 >= ua - hw;
         edge[kb] = !(k1 == k0 + 31 && k1 - ua <= hw && ub - k0 <= hw);
       }
+    } else if (!gdup) {
+      // No dedupe needed: keep the valid slots only.
+      const int nvalid = min(TK, n_glob - TK * (t - n_band));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        act[kb] = 32 * kb < nvalid;
+        edge[kb] = 32 * (kb + 1) > nvalid;
+        unsigned bits = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bits |= (unsigned)(32 * kb + block_row(i, hi) < nvalid) << i;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) keep[qb][kb] = bits;
+      }
     } else {
       const int g0 = TK * (t - n_band);
       const int nvalid = min(TK, n_glob - g0);
@@ -494,8 +566,8 @@ void band_bf16_kernel(BandArgs a) {
             const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsp[min(g0 + kk0, kGlobCap - 4)];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const bool k = (kk0 + c < nvalid) && u[qb] < Lr &&
-                             (unsigned)(sp[c] - u[qb] + hw) > span;
+              const bool k = (kk0 + c < nvalid) & (u[qb] < Lr) &
+                             ((unsigned)(sp[c] - u[qb] + hw) > span);
               bits |= (unsigned)k << (4 * g4 + c);
             }
           }
@@ -547,6 +619,17 @@ void band_bf16_kernel(BandArgs a) {
               S[qb][i] = ((keep[qb][kb] >> i) & 1u) ? S[qb][i] : -INFINITY;
           }
         }
+      }
+
+      if (fresh) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
+          m[qb] = fmaxf(kNegInit, pair_max(mx) * a.sl2);
+        }
+        fresh = false;
       }
 
       // Weights, packed to bf16 (the B operand of P.V), and their row sums.
@@ -693,6 +776,379 @@ void band_bf16_kernel(BandArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 band kernel for D = 64 with 32-key steps (band32_kernel).
+//
+// A workgroup of 4 wavefronts takes 64 consecutive rows of one (batch, head,
+// dilation residue): wavefronts 0,1 own rows 0-31 and 32-63 over the first
+// half of the workgroup's 32-key tiles, wavefronts 2,3 the same rows over the
+// second half (partial softmax states merged through LDS at the end).  Each
+// wavefront's state is one 32x32 MFMA block, so a wavefront fits in 168
+// registers and three workgroups (a 3-stage ring of 32-key K/V tiles, 52 KB
+// of LDS each) share a compute unit: three wavefronts per SIMD hide each
+// other's latencies.  Per step and wavefront: S^T = K Q^T (4 MFMAs), mask
+// where a band edge or global dedupe cuts the tile, weights with the lazy
+// rescale, O^T += V^T P^T (4 MFMAs).
+// ---------------------------------------------------------------------------
+namespace b32 {
+constexpr int TK = 32;          // keys per step
+constexpr int D = 64;
+constexpr int RB = 2 * D;       // bytes per key row
+constexpr int CPR = RB / 16;    // 16-byte chunks per row
+constexpr int RPI = 1024 / RB;  // rows one wave-wide direct load fills (8)
+constexpr int MAT = TK * RB;    // bytes of one K (or V) tile: 4 KB
+constexpr int NLD = TK / RPI;   // direct loads per matrix and tile (4)
+constexpr int KS = 2, NS = 3;
+constexpr int ROWS = 64;        // rows per workgroup
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
+struct Smem {
+  unsigned char st[NS][KS][2 * MAT];
+  int gpos[kGlobCap];
+  int gsp[kGlobCap];
+};
+}  // namespace b32
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void band32_kernel(BandArgs a) {
+  constexpr int TK = b32::TK, D = b32::D, RB = b32::RB, CPR = b32::CPR, RPI = b32::RPI;
+  constexpr int MAT = b32::MAT, NLD = b32::NLD, KS = b32::KS, NS = b32::NS, ROWS = b32::ROWS;
+  static_assert(KS * 2 * NLD == 16, "16 direct loads per step, 4 per wave");
+  __shared__ __attribute__((aligned(16))) b32::Smem sm;
+  auto swz = [](int row, int c) { return b32::swz(row, c); };
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int qblk = wave & 1, kh = wave >> 1;
+  const BandWork w = a.work[blockIdx.x];
+  const int h = w.bh % a.H;
+  const int d = a.dil[h];
+  const int r = w.r, t0 = w.t0, hw = a.hw, N = a.N;
+  const int Lr = (N - r + d - 1) / d;
+  const size_t base = (size_t)w.bh * N * D;
+  const unsigned short* Qp = (const unsigned short*)a.Q + base;
+  const unsigned short* Kp = (const unsigned short*)a.K + base;
+  const unsigned short* Vp = (const unsigned short*)a.V + base;
+  const int n_glob = a.n_glob;
+
+  // Global positions this thread stages (loaded first so that their latency
+  // overlaps the Q loads and the first tile loads).
+  constexpr int kStageIters = (kGlobCap + 255) / 256;
+  int gv[kStageIters];
+#pragma unroll
+  for (int it = 0; it < kStageIters; ++it) {
+    const int x = tid + 256 * it;
+    gv[it] = x < n_glob ? a.glob[x] : 0;
+  }
+
+  // This wave's rows: subsequence positions ua .. ub (one per lane % 32).
+  const int ua = t0 + 32 * qblk;
+  const int ub = min(ua + 31, Lr - 1);
+  const bool live = ua < Lr;
+  const int s_lo = max(0, t0 - hw);
+  const int s_hi = min(Lr - 1, t0 + ROWS - 1 + hw);
+  const int u = ua + l32;
+  const bool row_ok = u < Lr;
+
+  // Q operand (B of S^T = K Q^T): Q[row][16ks + 8hi + 0..7].
+  bf16x8 q[D / 16];
+  {
+    const size_t row = (size_t)(r + d * (row_ok ? u : 0));
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      q[ks] = *(const bf16x8*)(Qp + row * D + 16 * ks + 8 * hi);
+      if (!row_ok) q[ks] = bf16x8{};
+    }
+  }
+  // Band keys of the lane's row as an interval [lo, lo + rng] of subsequence
+  // positions (empty for rows past the end).
+  int lo;
+  unsigned rng;
+  {
+    int l0 = max(u - hw, 0), h0 = min(u + hw, s_hi);
+    if (!row_ok || h0 < l0) { l0 = 0x3fffffff; h0 = l0; }
+    lo = l0;
+    rng = (unsigned)(h0 - l0);
+  }
+
+  const int n_band = (s_hi - s_lo) / TK + 1;
+  const int n_tiles = n_band + (n_glob + TK - 1) / TK;
+  const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles kh*n_steps + j
+
+  // Direct loads of step j into stage sidx: wave w loads rows 8w..8w+7 of
+  // the K and V tiles of both key halves (4 loads; tiles past the end load a
+  // real row so that every wave issues the same count).
+  auto issue = [&](int j, int sidx) {
+    const int row = RPI * wave + lane / CPR;
+    const int c = swz(row, lane % CPR);
+#pragma unroll
+    for (int hh = 0; hh < KS; ++hh) {
+      const int tj = hh * n_steps + j;
+      const unsigned stb = (unsigned)(uintptr_t)(LDS_AS void*)sm.st[sidx][hh];
+      int grow;
+      if (tj < n_band) grow = r + d * min(s_lo + TK * tj + row, s_hi);
+      else if (tj < n_tiles) grow = sm.gpos[min(TK * (tj - n_band) + row, n_glob - 1)];
+      else grow = r;
+      const size_t off = (size_t)grow * D + 8 * c;
+      dma16(Kp + off, stb + 1024 * wave);
+      dma16(Vp + off, stb + MAT + 1024 * wave);
+    }
+  };
+
+  // The first stages go out before the global positions are staged unless
+  // one of their tiles is a gathered global tile.
+  bool early = true;
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+#pragma unroll
+    for (int hh = 0; hh < KS; ++hh) {
+      const int tj = hh * n_steps + j;
+      early &= !(j < n_steps && tj >= n_band && tj < n_tiles);
+    }
+  if (early) {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < n_steps) issue(j, j);
+  }
+#pragma unroll
+  for (int it = 0; it < kStageIters; ++it) {
+    const int x = tid + 256 * it;
+    if (x < n_glob) {
+      const int g = gv[it];
+      const int off = g - r;
+      sm.gpos[x] = g;
+      sm.gsp[x] = (off >= 0 && off % d == 0) ? off / d : kNotInClass;
+    }
+  }
+  __syncthreads();  // staged global positions visible
+  if (!early) {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < n_steps) issue(j, j);
+  }
+
+  // Whether a global key lies in the band of one of this wave's rows (then
+  // global tiles need the per-pair dedupe test).
+  bool gdup = false;
+  if (live) {
+    const int lo_w = ua - hw;
+    const unsigned span_w = (unsigned)(ub - ua + 2 * hw);
+    for (int x = lane; x < n_glob; x += 64) gdup |= (unsigned)(sm.gsp[x] - lo_w) <= span_w;
+  }
+  gdup = __any(gdup);
+
+  // Per-lane LDS offsets of the MFMA operands inside a tile.
+  unsigned koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * RB + 16 * swz(l32, 2 * ks + hi);
+  unsigned voff[D / 32][2];
+  {
+    const int g16 = lane >> 4, t16 = lane & 15;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+      const int dcol = 32 * b + 16 * (g16 & 1) + 4 * (t16 & 3);
+      const int c = dcol >> 3, half = (dcol >> 2) & 1;
+      const int row0 = 4 * (g16 >> 1) + (t16 >> 2), row1 = row0 + 8;
+      voff[b][0] = MAT + row0 * RB + 16 * swz(row0, c) + 8 * half;
+      voff[b][1] = MAT + row1 * RB + 16 * swz(row1, c) + 8 * half;
+    }
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) acc[b] = f32x16{};
+  float m = kNegInit, l = 0.0f;
+  bool fresh = true;  // no tile scored yet: maximum unset
+
+  for (int j = 0; j < n_steps; ++j) {
+    // This wave's loads of step j done (those of the next NS-2 steps may
+    // stay in flight), then every wave's.
+    if (j + NS - 2 < n_steps) wait_vm_lgkm0<2 * KS * (NS - 2)>();
+    else wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    if (j + NS - 1 < n_steps) issue(j + NS - 1, (j + NS - 1) % NS);
+
+    const int t = kh * n_steps + j;
+    if (!live || t >= n_tiles) continue;
+    const LDS_AS unsigned char* st = (const LDS_AS unsigned char*)sm.st[j % NS][kh];
+    const unsigned sbase = (unsigned)(uintptr_t)st;
+    const bool band = t < n_band;
+
+    // Whether any row of the wave scores the tile, and whether it needs a
+    // per-pair mask.
+    bool act, edge;
+    unsigned keep = 0;
+    if (band) {
+      const int k0 = s_lo + TK * t, k1 = min(k0 + TK - 1, s_hi);
+      act = k0 <= ub + hw && k1 >= ua - hw;
+      edge = !(k1 == k0 + TK - 1 && k1 - ua <= hw && ub - k0 <= hw);
+    } else {
+      const int g0 = TK * (t - n_band);
+      const int nvalid = min(TK, n_glob - g0);
+      if (!gdup) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) keep |= (unsigned)(block_row(i, hi) < nvalid) << i;
+        act = true;
+        edge = nvalid < TK;
+      } else {
+        const unsigned span = 2u * (unsigned)hw;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int kk0 = 8 * g4 + 4 * hi;
+          const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsp[min(g0 + kk0, kGlobCap - 4)];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bool k = (kk0 + c < nvalid) & row_ok & ((unsigned)(sp[c] - u + hw) > span);
+            keep |= (unsigned)k << (4 * g4 + c);
+          }
+        }
+        act = __any(keep != 0);
+        edge = true;
+      }
+    }
+    if (!act) continue;
+
+    // S^T = K Q^T.
+    f32x16 S;
+    {
+      bf16x8 kv[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) kv[ks] = *(const LDS_AS bf16x8*)(st + koff[ks]);
+      S = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks], q[ks], S, 0, 0, 0);
+    }
+    if (edge) {
+      if (band) {
+        const int basek = s_lo + TK * t + 4 * hi - lo;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const unsigned x = (unsigned)(basek + block_row(i, 0));
+          S[i] = x > rng ? -INFINITY : S[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[i] = ((keep >> i) & 1u) ? S[i] : -INFINITY;
+      }
+    }
+    if (fresh) {
+      // First scored tile: start the running maximum at its own maximum.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+      m = fmaxf(kNegInit, pair_max(mx) * a.sl2);
+      fresh = false;
+    }
+
+    // Weights, packed to bf16 (the B operand of P.V), and their sum.
+    unsigned P[8];
+    float ls;
+    auto weights = [&](float mq) {
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        f32x2 pf;
+        pf[0] = fast_exp2(fmaf(S[i], a.sl2, -mq));
+        pf[1] = fast_exp2(fmaf(S[i + 1], a.sl2, -mq));
+        const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
+        P[i / 2] = __builtin_bit_cast(unsigned, pb);
+        if (i & 2) s1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s1, false);
+        else s0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s0, false);
+      }
+      ls = s0 + s1;
+    };
+    weights(m);
+    if (__builtin_expect(__any(!(ls <= kSumLimit)), 0)) {
+      // Move the running maximum up to this tile's maximum and redo.  (The
+      // empty volatile statement keeps this rare path a real branch.)
+      asm volatile("" ::: "memory");
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+      const float mn = fmaxf(m, pair_max(mx) * a.sl2);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+      m = mn;
+      weights(mn);
+    }
+    l += ls;
+
+    // O^T += V^T P^T, V^T read transposed (see the 64-key kernel).
+    {
+      s16x4 vr[2][2][2];  // [k2][b][row0/row1]
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr)
+            vr[k2][b][rr] = ds_read_tr16(sbase + voff[b][rr] + 16 * k2 * RB);
+      lgkm_wait(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1],
+                vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1]);
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const uint4 pu = make_uint4(P[4 * k2], P[4 * k2 + 1], P[4 * k2 + 2], P[4 * k2 + 3]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const bf16x8 va = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(vr[k2][b][0], vr[k2][b][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8, pu),
+                                                           acc[b], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Merge the second key half's state into the first through LDS (the ring
+  // is free: every load was waited for in the last step).
+  {
+    constexpr int PER = 2 + D / 2;
+    static_assert((size_t)2 * 64 * PER * 4 <= sizeof(sm.st), "merge area");
+    __syncthreads();
+    float* mine = (float*)&sm.st[0][0][0] + ((size_t)qblk * 64 + lane) * PER;
+    if (kh == 1 && live) {
+      mine[0] = m;
+      mine[1] = l;
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mine[2 + 16 * b + i] = acc[b][i];
+    }
+    __syncthreads();
+    if (kh == 1 || !live) return;
+    const float m1 = mine[0], l1 = mine[1];
+    const float mn = fmaxf(m, m1);
+    const float a0 = fast_exp2(m - mn), a1 = fast_exp2(m1 - mn);
+    l = l * a0 + l1 * a1;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][i] = acc[b][i] * a0 + mine[2 + 16 * b + i] * a1;
+  }
+
+  const float lt = pair_sum(l);
+  if (!row_ok) return;
+  const int row = r + d * u;
+  if (a.is_glob[row]) return;
+  const float inv = 1.0f / lt;
+  unsigned short* Op = (unsigned short*)a.O + base + (size_t)row * D;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 o;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = (__bf16)(acc[b][4 * g4 + c] * inv);
+      *(bf16x4*)(Op + 32 * b + 8 * g4 + 4 * hi) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Global-row partials (bf16): the rows of global tokens score every key.  One
 // wavefront per workgroup takes QB blocks of 32 global rows of one (batch,
 // head) and one chunk of keys, streams the chunk's 64-key tiles through its
@@ -726,6 +1182,7 @@ void glob_bf16_kernel(GlobArgs a) {
   Wave<D, QB> w;
   w.sl2 = a.sl2;
   w.hi = hi;
+  w.fresh = true;
   int slot[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -812,6 +1269,8 @@ int band_bf16_global_cap() { return kGlobCap; }
 
 int glob_bf16_rows_per_set(int) { return 32; }  // one 32x32 MFMA column block
 
+int band_bf16_rows_per_workgroup(int D) { return D == 64 ? b32::ROWS : kBandRows; }
+
 hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t) {
   if (n_wg <= 0) return hipSuccess;
   if (a.rows_per_set != 32) return hipErrorInvalidValue;
@@ -825,7 +1284,7 @@ hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, c
   if (n_wg <= 0) return hipSuccess;
   if (a.n_glob > kGlobCap) return hipErrorInvalidValue;
   const dim3 grid(n_wg), block(256);
-  if (D == 64) return launch_kernel(band_bf16_kernel<64, 2, 2, 2>, grid, block, s, a, t);
+  if (D == 64) return launch_kernel(band32_kernel, grid, block, s, a, t);
   if (D == 128) return launch_kernel(band_bf16_kernel<128, 1, 1, 2>, grid, block, s, a, t);
   return hipErrorInvalidValue;
 }

@@ -169,16 +169,18 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
     c->pairs = total * B;
   }
 
-  // Band work: one item per 128 rows of each (b, h, residue r) subsequence,
+  // Band work: one item per workgroup's rows (64 or 128) of each (b, h,
+  // residue r) subsequence,
   // laid out so that the items the hardware sends to one XCD (blockIdx
   // congruent mod 8) are consecutive query blocks of the same head, which
   // share their band's K and V rows in that XCD's L2.
+  const int band_rows = lfattn::band_rows_per_workgroup(dtype, D);
   std::vector<BandWork> items;
   for (int bh = 0; bh < B * H; ++bh) {
     const int d = c->dil[bh % H];
     for (int r = 0; r < d && r < N; ++r) {
       const int Lr = (N - r + d - 1) / d;
-      for (int t0 = 0; t0 < Lr; t0 += kBandRows) items.push_back(BandWork{bh, r, t0, 0});
+      for (int t0 = 0; t0 < Lr; t0 += band_rows) items.push_back(BandWork{bh, r, t0, 0});
     }
   }
   const int n_items = (int)items.size();

@@ -79,6 +79,9 @@ hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_
 hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t);
 hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t);
 int glob_bf16_rows_per_set(int n_glob);
+// Query rows one band workgroup covers for the given element type and D.
+int band_rows_per_workgroup(int dtype, int D);
+int band_bf16_rows_per_workgroup(int D);
 hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s,
                        const Timing& t);
 hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s, const Timing& t);
