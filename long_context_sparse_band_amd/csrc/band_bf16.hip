@@ -782,9 +782,9 @@ void band_bf16_kernel(BandArgs a) {
 // dilation residue): wavefronts 0,1 own rows 0-31 and 32-63 over the first
 // half of the workgroup's 32-key tiles, wavefronts 2,3 the same rows over the
 // second half (partial softmax states merged through LDS at the end).  Each
-// wavefront's state is one 32x32 MFMA block, so a wavefront fits in 168
-// registers and three workgroups (a 3-stage ring of 32-key K/V tiles, 52 KB
-// of LDS each) share a compute unit: three wavefronts per SIMD hide each
+// wavefront's state is one 32x32 MFMA block, so a wavefront fits in 128
+// registers and four workgroups (a 2-stage ring of 32-key K/V tiles, 36 KB
+// of LDS each) share a compute unit: four wavefronts per SIMD hide each
 // other's latencies.  Per step and wavefront: S^T = K Q^T (4 MFMAs), mask
 // where a band edge or global dedupe cuts the tile, weights with the lazy
 // rescale, O^T += V^T P^T (4 MFMAs).
@@ -797,7 +797,7 @@ constexpr int CPR = RB / 16;    // 16-byte chunks per row
 constexpr int RPI = 1024 / RB;  // rows one wave-wide direct load fills (8)
 constexpr int MAT = TK * RB;    // bytes of one K (or V) tile: 4 KB
 constexpr int NLD = TK / RPI;   // direct loads per matrix and tile (4)
-constexpr int KS = 2, NS = 3;
+constexpr int KS = 2, NS = 2;
 constexpr int ROWS = 64;        // rows per workgroup
 __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
 struct Smem {
@@ -807,7 +807,7 @@ struct Smem {
 };
 }  // namespace b32
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void band32_kernel(BandArgs a) {
   constexpr int TK = b32::TK, D = b32::D, RB = b32::RB, CPR = b32::CPR, RPI = b32::RPI;
   constexpr int MAT = b32::MAT, NLD = b32::NLD, KS = b32::KS, NS = b32::NS, ROWS = b32::ROWS;
