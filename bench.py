@@ -121,8 +121,9 @@ def main():
                         list(inp.glob))
     pairs = L.lfattn_scored_pairs(h)
     n_g = len(inp.glob)
-    glob_pairs = wl.B * wl.H * n_g * wl.N           # global rows: all N keys
-    band_pairs = pairs - glob_pairs                 # band kernel: every other row
+    # Pairs the band kernel launch scores (the band rows, and the global rows
+    # where the same launch computes their partials).
+    band_pairs = L.lfattn_band_launch_pairs(h)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):

@@ -111,6 +111,14 @@ const char* lfattn_status_string(lfattn_status status);
 lfattn_status lfattn_scored_pairs(lfattn_t ctx, long long* pairs);
 
 /*
+ * Number of (query, key) pairs the band kernel launch scores per forward: the
+ * pairs of the rows not in G, plus those of the global rows where the band
+ * launch also computes them (bf16 with D = 64; elsewhere a separate kernel
+ * does).  The figure a per-kernel throughput is computed from.
+ */
+lfattn_status lfattn_band_launch_pairs(lfattn_t ctx, long long* pairs);
+
+/*
  * The canonical global list the handle uses: sorted, without repeats.
  * Writes min(n, capacity) positions to out (may be NULL when capacity is 0)
  * and the full count n to *n_out.
@@ -123,8 +131,10 @@ lfattn_status lfattn_global_list(lfattn_t ctx, int* out, int capacity, int* n_ou
  * kernel's own begin and end timestamps (at most 4096 forwards are recorded;
  * later ones run untimed).  lfattn_read_timing waits for the recorded events
  * and returns, summed over the recorded forwards, the milliseconds of the band
- * kernel and of the global-row kernels (partials plus merge; 0 without global
- * positions) and the number of forwards recorded, then clears the record.
+ * kernel and of the global-row kernels (0 without global positions): the
+ * partial and merge kernels, or only the merge where the band launch also
+ * computes the global rows' partials (bf16 with D = 64).  Also the number of
+ * forwards recorded; then clears the record.
  * Enabling or disabling also clears it.
  */
 lfattn_status lfattn_set_timing(lfattn_t ctx, int enable);

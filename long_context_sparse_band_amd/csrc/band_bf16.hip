@@ -820,9 +820,14 @@ void band32_kernel(BandArgs a) {
   const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
   const int qblk = wave & 1, kh = wave >> 1;
   const BandWork w = a.work[blockIdx.x];
+  // A global-row item is the band problem over plain key positions (d = 1),
+  // with a half-width no key reaches past and its rows taken from the global
+  // list, restricted to one key chunk.
+  const bool gi = w.kind != 0;
   const int h = w.bh % a.H;
-  const int d = a.dil[h];
-  const int r = w.r, t0 = w.t0, hw = a.hw, N = a.N;
+  const int d = gi ? 1 : a.dil[h];
+  const int r = gi ? 0 : w.r, t0 = gi ? 0 : w.t0, N = a.N;
+  const int hw = gi ? (1 << 29) : a.hw;
   const int Lr = (N - r + d - 1) / d;
   const size_t base = (size_t)w.bh * N * D;
   const unsigned short* Qp = (const unsigned short*)a.Q + base;
@@ -840,19 +845,22 @@ void band32_kernel(BandArgs a) {
     gv[it] = x < n_glob ? a.glob[x] : 0;
   }
 
-  // This wave's rows: subsequence positions ua .. ub (one per lane % 32).
-  const int ua = t0 + 32 * qblk;
-  const int ub = min(ua + 31, Lr - 1);
-  const bool live = ua < Lr;
-  const int s_lo = max(0, t0 - hw);
-  const int s_hi = min(Lr - 1, t0 + ROWS - 1 + hw);
+  // This wave's rows: subsequence positions ua .. ub (one per lane % 32); for
+  // a global-row item, slots of the global list, and keys s_lo .. s_hi.
+  const int n_rows = gi ? n_glob : Lr;
+  const int ua = (gi ? kGlobItemRows * w.r : t0) + 32 * qblk;
+  const int ub = min(ua + 31, n_rows - 1);
+  const bool live = ua < n_rows;
+  const int s_lo = gi ? w.t0 * a.chunk_keys : max(0, t0 - hw);
+  const int s_hi = gi ? min(N, s_lo + a.chunk_keys) - 1 : min(Lr - 1, t0 + ROWS - 1 + hw);
   const int u = ua + l32;
-  const bool row_ok = u < Lr;
+  const bool row_ok = u < n_rows;
 
   // Q operand (B of S^T = K Q^T): Q[row][16ks + 8hi + 0..7].
   bf16x8 q[D / 16];
   {
-    const size_t row = (size_t)(r + d * (row_ok ? u : 0));
+    const size_t row =
+        gi ? (size_t)(row_ok ? a.glob[u] : 0) : (size_t)(r + d * (row_ok ? u : 0));
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       q[ks] = *(const bf16x8*)(Qp + row * D + 16 * ks + 8 * hi);
@@ -864,14 +872,14 @@ void band32_kernel(BandArgs a) {
   int lo;
   unsigned rng;
   {
-    int l0 = max(u - hw, 0), h0 = min(u + hw, s_hi);
+    int l0 = gi ? s_lo : max(u - hw, 0), h0 = gi ? s_hi : min(u + hw, s_hi);
     if (!row_ok || h0 < l0) { l0 = 0x3fffffff; h0 = l0; }
     lo = l0;
     rng = (unsigned)(h0 - l0);
   }
 
   const int n_band = (s_hi - s_lo) / TK + 1;
-  const int n_tiles = n_band + (n_glob + TK - 1) / TK;
+  const int n_tiles = n_band + (gi ? 0 : (n_glob + TK - 1) / TK);
   const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles kh*n_steps + j
 
   // Direct loads of step j into stage sidx: wave w loads rows 8w..8w+7 of
@@ -1129,10 +1137,27 @@ void band32_kernel(BandArgs a) {
     for (int b = 0; b < D / 32; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[b][i] = acc[b][i] * a0 + mine[2 + 16 * b + i] * a1;
+    m = mn;
   }
 
   const float lt = pair_sum(l);
   if (!row_ok) return;
+  if (gi) {
+    // Partial record of this global row for this key chunk.
+    float* rec = a.part + ((((size_t)w.bh * a.n_sets + w.r) * a.n_chunks + w.t0) * kGlobItemRows +
+                           32 * qblk + l32) * (D + 4);
+    if (hi == 0) {
+      rec[0] = m;
+      rec[1] = lt;
+    }
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(float4*)(rec + 4 + 32 * b + 8 * g4 + 4 * hi) =
+            make_float4(acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2], acc[b][4 * g4 + 3]);
+    return;
+  }
   const int row = r + d * u;
   if (a.is_glob[row]) return;
   const float inv = 1.0f / lt;
@@ -1270,6 +1295,8 @@ int band_bf16_global_cap() { return kGlobCap; }
 int glob_bf16_rows_per_set(int) { return 32; }  // one 32x32 MFMA column block
 
 int band_bf16_rows_per_workgroup(int D) { return D == 64 ? b32::ROWS : kBandRows; }
+
+bool band_takes_global_items(int dtype, int D) { return dtype == 1 && D == 64; }
 
 hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t) {
   if (n_wg <= 0) return hipSuccess;

@@ -25,6 +25,7 @@ constexpr int kEvPerForward = 6;
 constexpr int kXcds = 8;           // MI355X: workgroups go round-robin over 8 XCDs
 constexpr int kMaxChunks = lfattn::kMergeBatch;  // key chunks per global row set
 constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
+constexpr int kGlobItemKeys = 512; // keys per global-row item of the band launch
 constexpr long long kMaxN = 1LL << 29;
 
 }  // namespace
@@ -45,6 +46,7 @@ struct lfattn_ctx {
 
   float* d_part = nullptr;
   int g_waves = 0, g_rows = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
+  bool glob_items = false;  // global-row partials run as items of the band launch
 
   bool timing = false;
   int n_timed = 0;
@@ -190,15 +192,25 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
     for (int x = 0; x < kXcds; ++x)
       for (int bid = x; bid < n_items; bid += kXcds) table[bid] = items[next++];
   }
-  c->n_band_wg = n_items;
 
   // Global rows: sets of rows (a workgroup's share of the global rows) times
-  // key chunks, at most kMaxChunks chunks so that the merge reads every
-  // chunk's record in one batch.  bf16: one wavefront of 32 rows per
-  // workgroup, chunks of at least four tiles; fp32: up to four wavefronts of
-  // 32 rows.
+  // key chunks.  Where the band kernel takes them (bf16, D = 64), each
+  // (b, h, 64-row set, 512-key chunk) is one more item at the end of the band
+  // launch, so that those workgroups are dispatched last and fill the slots
+  // the band items leave free.  Otherwise a separate kernel: bf16 one
+  // wavefront of 32 rows per workgroup, chunks of at least four tiles; fp32 up
+  // to four wavefronts of 32 rows; at most kMaxChunks chunks.
   const int n_g = (int)c->glob.size();
-  if (n_g > 0) {
+  c->glob_items = n_g > 0 && lfattn::band_takes_global_items(dtype, D);
+  if (c->glob_items) {
+    c->g_rows = lfattn::kGlobItemRows;
+    c->n_sets = (n_g + c->g_rows - 1) / c->g_rows;
+    c->chunk_keys = kGlobItemKeys;
+    c->n_chunks = (N + kGlobItemKeys - 1) / kGlobItemKeys;
+    for (int bh = 0; bh < B * H; ++bh)
+      for (int set = 0; set < c->n_sets; ++set)
+        for (int ch = 0; ch < c->n_chunks; ++ch) table.push_back(BandWork{bh, set, ch, 1});
+  } else if (n_g > 0) {
     const bool bf16 = dtype == LFATTN_BF16;
     int rows_per_set;
     if (bf16) {
@@ -221,6 +233,8 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
     c->n_chunks = (N + per - 1) / per;
     c->n_glob_wg = (int)(bhs * c->n_chunks);
   }
+  if (table.size() > (size_t)INT32_MAX) { free_ctx(c); return LFATTN_EUNSUPPORTED; }
+  c->n_band_wg = (int)table.size();
 
   // ---- device state ----
   lfattn_status st = LFATTN_OK;
@@ -288,7 +302,8 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
     g.rows_per_set = c->g_rows;
     g.n_sets = c->n_sets; g.n_chunks = c->n_chunks; g.chunk_keys = c->chunk_keys;
     g.sl2 = sl2;
-    if (lfattn::launch_glob(c->dtype, c->D, c->g_waves, g, c->n_glob_wg, stream, t_part) != hipSuccess)
+    if (!c->glob_items &&
+        lfattn::launch_glob(c->dtype, c->D, c->g_waves, g, c->n_glob_wg, stream, t_part) != hipSuccess)
       return LFATTN_EHIP;
   }
 
@@ -296,6 +311,8 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
   a.Q = Q; a.K = K; a.V = V; a.O = O;
   a.work = c->d_work; a.dil = c->d_dil; a.glob = c->d_glob; a.is_glob = c->d_isglob;
   a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
+  a.part = c->glob_items ? c->d_part : nullptr;
+  a.n_sets = c->n_sets; a.n_chunks = c->n_chunks; a.chunk_keys = c->chunk_keys;
   if (lfattn::launch_band(c->dtype, c->D, a, c->n_band_wg, stream, t_band) != hipSuccess)
     return LFATTN_EHIP;
 
@@ -316,6 +333,13 @@ lfattn_status lfattn_destroy(lfattn_t c) {
 lfattn_status lfattn_scored_pairs(lfattn_t c, long long* pairs) {
   if (!c || !pairs) return LFATTN_EINVAL;
   *pairs = c->pairs;
+  return LFATTN_OK;
+}
+
+lfattn_status lfattn_band_launch_pairs(lfattn_t c, long long* pairs) {
+  if (!c || !pairs) return LFATTN_EINVAL;
+  const long long glob_rows = (long long)c->B * c->H * (long long)c->glob.size() * c->N;
+  *pairs = c->glob_items ? c->pairs : c->pairs - glob_rows;
   return LFATTN_OK;
 }
 
@@ -357,9 +381,9 @@ lfattn_status lfattn_read_timing(lfattn_t c, double* band_ms, double* global_ms,
     hipEvent_t* e = &c->ev[kEvPerForward * t];
     float x = 0.0f, y = 0.0f, z = 0.0f;
     if (hipEventElapsedTime(&x, e[0], e[1]) != hipSuccess) return LFATTN_EHIP;
-    if (has_glob && (hipEventElapsedTime(&y, e[2], e[3]) != hipSuccess ||
-                     hipEventElapsedTime(&z, e[4], e[5]) != hipSuccess))
+    if (has_glob && !c->glob_items && hipEventElapsedTime(&y, e[2], e[3]) != hipSuccess)
       return LFATTN_EHIP;
+    if (has_glob && hipEventElapsedTime(&z, e[4], e[5]) != hipSuccess) return LFATTN_EHIP;
     b += x;
     g += y + z;
   }

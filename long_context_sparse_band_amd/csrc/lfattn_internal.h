@@ -22,11 +22,14 @@ constexpr int kMergeBatch = 16;
 
 // One band workgroup's work: batch-head bh, dilation residue r, and the first
 // position t0 (in the residue's subsequence r, r+d, r+2d, ...) of its rows.
+// With kind = 1 (kernels that take global-row work in the same launch) the
+// item is instead 64 global rows (set r of the sorted global list) against
+// key chunk t0, and it writes a partial (m, l, acc) record per row.
 struct BandWork {
   int bh;
   int r;
   int t0;
-  int pad;
+  int kind;
 };
 
 struct BandArgs {
@@ -40,6 +43,10 @@ struct BandArgs {
   const unsigned char* is_glob;  // [N] 1 where the position is global
   int H, N, hw, n_glob;
   float sl2;                   // softmax scale times log2(e)
+  // Global-row items (kind 1): partial records laid out as GlobArgs::part
+  // with 64 rows per set, and the chunking of the keys.
+  float* part;
+  int n_sets, n_chunks, chunk_keys;
 };
 
 struct GlobArgs {
@@ -79,6 +86,10 @@ hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_
 hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t);
 hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t);
 int glob_bf16_rows_per_set(int n_glob);
+// Whether the band kernel for this element type and D also takes the
+// global-row items (kind 1) in its launch, with 64 rows per set.
+bool band_takes_global_items(int dtype, int D);
+constexpr int kGlobItemRows = 64;
 // Query rows one band workgroup covers for the given element type and D.
 int band_rows_per_workgroup(int dtype, int D);
 int band_bf16_rows_per_workgroup(int D);

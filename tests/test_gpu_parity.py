@@ -325,3 +325,21 @@ def test_timing_records_both_kernels():
         L.lfattn_set_timing(h, False)
     finally:
         L.lfattn_destroy(h)
+
+
+@pytest.mark.parametrize("dtype,D,with_glob_rows", [(L.LFATTN_BF16, 64, True),
+                                                    (L.LFATTN_BF16, 128, False),
+                                                    (L.LFATTN_F32, 64, False)])
+def test_band_launch_pairs(dtype, D, with_glob_rows):
+    # The band launch scores every pair of the rows outside G, plus the global
+    # rows' pairs where it also computes their partials (bf16, D = 64).
+    glob = [0, 7, 300]
+    B, H, N = 1, 2, 1000
+    h = L.lfattn_create(B, H, N, D, dtype, 256, None, glob)
+    try:
+        total = L.lfattn_scored_pairs(h)
+        band = L.lfattn_band_launch_pairs(h)
+    finally:
+        L.lfattn_destroy(h)
+    assert total == oracle.count_pairs(B, H, N, 256, None, glob)
+    assert band == (total if with_glob_rows else total - B * H * len(glob) * N)
