@@ -596,72 +596,88 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
   }
 }
 
-// Merge of the global-row partials: one thread per (global row, 4 columns).
-// The records of up to kMergeBatch chunks are loaded together (independent
-// loads, one memory round trip), then combined against their common maximum.
+// Merge of the global-row partials: one workgroup per (batch-head, global
+// row); thread (g, q) combines chunks g, g + 16, ... for columns 4q .. 4q+3
+// (D = 64: 16 column quads; D = 128: each thread takes two quads), then the
+// 16 chunk groups are combined through LDS.  Every chunk record is loaded
+// once, in one round of independent loads per thread.
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
   typedef typename ElemT<BF16>::type E;
   constexpr int REC = D + 4;
-  constexpr int U = kMergeBatch;
+  constexpr int NQ = D / 4;          // column quads
+  constexpr int QPT = NQ / 16;       // quads per thread
+  constexpr int NG = 16;             // chunk groups
+  __shared__ float sm_m[NG][16], sm_l[NG][16];
+  __shared__ float4 sm_a[NG][NQ];
+  const int slot = blockIdx.x % a.n_glob;
+  const int bh = blockIdx.x / a.n_glob;
+  const int q0 = threadIdx.x & 15, g = threadIdx.x >> 4;
   const int rows = a.rows_per_set;
-  const long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)a.n_bh * a.n_glob * (D / 4);
-  if (x >= total) return;
-  const int dq = (int)(x % (D / 4));
-  const long long rs = x / (D / 4);
-  const int slot = (int)(rs % a.n_glob);
-  const int bh = (int)(rs / a.n_glob);
   const int set = slot / rows, rr = slot % rows;
-  const float* part0 =
-      a.part + ((size_t)(bh * a.n_sets + set) * a.n_chunks * rows + rr) * REC;
-  const size_t cs = (size_t)rows * REC;  // stride between chunks
-  const int nc = a.n_chunks;
+  const float* part0 = a.part + ((size_t)(bh * a.n_sets + set) * a.n_chunks * rows + rr) * REC;
+  const size_t cs = (size_t)rows * REC;
   float m = kNegInit, l = 0.0f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = 0; c < nc; c += U) {
-    float mm[U], ll[U];
-    float4 aa[U];
+  float4 acc[QPT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c + u < nc) {
-        const float* rec = part0 + (size_t)(c + u) * cs;
-        const float2 ml = *(const float2*)rec;
-        mm[u] = ml.x;
-        ll[u] = ml.y;
-        aa[u] = *(const float4*)(rec + 4 + 4 * dq);
-      } else {
-        mm[u] = kNegInit;
-        ll[u] = 0.0f;
-        aa[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+  for (int t = 0; t < QPT; ++t) acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = g; c < a.n_chunks; c += NG) {
+    const float* rec = part0 + (size_t)c * cs;
+    const float2 ml = *(const float2*)rec;
+    float4 v[QPT];
+#pragma unroll
+    for (int t = 0; t < QPT; ++t) v[t] = *(const float4*)(rec + 4 + 4 * (q0 + 16 * t));
+    const float mn = fmaxf(m, ml.x);
+    const float a0 = fast_exp2(m - mn), a1 = fast_exp2(ml.x - mn);
+    l = l * a0 + ml.y * a1;
+#pragma unroll
+    for (int t = 0; t < QPT; ++t) {
+      acc[t].x = acc[t].x * a0 + v[t].x * a1;
+      acc[t].y = acc[t].y * a0 + v[t].y * a1;
+      acc[t].z = acc[t].z * a0 + v[t].z * a1;
+      acc[t].w = acc[t].w * a0 + v[t].w * a1;
     }
-    float mx = m;
-#pragma unroll
-    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mm[u]);
-    const float sc = fast_exp2(m - mx);
-    l *= sc;
-    acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float wgt = fast_exp2(mm[u] - mx);
-      l += ll[u] * wgt;
-      acc.x += aa[u].x * wgt;
-      acc.y += aa[u].y * wgt;
-      acc.z += aa[u].z * wgt;
-      acc.w += aa[u].w * wgt;
-    }
-    m = mx;
+    m = mn;
   }
-  const float inv = 1.0f / l;
-  E* Op = (E*)a.O + (size_t)bh * a.N * D + (size_t)a.glob[slot] * D + 4 * dq;
-  if constexpr (BF16) {
-    bf16x4 o;
-    o[0] = (__bf16)(acc.x * inv); o[1] = (__bf16)(acc.y * inv);
-    o[2] = (__bf16)(acc.z * inv); o[3] = (__bf16)(acc.w * inv);
-    *(bf16x4*)Op = o;
-  } else {
-    *(float4*)Op = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  sm_m[g][q0] = m;
+  sm_l[g][q0] = l;
+#pragma unroll
+  for (int t = 0; t < QPT; ++t) sm_a[g][q0 + 16 * t] = acc[t];
+  __syncthreads();
+  if (g != 0) return;
+  float mt = kNegInit;
+#pragma unroll
+  for (int x = 0; x < NG; ++x) mt = fmaxf(mt, sm_m[x][q0]);
+  float lt = 0.0f;
+  float4 at[QPT];
+#pragma unroll
+  for (int t = 0; t < QPT; ++t) at[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int x = 0; x < NG; ++x) {
+    const float wgt = fast_exp2(sm_m[x][q0] - mt);
+    lt += sm_l[x][q0] * wgt;
+#pragma unroll
+    for (int t = 0; t < QPT; ++t) {
+      const float4 v = sm_a[x][q0 + 16 * t];
+      at[t].x += v.x * wgt;
+      at[t].y += v.y * wgt;
+      at[t].z += v.z * wgt;
+      at[t].w += v.w * wgt;
+    }
+  }
+  const float inv = 1.0f / lt;
+  E* Orow = (E*)a.O + (size_t)bh * a.N * D + (size_t)a.glob[slot] * D;
+#pragma unroll
+  for (int t = 0; t < QPT; ++t) {
+    E* Op = Orow + 4 * (q0 + 16 * t);
+    if constexpr (BF16) {
+      bf16x4 o;
+      o[0] = (__bf16)(at[t].x * inv); o[1] = (__bf16)(at[t].y * inv);
+      o[2] = (__bf16)(at[t].z * inv); o[3] = (__bf16)(at[t].w * inv);
+      *(bf16x4*)Op = o;
+    } else {
+      *(float4*)Op = make_float4(at[t].x * inv, at[t].y * inv, at[t].z * inv, at[t].w * inv);
+    }
   }
 }
 
@@ -699,9 +715,10 @@ hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg,
 }
 
 hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s, const Timing& t) {
-  const long long total = (long long)a.n_bh * a.n_glob * (D / 4);
-  if (total <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const long long n_wg = (long long)a.n_bh * a.n_glob;
+  if (n_wg <= 0) return hipSuccess;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n_wg), block(256);
   if (dtype == 1 && D == 64) return launch_kernel(glob_merge_kernel<true, 64>, grid, block, s, a, t);
   if (dtype == 1 && D == 128) return launch_kernel(glob_merge_kernel<true, 128>, grid, block, s, a, t);
   if (dtype == 0 && D == 64) return launch_kernel(glob_merge_kernel<false, 64>, grid, block, s, a, t);
