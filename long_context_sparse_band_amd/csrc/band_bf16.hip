@@ -867,16 +867,9 @@ void band32_kernel(BandArgs a) {
       if (!row_ok) q[ks] = bf16x8{};
     }
   }
-  // Band keys of the lane's row as an interval [lo, lo + rng] of subsequence
-  // positions (empty for rows past the end).
-  int lo;
-  unsigned rng;
-  {
-    int l0 = gi ? s_lo : max(u - hw, 0), h0 = gi ? s_hi : min(u + hw, s_hi);
-    if (!row_ok || h0 < l0) { l0 = 0x3fffffff; h0 = l0; }
-    lo = l0;
-    rng = (unsigned)(h0 - l0);
-  }
+  // A key at position k is in the band of the lane's row u when
+  // |k - u| <= hw and k <= s_hi (keys below 0 never occur: tiles start at
+  // s_lo >= 0).  Rows past the end are never stored, so they need no mask.
 
   const int n_band = (s_hi - s_lo) / TK + 1;
   const int n_tiles = n_band + (gi ? 0 : (n_glob + TK - 1) / TK);
@@ -999,8 +992,11 @@ void band32_kernel(BandArgs a) {
         act = true;
         edge = nvalid < TK;
       } else {
+        // Keep a valid slot unless its key lies in the row's band (then the
+        // band already scored it).  One group of 4 slots at a time, so that
+        // this rare path stays small in registers.
         const unsigned span = 2u * (unsigned)hw;
-#pragma unroll
+#pragma unroll 1
         for (int g4 = 0; g4 < 4; ++g4) {
           const int kk0 = 8 * g4 + 4 * hi;
           const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsp[min(g0 + kk0, kGlobCap - 4)];
@@ -1015,6 +1011,7 @@ void band32_kernel(BandArgs a) {
       }
     }
     if (!act) continue;
+    __builtin_amdgcn_sched_barrier(0);
 
     // S^T = K Q^T.
     f32x16 S;
@@ -1029,11 +1026,19 @@ void band32_kernel(BandArgs a) {
     }
     if (edge) {
       if (band) {
-        const int basek = s_lo + TK * t + 4 * hi - lo;
+        const int s0 = s_lo + TK * t;
+        const unsigned span = 2u * (unsigned)hw;
+        const int e = s0 + 4 * hi - u + hw;  // |key - u| <= hw  <=>  e + br <= 2hw
+        if (s0 + TK - 1 <= s_hi) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const unsigned x = (unsigned)(basek + block_row(i, 0));
-          S[i] = x > rng ? -INFINITY : S[i];
+          for (int i = 0; i < 16; ++i)
+            S[i] = (unsigned)(e + block_row(i, 0)) > span ? -INFINITY : S[i];
+        } else {
+          const int last = s_hi - s0 - 4 * hi;  // keys past s_hi: block row > last
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            S[i] = ((unsigned)(e + block_row(i, 0)) > span) | (block_row(i, 0) > last)
+                       ? -INFINITY : S[i];
         }
       } else {
 #pragma unroll
@@ -1049,6 +1054,7 @@ void band32_kernel(BandArgs a) {
       fresh = false;
     }
 
+    __builtin_amdgcn_sched_barrier(0);
     // Weights, packed to bf16 (the B operand of P.V), and their sum.
     unsigned P[8];
     float ls;
@@ -1085,6 +1091,7 @@ void band32_kernel(BandArgs a) {
       weights(mn);
     }
     l += ls;
+    __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T P^T, V^T read transposed (see the 64-key kernel).
     {
@@ -1141,12 +1148,19 @@ void band32_kernel(BandArgs a) {
   }
 
   const float lt = pair_sum(l);
-  if (!row_ok) return;
+  // Lane-derived values again, from a lane id the compiler cannot fold into
+  // the one computed at entry (so that nothing lane-dependent is kept live
+  // across the loop only for the stores).
+  int lid;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+  const int ehi = lid >> 5, el32 = lid & 31;
+  const int eu = ua + el32;
+  if (eu >= n_rows) return;
   if (gi) {
     // Partial record of this global row for this key chunk.
     float* rec = a.part + ((((size_t)w.bh * a.n_sets + w.r) * a.n_chunks + w.t0) * kGlobItemRows +
-                           32 * qblk + l32) * (D + 4);
-    if (hi == 0) {
+                           32 * qblk + el32) * (D + 4);
+    if (ehi == 0) {
       rec[0] = m;
       rec[1] = lt;
     }
@@ -1154,11 +1168,11 @@ void band32_kernel(BandArgs a) {
     for (int b = 0; b < D / 32; ++b)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        *(float4*)(rec + 4 + 32 * b + 8 * g4 + 4 * hi) =
+        *(float4*)(rec + 4 + 32 * b + 8 * g4 + 4 * ehi) =
             make_float4(acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2], acc[b][4 * g4 + 3]);
     return;
   }
-  const int row = r + d * u;
+  const int row = r + d * eu;
   if (a.is_glob[row]) return;
   const float inv = 1.0f / lt;
   unsigned short* Op = (unsigned short*)a.O + base + (size_t)row * D;
@@ -1169,7 +1183,7 @@ void band32_kernel(BandArgs a) {
       bf16x4 o;
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[c] = (__bf16)(acc[b][4 * g4 + c] * inv);
-      *(bf16x4*)(Op + 32 * b + 8 * g4 + 4 * hi) = o;
+      *(bf16x4*)(Op + 32 * b + 8 * g4 + 4 * ehi) = o;
     }
 }
 
