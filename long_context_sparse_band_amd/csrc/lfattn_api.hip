@@ -25,7 +25,11 @@ constexpr int kEvPerForward = 6;
 constexpr int kXcds = 8;           // MI355X: workgroups go round-robin over 8 XCDs
 constexpr int kMaxChunks = lfattn::kMergeBatch;  // key chunks per global row set
 constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
-constexpr int kGlobItemKeys = 512; // keys per global-row item of the band launch
+// Keys per global-row item of the band launch: short items when the whole
+// launch fits one round of workgroup slots (they then set the critical
+// path), longer ones otherwise (fewer items, less per-item overhead).
+constexpr int kGlobItemKeysShort = 256, kGlobItemKeysLong = 512;
+constexpr int kBand32WorkgroupsPerCu = 4;
 constexpr long long kMaxN = 1LL << 29;
 
 }  // namespace
@@ -187,10 +191,16 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   }
   const int n_items = (int)items.size();
   std::vector<BandWork> table(n_items);
+  // XCD that runs each band item, for placing the global-row items next to
+  // the band items that read the same keys.
+  std::vector<int> item_xcd(n_items);
   {
     int next = 0;
     for (int x = 0; x < kXcds; ++x)
-      for (int bid = x; bid < n_items; bid += kXcds) table[bid] = items[next++];
+      for (int bid = x; bid < n_items; bid += kXcds) {
+        item_xcd[next] = x;
+        table[bid] = items[next++];
+      }
   }
 
   // Global rows: sets of rows (a workgroup's share of the global rows) times
@@ -205,11 +215,46 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   if (c->glob_items) {
     c->g_rows = lfattn::kGlobItemRows;
     c->n_sets = (n_g + c->g_rows - 1) / c->g_rows;
-    c->chunk_keys = kGlobItemKeys;
-    c->n_chunks = (N + kGlobItemKeys - 1) / kGlobItemKeys;
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+    }
+    const long long short_items = (long long)B * H * c->n_sets *
+                                  ((N + kGlobItemKeysShort - 1) / kGlobItemKeysShort);
+    const int keys = n_items + short_items <= (long long)kBand32WorkgroupsPerCu * cus
+                         ? kGlobItemKeysShort : kGlobItemKeysLong;
+    c->chunk_keys = keys;
+    c->n_chunks = (N + keys - 1) / keys;
+    // Each global item goes to the XCD of the residue-0 band item whose rows
+    // start nearest its chunk (that XCD's L2 holds the chunk's K and V rows):
+    // items are queued per XCD and dealt to block indices congruent to it,
+    // falling back to another queue when one runs dry.
+    std::vector<std::vector<BandWork>> q(kXcds);
+    std::vector<int> first_item(B * H, -1);
+    for (int k = 0; k < n_items; ++k)
+      if (first_item[items[k].bh] < 0) first_item[items[k].bh] = k;
     for (int bh = 0; bh < B * H; ++bh)
       for (int set = 0; set < c->n_sets; ++set)
-        for (int ch = 0; ch < c->n_chunks; ++ch) table.push_back(BandWork{bh, set, ch, 1});
+        for (int ch = 0; ch < c->n_chunks; ++ch) {
+          const int d = c->dil[bh % H];
+          const long long key0 = (long long)ch * keys;
+          // residue 0's items come first for this head; its subsequence
+          // position of key0 is key0 / d.
+          const int k = std::min(first_item[bh] + (int)(key0 / d / band_rows), n_items - 1);
+          q[item_xcd[std::max(k, 0)]].push_back(BandWork{bh, set, ch, 1});
+        }
+    size_t left = 0;
+    for (auto& v : q) left += v.size();
+    std::vector<size_t> pos(kXcds, 0);
+    while (left > 0) {
+      int x = (int)(table.size() % kXcds);
+      for (int t = 0; t < kXcds && pos[x] >= q[x].size(); ++t) x = (x + 1) % kXcds;
+      table.push_back(q[x][pos[x]++]);
+      --left;
+    }
   } else if (n_g > 0) {
     const bool bf16 = dtype == LFATTN_BF16;
     int rows_per_set;
