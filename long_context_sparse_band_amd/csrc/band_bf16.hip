@@ -141,6 +141,14 @@ __device__ __forceinline__ void dma16(const void* gaddr, unsigned lds) {
                : "s"(lds), "v"(gaddr)
                : "memory", "m0");
 }
+// The same with the LDS address given as a sum of two wave-uniform parts
+// (one scalar add into M0).
+__device__ __forceinline__ void dma16_2(const void* gaddr, unsigned lds_a, unsigned lds_b) {
+  asm volatile("s_add_u32 m0, %0, %1\n\tglobal_load_lds_dwordx4 %2, off"
+               :
+               : "s"(lds_a), "s"(lds_b), "v"(gaddr)
+               : "memory", "m0", "scc");
+}
 
 // Per-wavefront state: queries, accumulators, softmax state, band intervals,
 // and the per-lane LDS offsets of the MFMA operands inside a tile.
@@ -875,40 +883,54 @@ void band32_kernel(BandArgs a) {
   const int n_tiles = n_band + (gi ? 0 : (n_glob + TK - 1) / TK);
   const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles kh*n_steps + j
 
-  // Direct loads of step j into stage sidx: wave w loads rows 8w..8w+7 of
-  // the K and V tiles of both key halves (4 loads; tiles past the end load a
-  // real row so that every wave issues the same count).
-  auto issue = [&](int j, int sidx) {
-    const int row = RPI * wave + lane / CPR;
-    const int c = swz(row, lane % CPR);
-#pragma unroll
-    for (int hh = 0; hh < KS; ++hh) {
-      const int tj = hh * n_steps + j;
-      const unsigned stb = (unsigned)(uintptr_t)(LDS_AS void*)sm.st[sidx][hh];
-      int grow;
-      if (tj < n_band) grow = r + d * min(s_lo + TK * tj + row, s_hi);
-      else if (tj < n_tiles) grow = sm.gpos[min(TK * (tj - n_band) + row, n_glob - 1)];
-      else grow = r;
-      const size_t off = (size_t)grow * D + 8 * c;
-      dma16(Kp + off, stb + 1024 * wave);
-      dma16(Vp + off, stb + MAT + 1024 * wave);
+  // Direct loads of step j into stage sidx: the two wavefronts of a key
+  // half load that half's K and V tiles, wavefront w rows 16(w&1) + 8e +
+  // lane/8 (e = 0, 1): 4 loads each (tiles past the end load a real row so
+  // that every wavefront issues the same count).
+  const int rbase = 16 * (wave & 1);
+  const unsigned st_base = (unsigned)(uintptr_t)(LDS_AS void*)sm.st[0][kh];
+  constexpr unsigned kStageBytes = KS * 2 * MAT;
+  const int row0 = rbase + (lane >> 3), row1 = row0 + 8;
+  const int c0 = swz(row0, lane & 7), c1 = swz(row1, lane & 7);
+  // LDS destinations of the four loads within a stage.
+  const unsigned ld_k0 = st_base + rbase * RB, ld_v0 = ld_k0 + MAT;
+  const unsigned ld_k1 = ld_k0 + 8 * RB, ld_v1 = ld_v0 + 8 * RB;
+  auto issue = [&](int j, int sidx, bool glob_tile) {
+    const int tj = kh * n_steps + j;
+    const unsigned soff = sidx * kStageBytes;
+    int g0, g1;
+    if (glob_tile) {  // gathered global keys
+      const int x0 = TK * (tj - n_band);
+      g0 = sm.gpos[min(x0 + row0, n_glob - 1)];
+      g1 = sm.gpos[min(x0 + row1, n_glob - 1)];
+    } else {  // band keys (tiles past the end clamp to a real row)
+      const int k0 = s_lo + TK * tj;
+      g0 = r + d * min(k0 + row0, s_hi);
+      g1 = r + d * min(k0 + row1, s_hi);
     }
+    const size_t off0 = (size_t)g0 * D + 8 * c0, off1 = (size_t)g1 * D + 8 * c1;
+    dma16_2(Kp + off0, ld_k0, soff);
+    dma16_2(Vp + off0, ld_v0, soff);
+    dma16_2(Kp + off1, ld_k1, soff);
+    dma16_2(Vp + off1, ld_v1, soff);
+  };
+  auto is_glob_tile = [&](int j) {
+    const int tj = kh * n_steps + j;
+    return tj >= n_band && tj < n_tiles;
   };
 
   // The first stages go out before the global positions are staged unless
   // one of their tiles is a gathered global tile.
   bool early = true;
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-#pragma unroll
-    for (int hh = 0; hh < KS; ++hh) {
-      const int tj = hh * n_steps + j;
-      early &= !(j < n_steps && tj >= n_band && tj < n_tiles);
-    }
+  for (int j = 0; j < NS - 1; ++j) {
+    const int tj = kh * n_steps + j;
+    early &= !(j < n_steps && tj >= n_band && tj < n_tiles);
+  }
   if (early) {
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j)
-      if (j < n_steps) issue(j, j);
+      if (j < n_steps) issue(j, j, is_glob_tile(j));
   }
 #pragma unroll
   for (int it = 0; it < kStageIters; ++it) {
@@ -924,7 +946,7 @@ void band32_kernel(BandArgs a) {
   if (!early) {
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j)
-      if (j < n_steps) issue(j, j);
+      if (j < n_steps) issue(j, j, is_glob_tile(j));
   }
 
   // Whether a global key lies in the band of one of this wave's rows (then
@@ -936,6 +958,32 @@ void band32_kernel(BandArgs a) {
     for (int x = lane; x < n_glob; x += 64) gdup |= (unsigned)(sm.gsp[x] - lo_w) <= span_w;
   }
   gdup = __any(gdup);
+
+  // Per-step flags, one step per lane: whether the wave scores any key of
+  // its tile (act) and whether the tile needs a per-pair mask (edge).
+  // Gathered global tiles are marked active and masked; their keep bits are
+  // worked out in the step itself.
+  unsigned long long act_m = 0, edge_m = 0, glob_m = 0, nglob_m = 0;
+  auto flags = [&](int j0) {
+    const int x = j0 + lane;
+    const int tt = kh * n_steps + x;
+    glob_m = __ballot(tt >= n_band && tt < n_tiles);
+    nglob_m = __ballot(tt + 1 >= n_band && tt + 1 < n_tiles);
+    bool fa = false, fe = false;
+    if (live && x < n_steps && tt < n_tiles) {
+      if (tt < n_band) {
+        const int k0 = s_lo + TK * tt, k1 = min(k0 + TK - 1, s_hi);
+        fa = (k0 <= ub + hw) & (k1 >= ua - hw);
+        fe = !((k1 == k0 + TK - 1) & (k1 - ua <= hw) & (ub - k0 <= hw));
+      } else {
+        fa = true;
+        fe = true;
+      }
+    }
+    act_m = __ballot(fa);
+    edge_m = __ballot(fe);
+  };
+  flags(0);
 
   // Per-lane LDS offsets of the MFMA operands inside a tile.
   unsigned koff[D / 16];
@@ -961,29 +1009,29 @@ void band32_kernel(BandArgs a) {
   float m = kNegInit, l = 0.0f;
   bool fresh = true;  // no tile scored yet: maximum unset
 
-  for (int j = 0; j < n_steps; ++j) {
-    // This wave's loads of step j done (those of the next NS-2 steps may
-    // stay in flight), then every wave's.
-    if (j + NS - 2 < n_steps) wait_vm_lgkm0<2 * KS * (NS - 2)>();
-    else wait_vm_lgkm0<0>();
+  static_assert(NS == 2, "the step loop alternates two stages");
+  for (int j0 = 0; j0 < n_steps; j0 += 64) {
+  if (j0 > 0) flags(j0);
+  const int j1 = min(n_steps, j0 + 64);
+  for (int j = j0; j < j1; ++j, act_m >>= 1, edge_m >>= 1, glob_m >>= 1, nglob_m >>= 1) {
+    // This wave's loads of step j done, then every wave's; then the next
+    // step's loads into the other stage (after the last step they load real
+    // rows nobody reads; the epilogue waits for them before reusing LDS).
+    wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
-    if (j + NS - 1 < n_steps) issue(j + NS - 1, (j + NS - 1) % NS);
+    issue(j + 1, (j + 1) & 1, nglob_m & 1);
 
+    if (!(act_m & 1)) continue;
     const int t = kh * n_steps + j;
-    if (!live || t >= n_tiles) continue;
-    const LDS_AS unsigned char* st = (const LDS_AS unsigned char*)sm.st[j % NS][kh];
-    const unsigned sbase = (unsigned)(uintptr_t)st;
-    const bool band = t < n_band;
+    const unsigned sbase = st_base + (j & 1) * kStageBytes;
+    const LDS_AS unsigned char* st = (const LDS_AS unsigned char*)(uintptr_t)sbase;
+    const bool band = !(glob_m & 1);
 
-    // Whether any row of the wave scores the tile, and whether it needs a
-    // per-pair mask.
-    bool act, edge;
+    // Global tiles: which slots the rows keep.
+    bool edge = edge_m & 1;
     unsigned keep = 0;
-    if (band) {
-      const int k0 = s_lo + TK * t, k1 = min(k0 + TK - 1, s_hi);
-      act = k0 <= ub + hw && k1 >= ua - hw;
-      edge = !(k1 == k0 + TK - 1 && k1 - ua <= hw && ub - k0 <= hw);
-    } else {
+    if (!band) {
+      bool act;
       const int g0 = TK * (t - n_band);
       const int nvalid = min(TK, n_glob - g0);
       if (!gdup) {
@@ -1009,8 +1057,8 @@ void band32_kernel(BandArgs a) {
         act = __any(keep != 0);
         edge = true;
       }
+      if (!act) continue;
     }
-    if (!act) continue;
     __builtin_amdgcn_sched_barrier(0);
 
     // S^T = K Q^T.
@@ -1118,6 +1166,10 @@ void band32_kernel(BandArgs a) {
       }
     }
   }
+
+  }
+  // The loads issued in the last step land before the ring is reused.
+  wait_vm_lgkm0<0>();
 
   // Merge the second key half's state into the first through LDS (the ring
   // is free: every load was waited for in the last step).
