@@ -881,7 +881,7 @@ void band32_kernel(BandArgs a) {
 
   const int n_band = (s_hi - s_lo) / TK + 1;
   const int n_tiles = n_band + (gi ? 0 : (n_glob + TK - 1) / TK);
-  const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles kh*n_steps + j
+  const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles KS*j + kh
 
   // Direct loads of step j into stage sidx: the two wavefronts of a key
   // half load that half's K and V tiles, wavefront w rows 16(w&1) + 8e +
@@ -896,7 +896,7 @@ void band32_kernel(BandArgs a) {
   const unsigned ld_k0 = st_base + rbase * RB, ld_v0 = ld_k0 + MAT;
   const unsigned ld_k1 = ld_k0 + 8 * RB, ld_v1 = ld_v0 + 8 * RB;
   auto issue = [&](int j, int sidx, bool glob_tile) {
-    const int tj = kh * n_steps + j;
+    const int tj = KS * j + kh;
     const unsigned soff = sidx * kStageBytes;
     int g0, g1;
     if (glob_tile) {  // gathered global keys
@@ -915,7 +915,7 @@ void band32_kernel(BandArgs a) {
     dma16_2(Vp + off1, ld_v1, soff);
   };
   auto is_glob_tile = [&](int j) {
-    const int tj = kh * n_steps + j;
+    const int tj = KS * j + kh;
     return tj >= n_band && tj < n_tiles;
   };
 
@@ -924,7 +924,7 @@ void band32_kernel(BandArgs a) {
   bool early = true;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j) {
-    const int tj = kh * n_steps + j;
+    const int tj = KS * j + kh;
     early &= !(j < n_steps && tj >= n_band && tj < n_tiles);
   }
   if (early) {
@@ -966,9 +966,9 @@ void band32_kernel(BandArgs a) {
   unsigned long long act_m = 0, edge_m = 0, glob_m = 0, nglob_m = 0;
   auto flags = [&](int j0) {
     const int x = j0 + lane;
-    const int tt = kh * n_steps + x;
+    const int tt = KS * x + kh;
     glob_m = __ballot(tt >= n_band && tt < n_tiles);
-    nglob_m = __ballot(tt + 1 >= n_band && tt + 1 < n_tiles);
+    nglob_m = __ballot(tt + KS >= n_band && tt + KS < n_tiles);
     bool fa = false, fe = false;
     if (live && x < n_steps && tt < n_tiles) {
       if (tt < n_band) {
@@ -1022,7 +1022,7 @@ void band32_kernel(BandArgs a) {
     issue(j + 1, (j + 1) & 1, nglob_m & 1);
 
     if (!(act_m & 1)) continue;
-    const int t = kh * n_steps + j;
+    const int t = KS * j + kh;
     const unsigned sbase = st_base + (j & 1) * kStageBytes;
     const LDS_AS unsigned char* st = (const LDS_AS unsigned char*)(uintptr_t)sbase;
     const bool band = !(glob_m & 1);
