@@ -784,49 +784,61 @@ void band_bf16_kernel(BandArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 band kernel for D = 64 with 32-key steps (band32_kernel).
+// bf16 band kernel with 32-key steps (band32_kernel<D>, D = 64 or 128).
 //
 // A workgroup of 4 wavefronts takes 64 consecutive rows of one (batch, head,
 // dilation residue): wavefronts 0,1 own rows 0-31 and 32-63 over the first
 // half of the workgroup's 32-key tiles, wavefronts 2,3 the same rows over the
 // second half (partial softmax states merged through LDS at the end).  Each
-// wavefront's state is one 32x32 MFMA block, so a wavefront fits in 128
-// registers and four workgroups (a 2-stage ring of 32-key K/V tiles, 36 KB
-// of LDS each) share a compute unit: four wavefronts per SIMD hide each
-// other's latencies.  Per step and wavefront: S^T = K Q^T (4 MFMAs), mask
-// where a band edge or global dedupe cuts the tile, weights with the lazy
-// rescale, O^T += V^T P^T (4 MFMAs).
+// wavefront's state is one 32x32 MFMA block.  D = 64: a wavefront fits in
+// 128 registers and four workgroups (a 2-stage ring of 32-key K/V tiles, 36
+// KB of LDS each) share a compute unit, four wavefronts per SIMD hiding each
+// other's latencies; D = 128: 256 registers, 68 KB, two per compute unit.
+// Per step and wavefront: S^T = K Q^T (D/16 MFMAs), mask where a band edge
+// or global dedupe cuts the tile, weights with the lazy rescale,
+// O^T += V^T P^T (D/16 MFMAs).
 // ---------------------------------------------------------------------------
-namespace b32 {
-constexpr int TK = 32;          // keys per step
-constexpr int D = 64;
-constexpr int RB = 2 * D;       // bytes per key row
-constexpr int CPR = RB / 16;    // 16-byte chunks per row
-constexpr int RPI = 1024 / RB;  // rows one wave-wide direct load fills (8)
-constexpr int MAT = TK * RB;    // bytes of one K (or V) tile: 4 KB
-constexpr int NLD = TK / RPI;   // direct loads per matrix and tile (4)
-constexpr int KS = 2, NS = 2;
-constexpr int ROWS = 64;        // rows per workgroup
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & 7); }
-struct Smem {
-  unsigned char st[NS][KS][2 * MAT];
-  int gpos[kGlobCap];
-  int gsp[kGlobCap];
+template <int D, int KS_>
+struct B32 {
+  static constexpr int TK = 32;          // keys per step
+  static constexpr int RB = 2 * D;       // bytes per key row
+  static constexpr int CPR = RB / 16;    // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;  // rows one wave-wide direct load fills
+  static constexpr int MAT = TK * RB;    // bytes of one K (or V) tile
+  static constexpr int KS = KS_, NS = 2;  // key halves, ring stages
+  static constexpr int QBLKS = 4 / KS;   // 32-row query blocks per workgroup
+  static constexpr int ROWS = 32 * QBLKS;  // rows per workgroup
+  static constexpr int RPW = TK / QBLKS;   // tile rows each wavefront loads
+  static constexpr int NE = RPW / RPI;   // loads per matrix and wavefront per step
+  static constexpr int WPE = D == 64 ? 4 : 2;  // wavefronts per SIMD
+  // Physical 16-byte chunk of logical chunk c in row `row` (an involution).
+  static __device__ __forceinline__ int swz(int row, int c) {
+    if constexpr (D == 64) return c ^ ((row >> 1) & 7);
+    else return c ^ (row & 15);
+  }
+  struct Smem {
+    unsigned char st[NS][KS][2 * MAT];
+    int gpos[kGlobCap];
+    int gsp[kGlobCap];
+  };
 };
-}  // namespace b32
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
+template <int D, int KS_>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(B32<D, KS_>::WPE, B32<D, KS_>::WPE)))
 void band32_kernel(BandArgs a) {
-  constexpr int TK = b32::TK, D = b32::D, RB = b32::RB, CPR = b32::CPR, RPI = b32::RPI;
-  constexpr int MAT = b32::MAT, NLD = b32::NLD, KS = b32::KS, NS = b32::NS, ROWS = b32::ROWS;
-  static_assert(KS * 2 * NLD == 16, "16 direct loads per step, 4 per wave");
-  __shared__ __attribute__((aligned(16))) b32::Smem sm;
-  auto swz = [](int row, int c) { return b32::swz(row, c); };
+  using C = B32<D, KS_>;
+  constexpr int TK = C::TK, RB = C::RB, CPR = C::CPR, RPI = C::RPI, MAT = C::MAT;
+  constexpr int NE = C::NE, KS = C::KS, NS = C::NS, ROWS = C::ROWS, QBLKS = C::QBLKS;
+  constexpr int RPW = C::RPW;
+  static_assert(QBLKS * NE * RPI == TK, "the wavefronts of a key half load its 32-row tiles");
+  __shared__ __attribute__((aligned(16))) typename C::Smem sm;
+  auto swz = [](int row, int c) { return C::swz(row, c); };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
-  const int qblk = wave & 1, kh = wave >> 1;
+  const int qblk = wave % QBLKS, kh = wave / QBLKS;
   const BandWork w = a.work[blockIdx.x];
   // A global-row item is the band problem over plain key positions (d = 1),
   // with a half-width no key reaches past and its rows taken from the global
@@ -856,7 +868,7 @@ void band32_kernel(BandArgs a) {
   // This wave's rows: subsequence positions ua .. ub (one per lane % 32); for
   // a global-row item, slots of the global list, and keys s_lo .. s_hi.
   const int n_rows = gi ? n_glob : Lr;
-  const int ua = (gi ? kGlobItemRows * w.r : t0) + 32 * qblk;
+  const int ua = (gi ? ROWS * w.r : t0) + 32 * qblk;
   const int ub = min(ua + 31, n_rows - 1);
   const bool live = ua < n_rows;
   const int s_lo = gi ? w.t0 * a.chunk_keys : max(0, t0 - hw);
@@ -884,35 +896,34 @@ void band32_kernel(BandArgs a) {
   const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles KS*j + kh
 
   // Direct loads of step j into stage sidx: the two wavefronts of a key
-  // half load that half's K and V tiles, wavefront w rows 16(w&1) + 8e +
-  // lane/8 (e = 0, 1): 4 loads each (tiles past the end load a real row so
-  // that every wavefront issues the same count).
-  const int rbase = 16 * (wave & 1);
+  // half load that half's K and V tiles, wavefront w rows RPW*qblk + RPI*e +
+  // lane/CPR (e < NE): 2*NE loads each (tiles past the end load a real row
+  // so that every wavefront issues the same count).
+  const int rbase = RPW * qblk;
   const unsigned st_base = (unsigned)(uintptr_t)(LDS_AS void*)sm.st[0][kh];
   constexpr unsigned kStageBytes = KS * 2 * MAT;
-  const int row0 = rbase + (lane >> 3), row1 = row0 + 8;
-  const int c0 = swz(row0, lane & 7), c1 = swz(row1, lane & 7);
-  // LDS destinations of the four loads within a stage.
-  const unsigned ld_k0 = st_base + rbase * RB, ld_v0 = ld_k0 + MAT;
-  const unsigned ld_k1 = ld_k0 + 8 * RB, ld_v1 = ld_v0 + 8 * RB;
+  const int rlane = rbase + lane / CPR;
+  // LDS destination of load e of K within a stage (V: + MAT).
+  const unsigned ld_k = st_base + rbase * RB;
   auto issue = [&](int j, int sidx, bool glob_tile) {
     const int tj = KS * j + kh;
     const unsigned soff = sidx * kStageBytes;
-    int g0, g1;
+    int g[NE];
     if (glob_tile) {  // gathered global keys
       const int x0 = TK * (tj - n_band);
-      g0 = sm.gpos[min(x0 + row0, n_glob - 1)];
-      g1 = sm.gpos[min(x0 + row1, n_glob - 1)];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) g[e] = sm.gpos[min(x0 + rlane + RPI * e, n_glob - 1)];
     } else {  // band keys (tiles past the end clamp to a real row)
       const int k0 = s_lo + TK * tj;
-      g0 = r + d * min(k0 + row0, s_hi);
-      g1 = r + d * min(k0 + row1, s_hi);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) g[e] = r + d * min(k0 + rlane + RPI * e, s_hi);
     }
-    const size_t off0 = (size_t)g0 * D + 8 * c0, off1 = (size_t)g1 * D + 8 * c1;
-    dma16_2(Kp + off0, ld_k0, soff);
-    dma16_2(Vp + off0, ld_v0, soff);
-    dma16_2(Kp + off1, ld_k1, soff);
-    dma16_2(Vp + off1, ld_v1, soff);
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const size_t off = (size_t)g[e] * D + 8 * swz(rlane + RPI * e, lane % CPR);
+      dma16_2(Kp + off, ld_k + 1024 * e, soff);
+      dma16_2(Vp + off, ld_k + MAT + 1024 * e, soff);
+    }
   };
   auto is_glob_tile = [&](int j) {
     const int tj = KS * j + kh;
@@ -1142,7 +1153,7 @@ void band32_kernel(BandArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T P^T, V^T read transposed (see the 64-key kernel).
-    {
+    if constexpr (D == 64) {
       s16x4 vr[2][2][2];  // [k2][b][row0/row1]
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
@@ -1164,6 +1175,26 @@ void band32_kernel(BandArgs a) {
                                                            acc[b], 0, 0, 0);
         }
       }
+    } else {
+      // D = 128: one 16-key k-step at a time (fewer live V operands).
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        s16x4 vr[4][2];  // [b][row0/row1]
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr)
+            vr[b][rr] = ds_read_tr16(sbase + voff[b][rr] + 16 * k2 * RB);
+        lgkm_wait(vr[0][0], vr[0][1], vr[1][0], vr[1][1], vr[2][0], vr[2][1], vr[3][0], vr[3][1]);
+        const uint4 pu = make_uint4(P[4 * k2], P[4 * k2 + 1], P[4 * k2 + 2], P[4 * k2 + 3]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bf16x8 va = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(vr[b][0], vr[b][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8, pu),
+                                                           acc[b], 0, 0, 0);
+        }
+      }
     }
   }
 
@@ -1173,7 +1204,7 @@ void band32_kernel(BandArgs a) {
 
   // Merge the second key half's state into the first through LDS (the ring
   // is free: every load was waited for in the last step).
-  {
+  if constexpr (KS == 2) {
     constexpr int PER = 2 + D / 2;
     static_assert((size_t)2 * 64 * PER * 4 <= sizeof(sm.st), "merge area");
     __syncthreads();
@@ -1210,7 +1241,7 @@ void band32_kernel(BandArgs a) {
   if (eu >= n_rows) return;
   if (gi) {
     // Partial record of this global row for this key chunk.
-    float* rec = a.part + ((((size_t)w.bh * a.n_sets + w.r) * a.n_chunks + w.t0) * kGlobItemRows +
+    float* rec = a.part + ((((size_t)w.bh * a.n_sets + w.r) * a.n_chunks + w.t0) * ROWS +
                            32 * qblk + el32) * (D + 4);
     if (ehi == 0) {
       rec[0] = m;
@@ -1360,9 +1391,11 @@ int band_bf16_global_cap() { return kGlobCap; }
 
 int glob_bf16_rows_per_set(int) { return 32; }  // one 32x32 MFMA column block
 
-int band_bf16_rows_per_workgroup(int D) { return D == 64 ? b32::ROWS : kBandRows; }
+int band_workgroups_per_cu(int dtype, int D) {
+  return dtype == 1 ? (D == 64 ? B32<64, 2>::WPE : B32<128, 2>::WPE) : 2;
+}
 
-bool band_takes_global_items(int dtype, int D) { return dtype == 1 && D == 64; }
+bool band_takes_global_items(int dtype, int D) { return dtype == 1 && (D == 64 || D == 128); }
 
 hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t) {
   if (n_wg <= 0) return hipSuccess;
@@ -1377,8 +1410,10 @@ hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, c
   if (n_wg <= 0) return hipSuccess;
   if (a.n_glob > kGlobCap) return hipErrorInvalidValue;
   const dim3 grid(n_wg), block(256);
-  if (D == 64) return launch_kernel(band32_kernel, grid, block, s, a, t);
-  if (D == 128) return launch_kernel(band_bf16_kernel<128, 1, 1, 2>, grid, block, s, a, t);
+  const bool wide = a.rows_per_wg == 128;  // one tile stream for four row blocks
+  if (!wide && a.rows_per_wg != 64) return hipErrorInvalidValue;
+  if (D == 64) return launch_kernel(wide ? band32_kernel<64, 1> : band32_kernel<64, 2>, grid, block, s, a, t);
+  if (D == 128) return launch_kernel(wide ? band32_kernel<128, 1> : band32_kernel<128, 2>, grid, block, s, a, t);
   return hipErrorInvalidValue;
 }
 

@@ -29,7 +29,7 @@ constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
 // launch fits one round of workgroup slots (they then set the critical
 // path), longer ones otherwise (fewer items, less per-item overhead).
 constexpr int kGlobItemKeysShort = 256, kGlobItemKeysLong = 512;
-constexpr int kBand32WorkgroupsPerCu = 4;
+constexpr int kWideRounds = 3;
 constexpr long long kMaxN = 1LL << 29;
 
 }  // namespace
@@ -49,6 +49,7 @@ struct lfattn_ctx {
   unsigned char* d_isglob = nullptr;
 
   float* d_part = nullptr;
+  int band_rows = 0;  // rows per band workgroup
   int g_waves = 0, g_rows = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
   bool glob_items = false;  // global-row partials run as items of the band launch
 
@@ -175,12 +176,39 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
     c->pairs = total * B;
   }
 
-  // Band work: one item per workgroup's rows (64 or 128) of each (b, h,
-  // residue r) subsequence,
-  // laid out so that the items the hardware sends to one XCD (blockIdx
-  // congruent mod 8) are consecutive query blocks of the same head, which
-  // share their band's K and V rows in that XCD's L2.
-  const int band_rows = lfattn::band_rows_per_workgroup(dtype, D);
+  // Compute units of the device (for sizing the work to one round of slots).
+  int cus = 0;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+    }
+  }
+  const long long slots = (long long)lfattn::band_workgroups_per_cu(dtype, D) * cus;
+
+  // Rows per band workgroup.  fp32: 128.  bf16: 64 (each key half of the
+  // workgroup's tiles on its own pair of wavefronts, twice the workgroups),
+  // or 128 (one tile stream shared by four 32-row blocks: half the K/V loads
+  // per row) when there are enough 64-row blocks to fill the slots
+  // kWideRounds times over.
+  int band_rows = kBandRows;
+  if (dtype == LFATTN_BF16) {
+    long long n64 = 0;
+    for (int h = 0; h < H; ++h) {
+      const int d = c->dil[h];
+      for (int r = 0; r < d && r < N; ++r) n64 += (long long)B * ((N - r + d - 1) / d + 63) / 64;
+    }
+    band_rows = n64 >= kWideRounds * slots ? 128 : 64;
+  }
+  c->band_rows = band_rows;
+
+  // Band work: one item per workgroup's rows of each (b, h, residue r)
+  // subsequence, laid out so that the items the hardware sends to one XCD
+  // (blockIdx congruent mod 8) are consecutive query blocks of the same head,
+  // which share their band's K and V rows in that XCD's L2.
   std::vector<BandWork> items;
   for (int bh = 0; bh < B * H; ++bh) {
     const int d = c->dil[bh % H];
@@ -213,19 +241,11 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   const int n_g = (int)c->glob.size();
   c->glob_items = n_g > 0 && lfattn::band_takes_global_items(dtype, D);
   if (c->glob_items) {
-    c->g_rows = lfattn::kGlobItemRows;
+    c->g_rows = band_rows;  // a global item's rows: one workgroup's rows of G
     c->n_sets = (n_g + c->g_rows - 1) / c->g_rows;
-    int cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0) {
-      (void)hipGetLastError();
-      cus = 256;
-    }
     const long long short_items = (long long)B * H * c->n_sets *
                                   ((N + kGlobItemKeysShort - 1) / kGlobItemKeysShort);
-    const int keys = n_items + short_items <= (long long)kBand32WorkgroupsPerCu * cus
-                         ? kGlobItemKeysShort : kGlobItemKeysLong;
+    const int keys = n_items + short_items <= slots ? kGlobItemKeysShort : kGlobItemKeysLong;
     c->chunk_keys = keys;
     c->n_chunks = (N + keys - 1) / keys;
     // Each global item goes to the XCD of the residue-0 band item whose rows
@@ -356,6 +376,7 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
   a.Q = Q; a.K = K; a.V = V; a.O = O;
   a.work = c->d_work; a.dil = c->d_dil; a.glob = c->d_glob; a.is_glob = c->d_isglob;
   a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
+  a.rows_per_wg = c->band_rows;
   a.part = c->glob_items ? c->d_part : nullptr;
   a.n_sets = c->n_sets; a.n_chunks = c->n_chunks; a.chunk_keys = c->chunk_keys;
   if (lfattn::launch_band(c->dtype, c->D, a, c->n_band_wg, stream, t_band) != hipSuccess)

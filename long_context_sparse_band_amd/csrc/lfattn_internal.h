@@ -23,8 +23,9 @@ constexpr int kMergeBatch = 16;
 // One band workgroup's work: batch-head bh, dilation residue r, and the first
 // position t0 (in the residue's subsequence r, r+d, r+2d, ...) of its rows.
 // With kind = 1 (kernels that take global-row work in the same launch) the
-// item is instead 64 global rows (set r of the sorted global list) against
-// key chunk t0, and it writes a partial (m, l, acc) record per row.
+// item is instead one workgroup's worth of global rows (set r of the sorted
+// global list) against key chunk t0, and it writes a partial (m, l, acc)
+// record per row.
 struct BandWork {
   int bh;
   int r;
@@ -43,8 +44,9 @@ struct BandArgs {
   const unsigned char* is_glob;  // [N] 1 where the position is global
   int H, N, hw, n_glob;
   float sl2;                   // softmax scale times log2(e)
+  int rows_per_wg;             // rows per band workgroup (bf16: 64 or 128)
   // Global-row items (kind 1): partial records laid out as GlobArgs::part
-  // with 64 rows per set, and the chunking of the keys.
+  // with rows_per_wg rows per set, and the chunking of the keys.
   float* part;
   int n_sets, n_chunks, chunk_keys;
 };
@@ -87,12 +89,10 @@ hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, c
 hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t);
 int glob_bf16_rows_per_set(int n_glob);
 // Whether the band kernel for this element type and D also takes the
-// global-row items (kind 1) in its launch, with 64 rows per set.
+// global-row items (kind 1) in its launch (one workgroup's rows per set).
 bool band_takes_global_items(int dtype, int D);
-constexpr int kGlobItemRows = 64;
-// Query rows one band workgroup covers for the given element type and D.
-int band_rows_per_workgroup(int dtype, int D);
-int band_bf16_rows_per_workgroup(int D);
+// Band workgroups one compute unit holds at once (registers and LDS).
+int band_workgroups_per_cu(int dtype, int D);
 hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s,
                        const Timing& t);
 hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s, const Timing& t);

@@ -683,10 +683,6 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
 
 }  // namespace
 
-int band_rows_per_workgroup(int dtype, int D) {
-  return dtype == 1 ? band_bf16_rows_per_workgroup(D) : kBandRows;
-}
-
 hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t) {
   if (n_wg <= 0) return hipSuccess;
   if (dtype == 1) return launch_band_bf16(D, a, n_wg, s, t);

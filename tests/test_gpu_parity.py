@@ -328,11 +328,11 @@ def test_timing_records_both_kernels():
 
 
 @pytest.mark.parametrize("dtype,D,with_glob_rows", [(L.LFATTN_BF16, 64, True),
-                                                    (L.LFATTN_BF16, 128, False),
+                                                    (L.LFATTN_BF16, 128, True),
                                                     (L.LFATTN_F32, 64, False)])
 def test_band_launch_pairs(dtype, D, with_glob_rows):
     # The band launch scores every pair of the rows outside G, plus the global
-    # rows' pairs where it also computes their partials (bf16, D = 64).
+    # rows' pairs where it also computes their partials (bf16).
     glob = [0, 7, 300]
     B, H, N = 1, 2, 1000
     h = L.lfattn_create(B, H, N, D, dtype, 256, None, glob)
