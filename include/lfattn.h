@@ -113,7 +113,7 @@ lfattn_status lfattn_scored_pairs(lfattn_t ctx, long long* pairs);
 /*
  * Number of (query, key) pairs the band kernel launch scores per forward: the
  * pairs of the rows not in G, plus those of the global rows where the band
- * launch also computes them (bf16 with D = 64; elsewhere a separate kernel
+ * launch also computes them (bf16; with fp32 a separate kernel
  * does).  The figure a per-kernel throughput is computed from.
  */
 lfattn_status lfattn_band_launch_pairs(lfattn_t ctx, long long* pairs);
@@ -133,7 +133,7 @@ lfattn_status lfattn_global_list(lfattn_t ctx, int* out, int capacity, int* n_ou
  * and returns, summed over the recorded forwards, the milliseconds of the band
  * kernel and of the global-row kernels (0 without global positions): the
  * partial and merge kernels, or only the merge where the band launch also
- * computes the global rows' partials (bf16 with D = 64).  Also the number of
+ * computes the global rows' partials (bf16).  Also the number of
  * forwards recorded; then clears the record.
  * Enabling or disabling also clears it.
  */

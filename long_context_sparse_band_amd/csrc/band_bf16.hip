@@ -1,18 +1,20 @@
-// bf16 band kernel for gfx950 (MI355X).
+// bf16 band kernel for gfx950 (MI355X): band32_kernel<D, KS>, D = 64 or 128.
 //
-// A workgroup of 4 wavefronts takes 128 consecutive query rows of one (batch,
-// head, dilation residue) and walks the 64-key tiles of their band, then the
-// tiles of gathered global keys.  Each wavefront owns QB blocks of 32 rows
-// (one 32x32 MFMA column block each).  With KS = 2 the workgroup's tile list
-// is split in two halves: wavefronts 0,1 take query blocks 0,1 over the first
-// half and wavefronts 2,3 the same query blocks over the second half; the two
-// partial softmax states of a row are merged through LDS at the end.  This
-// keeps twice as many wavefronts busy on short sequences.
+// A workgroup of 4 wavefronts takes 32*4/KS consecutive query rows of one
+// (batch, head, dilation residue) and walks the 32-key tiles of their band,
+// then the tiles of gathered global keys.  Each wavefront owns one block of
+// 32 rows (one 32x32 MFMA column block).  With KS = 2 the tile list is split
+// between two wavefront pairs (even and odd tiles) and the two partial
+// softmax states of a row are merged through LDS at the end, which keeps
+// twice as many wavefronts busy on short sequences; with KS = 1 four row
+// blocks share one tile stream.  The same launch also takes the global rows:
+// items that run the same code over a chunk of plain key positions with Q
+// gathered from the global positions and write partial softmax records.
 //
 // Memory path: the K and V tiles of a step go global -> LDS with direct loads
-// (global_load_lds_dwordx4) into a ring of NS stages; nothing is staged in
+// (global_load_lds_dwordx4) into a two-stage ring; nothing is staged in
 // registers.  Rows are 16-byte-chunk swizzled so that the MFMA operand reads
-// of 16 consecutive rows hit distinct LDS banks.  V stays row-major: the A
+// of consecutive rows hit distinct LDS banks.  V stays row-major: the A
 // operand of O^T += V^T P^T is read with ds_read_b64_tr_b16, whose lane
 // transpose delivers the 8 keys of one value column that a lane feeds to a
 // 32x32x16 k-step.  The global positions (and their place in the residue's
@@ -20,17 +22,16 @@
 // on a plain global load.
 //
 // Per tile and wavefront: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys on
-// the MFMA rows, queries across lanes, so a lane holds 16 keys of one query;
-// each K read serves the QB query blocks); weights exp2(s*scale*log2e - m)
-// against the running maximum m; P rounded to bf16 is already the B operand
-// of the P.V MFMA, and its row sum is taken with v_dot2_f32_bf16 on the packed
-// pairs (the same rounded weights as the numerator).  The maximum is not
+// the MFMA rows, queries across lanes, so a lane holds 16 keys of one query);
+// weights exp2(s*scale*log2e - m) against the running maximum m; P rounded to
+// bf16 is already the B operand of the P.V MFMA, and its row sum is taken
+// with v_dot2_f32_bf16 on the packed pairs (the same rounded weights as the
+// numerator).  The first scored tile sets the maximum; after that it is not
 // computed in the common case: a tile whose weights sum past 2^8 on any lane
-// (including the first tile, where m starts at -1e30, and any overflow) is
-// redone against its true maximum, rescaling the accumulators.  That is exact
-// because softmax ignores a constant added to all its inputs (Unlimiformer,
-// section 2.3, footnote 3).  32-key halves of a tile that no row of the wave
-// may score are skipped; only halves cut by a band edge evaluate the band
+// is redone against its true maximum, rescaling the accumulators.  That is
+// exact because softmax ignores a constant added to all its inputs
+// (Unlimiformer, section 2.3, footnote 3).  Tiles that no row of the wave
+// may score are skipped; only tiles cut by a band edge evaluate the band
 // predicate.
 //
 // The math is Eq. (1) of the Unlimiformer page (section 2.3) over the pattern
@@ -51,7 +52,6 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int TK = 64;
 constexpr float kNegInit = -1.0e30f;
 constexpr float kSumLimit = 256.0f;
 constexpr int kNotInClass = 0x40000000;
@@ -95,40 +95,7 @@ __device__ __forceinline__ constexpr int block_row(int i, int hi) {
   return 8 * (i >> 2) + 4 * hi + (i & 3);
 }
 
-// Tile geometry for head dimension D.
-template <int D>
-struct Geo {
-  static constexpr int RB = 2 * D;          // bytes per key row
-  static constexpr int CPR = RB / 16;       // 16-byte chunks per row
-  static constexpr int RPI = 1024 / RB;     // rows one wave-wide direct load fills
-  static constexpr int NI = TK / RPI / 4;   // direct loads per wave per matrix and tile
-  static constexpr int MAT = TK * RB;       // bytes of one K (or V) tile
-  // Physical chunk of logical chunk c in row `row` (an involution).  Only the
-  // low row bits enter, so rows 32 apart (the two halves of a tile) and the
-  // 16-row k-steps of the transposed reads share one lane pattern.
-  static __device__ __forceinline__ int swz(int row, int c) {
-    if constexpr (D == 64) return c ^ ((row >> 1) & 7);
-    else return c ^ (row & 15);
-  }
-};
-
 constexpr int kGlobCap = kMaxGlobalBf16;  // global positions staged in LDS
-
-template <int D, int KS, int NS>
-struct Smem {
-  unsigned char st[NS][KS][2 * Geo<D>::MAT];
-  int gpos[kGlobCap];
-  int gsp[kGlobCap];
-};
-
-// Kinds of a 32-key half of a tile for one wavefront.
-constexpr int kOff = 0;   // no row of the wave scores it
-constexpr int kFull = 1;  // every row scores every key
-constexpr int kEdge = 2;  // cut by a band edge: per-pair band predicate
-constexpr int kGlob = 3;  // gathered global keys: per-pair keep bits
-
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgValu = 0x2, kSgMfma = 0x8, kSgDsRead = 0x100, kSgTrans = 0x400;
 
 // One 16-byte direct global -> LDS load: lane i's 16 bytes land at LDS byte
 // address lds + 16*i.  Written as inline assembly so that the compiler does
@@ -150,638 +117,6 @@ __device__ __forceinline__ void dma16_2(const void* gaddr, unsigned lds_a, unsig
                : "memory", "m0", "scc");
 }
 
-// Per-wavefront state: queries, accumulators, softmax state, band intervals,
-// and the per-lane LDS offsets of the MFMA operands inside a tile.
-template <int D, int QB>
-struct Wave {
-  bf16x8 q[QB][D / 16];   // B operand of S^T = K Q^T: Q[row][16ks + 8hi + 0..7]
-  f32x16 acc[QB][D / 32]; // O^T: d = 32b + block_row(i, hi), query = lane % 32
-  float m[QB], l[QB];
-  int lo[QB];             // band keys of a row: subsequence positions lo .. lo + rng
-  unsigned rng[QB];
-  int u[QB];              // subsequence position of the lane's row (>= Lr: none)
-  int Lr;                 // length of the residue's subsequence
-  int hw;                 // band half-width
-  unsigned gsp;           // LDS address of the staged subsequence positions of G
-  unsigned koff[D / 16];  // K operand, k-step ks (the half adds 32 rows)
-  unsigned voff[D / 32][2];  // V^T operand, column block b, rows +0 / +8
-  float sl2;
-  int hi;
-  bool fresh;             // no half scored yet: maxima unset
-};
-
-// S^T for one half (kb): MFMAs on the K rows 32kb .. 32kb+31 of the tile.
-template <int D, int QB, int KB>
-__device__ __forceinline__ void half_scores(const Wave<D, QB>& w, unsigned sbase, f32x16 (&S)[QB]) {
-  using G = Geo<D>;
-  bf16x8 kv[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    kv[ks] = *(const LDS_AS bf16x8*)(uintptr_t)(sbase + w.koff[ks] + 32 * KB * G::RB);
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-      S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks], w.q[qb][ks], S[qb], 0, 0, 0);
-}
-
-// Mask of one half.  kEdge: the band predicate, key in [lo, lo + rng].
-// kGlob (gathered global keys g0 + kk): keep a key unless the row has no
-// valid slot there or the key already lies in the row's band (its position
-// in the residue's subsequence is within hw of the row's).  kTail: keep keys
-// below the end `s0` of a key range.
-constexpr int kTail = 4;
-template <int D, int QB, int KB, int KIND>
-__device__ __forceinline__ void half_mask(const Wave<D, QB>& w, int s0, f32x16 (&S)[QB],
-                                          int nvalid = 0) {
-  if constexpr (KIND == kEdge) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int basek = s0 + 32 * KB + 4 * w.hi - w.lo[qb];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const unsigned x = (unsigned)(basek + block_row(i, 0));
-        S[qb][i] = x > w.rng[qb] ? -INFINITY : S[qb][i];
-      }
-    }
-  } else if constexpr (KIND == kGlob) {
-    const unsigned span = 2u * (unsigned)w.hw;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int kk0 = 32 * KB + 8 * g4 + 4 * w.hi;
-      const i32x4 sp = *(const LDS_AS i32x4*)(uintptr_t)(w.gsp + 4 * (s0 + kk0));
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const bool keep = (kk0 + c < nvalid) & (w.u[qb] < w.Lr) &
-                            ((unsigned)(sp[c] - w.u[qb] + w.hw) > span);
-          S[qb][4 * g4 + c] = keep ? S[qb][4 * g4 + c] : -INFINITY;
-        }
-    }
-  } else if constexpr (KIND == kTail) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        S[qb][i] = 32 * KB + block_row(i, w.hi) < s0 ? S[qb][i] : -INFINITY;
-  }
-}
-
-// Weights of one half, packed to bf16 pairs, with their per-lane sums.
-template <int D, int QB>
-__device__ __forceinline__ void half_weights(const Wave<D, QB>& w, const f32x16 (&S)[QB],
-                                             unsigned (&P)[QB][8], float (&ls)[QB]) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      f32x2 pf;
-      pf[0] = fast_exp2(fmaf(S[qb][i], w.sl2, -w.m[qb]));
-      pf[1] = fast_exp2(fmaf(S[qb][i + 1], w.sl2, -w.m[qb]));
-      const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
-      P[qb][i / 2] = __builtin_bit_cast(unsigned, pb);
-      if (i & 2) s1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s1, false);
-      else s0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s0, false);
-    }
-    ls[qb] = s0 + s1;
-  }
-}
-
-// Accept a half's weights, or (rarely) move the running maxima up to the
-// half's maximum, rescale the accumulators and redo the weights.
-template <int D, int QB>
-__device__ __forceinline__ void half_accept(Wave<D, QB>& w, const f32x16 (&S)[QB],
-                                            unsigned (&P)[QB][8], float (&ls)[QB]) {
-  bool redo = false;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) redo |= !(ls[qb] <= kSumLimit);
-  if (__builtin_expect(__any(redo), 0)) {
-    asm volatile("" ::: "memory");  // keep this a real branch
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
-      const float mn = fmaxf(w.m[qb], pair_max(mx) * w.sl2);
-      const float alpha = fast_exp2(w.m[qb] - mn);
-      w.l[qb] *= alpha;
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w.acc[qb][b][i] *= alpha;
-      w.m[qb] = mn;
-    }
-    half_weights(w, S, P, ls);
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) w.l[qb] += ls[qb];
-}
-
-// O^T += V^T P^T for one half.  V^T operand for k-step ks (keys
-// 16ks..16ks+15) and column block b, read transposed: lane L gets keys
-// 16ks + 4*(L/32) + j (j < 4) and 16ks + 8 + 4*(L/32) + (j-4) (j >= 4) of
-// column 32b + L%32, the key order of the P^T registers 8*(ks%2) .. +7.
-template <int D, int QB, int KB>
-__device__ __forceinline__ void half_pv(Wave<D, QB>& w, unsigned sbase, const unsigned (&P)[QB][8]) {
-  using G = Geo<D>;
-  constexpr int NB = D / 32;
-  bf16x8 va[2][NB];
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const unsigned roff = (16 * (2 * KB + k2)) * G::RB;
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS s16x4*)(uintptr_t)(sbase + w.voff[b][0] + roff));
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (LDS_AS s16x4*)(uintptr_t)(sbase + w.voff[b][1] + roff));
-      va[k2][b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const uint4 pu = make_uint4(P[qb][4 * k2], P[qb][4 * k2 + 1], P[qb][4 * k2 + 2],
-                                    P[qb][4 * k2 + 3]);
-        w.acc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            va[k2][b], __builtin_bit_cast(bf16x8, pu), w.acc[qb][b], 0, 0, 0);
-      }
-}
-
-// One tile for one wavefront, halves of kinds K0 and K1, one half after the
-// other: scores, mask, weights, (rare) rescale, P.V.
-template <int D, int QB, int KB, int KIND>
-__device__ __forceinline__ void half(Wave<D, QB>& w, unsigned sbase, int s0, int nvalid) {
-  f32x16 S[QB];
-  unsigned P[QB][8];
-  float ls[QB];
-  half_scores<D, QB, KB>(w, sbase, S);
-  half_mask<D, QB, KB, KIND>(w, s0, S, nvalid);
-  if (w.fresh) {
-    // First half: start the running maxima at its own maxima.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
-      w.m[qb] = fmaxf(kNegInit, pair_max(mx) * w.sl2);
-    }
-    w.fresh = false;
-  }
-  half_weights(w, S, P, ls);
-  half_accept(w, S, P, ls);
-  half_pv<D, QB, KB>(w, sbase, P);
-}
-
-// s0: first key position of the tile (kEdge), first slot of G (kGlob), or
-// number of valid keys (kTail); nvalid: valid slots (kGlob).
-template <int D, int QB, int K0, int K1>
-__device__ __forceinline__ void tile(Wave<D, QB>& w, unsigned sbase, int s0, int nvalid = 0) {
-  if constexpr (K0 != kOff) half<D, QB, 0, K0>(w, sbase, s0, nvalid);
-  if constexpr (K1 != kOff) half<D, QB, 1, K1>(w, sbase, s0, nvalid);
-}
-
-template <int D, int QB, int KS, int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void band_bf16_kernel(BandArgs a) {
-  using G = Geo<D>;
-  constexpr int RW = 32 * QB;        // rows per wave
-  constexpr int QBLKS = 4 / KS;      // query blocks per workgroup
-  constexpr int BM = RW * QBLKS;     // rows per workgroup
-  constexpr int L = KS * 2 * G::NI;  // direct loads per wave per step
-  static_assert(BM == 128, "a workgroup covers 128 rows");
-  __shared__ __attribute__((aligned(16))) Smem<D, KS, NS> sm;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
-  const int qblk = wave % QBLKS, kh = wave / QBLKS;
-  const BandWork w = a.work[blockIdx.x];
-  const int h = w.bh % a.H;
-  const int d = a.dil[h];
-  const int r = w.r, t0 = w.t0, hw = a.hw, N = a.N;
-  const int Lr = (N - r + d - 1) / d;
-  const size_t base = (size_t)w.bh * N * D;
-  const unsigned short* Qp = (const unsigned short*)a.Q + base;
-  const unsigned short* Kp = (const unsigned short*)a.K + base;
-  const unsigned short* Vp = (const unsigned short*)a.V + base;
-  const int n_glob = a.n_glob;
-
-  // Global positions this thread stages in LDS (loaded first, so that their
-  // latency overlaps the Q loads and the first tile loads).
-  constexpr int kStageIters = (kGlobCap + 255) / 256;
-  int gv[kStageIters];
-#pragma unroll
-  for (int it = 0; it < kStageIters; ++it) {
-    const int x = tid + 256 * it;
-    gv[it] = x < n_glob ? a.glob[x] : 0;
-  }
-
-  // Rows of this wave: subsequence positions ua .. ub.
-  const int ua = t0 + RW * qblk;
-  const int ub = min(ua + RW - 1, Lr - 1);
-  const bool live = ua < Lr;
-  const int s_lo = max(0, t0 - hw);
-  const int s_hi = min(Lr - 1, t0 + BM - 1 + hw);
-
-  // Q operand (B of S^T = K Q^T): Q[row][16ks + 8hi + 0..7].
-  bf16x8 q[QB][D / 16];
-  int u[QB], lo[QB];
-  unsigned rng[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    u[qb] = ua + 32 * qb + l32;
-    const bool ok = u[qb] < Lr;
-    const size_t row = (size_t)(r + d * (ok ? u[qb] : 0));
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      q[qb][ks] = *(const bf16x8*)(Qp + row * D + 16 * ks + 8 * hi);
-      if (!ok) q[qb][ks] = bf16x8{};
-    }
-    // Band keys this row may score, as an interval [lo, lo + rng] of
-    // subsequence positions; rows past the end get an empty interval.
-    int l0 = max(u[qb] - hw, 0), h0 = min(u[qb] + hw, s_hi);
-    if (!ok || h0 < l0) { l0 = 0x3fffffff; h0 = l0; }
-    lo[qb] = l0;
-    rng[qb] = (unsigned)(h0 - l0);
-  }
-
-  f32x16 acc[QB][D / 32];
-  float m[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b) acc[qb][b] = f32x16{};
-    m[qb] = kNegInit;
-    l[qb] = 0.0f;
-  }
-
-  const int n_band = (s_hi - s_lo) / TK + 1;
-  const int n_tiles = n_band + (n_glob + TK - 1) / TK;
-  const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles kh*n_steps + j
-
-
-  // Issue the direct loads of step j into stage sidx: exactly L per wave, so
-  // the ring's vmcnt arithmetic holds (tiles past the end load a real row).
-  auto issue = [&](int j, int sidx) {
-#pragma unroll
-    for (int hh = 0; hh < KS; ++hh) {
-      const int tj = hh * n_steps + j;
-      LDS_AS unsigned char* st = (LDS_AS unsigned char*)sm.st[sidx][hh];
-#pragma unroll
-      for (int e = 0; e < G::NI; ++e) {
-        const int qd = wave + 4 * e;
-        const int row = G::RPI * qd + lane / G::CPR;
-        const int c = G::swz(row, lane % G::CPR);
-        int grow;
-        if (tj < n_band) grow = r + d * min(s_lo + TK * tj + row, s_hi);
-        else if (tj < n_tiles) grow = sm.gpos[min(TK * (tj - n_band) + row, n_glob - 1)];
-        else grow = r;
-        const size_t off = (size_t)grow * D + 8 * c;
-        __builtin_amdgcn_global_load_lds((const void*)(Kp + off), (LDS_AS void*)(st + 1024 * qd), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(Vp + off), (LDS_AS void*)(st + G::MAT + 1024 * qd), 16, 0, 0);
-      }
-    }
-  };
-
-  // The first stages' loads go out before the global positions are staged
-  // unless one of their tiles is a gathered global tile.
-  bool early = true;
-#pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-#pragma unroll
-    for (int hh = 0; hh < KS; ++hh) {
-      const int tj = hh * n_steps + j;
-      early &= !(j < n_steps && tj >= n_band && tj < n_tiles);
-    }
-  if (early) {
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
-      if (j < n_steps) issue(j, j);
-  }
-
-  // Global positions, and where each sits in this residue's subsequence (or
-  // a value no band reaches).
-#pragma unroll
-  for (int it = 0; it < kStageIters; ++it) {
-    const int x = tid + 256 * it;
-    if (x < n_glob) {
-      const int g = gv[it];
-      const int off = g - r;
-      sm.gpos[x] = g;
-      sm.gsp[x] = (off >= 0 && off % d == 0) ? off / d : kNotInClass;
-    }
-  }
-  __syncthreads();  // staged global positions visible
-
-  // Whether a global key lies in the band of one of this wave's rows.  If
-  // not, a global tile needs no per-pair dedupe test, only the count of its
-  // valid slots.
-  bool gdup = false;
-  if (live) {
-    const int lo_w = ua - hw;
-    const unsigned span_w = (unsigned)(ub - ua + 2 * hw);
-    for (int x = lane; x < n_glob; x += 64) gdup |= (unsigned)(sm.gsp[x] - lo_w) <= span_w;
-  }
-  gdup = __any(gdup);
-
-  if (!early) {
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
-      if (j < n_steps) issue(j, j);
-  }
-
-  // Per-lane LDS byte offsets of the MFMA operands inside a tile; the k-step
-  // and the 32-key half enter as immediate offsets.
-  unsigned koff[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * G::RB + 16 * G::swz(l32, 2 * ks + hi);
-  const int g16 = lane >> 4, t16 = lane & 15;
-  unsigned voff[D / 32][2];
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b) {
-    const int dcol = 32 * b + 16 * (g16 & 1) + 4 * (t16 & 3);
-    const int c = dcol >> 3, half = (dcol >> 2) & 1;
-    const int row0 = 4 * (g16 >> 1) + (t16 >> 2), row1 = row0 + 8;
-    voff[b][0] = G::MAT + row0 * G::RB + 16 * G::swz(row0, c) + 8 * half;
-    voff[b][1] = G::MAT + row1 * G::RB + 16 * G::swz(row1, c) + 8 * half;
-  }
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  // Until the wave has scored its first half, the running maxima are unset;
-  // that half starts them at its own maxima instead of going through the
-  // rescale path.
-  bool fresh = true;
-
-  for (int j = 0; j < n_steps; ++j) {
-    // Wait for this wave's loads of step j (those of up to NS-2 later steps
-    // may stay in flight), then for every wave's.
-    if (j + NS - 2 < n_steps) wait_vm_lgkm0<L * (NS - 2)>();
-    else wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    if (j + NS - 1 < n_steps) issue(j + NS - 1, (j + NS - 1) % NS);
-
-    const int t = kh * n_steps + j;
-    if (!live || t >= n_tiles) continue;
-    const LDS_AS unsigned char* st = (const LDS_AS unsigned char*)sm.st[j % NS][kh];
-    const unsigned sbase = (unsigned)(uintptr_t)st;
-    const bool band = t < n_band;
-
-    // Which 32-key halves of the tile any row of this wave scores, and which
-    // of them need the per-pair predicate.
-    bool act[2], edge[2];
-    unsigned keep[QB][2];
-    if (band) {
-      const int s0 = s_lo + TK * t;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int k0 = s0 + 32 * kb, k1 = min(k0 + 31, s_hi);
-        act[kb] = k0 <= s_hi && k0 <= ub + hw && k1 >= ua - hw;
-        edge[kb] = !(k1 == k0 + 31 && k1 - ua <= hw && ub - k0 <= hw);
-      }
-    } else if (!gdup) {
-      // No dedupe needed: keep the valid slots only.
-      const int nvalid = min(TK, n_glob - TK * (t - n_band));
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        act[kb] = 32 * kb < nvalid;
-        edge[kb] = 32 * (kb + 1) > nvalid;
-        unsigned bits = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bits |= (unsigned)(32 * kb + block_row(i, hi) < nvalid) << i;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) keep[qb][kb] = bits;
-      }
-    } else {
-      const int g0 = TK * (t - n_band);
-      const int nvalid = min(TK, n_glob - g0);
-      const unsigned span = 2u * (unsigned)hw;
-      bool any[2] = {false, false};
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          unsigned bits = 0;
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int kk0 = 32 * kb + 8 * g4 + 4 * hi;
-            const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsp[min(g0 + kk0, kGlobCap - 4)];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const bool k = (kk0 + c < nvalid) & (u[qb] < Lr) &
-                             ((unsigned)(sp[c] - u[qb] + hw) > span);
-              bits |= (unsigned)k << (4 * g4 + c);
-            }
-          }
-          keep[qb][kb] = bits;
-          any[kb] |= bits != 0;
-        }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        act[kb] = __any(any[kb]);
-        edge[kb] = true;
-      }
-    }
-    if (!act[0] && !act[1]) continue;
-
-    // Each active 32-key half goes through scores, weights and P.V in turn.
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!act[kb]) continue;
-
-      // S^T = K Q^T for this half (each K read serves all QB query blocks),
-      // then the band or global mask.
-      f32x16 S[QB];
-      {
-        bf16x8 kv[D / 16];
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          kv[ks] = *(const LDS_AS bf16x8*)(st + koff[ks] + 32 * kb * G::RB);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks], q[qb][ks], S[qb], 0, 0, 0);
-      }
-      if (edge[kb]) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if (band) {
-            const int basek = s_lo + TK * t + 32 * kb + 4 * hi - lo[qb];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const unsigned x = (unsigned)(basek + block_row(i, 0));
-              S[qb][i] = x > rng[qb] ? -INFINITY : S[qb][i];
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              S[qb][i] = ((keep[qb][kb] >> i) & 1u) ? S[qb][i] : -INFINITY;
-          }
-        }
-      }
-
-      if (fresh) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
-          m[qb] = fmaxf(kNegInit, pair_max(mx) * a.sl2);
-        }
-        fresh = false;
-      }
-
-      // Weights, packed to bf16 (the B operand of P.V), and their row sums.
-      unsigned P[QB][8];
-      float ls[QB];
-      auto weights = [&](int qb, float mq) {
-        float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          f32x2 pf;
-          pf[0] = fast_exp2(fmaf(S[qb][i], a.sl2, -mq));
-          pf[1] = fast_exp2(fmaf(S[qb][i + 1], a.sl2, -mq));
-          const bf16x2 pb = __builtin_convertvector(pf, bf16x2);
-          P[qb][i / 2] = __builtin_bit_cast(unsigned, pb);
-          if (i & 2) s1 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s1, false);
-          else s0 = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, s0, false);
-        }
-        ls[qb] = s0 + s1;
-      };
-      bool redo = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        weights(qb, m[qb]);
-        redo |= !(ls[qb] <= kSumLimit);
-      }
-      if (__builtin_expect(__any(redo), 0)) {
-        // Move each running maximum up to this half's maximum and redo it.
-        // (The empty volatile statement keeps this rare path a real branch:
-        // executed unconditionally it would double the exps of every tile.)
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
-          const float mn = fmaxf(m[qb], pair_max(mx) * a.sl2);
-          const float alpha = fast_exp2(m[qb] - mn);
-          l[qb] *= alpha;
-#pragma unroll
-          for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[qb][b][i] *= alpha;
-          m[qb] = mn;
-          weights(qb, mn);
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb];
-
-      // O^T += V^T P^T.  V^T operand for k-step ks (keys 16ks..16ks+15) and
-      // column block b, read transposed: lane L gets keys 16ks + 4*(L/32) + j
-      // (j < 4) and 16ks + 8 + 4*(L/32) + (j-4) (j >= 4) of column 32b + L%32,
-      // the same key order as the P^T registers 8*(ks%2) .. +7.
-      constexpr int NB = D / 32;
-      s16x4 vr[2][4][2];  // [k2][b][row0/row1]; b < NB used
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int rr = 0; rr < 2; ++rr)
-            vr[k2][b][rr] = ds_read_tr16(sbase + voff[b][rr] + (16 * (2 * kb + k2)) * G::RB);
-      if constexpr (NB == 2) {
-        lgkm_wait(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1],
-                  vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1]);
-      } else {
-        lgkm_wait(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1],
-                  vr[0][2][0], vr[0][2][1], vr[0][3][0], vr[0][3][1]);
-        lgkm_wait(vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1],
-                  vr[1][2][0], vr[1][2][1], vr[1][3][0], vr[1][3][1]);
-      }
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const bf16x8 va = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(vr[k2][b][0], vr[k2][b][1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const uint4 pu = make_uint4(P[qb][4 * k2], P[qb][4 * k2 + 1], P[qb][4 * k2 + 2],
-                                        P[qb][4 * k2 + 3]);
-            acc[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                va, __builtin_bit_cast(bf16x8, pu), acc[qb][b], 0, 0, 0);
-          }
-        }
-      }
-    }
-  }
-
-  if constexpr (KS == 2) {
-    // Merge the second key half's state into the first through LDS (the
-    // stage buffers are free: every load was waited for in the last step).
-    constexpr int PER = QB * (2 + D / 2);
-    static_assert((size_t)2 * 64 * PER * 4 <= sizeof(sm.st), "merge area");
-    __syncthreads();
-    float* mine = (float*)&sm.st[0][0][0] + ((size_t)qblk * 64 + lane) * PER;
-    if (kh == 1 && live) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        mine[qb * (2 + D / 2)] = m[qb];
-        mine[qb * (2 + D / 2) + 1] = l[qb];
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mine[qb * (2 + D / 2) + 2 + 16 * b + i] = acc[qb][b][i];
-      }
-    }
-    __syncthreads();
-    if (kh == 1 || !live) return;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m1 = mine[qb * (2 + D / 2)], l1 = mine[qb * (2 + D / 2) + 1];
-      const float mn = fmaxf(m[qb], m1);
-      const float a0 = fast_exp2(m[qb] - mn), a1 = fast_exp2(m1 - mn);
-      l[qb] = l[qb] * a0 + l1 * a1;
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          acc[qb][b][i] = acc[qb][b][i] * a0 + mine[qb * (2 + D / 2) + 2 + 16 * b + i] * a1;
-    }
-  } else {
-    if (!live) return;
-  }
-
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = pair_sum(l[qb]);
-    if (u[qb] >= Lr) continue;
-    const int row = r + d * u[qb];
-    if (a.is_glob[row]) continue;
-    const float inv = 1.0f / lt;
-    unsigned short* Op = (unsigned short*)a.O + base + (size_t)row * D;
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 o;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] = (__bf16)(acc[qb][b][4 * g4 + c] * inv);
-        *(bf16x4*)(Op + 32 * b + 8 * g4 + 4 * hi) = o;
-      }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // bf16 band kernel with 32-key steps (band32_kernel<D>, D = 64 or 128).
@@ -1152,7 +487,10 @@ void band32_kernel(BandArgs a) {
     l += ls;
     __builtin_amdgcn_sched_barrier(0);
 
-    // O^T += V^T P^T, V^T read transposed (see the 64-key kernel).
+    // O^T += V^T P^T.  V^T operand for k-step k2 (keys 16k2..16k2+15) and
+    // column block b, read transposed: lane L gets keys 16k2 + 4*(L/32) + j
+    // (j < 4) and 16k2 + 8 + 4*(L/32) + (j-4) (j >= 4) of column 32b + L%32,
+    // the key order of the P^T registers 4*k2 .. 4*k2+3.
     if constexpr (D == 64) {
       s16x4 vr[2][2][2];  // [k2][b][row0/row1]
 #pragma unroll
@@ -1270,141 +608,13 @@ void band32_kernel(BandArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Global-row partials (bf16): the rows of global tokens score every key.  One
-// wavefront per workgroup takes QB blocks of 32 global rows of one (batch,
-// head) and one chunk of keys, streams the chunk's 64-key tiles through its
-// own LDS ring with the same tile code as the band kernel (no band mask; the
-// ragged last tile uses keep bits), and writes a partial record (m, l, acc)
-// per row.  glob_merge_kernel combines the chunks after the band kernel.
-// ---------------------------------------------------------------------------
-template <int D, int QB, int NS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void glob_bf16_kernel(GlobArgs a) {
-  using G = Geo<D>;
-  constexpr int ROWS = 32 * QB;
-  constexpr int LPT = TK / G::RPI;  // direct loads per matrix per tile (one wave)
-  constexpr int L = 2 * LPT;
-  constexpr int REC = D + 4;
-  __shared__ __attribute__((aligned(16))) unsigned char st[NS][2 * G::MAT];
-
-  const int lane = threadIdx.x, hi = lane >> 5, l32 = lane & 31;
-  const int chunk = blockIdx.x % a.n_chunks;
-  const int bhs = blockIdx.x / a.n_chunks;
-  const int bh = bhs / a.n_sets, set = bhs % a.n_sets;
-  const int N = a.N;
-  const size_t base = (size_t)bh * N * D;
-  const unsigned short* Qp = (const unsigned short*)a.Q + base;
-  const unsigned short* Kp = (const unsigned short*)a.K + base;
-  const unsigned short* Vp = (const unsigned short*)a.V + base;
-  const int c0 = chunk * a.chunk_keys;
-  const int c1 = min(N, c0 + a.chunk_keys);
-  const int n_t = (c1 - c0 + TK - 1) / TK;
-
-  Wave<D, QB> w;
-  w.sl2 = a.sl2;
-  w.hi = hi;
-  w.fresh = true;
-  int slot[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    slot[qb] = set * ROWS + 32 * qb + l32;
-    const bool ok = slot[qb] < a.n_glob;
-    const size_t row = ok ? (size_t)a.glob[slot[qb]] : 0;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      w.q[qb][ks] = *(const bf16x8*)(Qp + row * D + 16 * ks + 8 * hi);
-      if (!ok) w.q[qb][ks] = bf16x8{};
-    }
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b) w.acc[qb][b] = f32x16{};
-    w.m[qb] = kNegInit;
-    w.l[qb] = 0.0f;
-    w.lo[qb] = 0;
-    w.rng[qb] = 0;
-  }
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) w.koff[ks] = l32 * G::RB + 16 * G::swz(l32, 2 * ks + hi);
-  {
-    const int g16 = lane >> 4, t16 = lane & 15;
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b) {
-      const int dcol = 32 * b + 16 * (g16 & 1) + 4 * (t16 & 3);
-      const int c = dcol >> 3, half = (dcol >> 2) & 1;
-      const int row0 = 4 * (g16 >> 1) + (t16 >> 2), row1 = row0 + 8;
-      w.voff[b][0] = G::MAT + row0 * G::RB + 16 * G::swz(row0, c) + 8 * half;
-      w.voff[b][1] = G::MAT + row1 * G::RB + 16 * G::swz(row1, c) + 8 * half;
-    }
-  }
-
-  // Direct loads of tile j into stage sidx (rows past the chunk repeat its
-  // last key; they are masked).
-  auto issue = [&](int j, int sidx) {
-    const unsigned sb = (unsigned)(uintptr_t)(LDS_AS void*)st[sidx];
-#pragma unroll
-    for (int qd = 0; qd < LPT; ++qd) {
-      const int row = G::RPI * qd + lane / G::CPR;
-      const int c = G::swz(row, lane % G::CPR);
-      const size_t off = (size_t)min(c0 + TK * j + row, c1 - 1) * D + 8 * c;
-      dma16(Kp + off, sb + 1024 * qd);
-      dma16(Vp + off, sb + G::MAT + 1024 * qd);
-    }
-  };
-#pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (j < n_t) issue(j, j);
-
-  for (int j = 0; j < n_t; ++j) {
-    if (j + NS - 2 < n_t) wait_vm_lgkm0<L * (NS - 2)>();
-    else wait_vm_lgkm0<0>();
-    if (j + NS - 1 < n_t) issue(j + NS - 1, (j + NS - 1) % NS);
-    const unsigned sbase = (unsigned)(uintptr_t)(LDS_AS void*)st[j % NS];
-    const int j0 = c0 + TK * j;
-    if (j0 + TK <= c1) tile<D, QB, kFull, kFull>(w, sbase, 0);
-    else tile<D, QB, kTail, kTail>(w, sbase, c1 - j0);
-  }
-
-  // Partial record of each row for this chunk.
-  float* part = a.part + ((size_t)bhs * a.n_chunks + chunk) * ROWS * REC;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = pair_sum(w.l[qb]);
-    if (slot[qb] >= a.n_glob) continue;
-    float* rec = part + (size_t)(32 * qb + l32) * REC;
-    if (hi == 0) {
-      rec[0] = w.m[qb];
-      rec[1] = lt;
-    }
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *(float4*)(rec + 4 + 32 * b + 8 * g4 + 4 * hi) =
-            make_float4(w.acc[qb][b][4 * g4], w.acc[qb][b][4 * g4 + 1], w.acc[qb][b][4 * g4 + 2],
-                        w.acc[qb][b][4 * g4 + 3]);
-  }
-}
-
 }  // namespace
-
-int band_bf16_global_cap() { return kGlobCap; }
-
-int glob_bf16_rows_per_set(int) { return 32; }  // one 32x32 MFMA column block
 
 int band_workgroups_per_cu(int dtype, int D) {
   return dtype == 1 ? (D == 64 ? B32<64, 2>::WPE : B32<128, 2>::WPE) : 2;
 }
 
 bool band_takes_global_items(int dtype, int D) { return dtype == 1 && (D == 64 || D == 128); }
-
-hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t) {
-  if (n_wg <= 0) return hipSuccess;
-  if (a.rows_per_set != 32) return hipErrorInvalidValue;
-  const dim3 grid(n_wg), block(64);
-  if (D == 64) return launch_kernel(glob_bf16_kernel<64, 1, 3>, grid, block, s, a, t);
-  if (D == 128) return launch_kernel(glob_bf16_kernel<128, 1, 2>, grid, block, s, a, t);
-  return hipErrorInvalidValue;
-}
 
 hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t) {
   if (n_wg <= 0) return hipSuccess;

@@ -189,11 +189,11 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   }
   const long long slots = (long long)lfattn::band_workgroups_per_cu(dtype, D) * cus;
 
-  // Rows per band workgroup.  fp32: 128.  bf16: 64 (each key half of the
-  // workgroup's tiles on its own pair of wavefronts, twice the workgroups),
-  // or 128 (one tile stream shared by four 32-row blocks: half the K/V loads
-  // per row) when there are enough 64-row blocks to fill the slots
-  // kWideRounds times over.
+  // Rows per band workgroup.  fp32: 128.  bf16: 64 (the workgroup's key tiles
+  // split in two halves, each on its own pair of 32-row wavefronts: twice the
+  // workgroups), or 128 (one tile stream shared by four 32-row blocks: half
+  // the K/V loads per row) when there are enough 64-row blocks to fill the
+  // slots kWideRounds times over.
   int band_rows = kBandRows;
   if (dtype == LFATTN_BF16) {
     long long n64 = 0;
@@ -232,12 +232,10 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   }
 
   // Global rows: sets of rows (a workgroup's share of the global rows) times
-  // key chunks.  Where the band kernel takes them (bf16, D = 64), each
-  // (b, h, 64-row set, 512-key chunk) is one more item at the end of the band
-  // launch, so that those workgroups are dispatched last and fill the slots
-  // the band items leave free.  Otherwise a separate kernel: bf16 one
-  // wavefront of 32 rows per workgroup, chunks of at least four tiles; fp32 up
-  // to four wavefronts of 32 rows; at most kMaxChunks chunks.
+  // key chunks.  bf16: each (b, h, row set, 256- or 512-key chunk) is one more
+  // item at the end of the band launch, so that those workgroups are
+  // dispatched last and fill the slots the band items leave free.  fp32: a
+  // separate kernel (below).
   const int n_g = (int)c->glob.size();
   c->glob_items = n_g > 0 && lfattn::band_takes_global_items(dtype, D);
   if (c->glob_items) {
@@ -276,20 +274,15 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
       --left;
     }
   } else if (n_g > 0) {
-    const bool bf16 = dtype == LFATTN_BF16;
-    int rows_per_set;
-    if (bf16) {
-      rows_per_set = lfattn::glob_bf16_rows_per_set(n_g);
-      c->g_waves = 1;
-    } else {
-      c->g_waves = n_g <= 32 ? 1 : (n_g <= 64 ? 2 : 4);
-      rows_per_set = c->g_waves * kWaveRows;
-    }
+    // fp32: a separate kernel, up to four wavefronts of 32 rows per
+    // workgroup, at most kMaxChunks key chunks.
+    c->g_waves = n_g <= 32 ? 1 : (n_g <= 64 ? 2 : 4);
+    const int rows_per_set = c->g_waves * kWaveRows;
     c->g_rows = rows_per_set;
     c->n_sets = (n_g + rows_per_set - 1) / rows_per_set;
     const long long bhs = (long long)B * H * c->n_sets;
     const int tiles = (N + kTileKeys - 1) / kTileKeys;
-    const int max_chunks = std::min(kMaxChunks, bf16 ? std::max(1, tiles / 4) : tiles);
+    const int max_chunks = std::min(kMaxChunks, tiles);
     int chunks = (int)std::min<long long>(max_chunks, (kGlobTarget + bhs - 1) / bhs);
     chunks = std::max(1, chunks);
     int per = (N + chunks - 1) / chunks;

@@ -86,8 +86,6 @@ inline hipError_t launch_kernel(void (*k)(A), dim3 grid, dim3 block, hipStream_t
 // Launchers (defined next to the kernels).  dtype: 0 fp32, 1 bf16.
 hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t);
 hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t);
-hipError_t launch_glob_bf16(int D, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t);
-int glob_bf16_rows_per_set(int n_glob);
 // Whether the band kernel for this element type and D also takes the
 // global-row items (kind 1) in its launch (one workgroup's rows per set).
 bool band_takes_global_items(int dtype, int D);

@@ -704,7 +704,7 @@ static hipError_t launch_glob_f32(int waves, const GlobArgs& a, int n_wg, hipStr
 hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s,
                        const Timing& t) {
   if (n_wg <= 0) return hipSuccess;
-  if (dtype == 1) return launch_glob_bf16(D, a, n_wg, s, t);
+  // (bf16: the band launch takes the global rows; no separate kernel.)
   if (dtype == 0 && D == 64) return launch_glob_f32<64>(waves, a, n_wg, s, t);
   if (dtype == 0 && D == 128) return launch_glob_f32<128>(waves, a, n_wg, s, t);
   return hipErrorInvalidValue;
