@@ -38,6 +38,8 @@
 // of the Ultralytics glossary page "Longformer" (section on how the attention
 // works): band |i-j| <= window//2 (dilated: j = i + d*k), global rows and
 // columns, a global key inside a row's band counted once.
+#include <type_traits>
+
 #include "lfattn_internal.h"
 
 namespace lfattn {
@@ -74,20 +76,47 @@ __device__ __forceinline__ float pair_max(float x) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// ds_read_b64_tr_b16 issued as inline assembly.  The compiler's builtin for it
+// ds_read_b64_tr_b16 at lds_addr + OFF issued as inline assembly.  The
+// compiler's builtin for it
 // is treated as possibly aliasing the in-flight direct-to-LDS loads and gets a
 // full vmcnt(0) wait in front of it, which would drain the load ring; the
 // ring's own waits already order these reads.  The result must not be used
 // before lgkm_wait() has been passed the same registers.
+template <unsigned OFF>
 __device__ __forceinline__ s16x4 ds_read_tr16(unsigned lds_addr) {
   s16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "n"(OFF));
   return r;
+}
+// 16-byte LDS read at lds_addr + OFF, the same way (the result must pass
+// lgkm_wait_n() before use).
+template <unsigned OFF>
+__device__ __forceinline__ bf16x8 ds_read_b128(unsigned lds_addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "n"(OFF));
+  return r;
+}
+// Wait until at most N LDS reads are outstanding, with x (the result of the
+// read issued N before the last one) ready afterwards.  LDS reads complete
+// in order; scalar loads in flight only make the wait longer.
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n(bf16x8& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
 }
 __device__ __forceinline__ void lgkm_wait(s16x4& a0, s16x4& a1, s16x4& a2, s16x4& a3,
                                           s16x4& a4, s16x4& a5, s16x4& a6, s16x4& a7) {
   asm volatile("s_waitcnt lgkmcnt(0)"
                : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7));
+}
+
+// The lane's index in the wavefront, computed afresh where it is called (the
+// compiler cannot merge it with another call), so that lane-derived values
+// used only on rare paths are recomputed there instead of being kept live in
+// registers across the step loop.
+__device__ __forceinline__ int lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 
 // Key of register i (0..15) of a 32x32 MFMA result block for lane half hi.
@@ -97,19 +126,22 @@ __device__ __forceinline__ constexpr int block_row(int i, int hi) {
 
 constexpr int kGlobCap = kMaxGlobalBf16;  // global positions staged in LDS
 
-// One 16-byte direct global -> LDS load: lane i's 16 bytes land at LDS byte
-// address lds + 16*i.  Written as inline assembly so that the compiler does
-// not treat every later LDS read as depending on it (which made it drain all
-// outstanding loads before the transposed reads); the ring's explicit waits
-// order the accesses.
-__device__ __forceinline__ void dma16(const void* gaddr, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// 16-byte direct global -> LDS loads: lane i's 16 bytes land at LDS byte
+// address M0 + 16*i.  Written as inline assembly so that the compiler does
+// not treat every later LDS read as depending on them (which made it drain
+// all outstanding loads before the transposed reads); the ring's explicit
+// waits order the accesses.  (M0 is written here only: nothing else in these
+// kernels uses it.)
+//
+// dma16_s: from a wave-uniform base address plus a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds), "v"(gaddr)
+               : "s"(lds), "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
-// The same with the LDS address given as a sum of two wave-uniform parts
-// (one scalar add into M0).
+// dma16_2: from a per-lane 64-bit address, with the LDS address given as a
+// sum of two wave-uniform parts (one scalar add into M0).
 __device__ __forceinline__ void dma16_2(const void* gaddr, unsigned lds_a, unsigned lds_b) {
   asm volatile("s_add_u32 m0, %0, %1\n\tglobal_load_lds_dwordx4 %2, off"
                :
@@ -155,6 +187,7 @@ struct B32 {
     unsigned char st[NS][KS][2 * MAT];
     int gpos[kGlobCap];
     int gsp[kGlobCap];
+    unsigned char rowg[ROWS];  // band rows that are global positions
   };
 };
 
@@ -178,9 +211,8 @@ void band32_kernel(BandArgs a) {
   // A global-row item is the band problem over plain key positions (d = 1),
   // with a half-width no key reaches past and its rows taken from the global
   // list, restricted to one key chunk.
-  const bool gi = w.kind != 0;
-  const int h = w.bh % a.H;
-  const int d = gi ? 1 : a.dil[h];
+  const bool gi = w.dil == 0;
+  const int d = gi ? 1 : w.dil;
   const int r = gi ? 0 : w.r, t0 = gi ? 0 : w.t0, N = a.N;
   const int hw = gi ? (1 << 29) : a.hw;
   const int Lr = (N - r + d - 1) / d;
@@ -211,6 +243,11 @@ void band32_kernel(BandArgs a) {
   const int u = ua + l32;
   const bool row_ok = u < n_rows;
 
+  // Whether the lane's band row is itself a global position (its output is
+  // the merge kernel's), read now (a plain load, waited for with the others)
+  // so that the epilogue finds it in LDS.  Meaningless for global-row items.
+  const unsigned char own_glob = a.is_glob[min(r + d * (row_ok ? u : 0), N - 1)];
+
   // Q operand (B of S^T = K Q^T): Q[row][16ks + 8hi + 0..7].
   bf16x8 q[D / 16];
   {
@@ -230,54 +267,69 @@ void band32_kernel(BandArgs a) {
   const int n_tiles = n_band + (gi ? 0 : (n_glob + TK - 1) / TK);
   const int n_steps = (n_tiles + KS - 1) / KS;  // half kh takes tiles KS*j + kh
 
-  // Direct loads of step j into stage sidx: the two wavefronts of a key
-  // half load that half's K and V tiles, wavefront w rows RPW*qblk + RPI*e +
-  // lane/CPR (e < NE): 2*NE loads each (tiles past the end load a real row
-  // so that every wavefront issues the same count).
+  // Direct loads of step j into the stage at byte offset soff: the wavefronts
+  // of a key half load that half's K and V tiles, wavefront w rows
+  // RPW*qblk + RPI*e + lane/CPR (e < NE): 2*NE loads each (tiles past the end
+  // load a real row so that every wavefront issues the same count).
   const int rbase = RPW * qblk;
   const unsigned st_base = (unsigned)(uintptr_t)(LDS_AS void*)sm.st[0][kh];
   constexpr unsigned kStageBytes = KS * 2 * MAT;
   const int rlane = rbase + lane / CPR;
   // LDS destination of load e of K within a stage (V: + MAT).
   const unsigned ld_k = st_base + rbase * RB;
-  auto issue = [&](int j, int sidx, bool glob_tile) {
+  // Byte offset of this lane's 16 bytes of row rlane + RPI*e of a band tile
+  // from the tile's first key row (rows d apart in memory).
+  unsigned boff[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+    boff[e] = (unsigned)(d * (rlane + RPI * e) * RB) + 16u * swz(rlane + RPI * e, lane % CPR);
+  // First key row of this half's band tile of step j: Kp/Vp + kt0 + j*kstep
+  // elements.
+  const size_t kt0 = (size_t)(r + d * (s_lo + TK * kh)) * D;
+  const size_t kstep = (size_t)d * KS * TK * D;
+  // Loads of a band tile that lies wholly in the key range, from its first
+  // K and V rows.
+  auto issue_band = [&](const unsigned short* kb, const unsigned short* vb, unsigned soff) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      dma16_s(kb, boff[e], ld_k + 1024 * e + soff);
+      dma16_s(vb, boff[e], ld_k + MAT + 1024 * e + soff);
+    }
+  };
+  // Loads of any tile of step j: gathered global keys, or band rows clamped
+  // to s_hi (the last band tile, or a tile past the end).
+  auto issue = [&](int j, unsigned soff) {
     const int tj = KS * j + kh;
-    const unsigned soff = sidx * kStageBytes;
+    const bool glob_tile = tj >= n_band && tj < n_tiles;
+    if (!glob_tile && s_lo + TK * tj + TK - 1 <= s_hi) {
+      const size_t row0 = kt0 + (size_t)j * kstep;
+      issue_band(Kp + row0, Vp + row0, soff);
+      return;
+    }
+    const int ln = lane_id(), rl = rbase + ln / CPR;
     int g[NE];
-    if (glob_tile) {  // gathered global keys
+    if (glob_tile) {
       const int x0 = TK * (tj - n_band);
 #pragma unroll
-      for (int e = 0; e < NE; ++e) g[e] = sm.gpos[min(x0 + rlane + RPI * e, n_glob - 1)];
-    } else {  // band keys (tiles past the end clamp to a real row)
+      for (int e = 0; e < NE; ++e) g[e] = sm.gpos[min(x0 + rl + RPI * e, n_glob - 1)];
+    } else {
       const int k0 = s_lo + TK * tj;
 #pragma unroll
-      for (int e = 0; e < NE; ++e) g[e] = r + d * min(k0 + rlane + RPI * e, s_hi);
+      for (int e = 0; e < NE; ++e) g[e] = r + d * min(k0 + rl + RPI * e, s_hi);
     }
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
-      const size_t off = (size_t)g[e] * D + 8 * swz(rlane + RPI * e, lane % CPR);
+      const size_t off = (size_t)g[e] * D + 8 * swz(rl + RPI * e, ln % CPR);
       dma16_2(Kp + off, ld_k + 1024 * e, soff);
       dma16_2(Vp + off, ld_k + MAT + 1024 * e, soff);
     }
   };
-  auto is_glob_tile = [&](int j) {
-    const int tj = KS * j + kh;
-    return tj >= n_band && tj < n_tiles;
-  };
 
-  // The first stages go out before the global positions are staged unless
-  // one of their tiles is a gathered global tile.
-  bool early = true;
-#pragma unroll
-  for (int j = 0; j < NS - 1; ++j) {
-    const int tj = KS * j + kh;
-    early &= !(j < n_steps && tj >= n_band && tj < n_tiles);
-  }
-  if (early) {
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
-      if (j < n_steps) issue(j, j, is_glob_tile(j));
-  }
+  // The first stage goes out before the global positions are staged unless
+  // its tile is a gathered global tile.
+  static_assert(NS == 2, "the step loop alternates two stages");
+  const bool early = !(kh >= n_band && kh < n_tiles);
+  if (early) issue(0, 0);
 #pragma unroll
   for (int it = 0; it < kStageIters; ++it) {
     const int x = tid + 256 * it;
@@ -288,12 +340,9 @@ void band32_kernel(BandArgs a) {
       sm.gsp[x] = (off >= 0 && off % d == 0) ? off / d : kNotInClass;
     }
   }
+  if (!gi && kh == 0 && hi == 0) sm.rowg[32 * qblk + l32] = own_glob;
   __syncthreads();  // staged global positions visible
-  if (!early) {
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
-      if (j < n_steps) issue(j, j, is_glob_tile(j));
-  }
+  if (!early) issue(0, 0);
 
   // Whether a global key lies in the band of one of this wave's rows (then
   // global tiles need the per-pair dedupe test).
@@ -305,36 +354,43 @@ void band32_kernel(BandArgs a) {
   }
   gdup = __any(gdup);
 
-  // Per-step flags, one step per lane: whether the wave scores any key of
-  // its tile (act) and whether the tile needs a per-pair mask (edge).
-  // Gathered global tiles are marked active and masked; their keep bits are
-  // worked out in the step itself.
-  unsigned long long act_m = 0, edge_m = 0, glob_m = 0, nglob_m = 0;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) acc[b] = f32x16{};
+  float m = kNegInit, l = 0.0f;
+  bool fresh = true;  // no tile scored yet: maximum unset
+
+  // Per-step flags for steps j0 .. j0+63, one step per lane: act, the wave
+  // scores some key of the step's tile; fast, an active band tile that needs
+  // no mask and is not the wave's first scored tile (the common case, taken
+  // without any of the tests below); nfast, the next step's tile is a band
+  // tile wholly in the key range (its loads take the short path).
+  unsigned long long act_m = 0, fast_m = 0, nfast_m = 0;
   auto flags = [&](int j0) {
-    const int x = j0 + lane;
+    const int x = j0 + lane_id();
     const int tt = KS * x + kh;
-    glob_m = __ballot(tt >= n_band && tt < n_tiles);
-    nglob_m = __ballot(tt + KS >= n_band && tt + KS < n_tiles);
-    bool fa = false, fe = false;
+    bool fa = false, ff = false;
     if (live && x < n_steps && tt < n_tiles) {
       if (tt < n_band) {
         const int k0 = s_lo + TK * tt, k1 = min(k0 + TK - 1, s_hi);
         fa = (k0 <= ub + hw) & (k1 >= ua - hw);
-        fe = !((k1 == k0 + TK - 1) & (k1 - ua <= hw) & (ub - k0 <= hw));
+        ff = fa & (k1 == k0 + TK - 1) & (k1 - ua <= hw) & (ub - k0 <= hw);
       } else {
         fa = true;
-        fe = true;
       }
     }
     act_m = __ballot(fa);
-    edge_m = __ballot(fe);
+    fast_m = __ballot(ff);
+    if (fresh) fast_m &= ~(act_m & (0 - act_m));  // the first scored tile
+    const int tn = tt + KS;
+    nfast_m = __ballot(tn < n_band && s_lo + TK * tn + TK - 1 <= s_hi);
   };
-  flags(0);
 
-  // Per-lane LDS offsets of the MFMA operands inside a tile.
+  // Per-lane LDS addresses of the MFMA operands in stage 0 (stage 1: plus
+  // kStageBytes, an immediate offset).
   unsigned koff[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * RB + 16 * swz(l32, 2 * ks + hi);
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = st_base + l32 * RB + 16 * swz(l32, 2 * ks + hi);
   unsigned voff[D / 32][2];
   {
     const int g16 = lane >> 4, t16 = lane & 15;
@@ -343,67 +399,56 @@ void band32_kernel(BandArgs a) {
       const int dcol = 32 * b + 16 * (g16 & 1) + 4 * (t16 & 3);
       const int c = dcol >> 3, half = (dcol >> 2) & 1;
       const int row0 = 4 * (g16 >> 1) + (t16 >> 2), row1 = row0 + 8;
-      voff[b][0] = MAT + row0 * RB + 16 * swz(row0, c) + 8 * half;
-      voff[b][1] = MAT + row1 * RB + 16 * swz(row1, c) + 8 * half;
+      voff[b][0] = st_base + MAT + row0 * RB + 16 * swz(row0, c) + 8 * half;
+      voff[b][1] = st_base + MAT + row1 * RB + 16 * swz(row1, c) + 8 * half;
     }
   }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b) acc[b] = f32x16{};
-  float m = kNegInit, l = 0.0f;
-  bool fresh = true;  // no tile scored yet: maximum unset
-
-  static_assert(NS == 2, "the step loop alternates two stages");
-  for (int j0 = 0; j0 < n_steps; j0 += 64) {
-  if (j0 > 0) flags(j0);
-  const int j1 = min(n_steps, j0 + 64);
-  for (int j = j0; j < j1; ++j, act_m >>= 1, edge_m >>= 1, glob_m >>= 1, nglob_m >>= 1) {
-    // This wave's loads of step j done, then every wave's; then the next
-    // step's loads into the other stage (after the last step they load real
-    // rows nobody reads; the epilogue waits for them before reusing LDS).
-    wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    issue(j + 1, (j + 1) & 1, nglob_m & 1);
-
-    if (!(act_m & 1)) continue;
+  // Scoring of step j's tile t = KS*j + kh from the stage at SOFF.  fast: a
+  // band tile with no mask, not the first scored one (the tests are skipped).
+  auto score = [&](const int j, auto stage, const bool fast) {
+    constexpr unsigned SOFF = decltype(stage)::value * kStageBytes;
     const int t = KS * j + kh;
-    const unsigned sbase = st_base + (j & 1) * kStageBytes;
-    const LDS_AS unsigned char* st = (const LDS_AS unsigned char*)(uintptr_t)sbase;
-    const bool band = !(glob_m & 1);
+    const bool band = t < n_band;
 
     // Global tiles: which slots the rows keep.
-    bool edge = edge_m & 1;
+    bool edge = false;
     unsigned keep = 0;
-    if (!band) {
-      bool act;
-      const int g0 = TK * (t - n_band);
-      const int nvalid = min(TK, n_glob - g0);
-      if (!gdup) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) keep |= (unsigned)(block_row(i, hi) < nvalid) << i;
-        act = true;
-        edge = nvalid < TK;
+    if (!fast) {
+      if (band) {
+        const int k0 = s_lo + TK * t, k1 = min(k0 + TK - 1, s_hi);
+        edge = !((k1 == k0 + TK - 1) & (k1 - ua <= hw) & (ub - k0 <= hw));
       } else {
-        // Keep a valid slot unless its key lies in the row's band (then the
-        // band already scored it).  One group of 4 slots at a time, so that
-        // this rare path stays small in registers.
-        const unsigned span = 2u * (unsigned)hw;
-#pragma unroll 1
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int kk0 = 8 * g4 + 4 * hi;
-          const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsp[min(g0 + kk0, kGlobCap - 4)];
+        bool act;
+        const int ln = lane_id(), lh = ln >> 5, lu = ua + (ln & 31);
+        const int g0 = TK * (t - n_band);
+        const int nvalid = min(TK, n_glob - g0);
+        if (!gdup) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const bool k = (kk0 + c < nvalid) & row_ok & ((unsigned)(sp[c] - u + hw) > span);
-            keep |= (unsigned)k << (4 * g4 + c);
+          for (int i = 0; i < 16; ++i) keep |= (unsigned)(block_row(i, lh) < nvalid) << i;
+          act = true;
+          edge = nvalid < TK;
+        } else {
+          // Keep a valid slot unless its key lies in the row's band (then the
+          // band already scored it).  One group of 4 slots at a time, so that
+          // this rare path stays small in registers.
+          const unsigned span = 2u * (unsigned)hw;
+#pragma unroll 1
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int kk0 = 8 * g4 + 4 * lh;
+            const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsp[min(g0 + kk0, kGlobCap - 4)];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const bool k = (kk0 + c < nvalid) & (lu < n_rows) & ((unsigned)(sp[c] - lu + hw) > span);
+              keep |= (unsigned)k << (4 * g4 + c);
+            }
           }
+          act = __any(keep != 0);
+          edge = true;
         }
-        act = __any(keep != 0);
-        edge = true;
+        if (!act) return;
       }
-      if (!act) continue;
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -412,40 +457,56 @@ void band32_kernel(BandArgs a) {
     {
       bf16x8 kv[D / 16];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) kv[ks] = *(const LDS_AS bf16x8*)(st + koff[ks]);
+      for (int ks = 0; ks < D / 16; ++ks) kv[ks] = ds_read_b128<SOFF>(koff[ks]);
       S = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
+      auto kstep1 = [&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        lgkm_wait_n<D / 16 - 1 - ks>(kv[ks]);
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks], q[ks], S, 0, 0, 0);
-    }
-    if (edge) {
-      if (band) {
-        const int s0 = s_lo + TK * t;
-        const unsigned span = 2u * (unsigned)hw;
-        const int e = s0 + 4 * hi - u + hw;  // |key - u| <= hw  <=>  e + br <= 2hw
-        if (s0 + TK - 1 <= s_hi) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            S[i] = (unsigned)(e + block_row(i, 0)) > span ? -INFINITY : S[i];
-        } else {
-          const int last = s_hi - s0 - 4 * hi;  // keys past s_hi: block row > last
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            S[i] = ((unsigned)(e + block_row(i, 0)) > span) | (block_row(i, 0) > last)
-                       ? -INFINITY : S[i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) S[i] = ((keep >> i) & 1u) ? S[i] : -INFINITY;
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      kstep1(std::integral_constant<int, 0>{});
+      kstep1(std::integral_constant<int, 1>{});
+      kstep1(std::integral_constant<int, 2>{});
+      kstep1(std::integral_constant<int, 3>{});
+      if constexpr (D == 128) {
+        kstep1(std::integral_constant<int, 4>{});
+        kstep1(std::integral_constant<int, 5>{});
+        kstep1(std::integral_constant<int, 6>{});
+        kstep1(std::integral_constant<int, 7>{});
       }
     }
-    if (fresh) {
-      // First scored tile: start the running maximum at its own maximum.
-      float mx = -INFINITY;
+    if (!fast) {
+      if (edge) {
+        if (band) {
+          const int s0 = s_lo + TK * t;
+          const unsigned span = 2u * (unsigned)hw;
+          const int ln = lane_id(), lh = ln >> 5;
+          const int e = s0 + 4 * lh - (ua + (ln & 31)) + hw;  // |key - u| <= hw  <=>  e + br <= 2hw
+          if (s0 + TK - 1 <= s_hi) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
-      m = fmaxf(kNegInit, pair_max(mx) * a.sl2);
-      fresh = false;
+            for (int i = 0; i < 16; ++i)
+              S[i] = (unsigned)(e + block_row(i, 0)) > span ? -INFINITY : S[i];
+          } else {
+            const int last = s_hi - s0 - 4 * lh;  // keys past s_hi: block row > last
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              S[i] = ((int)((unsigned)(e + block_row(i, 0)) > span) | (int)(block_row(i, 0) > last))
+                         ? -INFINITY : S[i];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) S[i] = ((keep >> i) & 1u) ? S[i] : -INFINITY;
+        }
+      }
+      if (fresh) {
+        // First scored tile: start the running maximum at its own maximum.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[i]);
+        m = fmaxf(kNegInit, pair_max(mx) * a.sl2);
+        fresh = false;
+      }
     }
 
     __builtin_amdgcn_sched_barrier(0);
@@ -494,12 +555,15 @@ void band32_kernel(BandArgs a) {
     if constexpr (D == 64) {
       s16x4 vr[2][2][2];  // [k2][b][row0/row1]
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+      for (int b = 0; b < 2; ++b) {
+        vr[0][b][0] = ds_read_tr16<SOFF>(voff[b][0]);
+        vr[0][b][1] = ds_read_tr16<SOFF>(voff[b][1]);
+      }
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int rr = 0; rr < 2; ++rr)
-            vr[k2][b][rr] = ds_read_tr16(sbase + voff[b][rr] + 16 * k2 * RB);
+      for (int b = 0; b < 2; ++b) {
+        vr[1][b][0] = ds_read_tr16<SOFF + 16 * RB>(voff[b][0]);
+        vr[1][b][1] = ds_read_tr16<SOFF + 16 * RB>(voff[b][1]);
+      }
       lgkm_wait(vr[0][0][0], vr[0][0][1], vr[0][1][0], vr[0][1][1],
                 vr[1][0][0], vr[1][0][1], vr[1][1][0], vr[1][1][1]);
 #pragma unroll
@@ -515,14 +579,14 @@ void band32_kernel(BandArgs a) {
       }
     } else {
       // D = 128: one 16-key k-step at a time (fewer live V operands).
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
+      auto pv = [&](auto k2c) {
+        constexpr int k2 = decltype(k2c)::value;
         s16x4 vr[4][2];  // [b][row0/row1]
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int rr = 0; rr < 2; ++rr)
-            vr[b][rr] = ds_read_tr16(sbase + voff[b][rr] + 16 * k2 * RB);
+        for (int b = 0; b < 4; ++b) {
+          vr[b][0] = ds_read_tr16<SOFF + 16 * RB * k2>(voff[b][0]);
+          vr[b][1] = ds_read_tr16<SOFF + 16 * RB * k2>(voff[b][1]);
+        }
         lgkm_wait(vr[0][0], vr[0][1], vr[1][0], vr[1][1], vr[2][0], vr[2][1], vr[3][0], vr[3][1]);
         const uint4 pu = make_uint4(P[4 * k2], P[4 * k2 + 1], P[4 * k2 + 2], P[4 * k2 + 3]);
 #pragma unroll
@@ -532,11 +596,41 @@ void band32_kernel(BandArgs a) {
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8, pu),
                                                            acc[b], 0, 0, 0);
         }
-      }
+      };
+      pv(std::integral_constant<int, 0>{});
+      pv(std::integral_constant<int, 1>{});
+    }
+  };
+
+  // One step: bit x (= j - j0) of the flags, tile KS*j + kh in stage SG
+  // (= j % 2).  This wave's loads of step j done, then every wave's; then the
+  // next step's loads into the other stage (after the last step they load
+  // real rows nobody reads; the epilogue waits for them before reusing LDS).
+  const unsigned short* kn = Kp + kt0;  // first K row of the last issued band step
+  const unsigned short* vn = Vp + kt0;
+  auto step = [&](const int j, const int x, auto stage) {
+    constexpr int SG = decltype(stage)::value;
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    kn += kstep;
+    vn += kstep;
+    if ((nfast_m >> x) & 1)
+      issue_band(kn, vn, (1 - SG) * kStageBytes);
+    else
+      issue(j + 1, (1 - SG) * kStageBytes);
+    if ((act_m >> x) & 1) score(j, stage, ((fast_m >> x) & 1) != 0);
+  };
+
+  // Steps in pairs (stage 0 then stage 1), flags refreshed every 64 steps.
+  for (int j0 = 0; j0 < n_steps; j0 += 64) {
+    flags(j0);
+    const int j1 = min(n_steps, j0 + 64);
+    for (int j = j0; j < j1; j += 2) {
+      step(j, j - j0, std::integral_constant<int, 0>{});
+      if (j + 1 < j1) step(j + 1, j + 1 - j0, std::integral_constant<int, 1>{});
     }
   }
 
-  }
   // The loads issued in the last step land before the ring is reused.
   wait_vm_lgkm0<0>();
 
@@ -572,8 +666,7 @@ void band32_kernel(BandArgs a) {
   // Lane-derived values again, from a lane id the compiler cannot fold into
   // the one computed at entry (so that nothing lane-dependent is kept live
   // across the loop only for the stores).
-  int lid;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+  const int lid = lane_id();
   const int ehi = lid >> 5, el32 = lid & 31;
   const int eu = ua + el32;
   if (eu >= n_rows) return;
@@ -594,7 +687,7 @@ void band32_kernel(BandArgs a) {
     return;
   }
   const int row = r + d * eu;
-  if (a.is_glob[row]) return;
+  if (sm.rowg[32 * qblk + el32]) return;
   const float inv = 1.0f / lt;
   unsigned short* Op = (unsigned short*)a.O + base + (size_t)row * D;
 #pragma unroll

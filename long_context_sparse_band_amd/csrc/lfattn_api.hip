@@ -214,7 +214,7 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
     const int d = c->dil[bh % H];
     for (int r = 0; r < d && r < N; ++r) {
       const int Lr = (N - r + d - 1) / d;
-      for (int t0 = 0; t0 < Lr; t0 += band_rows) items.push_back(BandWork{bh, r, t0, 0});
+      for (int t0 = 0; t0 < Lr; t0 += band_rows) items.push_back(BandWork{bh, r, t0, d});
     }
   }
   const int n_items = (int)items.size();
@@ -262,7 +262,7 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
           // residue 0's items come first for this head; its subsequence
           // position of key0 is key0 / d.
           const int k = std::min(first_item[bh] + (int)(key0 / d / band_rows), n_items - 1);
-          q[item_xcd[std::max(k, 0)]].push_back(BandWork{bh, set, ch, 1});
+          q[item_xcd[std::max(k, 0)]].push_back(BandWork{bh, set, ch, 0});
         }
     size_t left = 0;
     for (auto& v : q) left += v.size();

@@ -30,7 +30,7 @@ struct BandWork {
   int bh;
   int r;
   int t0;
-  int kind;
+  int dil;  // band item: its head's dilation (>= 1); global-row item: 0
 };
 
 struct BandArgs {
@@ -45,7 +45,7 @@ struct BandArgs {
   int H, N, hw, n_glob;
   float sl2;                   // softmax scale times log2(e)
   int rows_per_wg;             // rows per band workgroup (bf16: 64 or 128)
-  // Global-row items (kind 1): partial records laid out as GlobArgs::part
+  // Global-row items (dil 0): partial records laid out as GlobArgs::part
   // with rows_per_wg rows per set, and the chunking of the keys.
   float* part;
   int n_sets, n_chunks, chunk_keys;

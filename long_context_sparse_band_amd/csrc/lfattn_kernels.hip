@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
   const BandWork w = a.work[blockIdx.x];
   const int h = w.bh % a.H;
-  const int d = a.dil[h];
+  const int d = w.dil;
   const int r = w.r, t0 = w.t0, hw = a.hw, N = a.N;
   const int Lr = (N - r + d - 1) / d;  // length of the residue's subsequence
   const size_t base = (size_t)w.bh * N * D;
