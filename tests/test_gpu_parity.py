@@ -269,10 +269,13 @@ def test_deterministic_and_repeatable():
         outs = []
         say("determinism: 6 forwards")
         for _ in range(6):
-            o = torch.empty_like(q)
+            # NaN-filled: every row, the global rows included, must be written
+            # by every forward.
+            o = torch.full_like(q, float("nan"))
             L.lfattn_forward(h, q, k, v, o)
             outs.append(o)
         torch.cuda.synchronize()
+        assert not torch.isnan(outs[0]).any()
         for o in outs[1:]:
             assert torch.equal(o, outs[0])
     finally:
@@ -310,12 +313,14 @@ def test_forward_rejects_bad_pointers():
         L.lfattn_destroy(h)
 
 
-def test_timing_records_both_kernels():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_timing_records_both_kernels(dtype):
     import torch
-    inp = W.small_case(1, 2, 2048, 64, "bf16", 512, glob=[0, 1, 2], seed=43)
+    inp = W.small_case(1, 2, 2048, 64, dtype, 512, glob=[0, 1, 2], seed=43)
     q, k, v = to_device(inp)
     o = torch.empty_like(q)
-    h = L.lfattn_create(1, 2, 2048, 64, L.LFATTN_BF16, 512, None, [0, 1, 2])
+    code = L.LFATTN_BF16 if dtype == "bf16" else L.LFATTN_F32
+    h = L.lfattn_create(1, 2, 2048, 64, code, 512, None, [0, 1, 2])
     try:
         L.lfattn_set_timing(h, True)
         for _ in range(5):
