@@ -177,11 +177,24 @@ struct B32 {
   static constexpr int ROWS = 32 * QBLKS;  // rows per workgroup
   static constexpr int RPW = TK / QBLKS;   // tile rows each wavefront loads
   static constexpr int NE = RPW / RPI;   // loads per matrix and wavefront per step
-  static constexpr int WPE = D == 64 ? 4 : 2;  // wavefronts per SIMD
-  // Physical 16-byte chunk of logical chunk c in row `row` (an involution).
+  // Wavefronts per SIMD: D = 64 fits 128 registers (4); D = 128 fits 168
+  // (3) with the 36 KB ring of one key split, 256 (2) with two.
+  static constexpr int WPE = D == 64 ? 4 : (KS_ == 1 ? 3 : 2);
+  // Physical 16-byte chunk of logical chunk c in row `row` (an involution),
+  // chosen for 64 LDS banks (256 bytes per cycle): a K-operand read (chunk c
+  // of 32 consecutive rows) is served 16 lanes = 16 rows at a time, a
+  // transposed V read 32 lanes = 4 consecutive rows x 4 adjacent chunks at a
+  // time.  D = 64 (two rows per 256 bytes): the XOR term is a bijection of
+  // row/2 and moves the 4-chunk block of row pairs 2 apart; D = 128: a
+  // bijection of the row whose block bits differ over any 4 consecutive rows.
+  // Neither read then repeats a bank.
   static __device__ __forceinline__ int swz(int row, int c) {
-    if constexpr (D == 64) return c ^ ((row >> 1) & 7);
-    else return c ^ (row & 15);
+    if constexpr (D == 64) {
+      const int j = (row >> 1) & 7;
+      return c ^ (((j & 1) << 2) | ((j >> 1) & 3));
+    } else {
+      return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+    }
   }
   struct Smem {
     unsigned char st[NS][KS][2 * MAT];
@@ -215,7 +228,7 @@ void band32_kernel(BandArgs a) {
   const int d = gi ? 1 : w.dil;
   const int r = gi ? 0 : w.r, t0 = gi ? 0 : w.t0, N = a.N;
   const int hw = gi ? (1 << 29) : a.hw;
-  const int Lr = (N - r + d - 1) / d;
+  const int Lr = d == 1 ? N - r : (N - r + d - 1) / d;
   const size_t base = (size_t)w.bh * N * D;
   const unsigned short* Qp = (const unsigned short*)a.Q + base;
   const unsigned short* Kp = (const unsigned short*)a.K + base;
@@ -337,7 +350,8 @@ void band32_kernel(BandArgs a) {
       const int g = gv[it];
       const int off = g - r;
       sm.gpos[x] = g;
-      sm.gsp[x] = (off >= 0 && off % d == 0) ? off / d : kNotInClass;
+      // (d = 1: every position is in the one residue class, r = 0.)
+      sm.gsp[x] = d == 1 ? off : ((off >= 0 && off % d == 0) ? off / d : kNotInClass);
     }
   }
   if (!gi && kh == 0 && hi == 0) sm.rowg[32 * qblk + l32] = own_glob;
