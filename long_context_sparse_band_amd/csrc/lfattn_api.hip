@@ -44,7 +44,6 @@ struct lfattn_ctx {
 
   BandWork* d_work = nullptr;
   int n_band_wg = 0;
-  int* d_dil = nullptr;
   int* d_glob = nullptr;
   unsigned char* d_isglob = nullptr;
 
@@ -75,7 +74,6 @@ lfattn_status dev_alloc(T** p, size_t count) {
 void free_ctx(lfattn_ctx* c) {
   if (!c) return;
   (void)hipFree(c->d_work);
-  (void)hipFree(c->d_dil);
   (void)hipFree(c->d_glob);
   (void)hipFree(c->d_isglob);
   (void)hipFree(c->d_part);
@@ -298,7 +296,6 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   lfattn_status st = LFATTN_OK;
   if (hipGetDevice(&c->device) != hipSuccess) { free_ctx(c); return LFATTN_EHIP; }
   if ((st = dev_alloc(&c->d_work, table.size())) != LFATTN_OK ||
-      (st = dev_alloc(&c->d_dil, (size_t)H)) != LFATTN_OK ||
       (st = dev_alloc(&c->d_isglob, (size_t)N)) != LFATTN_OK ||
       (st = dev_alloc(&c->d_glob, (size_t)std::max(n_g, 1))) != LFATTN_OK) {
     free_ctx(c);
@@ -314,7 +311,6 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   }
   bool ok = hipMemcpy(c->d_work, table.data(), table.size() * sizeof(BandWork),
                       hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(c->d_dil, c->dil.data(), H * sizeof(int), hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(c->d_isglob, isg.data(), N, hipMemcpyHostToDevice) == hipSuccess;
   if (n_g > 0) {
     ok = ok && hipMemcpy(c->d_glob, c->glob.data(), n_g * sizeof(int), hipMemcpyHostToDevice) == hipSuccess;
@@ -367,7 +363,7 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
 
   lfattn::BandArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O;
-  a.work = c->d_work; a.dil = c->d_dil; a.glob = c->d_glob; a.is_glob = c->d_isglob;
+  a.work = c->d_work; a.glob = c->d_glob; a.is_glob = c->d_isglob;
   a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
   a.rows_per_wg = c->band_rows;
   a.part = c->glob_items ? c->d_part : nullptr;

@@ -39,7 +39,6 @@ struct BandArgs {
   const void* V;
   void* O;
   const BandWork* work;        // one entry per workgroup
-  const int* dil;              // [H] dilation per head
   const int* glob;             // [n_glob] sorted global positions
   const unsigned char* is_glob;  // [N] 1 where the position is global
   int H, N, hw, n_glob;

@@ -1,10 +1,12 @@
-// HIP kernels for band + global sparse attention on gfx950 (MI355X).
+// HIP kernels for band + global sparse attention on gfx950 (MI355X): the
+// fp32 band and global-row partial kernels, and the merge of global-row
+// partials shared by both dtypes (the bf16 band kernel is in band_bf16.hip).
 //
-// Band kernel: one workgroup of 4 wavefronts takes 128 consecutive query rows
-// of one (batch, head, dilation residue) and walks the key tiles of their band
-// (64 keys each, staged in LDS), then the tiles of gathered global keys.  Each
-// wavefront owns 32 query rows and computes, per tile,
-//   S^T = K_tile Q^T          (v_mfma_f32_32x32x16_bf16, or _32x32x2f32)
+// Band kernel (fp32): one workgroup of 4 wavefronts takes 128 consecutive
+// query rows of one (batch, head, dilation residue) and walks the 64-key tiles
+// of their band (staged in LDS through registers), then the tiles of gathered
+// global keys.  Each wavefront owns 32 query rows and computes, per tile,
+//   S^T = K_tile Q^T          (v_mfma_f32_32x32x2f32)
 //   online softmax on S^T     (running max and sum per query row)
 //   O^T += V_tile^T P^T       (same MFMA shape, fp32 accumulators)
 // Scores are kept transposed (keys down the MFMA rows, queries across lanes)
@@ -28,7 +30,6 @@
 namespace lfattn {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
@@ -57,101 +58,22 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // lane half hi = lane / 32: row 8*(i/4) + 4*hi + i%4 of the block.
 __device__ __forceinline__ int block_row(int i, int hi) { return 8 * (i >> 2) + 4 * hi + (i & 3); }
 
-// Position of key kk (0..63) inside a V^T row in LDS.  Within each group of 16
-// keys, keys 16s + 8a + 4b + c (a, b in {0,1}, c in 0..3) go to slot
-// 16s + 8b + 4a + c, so that the 8 keys one lane feeds to a 32x32x16 MFMA
-// k-step (registers 8*(ks%2) .. +7 of its score block) are contiguous.
-__device__ __forceinline__ int vt_slot(int kk) {
-  return (kk & ~15) | (((kk >> 2) & 1) << 3) | (((kk >> 3) & 1) << 2) | (kk & 3);
-}
-
 // ---------------------------------------------------------------------------
 // LDS tiles and the cooperative loaders.
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D>
-struct Tile;
-
-// bf16: K row-major [key][d] (16-byte row padding), V transposed [d][slot].
-template <int D>
-struct Tile<true, D> {
-  static constexpr int KP = D + 8;
-  static constexpr int VP = TK + 8;
-  unsigned short k[TK * KP];
-  unsigned short vt[D * VP];
-};
-
 // fp32: K and V both row-major [key][d]; the pitches spread the MFMA operand
 // reads over the LDS banks.
 template <int D>
-struct Tile<false, D> {
+struct Tile {
   static constexpr int KP = D + 4;
   static constexpr int VP = D + 8;
   float k[TK * KP];
   float v[TK * VP];
 };
 
-template <bool BF16, int D, int NT>
-struct Loader;
-
 template <int D, int NT>
-struct Loader<true, D, NT> {
-  static constexpr int C8 = D / 8;                  // 16-byte chunks per row
-  static constexpr int NK = TK * C8 / NT;           // K chunks per thread
-  static constexpr int NV = (TK / 2) * C8 / NT;     // V key-pair chunks per thread
-  static_assert(NK >= 1 && NV >= 1, "tile too small for the workgroup");
-  uint4 k[NK];
-  uint4 v[2 * NV];
-
-  // row_of(kk) gives the sequence position of tile key kk, or -1.
-  template <typename RowOf>
-  __device__ __forceinline__ void fetch(const unsigned short* Kp, const unsigned short* Vp,
-                                        RowOf row_of, int tid) {
-#pragma unroll
-    for (int e = 0; e < NK; ++e) {
-      const int c = tid + NT * e;
-      const int kk = c / C8, c8 = c % C8;
-      const int row = row_of(kk);
-      k[e] = row >= 0 ? *(const uint4*)(Kp + (size_t)row * D + c8 * 8) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < NV; ++e) {
-      const int c = tid + NT * e;
-      const int p = c % (TK / 2), c8 = c / (TK / 2);
-      const int r0 = row_of(2 * p), r1 = row_of(2 * p + 1);
-      v[2 * e] = r0 >= 0 ? *(const uint4*)(Vp + (size_t)r0 * D + c8 * 8) : make_uint4(0, 0, 0, 0);
-      v[2 * e + 1] = r1 >= 0 ? *(const uint4*)(Vp + (size_t)r1 * D + c8 * 8) : make_uint4(0, 0, 0, 0);
-    }
-  }
-
-  __device__ __forceinline__ void store(Tile<true, D>& t, int tid) const {
-#pragma unroll
-    for (int e = 0; e < NK; ++e) {
-      const int c = tid + NT * e;
-      const int kk = c / C8, c8 = c % C8;
-      *(uint4*)&t.k[kk * Tile<true, D>::KP + c8 * 8] = k[e];
-    }
-#pragma unroll
-    for (int e = 0; e < NV; ++e) {
-      const int c = tid + NT * e;
-      const int p = c % (TK / 2), c8 = c / (TK / 2);
-      const int slot = vt_slot(2 * p);  // even; key 2p+1 lands in slot + 1
-      const unsigned* a = (const unsigned*)&v[2 * e];
-      const unsigned* b = (const unsigned*)&v[2 * e + 1];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // d = c8*8 + 2w (low halves) and c8*8 + 2w + 1 (high halves).
-        const unsigned lo = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);
-        const unsigned hi = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);
-        *(unsigned*)&t.vt[(c8 * 8 + 2 * w) * Tile<true, D>::VP + slot] = lo;
-        *(unsigned*)&t.vt[(c8 * 8 + 2 * w + 1) * Tile<true, D>::VP + slot] = hi;
-      }
-    }
-  }
-};
-
-template <int D, int NT>
-struct Loader<false, D, NT> {
+struct Loader {
   static constexpr int C4 = D / 4;           // 16-byte chunks per row
   static constexpr int NC = TK * C4 / NT;    // chunks per thread, each of K and V
   static_assert(NC >= 1, "tile too small for the workgroup");
@@ -171,13 +93,13 @@ struct Loader<false, D, NT> {
     }
   }
 
-  __device__ __forceinline__ void store(Tile<false, D>& t, int tid) const {
+  __device__ __forceinline__ void store(Tile<D>& t, int tid) const {
 #pragma unroll
     for (int e = 0; e < NC; ++e) {
       const int c = tid + NT * e;
       const int kk = c / C4, c4 = c % C4;
-      *(float4*)&t.k[kk * Tile<false, D>::KP + c4 * 4] = k[e];
-      *(float4*)&t.v[kk * Tile<false, D>::VP + c4 * 4] = v[e];
+      *(float4*)&t.k[kk * Tile<D>::KP + c4 * 4] = k[e];
+      *(float4*)&t.v[kk * Tile<D>::VP + c4 * 4] = v[e];
     }
   }
 };
@@ -186,80 +108,8 @@ struct Loader<false, D, NT> {
 // Per-wavefront attention state for 32 query rows, and one tile step.
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D>
-struct WaveAttn;
-
 template <int D>
-struct WaveAttn<true, D> {
-  bf16x8 q[D / 16];     // B operand of S^T = K Q^T: Q[row][16*ks + 8*hi + 0..7]
-  f32x16 acc[D / 32];   // O^T blocks: d = 32*blk + block_row(i, hi), query = lane % 32
-  float m, l;
-
-  __device__ __forceinline__ void load_q(const unsigned short* Qp, int row, int hi) {
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      if (row >= 0) {
-        q[ks] = *(const bf16x8*)(Qp + (size_t)row * D + 16 * ks + 8 * hi);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) q[ks][j] = (__bf16)0.0f;
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
-    m = kNegInit;
-    l = 0.0f;
-  }
-
-  __device__ __forceinline__ void scores(const Tile<true, D>& t, int lane, f32x16 (&s)[2]) const {
-    const int hi = lane >> 5, r = lane & 31;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = *(const bf16x8*)&t.k[(32 * kb + r) * Tile<true, D>::KP + 16 * ks + 8 * hi];
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[ks], s[kb], 0, 0, 0);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void accumulate(const Tile<true, D>& t, int lane, const f32x16 (&p)[2]) {
-    const int hi = lane >> 5, r = lane & 31;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pb[ks][j] = (__bf16)p[ks >> 1][8 * (ks & 1) + j];
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = *(const bf16x8*)&t.vt[(32 * b + r) * Tile<true, D>::VP + 16 * ks + 8 * hi];
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc[b], 0, 0, 0);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store_row(unsigned short* Op, int row, int hi, float inv) const {
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 o;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] = (__bf16)(acc[b][4 * g + c] * inv);
-        *(bf16x4*)(Op + (size_t)row * D + 32 * b + 8 * g + 4 * hi) = o;
-      }
-    }
-  }
-};
-
-template <int D>
-struct WaveAttn<false, D> {
+struct WaveAttn {
   // B operand of the fp32 MFMA k-steps: step t pairs d = t (hi = 0) with
   // d = t + D/2 (hi = 1); any fixed pairing of d values is a valid split.
   float q[D / 2];
@@ -281,7 +131,7 @@ struct WaveAttn<false, D> {
     l = 0.0f;
   }
 
-  __device__ __forceinline__ void scores(const Tile<false, D>& t, int lane, f32x16 (&s)[2]) const {
+  __device__ __forceinline__ void scores(const Tile<D>& t, int lane, f32x16 (&s)[2]) const {
     const int hi = lane >> 5, r = lane & 31;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -289,7 +139,7 @@ struct WaveAttn<false, D> {
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
 #pragma unroll
       for (int t4 = 0; t4 < D / 8; ++t4) {
-        const float4 a = *(const float4*)&t.k[(32 * kb + r) * Tile<false, D>::KP + (D / 2) * hi + 4 * t4];
+        const float4 a = *(const float4*)&t.k[(32 * kb + r) * Tile<D>::KP + (D / 2) * hi + 4 * t4];
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, q[4 * t4], s[kb], 0, 0, 0);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, q[4 * t4 + 1], s[kb], 0, 0, 0);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, q[4 * t4 + 2], s[kb], 0, 0, 0);
@@ -298,7 +148,7 @@ struct WaveAttn<false, D> {
     }
   }
 
-  __device__ __forceinline__ void accumulate(const Tile<false, D>& t, int lane, const f32x16 (&p)[2]) {
+  __device__ __forceinline__ void accumulate(const Tile<D>& t, int lane, const f32x16 (&p)[2]) {
     const int hi = lane >> 5, r = lane & 31;
     // k-step (kb, i) pairs key 32*kb + block_row(i, 0) (hi = 0) with
     // 32*kb + block_row(i, 1) (hi = 1): exactly the keys whose weights the two
@@ -309,7 +159,7 @@ struct WaveAttn<false, D> {
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float a = t.v[(32 * kb + block_row(i, hi)) * Tile<false, D>::VP + 32 * b + r];
+          const float a = t.v[(32 * kb + block_row(i, hi)) * Tile<D>::VP + 32 * b + r];
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[kb][i], acc[b], 0, 0, 0);
         }
       }
@@ -332,8 +182,8 @@ struct WaveAttn<false, D> {
 // Online softmax over one tile of transposed scores s (raw, -inf where the
 // pair is not scored), then the P.V accumulation.  m is kept in log2 units
 // of the scaled scores.
-template <bool BF16, int D, typename Tl>
-__device__ __forceinline__ void softmax_accumulate(WaveAttn<BF16, D>& st, const Tl& tile,
+template <int D, typename Tl>
+__device__ __forceinline__ void softmax_accumulate(WaveAttn<D>& st, const Tl& tile,
                                                    int lane, f32x16 (&s)[2], float sl2) {
   float mx = -INFINITY;
 #pragma unroll
@@ -375,17 +225,16 @@ struct ElemT<false> { typedef float type; };
 // Band kernel.
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D>
+template <int D>
 __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
-  typedef typename ElemT<BF16>::type E;
+  typedef float E;
   constexpr int NT = kBandWaves * 64;
-  __shared__ Tile<BF16, D> tile;
+  __shared__ Tile<D> tile;
   __shared__ __attribute__((aligned(16))) int gsub[TK];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
   const BandWork w = a.work[blockIdx.x];
-  const int h = w.bh % a.H;
   const int d = w.dil;
   const int r = w.r, t0 = w.t0, hw = a.hw, N = a.N;
   const int Lr = (N - r + d - 1) / d;  // length of the residue's subsequence
@@ -401,7 +250,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   const int u = ua + (lane & 31);
   const int qrow = u < Lr ? r + d * u : -1;
 
-  WaveAttn<BF16, D> st;
+  WaveAttn<D> st;
   st.load_q(Qp, qrow, hi);
 
   // Key range of the workgroup's band, in subsequence positions.
@@ -433,7 +282,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   const unsigned rng = (unsigned)(hi_key - lo);
   constexpr int kNotInClass = 0x40000000;
 
-  Loader<BF16, D, NT> ld;
+  Loader<D, NT> ld;
   ld.fetch(Kp, Vp, row_of_tile(0), tid);
 
   for (int tt = 0; tt < n_tiles; ++tt) {
@@ -518,13 +367,13 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
 // Global-row partial kernel: one (batch-head, row set, key chunk) per workgroup.
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D, int WAVES>
+template <int D, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
-  typedef typename ElemT<BF16>::type E;
+  typedef float E;
   constexpr int NT = WAVES * 64;
   constexpr int ROWS = WAVES * kWaveRows;   // global rows per set
   constexpr int REC = D + 4;                // partial record: m, l, 2 pad, acc[D]
-  __shared__ Tile<BF16, D> tile;
+  __shared__ Tile<D> tile;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
@@ -542,7 +391,7 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
   const int gslot = gfirst + (lane & 31);
   const int qrow = gslot < a.n_glob ? a.glob[gslot] : -1;
 
-  WaveAttn<BF16, D> st;
+  WaveAttn<D> st;
   st.load_q(Qp, qrow, hi);
 
   const int c0 = chunk * a.chunk_keys;
@@ -555,7 +404,7 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
     };
   };
 
-  Loader<BF16, D, NT> ld;
+  Loader<D, NT> ld;
   ld.fetch(Kp, Vp, row_of_tile(0), tid);
   for (int tt = 0; tt < n_tiles; ++tt) {
     ld.store(tile, tid);
@@ -687,17 +536,17 @@ hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_
   if (n_wg <= 0) return hipSuccess;
   if (dtype == 1) return launch_band_bf16(D, a, n_wg, s, t);
   const dim3 grid(n_wg), block(kBandWaves * 64);
-  if (dtype == 0 && D == 64) return launch_kernel(band_kernel<false, 64>, grid, block, s, a, t);
-  if (dtype == 0 && D == 128) return launch_kernel(band_kernel<false, 128>, grid, block, s, a, t);
+  if (dtype == 0 && D == 64) return launch_kernel(band_kernel<64>, grid, block, s, a, t);
+  if (dtype == 0 && D == 128) return launch_kernel(band_kernel<128>, grid, block, s, a, t);
   return hipErrorInvalidValue;
 }
 
 template <int D>
 static hipError_t launch_glob_f32(int waves, const GlobArgs& a, int n_wg, hipStream_t s, const Timing& t) {
   const dim3 grid(n_wg);
-  if (waves == 1) return launch_kernel(glob_kernel<false, D, 1>, grid, dim3(64), s, a, t);
-  if (waves == 2) return launch_kernel(glob_kernel<false, D, 2>, grid, dim3(128), s, a, t);
-  if (waves == 4) return launch_kernel(glob_kernel<false, D, 4>, grid, dim3(256), s, a, t);
+  if (waves == 1) return launch_kernel(glob_kernel<D, 1>, grid, dim3(64), s, a, t);
+  if (waves == 2) return launch_kernel(glob_kernel<D, 2>, grid, dim3(128), s, a, t);
+  if (waves == 4) return launch_kernel(glob_kernel<D, 4>, grid, dim3(256), s, a, t);
   return hipErrorInvalidValue;
 }
 
