@@ -296,10 +296,25 @@ void band32_kernel(BandArgs a) {
 #pragma unroll
   for (int e = 0; e < NE; ++e)
     boff[e] = (unsigned)(d * (rlane + RPI * e) * RB) + 16u * swz(rlane + RPI * e, lane % CPR);
-  // First key row of this half's band tile of step j: Kp/Vp + kt0 + j*kstep
-  // elements.
-  const size_t kt0 = (size_t)(r + d * (s_lo + TK * kh)) * D;
-  const size_t kstep = (size_t)d * KS * TK * D;
+  // Tile of step j.  KS = 2: tile KS*j + kh.  KS = 1: the band tiles in a
+  // rotated order, chosen so that the workgroups of one (head, residue) read
+  // tiles whose index from the sequence start is congruent mod n_band at the
+  // same step: the workgroups that share a tile (their bands overlap) read it
+  // at nearly the same time, and a tile stays in L2 only briefly.  Then the
+  // gathered global tiles.
+  const int rot = KS == 1 ? (n_band - (s_lo / TK) % n_band) % n_band : 0;
+  auto tile_of = [&](int j) -> int {
+    if constexpr (KS == 1) {
+      if (j >= n_band) return j;
+      const int t = j + rot;
+      return t >= n_band ? t - n_band : t;
+    } else {
+      return KS * j + kh;
+    }
+  };
+  // First key row of band tile t: Kp/Vp + kt0 + t*tstep elements.
+  const size_t kt0 = (size_t)(r + d * s_lo) * D;
+  const size_t tstep = (size_t)d * TK * D;
   // Loads of a band tile that lies wholly in the key range, from its first
   // K and V rows.
   auto issue_band = [&](const unsigned short* kb, const unsigned short* vb, unsigned soff) {
@@ -312,10 +327,10 @@ void band32_kernel(BandArgs a) {
   // Loads of any tile of step j: gathered global keys, or band rows clamped
   // to s_hi (the last band tile, or a tile past the end).
   auto issue = [&](int j, unsigned soff) {
-    const int tj = KS * j + kh;
+    const int tj = tile_of(j);
     const bool glob_tile = tj >= n_band && tj < n_tiles;
     if (!glob_tile && s_lo + TK * tj + TK - 1 <= s_hi) {
-      const size_t row0 = kt0 + (size_t)j * kstep;
+      const size_t row0 = kt0 + (size_t)tj * tstep;
       issue_band(Kp + row0, Vp + row0, soff);
       return;
     }
@@ -341,7 +356,7 @@ void band32_kernel(BandArgs a) {
   // The first stage goes out before the global positions are staged unless
   // its tile is a gathered global tile.
   static_assert(NS == 2, "the step loop alternates two stages");
-  const bool early = !(kh >= n_band && kh < n_tiles);
+  const bool early = !(tile_of(0) >= n_band && tile_of(0) < n_tiles);
   if (early) issue(0, 0);
 #pragma unroll
   for (int it = 0; it < kStageIters; ++it) {
@@ -382,7 +397,7 @@ void band32_kernel(BandArgs a) {
   unsigned long long act_m = 0, fast_m = 0, nfast_m = 0;
   auto flags = [&](int j0) {
     const int x = j0 + lane_id();
-    const int tt = KS * x + kh;
+    const int tt = tile_of(x);
     bool fa = false, ff = false;
     if (live && x < n_steps && tt < n_tiles) {
       if (tt < n_band) {
@@ -396,7 +411,7 @@ void band32_kernel(BandArgs a) {
     act_m = __ballot(fa);
     fast_m = __ballot(ff);
     if (fresh) fast_m &= ~(act_m & (0 - act_m));  // the first scored tile
-    const int tn = tt + KS;
+    const int tn = tile_of(x + 1);
     nfast_m = __ballot(tn < n_band && s_lo + TK * tn + TK - 1 <= s_hi);
   };
 
@@ -423,7 +438,7 @@ void band32_kernel(BandArgs a) {
   // band tile with no mask, not the first scored one (the tests are skipped).
   auto score = [&](const int j, auto stage, const bool fast) {
     constexpr unsigned SOFF = decltype(stage)::value * kStageBytes;
-    const int t = KS * j + kh;
+    const int t = tile_of(j);
     const bool band = t < n_band;
 
     // Global tiles: which slots the rows keep.
@@ -616,18 +631,24 @@ void band32_kernel(BandArgs a) {
     }
   };
 
-  // One step: bit x (= j - j0) of the flags, tile KS*j + kh in stage SG
+  // One step: bit x (= j - j0) of the flags, tile tile_of(j) in stage SG
   // (= j % 2).  This wave's loads of step j done, then every wave's; then the
   // next step's loads into the other stage (after the last step they load
   // real rows nobody reads; the epilogue waits for them before reusing LDS).
-  const unsigned short* kn = Kp + kt0;  // first K row of the last issued band step
-  const unsigned short* vn = Vp + kt0;
+  const unsigned short* kn = Kp + kt0 + (size_t)kh * tstep;  // last issued band step (KS = 2)
+  const unsigned short* vn = Vp + kt0 + (size_t)kh * tstep;
   auto step = [&](const int j, const int x, auto stage) {
     constexpr int SG = decltype(stage)::value;
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
-    kn += kstep;
-    vn += kstep;
+    if constexpr (KS == 1) {
+      const size_t row0 = kt0 + (size_t)tile_of(j + 1) * tstep;
+      kn = Kp + row0;
+      vn = Vp + row0;
+    } else {
+      kn += KS * tstep;
+      vn += KS * tstep;
+    }
     if ((nfast_m >> x) & 1)
       issue_band(kn, vn, (1 - SG) * kStageBytes);
     else
