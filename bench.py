@@ -5,6 +5,11 @@ Longformer-base workload (B 1, H 12, N 4096, D 64, bf16, window 512, global
 tokens 0..31) with inputs already resident in device memory.  Prints one JSON
 line.  Options: --gpus (only 1 is supported: the path runs on one GPU),
 --steps, --warmup, --workload (another of the named workloads), --no-cpu.
+The default warm-up (2000 forwards) runs long enough for the GPU's clock to
+settle under the load (a short warm-up times part of the steps at a lower
+clock).  Besides the timed steps (warm: inputs resident in the caches as well), the
+line carries 20-trial medians and interquartile ranges of the warm time and
+of cold-cache forwards (caches flushed by a 512 MB write before each).
 """
 
 from __future__ import annotations
@@ -30,7 +35,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--workload", default="longformer_base_n4096")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--copy-calibration", action="store_true",
@@ -74,6 +79,13 @@ def copy_calibration():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+
+
+def quantiles(xs):
+    """(25th percentile, median, 75th percentile) of a list."""
+    import numpy as np
+    q = np.percentile(np.asarray(xs, dtype=np.float64), [25, 50, 75])
+    return float(q[0]), float(q[1]), float(q[2])
 
 
 def cpu_baseline(inp, wl, pairs_per_head_total):
@@ -148,13 +160,47 @@ def main():
         L.lfattn_forward(h, q, k, v, o, stream)
     band_ms, glob_ms, n = L.lfattn_read_timing(h)
     L.lfattn_set_timing(h, False)
-    L.lfattn_destroy(h)
     band_ms /= max(n, 1)
     glob_ms /= max(n, 1)
+
+    # Spread of the warm time: 20 trials of R back-to-back forwards.  Cold
+    # cache: before each of 20 single forwards, a 512 MB device write (more
+    # than the 256 MB Infinity Cache and the L2s hold) evicts Q, K and V; the
+    # events bracket the forward only.
+    rep = max(1, min(args.steps, 200))
+    warm = []
+    for _ in range(20):
+        e0.record(stream)
+        for _ in range(rep):
+            L.lfattn_forward(h, q, k, v, o, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        warm.append(e0.elapsed_time(e1) / rep)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for t in range(20):
+        scratch.fill_(t + 1)
+        e0.record(stream)
+        L.lfattn_forward(h, q, k, v, o, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    L.lfattn_set_timing(h, True)
+    cold_band = []
+    for t in range(20):
+        scratch.fill_(t + 101)
+        L.lfattn_forward(h, q, k, v, o, stream)
+        torch.cuda.synchronize()
+        b_ms, _, _ = L.lfattn_read_timing(h)
+        cold_band.append(b_ms)
+    L.lfattn_set_timing(h, False)
+    del scratch
+    L.lfattn_destroy(h)
 
     flops_per_pair = 4 * wl.D                       # 2D for Q.K, 2D for P.V
     band_tflops = band_pairs * flops_per_pair / (band_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
+    band_cold_ms = quantiles(cold_band)[1]
     value = pairs / (ms * 1e-3)
     elem = 2 if wl.dtype == "bf16" else 4
     line = {
@@ -176,6 +222,14 @@ def main():
         "whole_forward_tflops": pairs * flops_per_pair / (ms * 1e-3) / 1e12,
         "whole_forward_mfma_frac": pairs * flops_per_pair / (ms * 1e-3) / 1e12 / peak,
         "kernels_ms": {"band": band_ms, "global_rows": glob_ms},
+        "warm_trials": {"trials": len(warm), "forwards_per_trial": rep,
+                        "median_ms": quantiles(warm)[1],
+                        "iqr_ms": quantiles(warm)[2] - quantiles(warm)[0]},
+        "cold_cache": {"trials": len(cold), "median_ms": quantiles(cold)[1],
+                       "iqr_ms": quantiles(cold)[2] - quantiles(cold)[0],
+                       "band_median_ms": band_cold_ms,
+                       "band_frac": band_pairs * flops_per_pair / (band_cold_ms * 1e-3) / 1e12
+                       / peak},
         "roofline": {
             "kernel": "band_kernel",
             "bound": "mfma",

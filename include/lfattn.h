@@ -40,6 +40,13 @@
  * handle per stream instead.  All calls on a handle must be made with the
  * device that was current at lfattn_create.
  *
+ * Tuning.  bf16 handles run the band work in 64-row workgroups (the keys of
+ * each split in two halves) or 128-row ones (one key stream shared by four
+ * 32-row blocks), chosen at lfattn_create from the number of row blocks and
+ * the device's compute units.  The environment variable LFATTN_BAND_ROWS,
+ * set to 64 or 128 when lfattn_create runs, overrides that choice; results
+ * are the same either way up to floating-point summation order.
+ *
  * Errors.  Every entry point returns a status synchronously.  Arguments are
  * checked before any HIP call is made, so invalid arguments never touch the
  * device.
@@ -117,6 +124,12 @@ lfattn_status lfattn_scored_pairs(lfattn_t ctx, long long* pairs);
  * does).  The figure a per-kernel throughput is computed from.
  */
 lfattn_status lfattn_band_launch_pairs(lfattn_t ctx, long long* pairs);
+
+/*
+ * Rows per workgroup of the handle's band launch (*rows: 64 or 128; see
+ * Tuning above).  EINVAL for a null argument.
+ */
+lfattn_status lfattn_band_rows(lfattn_t ctx, int* rows);
 
 /*
  * The canonical global list the handle uses: sorted, without repeats.

@@ -6,6 +6,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -29,7 +31,7 @@ constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
 // launch fits one round of workgroup slots (they then set the critical
 // path), longer ones otherwise (fewer items, less per-item overhead).
 constexpr int kGlobItemKeysShort = 256, kGlobItemKeysLong = 512;
-constexpr int kWideRounds = 3;
+constexpr int kWideRounds = 2;
 constexpr long long kMaxN = 1LL << 29;
 
 }  // namespace
@@ -200,6 +202,12 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
       for (int r = 0; r < d && r < N; ++r) n64 += (long long)B * ((N - r + d - 1) / d + 63) / 64;
     }
     band_rows = n64 >= kWideRounds * slots ? 128 : 64;
+    // LFATTN_BAND_ROWS=64 or 128 overrides the choice (both kernels give the
+    // same results; this lets small problems exercise the 128-row one).
+    if (const char* e = std::getenv("LFATTN_BAND_ROWS")) {
+      if (std::strcmp(e, "64") == 0) band_rows = 64;
+      if (std::strcmp(e, "128") == 0) band_rows = 128;
+    }
   }
   c->band_rows = band_rows;
 
@@ -395,6 +403,12 @@ lfattn_status lfattn_band_launch_pairs(lfattn_t c, long long* pairs) {
   if (!c || !pairs) return LFATTN_EINVAL;
   const long long glob_rows = (long long)c->B * c->H * (long long)c->glob.size() * c->N;
   *pairs = c->glob_items ? c->pairs : c->pairs - glob_rows;
+  return LFATTN_OK;
+}
+
+lfattn_status lfattn_band_rows(lfattn_t c, int* rows) {
+  if (!c || !rows) return LFATTN_EINVAL;
+  *rows = c->band_rows;
   return LFATTN_OK;
 }
 

@@ -25,7 +25,8 @@ LFATTN_BF16 = 1
 
 # Every entry point include/lfattn.h declares.
 EXPORTS = ("lfattn_create", "lfattn_forward", "lfattn_destroy", "lfattn_status_string",
-           "lfattn_scored_pairs", "lfattn_band_launch_pairs", "lfattn_global_list",
+           "lfattn_scored_pairs", "lfattn_band_launch_pairs", "lfattn_band_rows",
+           "lfattn_global_list",
            "lfattn_set_timing", "lfattn_read_timing")
 
 _lib = None
@@ -62,6 +63,8 @@ def load():
     lib.lfattn_scored_pairs.argtypes = [vp, ctypes.POINTER(ctypes.c_longlong)]
     lib.lfattn_band_launch_pairs.restype = ctypes.c_int
     lib.lfattn_band_launch_pairs.argtypes = [vp, ctypes.POINTER(ctypes.c_longlong)]
+    lib.lfattn_band_rows.restype = ctypes.c_int
+    lib.lfattn_band_rows.argtypes = [vp, i32p]
     lib.lfattn_global_list.restype = ctypes.c_int
     lib.lfattn_global_list.argtypes = [vp, i32p, ctypes.c_int, i32p]
     lib.lfattn_set_timing.restype = ctypes.c_int
@@ -133,6 +136,12 @@ def lfattn_scored_pairs(handle: int) -> int:
 def lfattn_band_launch_pairs(handle: int) -> int:
     n = ctypes.c_longlong()
     _check(load().lfattn_band_launch_pairs(handle, ctypes.byref(n)), "lfattn_band_launch_pairs")
+    return int(n.value)
+
+
+def lfattn_band_rows(handle: int) -> int:
+    n = ctypes.c_int()
+    _check(load().lfattn_band_rows(handle, ctypes.byref(n)), "lfattn_band_rows")
     return int(n.value)
 
 

@@ -92,6 +92,8 @@ def test_null_handle_calls(lib):
     n = ctypes.c_longlong()
     assert lib.lfattn_scored_pairs(None, ctypes.byref(n)) == L.LFATTN_EINVAL
     assert lib.lfattn_band_launch_pairs(None, ctypes.byref(n)) == L.LFATTN_EINVAL
+    rows = ctypes.c_int()
+    assert lib.lfattn_band_rows(None, ctypes.byref(rows)) == L.LFATTN_EINVAL
     assert lib.lfattn_forward(None, 16, 16, 16, 16, None) == L.LFATTN_EINVAL
     assert lib.lfattn_destroy(None) == L.LFATTN_OK
     assert lib.lfattn_set_timing(None, 1) == L.LFATTN_EINVAL

@@ -59,6 +59,30 @@ def test_small_cases_every_element(case):
     assert pairs == oracle.count_pairs(B, H, N, window, list(inp.dilation), list(inp.glob))
 
 
+# bf16 runs in 64-row or 128-row workgroups (chosen from the problem size:
+# small problems take 64); both kernels on every small bf16 shape.
+SMALL_BF16 = [c for c in SMALL if c[4] == "bf16"]
+
+
+@pytest.mark.parametrize("rows", [64, 128])
+@pytest.mark.parametrize("case", SMALL_BF16, ids=lambda c: "B%dH%dN%dD%d_w%d_s%d" % (
+    c[0], c[1], c[2], c[3], c[5], c[8]))
+def test_small_cases_both_band_kernels(case, rows, monkeypatch):
+    monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows))
+    B, H, N, D, dt, window, dil, glob, seed = case
+    inp = W.small_case(B, H, N, D, dt, window, dilation=dil, glob=glob, seed=seed)
+    h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, window, list(inp.dilation), list(inp.glob))
+    try:
+        assert L.lfattn_band_rows(h) == rows
+        say(f"small case {case}, {rows}-row band workgroups")
+        got, pairs = run(inp, handle=h)
+    finally:
+        L.lfattn_destroy(h)
+    want = oracle.attention(inp.q, inp.k, inp.v, window, list(inp.dilation), list(inp.glob))
+    compare(got, want, dt, f"{case} rows {rows}")
+    assert pairs == oracle.count_pairs(B, H, N, window, list(inp.dilation), list(inp.glob))
+
+
 def test_random_sweep_every_element():
     rng = np.random.default_rng(123)
     for t in range(24):
@@ -238,6 +262,28 @@ def test_mask_readout_bit_exact(case):
         for (b, h, i, c), n in zip(idx[:500], cnt[:500]):
             d = (dil or [1] * H)[h]
             assert n == len(oracle.allowed_set(N, window, d, glob, int(i)))
+
+
+READOUT_ROWS = [
+    # B, H, N, D, window, dilation, globals
+    (1, 2, 257, 64, 513, [1, 1], [256]),
+    (2, 2, 200, 64, 40, [1, 3], [5, 100, 199]),
+    (1, 4, 700, 64, 128, [1, 2, 3, 4], list(range(0, 700, 7))),
+    (1, 3, 333, 128, 100, [1, 2, 5], [0, 17, 300]),
+    (1, 2, 1201, 128, 300, [2, 1], [1200, 600, 3]),
+    (1, 1, 4099, 64, 300, [3], [4098, 1, 2048]),
+]
+
+
+@pytest.mark.parametrize("rows", [64, 128])
+@pytest.mark.parametrize("case", READOUT_ROWS, ids=lambda c: "H%dN%dD%d_w%d" % c[1:5])
+def test_mask_readout_both_band_kernels(case, rows, monkeypatch):
+    monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows))
+    B, H, N, D, window, dil, glob = case
+    say(f"mask readout {case}, {rows}-row band workgroups")
+    pairs, _ = _readout(B, H, N, D, "bf16", window, dil, glob)
+    want = _oracle_codes(B, H, N, window, dil, glob)
+    assert np.array_equal(pairs, want)
 
 
 def test_mask_readout_long_stress_chunks():
