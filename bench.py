@@ -81,6 +81,29 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def input_record(inp):
+    """Library versions and a SHA-256 of each generated input array (float32
+    values as generated, before any device copy)."""
+    import hashlib
+    import numpy as np
+    import torch
+    return {"numpy": np.__version__, "torch": torch.__version__,
+            "sha256": {n: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+                       for n, a in (("q", inp.q), ("k", inp.k), ("v", inp.v))}}
+
+
 def quantiles(xs):
     """(25th percentile, median, 75th percentile) of a list."""
     import numpy as np
@@ -102,10 +125,27 @@ def cpu_baseline(inp, wl, pairs_per_head_total):
         el = time.perf_counter() - t0
         if el >= 10.0:
             break
+    # One thread, on the first (at most 4096) rows of the first (batch, head),
+    # for at least 2 s.
+    rows = list(range(min(wl.N, 4096)))
+    d0 = int(inp.dilation[0])
+    head_pairs = sum(len(oracle.allowed_set(wl.N, wl.window, d0, list(inp.glob), i))
+                     for i in rows)
+    passes1, t1 = 0, time.perf_counter()
+    while True:
+        oracle.attention(*args, rows=rows, nthreads=1)
+        passes1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= 2.0:
+            break
     return {"value": pairs_per_head_total * passes / el, "unit": "pairs/s", "cores": threads,
             "kind": "oracle",
             "sample": f"the whole {wl.name} workload (all {wl.B * wl.H * wl.N} rows), "
-                      f"{passes} pass(es) in {el:.2f} s, double precision, {threads} threads"}
+                      f"{passes} pass(es) in {el:.2f} s, double precision, {threads} threads",
+            "single_thread": {"value": head_pairs * passes1 / el1, "unit": "pairs/s",
+                              "sample": f"the first {len(rows)} rows of the first (batch, head), "
+                                        f"{passes1} pass(es) in {el1:.2f} s"},
+            "cpu_model": cpu_model()}
 
 
 def main():
@@ -216,6 +256,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded i.i.d. Gaussian Q, K, V)",
+        "inputs": input_record(inp),
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
                    "window": wl.window, "dilation": [int(x) for x in inp.dilation],
                    "n_global": n_g, "scored_pairs": pairs, "parallelism": "single GPU"},
