@@ -57,6 +57,11 @@ def _load():
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p,
                                       ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64,
                                       ctypes.c_int]
+        lib.lfo_attention_ex.restype = ctypes.c_int
+        lib.lfo_attention_ex.argtypes = [f32p, f32p, f32p, f32p, f32p, f32p, f64p,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, i32p, i32p, i32p, ctypes.c_int,
+                                         ctypes.c_double, i64p, ctypes.c_int64, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -80,8 +85,13 @@ def allowed_set(n: int, window: int, dilation: int, glob, i: int) -> np.ndarray:
     return keys[:cnt].copy()
 
 
-def count_pairs(B: int, H: int, n: int, window: int, dilation=None, glob=()) -> int:
-    """Total scored pairs over B x H x n rows, by explicit set construction."""
+def count_pairs(B: int, H: int, n: int, window: int, dilation=None, glob=(),
+                batch_glob=None) -> int:
+    """Total scored pairs over B x H x n rows, by explicit set construction.
+    batch_glob: B lists, one global set per batch element (glob ignored)."""
+    if batch_glob is not None:
+        assert len(batch_glob) == B
+        return sum(count_pairs(1, H, n, window, dilation, list(g)) for g in batch_glob)
     lib = _load()
     g, gp = _i32(list(glob))
     d, dp = _i32(dilation)
@@ -92,12 +102,16 @@ def count_pairs(B: int, H: int, n: int, window: int, dilation=None, glob=()) -> 
 
 
 def attention(q, k, v, window: int, dilation=None, glob=(), scale: float = 0.0,
-              rows=None, nthreads: int | None = None) -> np.ndarray:
+              rows=None, nthreads: int | None = None, qg=None, kg=None, vg=None,
+              batch_glob=None) -> np.ndarray:
     """Oracle attention output in float64.
 
     q, k, v: float32 arrays [B, H, N, D] (bf16 data already widened).
     rows: None for every row (returns [B, H, N, D]) or flat indices
     (b*H + h)*N + i (returns [len(rows), D]).
+    qg, kg, vg: the global rows' own projections (same shape), or None for q,
+    k, v.  batch_glob: B lists, one global set per batch element (then glob is
+    ignored), or None for glob shared by all.
     """
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.float32)
@@ -105,7 +119,23 @@ def attention(q, k, v, window: int, dilation=None, glob=(), scale: float = 0.0,
     v = np.ascontiguousarray(v, dtype=np.float32)
     B, H, N, D = q.shape
     assert k.shape == q.shape and v.shape == q.shape
-    g, gp = _i32(list(glob))
+    proj = []
+    for x in (qg, kg, vg):
+        if x is None:
+            proj.append(None)
+        else:
+            x = np.ascontiguousarray(x, dtype=np.float32)
+            assert x.shape == q.shape
+            proj.append(x)
+    if batch_glob is not None:
+        assert len(batch_glob) == B
+        flat = [int(x) for lst in batch_glob for x in lst]
+        offs = np.cumsum([0] + [len(lst) for lst in batch_glob]).astype(np.int32)
+        g, gp = _i32(flat)
+        go, gop = _i32(offs)
+    else:
+        g, gp = _i32(list(glob))
+        go, gop = None, None
     d, dp = _i32(dilation)
     if d is not None:
         assert len(d) == H
@@ -121,10 +151,12 @@ def attention(q, k, v, window: int, dilation=None, glob=(), scale: float = 0.0,
         rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
         out = np.empty((n_rows, D), dtype=np.float64)
     f32p = ctypes.POINTER(ctypes.c_float)
-    st = lib.lfo_attention(q.ctypes.data_as(f32p), k.ctypes.data_as(f32p), v.ctypes.data_as(f32p),
-                           out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                           B, H, N, D, window, dp, gp, len(g), float(scale), rp, n_rows,
-                           int(nthreads))
+    pp = [None if x is None else x.ctypes.data_as(f32p) for x in proj]
+    st = lib.lfo_attention_ex(q.ctypes.data_as(f32p), k.ctypes.data_as(f32p),
+                              v.ctypes.data_as(f32p), pp[0], pp[1], pp[2],
+                              out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                              B, H, N, D, window, dp, gp, gop, len(g), float(scale), rp, n_rows,
+                              int(nthreads))
     if st != 0:
         raise ValueError("oracle: attention failed (code %d)" % st)
     return out

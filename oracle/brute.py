@@ -58,3 +58,42 @@ def attention(q, k, v, window: int, dilation=None, glob=(), scale: float | None 
             w = np.exp(z)
             out[b, h] = (w @ v[b, h]) / w.sum(axis=1, keepdims=True)
     return out
+
+
+def attention_ex(q, k, v, window: int, dilation=None, batch_glob=None, qg=None, kg=None,
+                 vg=None, scale: float | None = None):
+    """The general form: one global set per batch element (batch_glob: B lists)
+    and separate projections qg, kg, vg (None: q, k, v) for the global rows.
+
+    Same mask construction per batch element; a global row's scores are
+    qg_i . kg_j over every key, weighting vg (the Longformer glossary page's
+    global-attention bullet: global attention has its own query, key and value
+    projections); every other row keeps q, k, v and its mask row.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    qg = q if qg is None else np.asarray(qg, dtype=np.float64)
+    kg = k if kg is None else np.asarray(kg, dtype=np.float64)
+    vg = v if vg is None else np.asarray(vg, dtype=np.float64)
+    B, H, N, D = q.shape
+    if batch_glob is None:
+        batch_glob = [[]] * B
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, H, N, D), dtype=np.float64)
+    for b in range(B):
+        gset = sorted(set(int(x) for x in batch_glob[b]))
+        for h in range(H):
+            d = 1 if dilation is None else int(dilation[h])
+            additive = np.where(band_global_mask(N, window, d, gset), 0.0, -np.inf)
+            z = scale * (q[b, h] @ k[b, h].T) + additive
+            z = z - z.max(axis=1, keepdims=True)
+            w = np.exp(z)
+            out[b, h] = (w @ v[b, h]) / w.sum(axis=1, keepdims=True)
+            if gset:
+                zg = scale * (qg[b, h][gset] @ kg[b, h].T)
+                zg = zg - zg.max(axis=1, keepdims=True)
+                wg = np.exp(zg)
+                out[b, h][gset] = (wg @ vg[b, h]) / wg.sum(axis=1, keepdims=True)
+    return out

@@ -15,7 +15,13 @@
  *   O_i = sum_{j in S_i} exp(z_j - max z) V_j / sum_{j in S_i} exp(z_j - max z)
  *
  * with hw = floor(window / 2), d = the head's dilation and G the set of global
- * token positions.  Sources:
+ * token positions.  The general form (lfo_attention_ex) also takes
+ *   - a set G_b per batch element b (G above is then G_b of the row's batch);
+ *   - separate projections Qg, Kg, Vg: a global row i takes
+ *       z_j = scale * sum_c Qg[i,c] * Kg[j,c],  O_i = sum_j softmax(z)_j Vg_j
+ *     over all N keys, while every other row keeps Q, K, V, for its band and
+ *     for the global keys alike.
+ * Sources:
  *   - attention itself, softmax(Q K^T / sqrt(d_k)) V: "Unlimiformer:
  *     Long-Range Transformers with Unlimited Length Input", section 2.3, Eq. (1);
  *     the default scale is 1/sqrt(D) from that equation.
@@ -33,6 +39,14 @@
  *     to every position and every position attends to them); the sample sets
  *     row 0 and column 0 of the boolean mask, so a global key that is already
  *     inside a row's band is counted once (set union).
+ *   - separate projections: same bullet (global attention has its own query,
+ *     key and value projections).  The page does not say which scores they
+ *     enter; the reading taken is that they are the global rows' own attention
+ *     (a global query over every key), and that the other rows score the global
+ *     keys with the ordinary projections, as part of their own attention.
+ *   - one global set per batch element: the page's closing paragraph (the
+ *     Hugging Face implementation takes the global tokens as a
+ *     global_attention_mask input, one mask row per sequence of the batch).
  *   - memory tokens: "GMAT: Global Memory Augmentation for Transformers",
  *     section "Global Memory": M memory tokens are prefixed; they attend to all
  *     M+L positions, and main tokens attend to all memory tokens plus a sparse
@@ -148,10 +162,12 @@ int64_t lfo_count_pairs(int B, int H, int N, int window, const int* dilation,
 
 typedef struct {
   const float *Q, *K, *V;
+  const float *Qg, *Kg, *Vg; /* the global rows' projections (= Q, K, V if none) */
   double* O;
   int B, H, N, D, window, n_glob;
   const int* dilation;
   const int* glob;
+  const int* goff; /* per-batch lists: G_b = glob[goff[b] .. goff[b+1]), or NULL */
   double scale;
   const int64_t* rows; /* flattened (b*H + h)*N + i, or NULL for all rows */
   int64_t n_rows;
@@ -170,12 +186,18 @@ static int one_row(const lfo_job* jb, int64_t flat, int* keys, double* z,
   const int64_t bh = flat / N;
   const int i = (int)(flat % N);
   const int h = (int)(bh % jb->H);
+  const int b = (int)(bh / jb->H);
   const int d = jb->dilation ? jb->dilation[h] : 1;
-  const float* q = jb->Q + (size_t)flat * D;
-  const float* Kbh = jb->K + (size_t)bh * N * D;
-  const float* Vbh = jb->V + (size_t)bh * N * D;
+  /* The global set of this row's batch element. */
+  const int* gl = jb->goff ? jb->glob + jb->goff[b] : jb->glob;
+  const int ng = jb->goff ? jb->goff[b + 1] - jb->goff[b] : jb->n_glob;
+  /* A global row takes its own projections. */
+  const int grow = is_global(gl, ng, i);
+  const float* q = (grow ? jb->Qg : jb->Q) + (size_t)flat * D;
+  const float* Kbh = (grow ? jb->Kg : jb->K) + (size_t)bh * N * D;
+  const float* Vbh = (grow ? jb->Vg : jb->V) + (size_t)bh * N * D;
 
-  int64_t n = lfo_allowed_set(N, jb->window, d, jb->glob, jb->n_glob, i, keys);
+  int64_t n = lfo_allowed_set(N, jb->window, d, gl, ng, i, keys);
   if (n <= 0) return LFO_EINVAL; /* never empty: k = 0 gives j = i */
 
   double zmax = -INFINITY;
@@ -218,19 +240,29 @@ static void* worker(void* arg) {
 }
 
 /*
- * Attention output for a list of rows.  Q, K, V: [B, H, N, D] row-major
- * floats.  rows: flattened indices (b*H + h)*N + i, n_rows of them, or NULL
- * with n_rows = B*H*N for every row.  O: n_rows x D doubles, in the order of
- * rows.  scale <= 0 selects 1/sqrt(D).  nthreads >= 1 workers split the row
- * list into contiguous ranges.  Returns LFO_OK or a negative error.
+ * Attention output for a list of rows, general form.  Q, K, V: [B, H, N, D]
+ * row-major floats; Qg, Kg, Vg: the same shape, the global rows' projections,
+ * each NULL to use Q, K or V.  goff: NULL for one global set glob[0..n_glob)
+ * shared by every batch element, or B+1 offsets with G_b = glob[goff[b] ..
+ * goff[b+1]) (then n_glob = goff[B]).  rows: flattened indices
+ * (b*H + h)*N + i, n_rows of them, or NULL with n_rows = B*H*N for every row.
+ * O: n_rows x D doubles, in the order of rows.  scale <= 0 selects 1/sqrt(D).
+ * nthreads >= 1 workers split the row list into contiguous ranges.  Returns
+ * LFO_OK or a negative error.
  */
-int lfo_attention(const float* Q, const float* K, const float* V, double* O,
-                  int B, int H, int N, int D, int window, const int* dilation,
-                  const int* glob, int n_glob, double scale,
-                  const int64_t* rows, int64_t n_rows, int nthreads) {
+int lfo_attention_ex(const float* Q, const float* K, const float* V,
+                     const float* Qg, const float* Kg, const float* Vg, double* O,
+                     int B, int H, int N, int D, int window, const int* dilation,
+                     const int* glob, const int* goff, int n_glob, double scale,
+                     const int64_t* rows, int64_t n_rows, int nthreads) {
   if (!Q || !K || !V || !O || B <= 0 || H <= 0 || N <= 0 || D <= 0 ||
       window < 0 || n_rows < 0)
     return LFO_EINVAL;
+  if (goff) {
+    if (goff[0] != 0 || goff[B] != n_glob) return LFO_EINVAL;
+    for (int b = 0; b < B; ++b)
+      if (goff[b + 1] < goff[b]) return LFO_EINVAL;
+  }
   if (!check_globals(N, glob, n_glob)) return LFO_EINVAL;
   if (dilation)
     for (int h = 0; h < H; ++h)
@@ -251,8 +283,9 @@ int lfo_attention(const float* Q, const float* K, const float* V, double* O,
   for (int t = 0; t < nthreads; ++t) {
     lfo_job* jb = &jobs[t];
     jb->Q = Q; jb->K = K; jb->V = V; jb->O = O;
+    jb->Qg = Qg ? Qg : Q; jb->Kg = Kg ? Kg : K; jb->Vg = Vg ? Vg : V;
     jb->B = B; jb->H = H; jb->N = N; jb->D = D; jb->window = window;
-    jb->dilation = dilation; jb->glob = glob; jb->n_glob = n_glob;
+    jb->dilation = dilation; jb->glob = glob; jb->n_glob = n_glob; jb->goff = goff;
     jb->scale = scale; jb->rows = rows; jb->n_rows = n_rows;
     jb->first = n_rows * t / nthreads;
     jb->last = n_rows * (t + 1) / nthreads;
@@ -272,4 +305,13 @@ int lfo_attention(const float* Q, const float* K, const float* V, double* O,
     if (jobs[t].status != LFO_OK) st = jobs[t].status;
   free(jobs); free(tids); free(created);
   return st;
+}
+
+/* One global set for every batch element, the ordinary projections. */
+int lfo_attention(const float* Q, const float* K, const float* V, double* O,
+                  int B, int H, int N, int D, int window, const int* dilation,
+                  const int* glob, int n_glob, double scale,
+                  const int64_t* rows, int64_t n_rows, int nthreads) {
+  return lfo_attention_ex(Q, K, V, NULL, NULL, NULL, O, B, H, N, D, window, dilation, glob,
+                          NULL, n_glob, scale, rows, n_rows, nthreads);
 }
