@@ -21,18 +21,30 @@
  * library reads it as "the same 2*hw+1 offsets, spaced d_h apart".  A global
  * key that already lies in a row's band is scored once (set union).
  *
+ * Two generalisations, both from the same glossary section: G may differ
+ * between batch elements (G_b; the page's closing paragraph notes that the
+ * Hugging Face implementation takes the global tokens as a per-sequence
+ * global_attention_mask), and the global rows may have their own projections
+ * (the global-attention bullet: global attention uses separate query, key and
+ * value projections).  The page does not say which scores those enter; this
+ * library reads them as the global rows' own attention:
+ *
+ *   O_i = sum_{j < N} softmax_j(scale * Qg_i . Kg_j) Vg_j        if i in G_b
+ *
+ * while every other row keeps Q, K, V for its band and for the global keys.
+ *
  * Layouts.  Q, K, V, O: contiguous [B, H, N, D] arrays in device memory, D
  * fastest, 16-byte aligned, element type set at create (float, or bfloat16
  * stored as 16-bit words).  Accumulation is always fp32; bf16 outputs are
  * rounded to nearest even.
  *
- * Ownership.  Q, K, V, O belong to the caller.  Q, K, V are only read; O is
- * fully overwritten and must not overlap Q, K or V.  The host arrays passed to
- * lfattn_create (dilation, global_idx) are copied; the caller may free them on
- * return.  The handle owns its device tables and workspace and frees them in
+ * Ownership.  Q, K, V, O (and Qg, Kg, Vg) belong to the caller.  The inputs
+ * are only read; O is fully overwritten and must not overlap any input.  The
+ * host arrays passed to the create calls (dilation, global_idx, global_mask)
+ * are copied; the caller may free them on return.  The handle owns its device tables and workspace and frees them in
  * lfattn_destroy.
  *
- * Execution.  lfattn_forward allocates nothing and does not wait on the host:
+ * Execution.  The forward calls allocate nothing and do not wait on the host:
  * it enqueues its kernels on the given HIP stream and returns.  Device-side
  * errors surface at the caller's next synchronisation, as for any HIP call.
  * A handle keeps per-call workspace, so one handle must not be used by two
@@ -96,6 +108,18 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
                             int n_global, float scale);
 
 /*
+ * As lfattn_create, with one global set per batch element given as a host
+ * byte mask: global_mask[b * N + i] nonzero makes position i global in batch
+ * element b (the global_attention_mask form the Longformer glossary page's
+ * closing paragraph mentions).  NULL: no global positions.  The mask is read
+ * during the call only.  bf16 handles take at most 512 global positions per
+ * batch element (EUNSUPPORTED beyond).
+ */
+lfattn_status lfattn_create_masked(lfattn_t* out, int B, int H, int N, int D,
+                                   lfattn_dtype dtype, int window, const int* dilation,
+                                   const unsigned char* global_mask, float scale);
+
+/*
  * Enqueue one forward pass on `stream` (NULL: the null stream).
  * Q, K, V: device pointers to [B, H, N, D] inputs; O: device pointer to the
  * [B, H, N, D] output.  Returns EINVAL for a null or misaligned pointer or an
@@ -103,6 +127,20 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
  */
 lfattn_status lfattn_forward(lfattn_t ctx, const void* Q, const void* K, const void* V,
                              void* O, hipStream_t stream);
+
+/*
+ * Forward pass in which the global rows take their own projections (the
+ * global-attention bullet of the Longformer glossary page; see the operation
+ * above).  Qg, Kg, Vg: device pointers to [B, H, N, D] arrays laid out like Q
+ * (only Qg's global rows are read; Kg and Vg are read at every position); each
+ * may be NULL to use Q, K or V instead.  Every row outside its batch element's
+ * global set reads only Q, K and V.  lfattn_forward(ctx, Q, K, V, O, s) is this
+ * call with Qg = Kg = Vg = NULL.  Errors as lfattn_forward, checked over all
+ * seven pointers (O must overlap none of the six inputs).
+ */
+lfattn_status lfattn_forward_global_proj(lfattn_t ctx, const void* Q, const void* K,
+                                         const void* V, const void* Qg, const void* Kg,
+                                         const void* Vg, void* O, hipStream_t stream);
 
 /* Release the handle and its device memory (waits for the device first).
  * NULL is accepted and ignored. */
@@ -132,11 +170,17 @@ lfattn_status lfattn_band_launch_pairs(lfattn_t ctx, long long* pairs);
 lfattn_status lfattn_band_rows(lfattn_t ctx, int* rows);
 
 /*
- * The canonical global list the handle uses: sorted, without repeats.
- * Writes min(n, capacity) positions to out (may be NULL when capacity is 0)
- * and the full count n to *n_out.
+ * The canonical global list the handle uses: sorted, without repeats (batch
+ * element 0's, for a handle from lfattn_create_masked).  Writes
+ * min(n, capacity) positions to out (may be NULL when capacity is 0) and the
+ * full count n to *n_out.
  */
 lfattn_status lfattn_global_list(lfattn_t ctx, int* out, int capacity, int* n_out);
+
+/* The global list of batch element b (0 <= b < B, else EINVAL), as
+ * lfattn_global_list. */
+lfattn_status lfattn_global_list_batch(lfattn_t ctx, int b, int* out, int capacity,
+                                       int* n_out);
 
 /*
  * Per-kernel timing with HIP events, for measurement.  While enabled, each

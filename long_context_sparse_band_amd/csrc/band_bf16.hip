@@ -230,10 +230,13 @@ void band32_kernel(BandArgs a) {
   const int hw = gi ? (1 << 29) : a.hw;
   const int Lr = d == 1 ? N - r : (N - r + d - 1) / d;
   const size_t base = (size_t)w.bh * N * D;
-  const unsigned short* Qp = (const unsigned short*)a.Q + base;
-  const unsigned short* Kp = (const unsigned short*)a.K + base;
-  const unsigned short* Vp = (const unsigned short*)a.V + base;
-  const int n_glob = a.n_glob;
+  // A global-row item reads the global rows' own projections.
+  const unsigned short* Qp = (const unsigned short*)(gi ? a.Qg : a.Q) + base;
+  const unsigned short* Kp = (const unsigned short*)(gi ? a.Kg : a.K) + base;
+  const unsigned short* Vp = (const unsigned short*)(gi ? a.Vg : a.V) + base;
+  // The global list of this item's batch element.
+  const int* gl = a.glob + w.g0;
+  const int n_glob = w.ng;
 
   // Global positions this thread stages (loaded first so that their latency
   // overlaps the Q loads and the first tile loads).
@@ -242,7 +245,7 @@ void band32_kernel(BandArgs a) {
 #pragma unroll
   for (int it = 0; it < kStageIters; ++it) {
     const int x = tid + 256 * it;
-    gv[it] = x < n_glob ? a.glob[x] : 0;
+    gv[it] = x < n_glob ? gl[x] : 0;
   }
 
   // This wave's rows: subsequence positions ua .. ub (one per lane % 32); for
@@ -259,13 +262,14 @@ void band32_kernel(BandArgs a) {
   // Whether the lane's band row is itself a global position (its output is
   // the merge kernel's), read now (a plain load, waited for with the others)
   // so that the epilogue finds it in LDS.  Meaningless for global-row items.
-  const unsigned char own_glob = a.is_glob[min(r + d * (row_ok ? u : 0), N - 1)];
+  const unsigned char own_glob =
+      a.is_glob[w.b * a.isg_stride + min(r + d * (row_ok ? u : 0), N - 1)];
 
   // Q operand (B of S^T = K Q^T): Q[row][16ks + 8hi + 0..7].
   bf16x8 q[D / 16];
   {
     const size_t row =
-        gi ? (size_t)(row_ok ? a.glob[u] : 0) : (size_t)(r + d * (row_ok ? u : 0));
+        gi ? (size_t)(row_ok ? gl[u] : 0) : (size_t)(r + d * (row_ok ? u : 0));
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       q[ks] = *(const bf16x8*)(Qp + row * D + 16 * ks + 8 * hi);

@@ -40,14 +40,21 @@ struct lfattn_ctx {
   int B = 0, H = 0, N = 0, D = 0, dtype = 0, window = 0, hw = 0;
   float scale = 0.0f;
   std::vector<int> dil;
-  std::vector<int> glob;  // sorted, unique
+  // Global lists, sorted and without repeats: gl[0] for every batch element
+  // (shared), or gl[b] for batch element b.
+  std::vector<std::vector<int>> gl;
+  bool shared = true;
+  int n_gmax = 0;  // the longest list
+  long long n_gsum = 0;  // sum over the batch of the list lengths
+  const std::vector<int>& G(int b) const { return gl[shared ? 0 : b]; }
   long long pairs = 0;
   int device = 0;
 
   BandWork* d_work = nullptr;
   int n_band_wg = 0;
-  int* d_glob = nullptr;
-  unsigned char* d_isglob = nullptr;
+  int* d_glob = nullptr;           // the distinct lists, one after another
+  int2* d_gsel = nullptr;          // [B]: (offset, length) of each batch element's list
+  unsigned char* d_isglob = nullptr;  // [1 or B][N]
 
   float* d_part = nullptr;
   int band_rows = 0;  // rows per band workgroup
@@ -77,6 +84,7 @@ void free_ctx(lfattn_ctx* c) {
   if (!c) return;
   (void)hipFree(c->d_work);
   (void)hipFree(c->d_glob);
+  (void)hipFree(c->d_gsel);
   (void)hipFree(c->d_isglob);
   (void)hipFree(c->d_part);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
@@ -126,24 +134,33 @@ const char* lfattn_status_string(lfattn_status s) {
   return "unknown status";
 }
 
-lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dtype dtype,
-                            int window, const int* dilation, const int* global_idx,
-                            int n_global, float scale) {
-  // ---- argument checks: no HIP call before all of them pass ----
-  if (!out) return LFATTN_EINVAL;
-  *out = nullptr;
-  if (B < 1 || H < 1 || N < 1 || D < 1 || window < 0 || n_global < 0) return LFATTN_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the create entry points (no HIP call).
+lfattn_status check_shape(int B, int H, int N, int D, lfattn_dtype dtype, int window,
+                          const int* dilation, float scale) {
+  if (B < 1 || H < 1 || N < 1 || D < 1 || window < 0) return LFATTN_EINVAL;
   if (dtype != LFATTN_F32 && dtype != LFATTN_BF16) return LFATTN_EINVAL;
-  if (n_global > 0 && !global_idx) return LFATTN_EINVAL;
   if (std::isnan(scale) || std::isinf(scale)) return LFATTN_EINVAL;
   if (dilation)
     for (int h = 0; h < H; ++h)
       if (dilation[h] < 1) return LFATTN_EINVAL;
-  for (int t = 0; t < n_global; ++t)
-    if (global_idx[t] < 0 || global_idx[t] >= N) return LFATTN_EINVAL;
+  return LFATTN_OK;
+}
+
+lfattn_status check_support(int B, int H, int N, int D) {
   if (D != 64 && D != 128) return LFATTN_EUNSUPPORTED;
   if ((long long)N >= kMaxN || (long long)B * H > (1LL << 24)) return LFATTN_EUNSUPPORTED;
+  return LFATTN_OK;
+}
 
+// The handle, once the arguments are checked: gl holds one canonical list
+// (shared) or one per batch element.
+lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtype dtype,
+                          int window, const int* dilation,
+                          std::vector<std::vector<int>>&& gl, bool shared, float scale) {
   lfattn_ctx* c = new (std::nothrow) lfattn_ctx;
   if (!c) return LFATTN_ENOMEM;
   c->B = B; c->H = H; c->N = N; c->D = D; c->dtype = (int)dtype; c->window = window;
@@ -151,29 +168,45 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   c->scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
   c->dil.assign(H, 1);
   if (dilation) c->dil.assign(dilation, dilation + H);
-  // Canonical global list: sorted, repeats removed (a position listed twice is
-  // global once, as setting a mask row or column twice changes nothing).
-  c->glob.assign(global_idx, global_idx + n_global);
-  std::sort(c->glob.begin(), c->glob.end());
-  c->glob.erase(std::unique(c->glob.begin(), c->glob.end()), c->glob.end());
-  if (dtype == LFATTN_BF16 && (int)c->glob.size() > lfattn::kMaxGlobalBf16) {
+  c->gl = std::move(gl);
+  c->shared = shared;
+  for (int b = 0; b < B; ++b) {
+    c->n_gmax = std::max(c->n_gmax, (int)c->G(b).size());
+    c->n_gsum += (long long)c->G(b).size();
+  }
+  if (dtype == LFATTN_BF16 && c->n_gmax > lfattn::kMaxGlobalBf16) {
     delete c;
     return LFATTN_EUNSUPPORTED;
   }
-  std::vector<unsigned char> isg(N, 0);
-  for (int g : c->glob) isg[g] = 1;
+  const int n_lists = (int)c->gl.size();
+  std::vector<unsigned char> isg((size_t)n_lists * N, 0);
+  for (int t = 0; t < n_lists; ++t)
+    for (int g : c->gl[t]) isg[(size_t)t * N + g] = 1;
 
-  // Scored pairs, per distinct dilation value.
+  // Scored pairs, per list and distinct dilation value.
   {
     std::vector<int> ds = c->dil;
     std::sort(ds.begin(), ds.end());
     ds.erase(std::unique(ds.begin(), ds.end()), ds.end());
-    long long total = 0;
-    for (int d : ds) {
-      long long per = head_pairs(N, window / 2, d, c->glob, isg);
-      total += per * (long long)std::count(c->dil.begin(), c->dil.end(), d);
+    c->pairs = 0;
+    for (int t = 0; t < n_lists; ++t) {
+      const std::vector<unsigned char> row(isg.begin() + (size_t)t * N,
+                                           isg.begin() + (size_t)(t + 1) * N);
+      long long total = 0;
+      for (int d : ds) {
+        long long per = head_pairs(N, window / 2, d, c->gl[t], row);
+        total += per * (long long)std::count(c->dil.begin(), c->dil.end(), d);
+      }
+      c->pairs += total * (shared ? B : 1);
     }
-    c->pairs = total * B;
+  }
+  // Offset and length of each batch element's list in the device array.
+  std::vector<int> goff(n_lists + 1, 0);
+  for (int t = 0; t < n_lists; ++t) goff[t + 1] = goff[t] + (int)c->gl[t].size();
+  std::vector<int2> gsel(B);
+  for (int b = 0; b < B; ++b) {
+    const int t = shared ? 0 : b;
+    gsel[b] = make_int2(goff[t], goff[t + 1] - goff[t]);
   }
 
   // Compute units of the device (for sizing the work to one round of slots).
@@ -217,10 +250,11 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   // which share their band's K and V rows in that XCD's L2.
   std::vector<BandWork> items;
   for (int bh = 0; bh < B * H; ++bh) {
-    const int d = c->dil[bh % H];
+    const int d = c->dil[bh % H], b = bh / H;
     for (int r = 0; r < d && r < N; ++r) {
       const int Lr = (N - r + d - 1) / d;
-      for (int t0 = 0; t0 < Lr; t0 += band_rows) items.push_back(BandWork{bh, r, t0, d});
+      for (int t0 = 0; t0 < Lr; t0 += band_rows)
+        items.push_back(BandWork{bh, r, t0, d, gsel[b].x, gsel[b].y, b, 0});
     }
   }
   const int n_items = (int)items.size();
@@ -242,13 +276,18 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   // item at the end of the band launch, so that those workgroups are
   // dispatched last and fill the slots the band items leave free.  fp32: a
   // separate kernel (below).
-  const int n_g = (int)c->glob.size();
+  // (Sets are counted per batch element; records are laid out for the
+  // longest list.)
+  const int n_g = c->n_gmax;
   c->glob_items = n_g > 0 && lfattn::band_takes_global_items(dtype, D);
   if (c->glob_items) {
     c->g_rows = band_rows;  // a global item's rows: one workgroup's rows of G
     c->n_sets = (n_g + c->g_rows - 1) / c->g_rows;
-    const long long short_items = (long long)B * H * c->n_sets *
-                                  ((N + kGlobItemKeysShort - 1) / kGlobItemKeysShort);
+    long long set_count = 0;  // sum over (b, h) of the row sets
+    for (int b = 0; b < B; ++b)
+      set_count += (long long)H * ((gsel[b].y + c->g_rows - 1) / c->g_rows);
+    const long long short_items =
+        set_count * ((N + kGlobItemKeysShort - 1) / kGlobItemKeysShort);
     const int keys = n_items + short_items <= slots ? kGlobItemKeysShort : kGlobItemKeysLong;
     c->chunk_keys = keys;
     c->n_chunks = (N + keys - 1) / keys;
@@ -260,16 +299,20 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
     std::vector<int> first_item(B * H, -1);
     for (int k = 0; k < n_items; ++k)
       if (first_item[items[k].bh] < 0) first_item[items[k].bh] = k;
-    for (int bh = 0; bh < B * H; ++bh)
-      for (int set = 0; set < c->n_sets; ++set)
+    for (int bh = 0; bh < B * H; ++bh) {
+      const int b = bh / H;
+      const int sets_b = (gsel[b].y + c->g_rows - 1) / c->g_rows;
+      for (int set = 0; set < sets_b; ++set)
         for (int ch = 0; ch < c->n_chunks; ++ch) {
           const int d = c->dil[bh % H];
           const long long key0 = (long long)ch * keys;
           // residue 0's items come first for this head; its subsequence
           // position of key0 is key0 / d.
           const int k = std::min(first_item[bh] + (int)(key0 / d / band_rows), n_items - 1);
-          q[item_xcd[std::max(k, 0)]].push_back(BandWork{bh, set, ch, 0});
+          q[item_xcd[std::max(k, 0)]].push_back(
+              BandWork{bh, set, ch, 0, gsel[b].x, gsel[b].y, b, 0});
         }
+    }
     size_t left = 0;
     for (auto& v : q) left += v.size();
     std::vector<size_t> pos(kXcds, 0);
@@ -304,8 +347,9 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   lfattn_status st = LFATTN_OK;
   if (hipGetDevice(&c->device) != hipSuccess) { free_ctx(c); return LFATTN_EHIP; }
   if ((st = dev_alloc(&c->d_work, table.size())) != LFATTN_OK ||
-      (st = dev_alloc(&c->d_isglob, (size_t)N)) != LFATTN_OK ||
-      (st = dev_alloc(&c->d_glob, (size_t)std::max(n_g, 1))) != LFATTN_OK) {
+      (st = dev_alloc(&c->d_isglob, isg.size())) != LFATTN_OK ||
+      (st = dev_alloc(&c->d_glob, (size_t)std::max(goff[n_lists], 1))) != LFATTN_OK ||
+      (st = dev_alloc(&c->d_gsel, (size_t)B)) != LFATTN_OK) {
     free_ctx(c);
     return st;
   }
@@ -319,9 +363,13 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   }
   bool ok = hipMemcpy(c->d_work, table.data(), table.size() * sizeof(BandWork),
                       hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(c->d_isglob, isg.data(), N, hipMemcpyHostToDevice) == hipSuccess;
-  if (n_g > 0) {
-    ok = ok && hipMemcpy(c->d_glob, c->glob.data(), n_g * sizeof(int), hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(c->d_isglob, isg.data(), isg.size(), hipMemcpyHostToDevice) == hipSuccess;
+  ok = ok && hipMemcpy(c->d_gsel, gsel.data(), B * sizeof(int2), hipMemcpyHostToDevice) == hipSuccess;
+  if (goff[n_lists] > 0) {
+    std::vector<int> flat;
+    for (const auto& v : c->gl) flat.insert(flat.end(), v.begin(), v.end());
+    ok = ok && hipMemcpy(c->d_glob, flat.data(), flat.size() * sizeof(int),
+                         hipMemcpyHostToDevice) == hipSuccess;
   }
   if (!ok) {
     (void)hipGetLastError();
@@ -332,13 +380,70 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   return LFATTN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dtype dtype,
+                            int window, const int* dilation, const int* global_idx,
+                            int n_global, float scale) {
+  // ---- argument checks: no HIP call before all of them pass ----
+  if (!out) return LFATTN_EINVAL;
+  *out = nullptr;
+  lfattn_status st = check_shape(B, H, N, D, dtype, window, dilation, scale);
+  if (st != LFATTN_OK) return st;
+  if (n_global < 0 || (n_global > 0 && !global_idx)) return LFATTN_EINVAL;
+  for (int t = 0; t < n_global; ++t)
+    if (global_idx[t] < 0 || global_idx[t] >= N) return LFATTN_EINVAL;
+  if ((st = check_support(B, H, N, D)) != LFATTN_OK) return st;
+  // Canonical global list: sorted, repeats removed (a position listed twice is
+  // global once, as setting a mask row or column twice changes nothing).
+  std::vector<std::vector<int>> gl(1);
+  gl[0].assign(global_idx, global_idx + n_global);
+  std::sort(gl[0].begin(), gl[0].end());
+  gl[0].erase(std::unique(gl[0].begin(), gl[0].end()), gl[0].end());
+  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), true, scale);
+}
+
+lfattn_status lfattn_create_masked(lfattn_t* out, int B, int H, int N, int D,
+                                   lfattn_dtype dtype, int window, const int* dilation,
+                                   const unsigned char* global_mask, float scale) {
+  if (!out) return LFATTN_EINVAL;
+  *out = nullptr;
+  lfattn_status st = check_shape(B, H, N, D, dtype, window, dilation, scale);
+  if (st != LFATTN_OK) return st;
+  if ((st = check_support(B, H, N, D)) != LFATTN_OK) return st;
+  // One list per batch element, from its mask row; a single shared list when
+  // every row is the same.
+  std::vector<std::vector<int>> gl(B);
+  if (global_mask)
+    for (int b = 0; b < B; ++b)
+      for (int i = 0; i < N; ++i)
+        if (global_mask[(size_t)b * N + i]) gl[b].push_back(i);
+  bool shared = true;
+  for (int b = 1; b < B && shared; ++b) shared = gl[b] == gl[0];
+  if (shared) gl.resize(1);
+  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), shared, scale);
+}
+
 lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const void* V, void* O,
                              hipStream_t stream) {
+  return lfattn_forward_global_proj(c, Q, K, V, nullptr, nullptr, nullptr, O, stream);
+}
+
+lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* K,
+                                         const void* V, const void* Qg, const void* Kg,
+                                         const void* Vg, void* O, hipStream_t stream) {
   if (!c || !Q || !K || !V || !O) return LFATTN_EINVAL;
-  const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u;
+  if (!Qg) Qg = Q;
+  if (!Kg) Kg = K;
+  if (!Vg) Vg = V;
+  const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O |
+                         (uintptr_t)Qg | (uintptr_t)Kg | (uintptr_t)Vg) & 15u;
   if (mis) return LFATTN_EINVAL;
   const size_t bytes = (size_t)c->B * c->H * c->N * c->D * (c->dtype == LFATTN_BF16 ? 2 : 4);
-  if (overlaps(O, Q, bytes) || overlaps(O, K, bytes) || overlaps(O, V, bytes)) return LFATTN_EINVAL;
+  for (const void* in : {Q, K, V, Qg, Kg, Vg})
+    if (overlaps(O, in, bytes)) return LFATTN_EINVAL;
 
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != c->device) return LFATTN_EINVAL;
@@ -355,11 +460,11 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
 
   // Global rows: partials first, then the band kernel, then the merge (which
   // reads the partials after the kernel boundary made them visible).
-  const int n_g = (int)c->glob.size();
+  const int n_g = c->n_gmax;
   lfattn::GlobArgs g;
   if (n_g > 0) {
-    g.Q = Q; g.K = K; g.V = V; g.O = O;
-    g.glob = c->d_glob; g.part = c->d_part;
+    g.Q = Qg; g.K = Kg; g.V = Vg; g.O = O;
+    g.glob = c->d_glob; g.gsel = c->d_gsel; g.part = c->d_part;
     g.H = c->H; g.N = c->N; g.n_glob = n_g; g.n_bh = c->B * c->H;
     g.rows_per_set = c->g_rows;
     g.n_sets = c->n_sets; g.n_chunks = c->n_chunks; g.chunk_keys = c->chunk_keys;
@@ -371,7 +476,9 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
 
   lfattn::BandArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O;
+  a.Qg = Qg; a.Kg = Kg; a.Vg = Vg;
   a.work = c->d_work; a.glob = c->d_glob; a.is_glob = c->d_isglob;
+  a.isg_stride = c->shared ? 0 : c->N;
   a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
   a.rows_per_wg = c->band_rows;
   a.part = c->glob_items ? c->d_part : nullptr;
@@ -401,7 +508,7 @@ lfattn_status lfattn_scored_pairs(lfattn_t c, long long* pairs) {
 
 lfattn_status lfattn_band_launch_pairs(lfattn_t c, long long* pairs) {
   if (!c || !pairs) return LFATTN_EINVAL;
-  const long long glob_rows = (long long)c->B * c->H * (long long)c->glob.size() * c->N;
+  const long long glob_rows = (long long)c->H * c->n_gsum * c->N;
   *pairs = c->glob_items ? c->pairs : c->pairs - glob_rows;
   return LFATTN_OK;
 }
@@ -413,9 +520,15 @@ lfattn_status lfattn_band_rows(lfattn_t c, int* rows) {
 }
 
 lfattn_status lfattn_global_list(lfattn_t c, int* out, int capacity, int* n_out) {
+  return lfattn_global_list_batch(c, 0, out, capacity, n_out);
+}
+
+lfattn_status lfattn_global_list_batch(lfattn_t c, int b, int* out, int capacity, int* n_out) {
   if (!c || !n_out || capacity < 0 || (capacity > 0 && !out)) return LFATTN_EINVAL;
-  const int n = (int)c->glob.size();
-  for (int t = 0; t < n && t < capacity; ++t) out[t] = c->glob[t];
+  if (b < 0 || b >= c->B) return LFATTN_EINVAL;
+  const std::vector<int>& g = c->G(b);
+  const int n = (int)g.size();
+  for (int t = 0; t < n && t < capacity; ++t) out[t] = g[t];
   *n_out = n;
   return LFATTN_OK;
 }
@@ -441,7 +554,7 @@ lfattn_status lfattn_set_timing(lfattn_t c, int enable) {
 lfattn_status lfattn_read_timing(lfattn_t c, double* band_ms, double* global_ms, int* n_forwards) {
   if (!c || !band_ms || !global_ms || !n_forwards) return LFATTN_EINVAL;
   double b = 0.0, g = 0.0;
-  const bool has_glob = !c->glob.empty();
+  const bool has_glob = c->n_gmax > 0;
   if (c->n_timed > 0) {
     hipEvent_t* last = &c->ev[kEvPerForward * (c->n_timed - 1)];
     if (hipEventSynchronize(last[has_glob ? 5 : 1]) != hipSuccess) return LFATTN_EHIP;

@@ -22,26 +22,37 @@ constexpr int kMergeBatch = 16;
 
 // One band workgroup's work: batch-head bh, dilation residue r, and the first
 // position t0 (in the residue's subsequence r, r+d, r+2d, ...) of its rows.
-// With kind = 1 (kernels that take global-row work in the same launch) the
-// item is instead one workgroup's worth of global rows (set r of the sorted
-// global list) against key chunk t0, and it writes a partial (m, l, acc)
-// record per row.
+// A global-row item (dil = 0, kernels that take global-row work in the same
+// launch) is instead one workgroup's worth of global rows (set r of its batch
+// element's sorted global list) against key chunk t0, and it writes a partial
+// (m, l, acc) record per row.  Either kind carries its batch element b and
+// that element's global list: ng positions from BandArgs::glob + g0.
 struct BandWork {
   int bh;
   int r;
   int t0;
   int dil;  // band item: its head's dilation (>= 1); global-row item: 0
+  int g0;   // offset of the batch element's global list
+  int ng;   // its length
+  int b;    // batch element (bh / H)
+  int pad;
 };
 
 struct BandArgs {
   const void* Q;
   const void* K;
   const void* V;
+  // The global rows' projections (the same pointers as Q, K, V when the
+  // caller gives none): global-row items read these.
+  const void* Qg;
+  const void* Kg;
+  const void* Vg;
   void* O;
   const BandWork* work;        // one entry per workgroup
-  const int* glob;             // [n_glob] sorted global positions
-  const unsigned char* is_glob;  // [N] 1 where the position is global
-  int H, N, hw, n_glob;
+  const int* glob;             // the sorted global lists, one after another
+  const unsigned char* is_glob;  // [B or 1][N]: 1 where the position is global
+  long long isg_stride;        // N (one row per batch element) or 0 (one shared row)
+  int H, N, hw, n_glob;        // n_glob: the longest global list
   float sl2;                   // softmax scale times log2(e)
   int rows_per_wg;             // rows per band workgroup (bf16: 64 or 128)
   // Global-row items (dil 0): partial records laid out as GlobArgs::part
@@ -51,13 +62,14 @@ struct BandArgs {
 };
 
 struct GlobArgs {
-  const void* Q;
+  const void* Q;               // the global rows' projections
   const void* K;
   const void* V;
   void* O;
-  const int* glob;             // [n_glob] sorted global positions
+  const int* glob;             // the sorted global lists, one after another
+  const int2* gsel;            // [B]: (offset into glob, length) of each batch element's list
   float* part;                 // partial (m, l, 2 pad, acc[D]) records
-  int H, N, n_glob;
+  int H, N, n_glob;            // n_glob: the longest global list
   int n_bh;                    // B * H
   int rows_per_set;            // waves * 32
   int n_sets;                  // sets of up to waves*32 global rows per head

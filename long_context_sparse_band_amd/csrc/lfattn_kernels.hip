@@ -237,6 +237,9 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   const BandWork w = a.work[blockIdx.x];
   const int d = w.dil;
   const int r = w.r, t0 = w.t0, hw = a.hw, N = a.N;
+  // The global list of this item's batch element.
+  const int* gl = a.glob + w.g0;
+  const int n_glob = w.ng;
   const int Lr = (N - r + d - 1) / d;  // length of the residue's subsequence
   const size_t base = (size_t)w.bh * N * D;
   const E* Qp = (const E*)a.Q + base;
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   const int s_lo = max(0, t0 - hw);
   const int s_hi = min(Lr - 1, t0 + kBandRows - 1 + hw);
   const int n_band = (s_hi - s_lo) / TK + 1;
-  const int n_glob_tiles = (a.n_glob + TK - 1) / TK;
+  const int n_glob_tiles = (n_glob + TK - 1) / TK;
   const int n_tiles = n_band + n_glob_tiles;
 
   auto row_of_tile = [&](int tt) {
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
         return s <= s_hi ? r + d * s : -1;
       }
       const int slot = TK * (tt - n_band) + kk;
-      return slot < a.n_glob ? a.glob[slot] : -1;
+      return slot < n_glob ? gl[slot] : -1;
     };
   };
 
@@ -292,8 +295,8 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
       // no row's band reaches when the key belongs to another residue class.
       const int slot = TK * (tt - n_band) + tid;
       int sp = kNotInClass;
-      if (slot < a.n_glob) {
-        const int off = a.glob[slot] - r;
+      if (slot < n_glob) {
+        const int off = gl[slot] - r;
         if (off >= 0 && off % d == 0) sp = off / d;
       }
       gsub[tid] = sp;
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
         }
       } else {
         // Global keys, minus those already inside this row's band.
-        const int nvalid = min(TK, a.n_glob - TK * (tt - n_band));
+        const int nvalid = min(TK, n_glob - TK * (tt - n_band));
         const unsigned span = 2u * (unsigned)hw;
         bool any = false;
         unsigned keep = 0;  // bit 16*kb + i
@@ -359,7 +362,8 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
 
   if (wave_live) {
     const float lt = pair_sum(st.l);
-    if (qrow >= 0 && !a.is_glob[qrow]) st.store_row((E*)a.O + base, qrow, hi, 1.0f / lt);
+    if (qrow >= 0 && !a.is_glob[w.b * a.isg_stride + qrow])
+      st.store_row((E*)a.O + base, qrow, hi, 1.0f / lt);
   }
 }
 
@@ -386,10 +390,13 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
   const E* Kp = (const E*)a.K + base;
   const E* Vp = (const E*)a.V + base;
 
+  // The global list of this batch element (sets past its end have no rows).
+  const int2 gs = a.gsel[bh / a.H];
+  const int* gl = a.glob + gs.x;
   const int gfirst = set * ROWS + kWaveRows * wave;  // first global slot of this wave
-  const bool wave_live = gfirst < a.n_glob;
+  const bool wave_live = gfirst < gs.y;
   const int gslot = gfirst + (lane & 31);
-  const int qrow = gslot < a.n_glob ? a.glob[gslot] : -1;
+  const int qrow = gslot < gs.y ? gl[gslot] : -1;
 
   WaveAttn<D> st;
   st.load_q(Qp, qrow, hi);
@@ -461,6 +468,9 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
   __shared__ float4 sm_a[NG][NQ];
   const int slot = blockIdx.x % a.n_glob;
   const int bh = blockIdx.x / a.n_glob;
+  // Slots past the end of this batch element's global list have no row.
+  const int2 gs = a.gsel[bh / a.H];
+  if (slot >= gs.y) return;
   const int q0 = threadIdx.x & 15, g = threadIdx.x >> 4;
   const int rows = a.rows_per_set;
   const int set = slot / rows, rr = slot % rows;
@@ -515,7 +525,7 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
     }
   }
   const float inv = 1.0f / lt;
-  E* Orow = (E*)a.O + (size_t)bh * a.N * D + (size_t)a.glob[slot] * D;
+  E* Orow = (E*)a.O + (size_t)bh * a.N * D + (size_t)a.glob[gs.x + slot] * D;
 #pragma unroll
   for (int t = 0; t < QPT; ++t) {
     E* Op = Orow + 4 * (q0 + 16 * t);

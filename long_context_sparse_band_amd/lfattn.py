@@ -24,9 +24,10 @@ LFATTN_F32 = 0
 LFATTN_BF16 = 1
 
 # Every entry point include/lfattn.h declares.
-EXPORTS = ("lfattn_create", "lfattn_forward", "lfattn_destroy", "lfattn_status_string",
+EXPORTS = ("lfattn_create", "lfattn_create_masked", "lfattn_forward",
+           "lfattn_forward_global_proj", "lfattn_destroy", "lfattn_status_string",
            "lfattn_scored_pairs", "lfattn_band_launch_pairs", "lfattn_band_rows",
-           "lfattn_global_list",
+           "lfattn_global_list", "lfattn_global_list_batch",
            "lfattn_set_timing", "lfattn_read_timing")
 
 _lib = None
@@ -53,8 +54,14 @@ def load():
     lib.lfattn_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p,
                                   ctypes.c_int, ctypes.c_float]
+    lib.lfattn_create_masked.restype = ctypes.c_int
+    lib.lfattn_create_masked.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         i32p, ctypes.POINTER(ctypes.c_ubyte), ctypes.c_float]
     lib.lfattn_forward.restype = ctypes.c_int
     lib.lfattn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.lfattn_forward_global_proj.restype = ctypes.c_int
+    lib.lfattn_forward_global_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.lfattn_destroy.restype = ctypes.c_int
     lib.lfattn_destroy.argtypes = [vp]
     lib.lfattn_status_string.restype = ctypes.c_char_p
@@ -67,6 +74,8 @@ def load():
     lib.lfattn_band_rows.argtypes = [vp, i32p]
     lib.lfattn_global_list.restype = ctypes.c_int
     lib.lfattn_global_list.argtypes = [vp, i32p, ctypes.c_int, i32p]
+    lib.lfattn_global_list_batch.restype = ctypes.c_int
+    lib.lfattn_global_list_batch.argtypes = [vp, ctypes.c_int, i32p, ctypes.c_int, i32p]
     lib.lfattn_set_timing.restype = ctypes.c_int
     lib.lfattn_set_timing.argtypes = [vp, ctypes.c_int]
     lib.lfattn_read_timing.restype = ctypes.c_int
@@ -105,8 +114,34 @@ def lfattn_create(B: int, H: int, N: int, D: int, dtype: int, window: int,
     return handle.value
 
 
+def lfattn_create_masked(B: int, H: int, N: int, D: int, dtype: int, window: int,
+                         dilation=None, global_mask=None, scale: float = 0.0) -> int:
+    """As lfattn_create, with one global set per batch element: global_mask is
+    a [B, N] array-like of booleans/bytes (nonzero: global), or None."""
+    lib = load()
+    handle = ctypes.c_void_p()
+    mp = None
+    if global_mask is not None:
+        import numpy as np
+        m = np.ascontiguousarray(np.asarray(global_mask).astype(np.uint8).reshape(B * N))
+        mp = (ctypes.c_ubyte * (B * N)).from_buffer_copy(m.tobytes())
+    st = lib.lfattn_create_masked(ctypes.byref(handle), B, H, N, D, dtype, window,
+                                  _int_array(dilation), mp, float(scale))
+    _check(st, "lfattn_create_masked")
+    return handle.value
+
+
 def _ptr(x) -> int:
+    if x is None:
+        return None
     return x if isinstance(x, int) else x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
 
 
 def lfattn_forward(handle: int, Q, K, V, O, stream=None) -> None:
@@ -114,13 +149,17 @@ def lfattn_forward(handle: int, Q, K, V, O, stream=None) -> None:
     stream: a HIP stream handle (int), a torch stream, or None for torch's
     current stream on the current device."""
     lib = load()
-    if stream is None:
-        import torch
-        stream = torch.cuda.current_stream().cuda_stream
-    elif not isinstance(stream, int):
-        stream = stream.cuda_stream
-    _check(lib.lfattn_forward(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), stream),
+    _check(lib.lfattn_forward(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _stream(stream)),
            "lfattn_forward")
+
+
+def lfattn_forward_global_proj(handle: int, Q, K, V, Qg, Kg, Vg, O, stream=None) -> None:
+    """Enqueue one forward in which the global rows take Qg, Kg, Vg (each may be
+    None for Q, K, V)."""
+    lib = load()
+    _check(lib.lfattn_forward_global_proj(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(Qg),
+                                          _ptr(Kg), _ptr(Vg), _ptr(O), _stream(stream)),
+           "lfattn_forward_global_proj")
 
 
 def lfattn_destroy(handle: int) -> None:
@@ -154,6 +193,17 @@ def lfattn_global_list(handle: int) -> list:
     return list(buf[: n.value])
 
 
+def lfattn_global_list_batch(handle: int, b: int) -> list:
+    lib = load()
+    n = ctypes.c_int()
+    _check(lib.lfattn_global_list_batch(handle, b, None, 0, ctypes.byref(n)),
+           "lfattn_global_list_batch")
+    buf = (ctypes.c_int * max(1, n.value))()
+    _check(lib.lfattn_global_list_batch(handle, b, buf, n.value, ctypes.byref(n)),
+           "lfattn_global_list_batch")
+    return list(buf[: n.value])
+
+
 def lfattn_set_timing(handle: int, enable: bool) -> None:
     _check(load().lfattn_set_timing(handle, 1 if enable else 0), "lfattn_set_timing")
 
@@ -174,8 +224,12 @@ class LFAttention:
         self.dtype = dtype
         self.handle = lfattn_create(B, H, N, D, dtype, window, dilation, global_idx, scale)
 
-    def forward(self, Q, K, V, O, stream=None):
-        lfattn_forward(self.handle, Q, K, V, O, stream)
+    def forward(self, Q, K, V, O, stream=None, Qg=None, Kg=None, Vg=None):
+        """Qg, Kg, Vg: the global rows' own projections (None: Q, K, V)."""
+        if Qg is None and Kg is None and Vg is None:
+            lfattn_forward(self.handle, Q, K, V, O, stream)
+        else:
+            lfattn_forward_global_proj(self.handle, Q, K, V, Qg, Kg, Vg, O, stream)
         return O
 
     @property

@@ -101,6 +101,35 @@ def test_null_handle_calls(lib):
     assert lib.lfattn_global_list(None, None, 0, ctypes.byref(cnt)) == L.LFATTN_EINVAL
 
 
+@pytest.mark.parametrize("kw", [
+    dict(B=0), dict(N=0), dict(window=-1), dict(dtype=7), dict(dil=[0]),
+    dict(scale=float("nan")), dict(out=False)])
+def test_create_masked_rejects_invalid(lib, kw):
+    B, H, N = kw.get("B", 2), 1, kw.get("N", 16)
+    mask = (ctypes.c_ubyte * max(1, B * N))()
+    h = ctypes.c_void_p(1234)
+    dil = (ctypes.c_int * 1)(*kw["dil"]) if "dil" in kw else None
+    st = lib.lfattn_create_masked(ctypes.byref(h) if kw.get("out", True) else None, B, H, N, 64,
+                                  kw.get("dtype", 1), kw.get("window", 4), dil, mask,
+                                  kw.get("scale", 0.0))
+    assert st == L.LFATTN_EINVAL
+    if kw.get("out", True):
+        assert h.value is None
+
+
+def test_create_masked_unsupported_head_dim(lib):
+    h = ctypes.c_void_p()
+    assert lib.lfattn_create_masked(ctypes.byref(h), 1, 1, 16, 96, 1, 4, None, None, 0.0) == \
+        L.LFATTN_EUNSUPPORTED
+
+
+def test_new_entry_points_reject_null_handle(lib):
+    assert lib.lfattn_forward_global_proj(None, 16, 16, 16, None, None, None, 16, None) == \
+        L.LFATTN_EINVAL
+    cnt = ctypes.c_int()
+    assert lib.lfattn_global_list_batch(None, 0, None, 0, ctypes.byref(cnt)) == L.LFATTN_EINVAL
+
+
 def test_binding_raises_on_missing_library(tmp_path, monkeypatch):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(L, "_lib", None)
