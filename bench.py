@@ -38,6 +38,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--workload", default="longformer_base_n4096")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--variant", default="plain", choices=["plain", "global_proj", "two_sequences"],
+                   help="global_proj: the global rows take their own projections (a second "
+                        "seeded Q, K, V); two_sequences: B = 2 with a different global set per "
+                        "sequence ([CLS] + 10 seeded positions for the second), and own "
+                        "projections")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -163,24 +168,54 @@ def main():
     from long_context_sparse_band_amd import lfattn as L
     from long_context_sparse_band_amd import workloads as W
 
+    import dataclasses
+
+    import numpy as np
+
     wl = W.BY_NAME[args.workload]
+    if args.variant == "two_sequences":
+        wl = dataclasses.replace(wl, B=2)
     inp = W.generate(wl)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    q, k, v = (torch.from_numpy(a).to(dev).to(tdt).contiguous() for a in (inp.q, inp.k, inp.v))
+
+    def upload(x):
+        return torch.from_numpy(x).to(dev).to(tdt).contiguous()
+
+    q, k, v = (upload(a) for a in (inp.q, inp.k, inp.v))
     o = torch.empty_like(q)
     dtype = L.LFATTN_BF16 if wl.dtype == "bf16" else L.LFATTN_F32
-    h = L.lfattn_create(wl.B, wl.H, wl.N, wl.D, dtype, wl.window, list(inp.dilation),
-                        list(inp.glob))
+    sets = [list(inp.glob)] * wl.B
+    if args.variant == "two_sequences":
+        rng = np.random.default_rng(wl.seed + 2000)
+        sets = [list(inp.glob),
+                sorted({0} | set(rng.choice(wl.N, size=10, replace=False).tolist()))]
+        mask = np.zeros((wl.B, wl.N), dtype=np.uint8)
+        for b, st in enumerate(sets):
+            mask[b, st] = 1
+        h = L.lfattn_create_masked(wl.B, wl.H, wl.N, wl.D, dtype, wl.window,
+                                   list(inp.dilation), mask)
+    else:
+        h = L.lfattn_create(wl.B, wl.H, wl.N, wl.D, dtype, wl.window, list(inp.dilation),
+                            list(inp.glob))
+    if args.variant == "plain":
+        def forward():
+            L.lfattn_forward(h, q, k, v, o, stream)
+    else:
+        ginp = W.generate(dataclasses.replace(wl, seed=wl.seed + 1000))
+        qg, kg, vg = (upload(a) for a in (ginp.q, ginp.k, ginp.v))
+
+        def forward():
+            L.lfattn_forward_global_proj(h, q, k, v, qg, kg, vg, o, stream)
     pairs = L.lfattn_scored_pairs(h)
-    n_g = len(inp.glob)
+    n_g = [len(st) for st in sets] if args.variant == "two_sequences" else len(inp.glob)
     # Pairs the band kernel launch scores (the band rows, and the global rows
     # where the same launch computes their partials).
     band_pairs = L.lfattn_band_launch_pairs(h)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
-        L.lfattn_forward(h, q, k, v, o, stream)
+        forward()
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` forwards between two events on the stream.
@@ -188,7 +223,7 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        L.lfattn_forward(h, q, k, v, o, stream)
+        forward()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -197,7 +232,7 @@ def main():
     # each kernel (a second pass, so the first timing is undisturbed).
     L.lfattn_set_timing(h, True)
     for _ in range(args.steps):
-        L.lfattn_forward(h, q, k, v, o, stream)
+        forward()
     band_ms, glob_ms, n = L.lfattn_read_timing(h)
     L.lfattn_set_timing(h, False)
     band_ms /= max(n, 1)
@@ -212,7 +247,7 @@ def main():
     for _ in range(20):
         e0.record(stream)
         for _ in range(rep):
-            L.lfattn_forward(h, q, k, v, o, stream)
+            forward()
         e1.record(stream)
         torch.cuda.synchronize()
         warm.append(e0.elapsed_time(e1) / rep)
@@ -221,7 +256,7 @@ def main():
     for t in range(20):
         scratch.fill_(t + 1)
         e0.record(stream)
-        L.lfattn_forward(h, q, k, v, o, stream)
+        forward()
         e1.record(stream)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
@@ -229,7 +264,7 @@ def main():
     cold_band = []
     for t in range(20):
         scratch.fill_(t + 101)
-        L.lfattn_forward(h, q, k, v, o, stream)
+        forward()
         torch.cuda.synchronize()
         b_ms, _, _ = L.lfattn_read_timing(h)
         cold_band.append(b_ms)
@@ -257,7 +292,8 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded i.i.d. Gaussian Q, K, V)",
         "inputs": input_record(inp),
-        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
+        "config": {"workload": wl.name, "variant": args.variant,
+                   "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
                    "window": wl.window, "dilation": [int(x) for x in inp.dilation],
                    "n_global": n_g, "scored_pairs": pairs, "parallelism": "single GPU"},
         "whole_forward_tflops": pairs * flops_per_pair / (ms * 1e-3) / 1e12,
@@ -278,12 +314,12 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": band_tflops / peak,
-            "traffic": recorded_traffic(wl.name),
+            "traffic": recorded_traffic(wl.name) if args.variant == "plain" else None,
             "algorithmic_flops_per_launch": band_pairs * flops_per_pair,
             "ideal_bytes_per_launch": 4 * wl.B * wl.H * wl.N * wl.D * elem,
         },
     }
-    if not args.no_cpu:
+    if not args.no_cpu and args.variant == "plain":
         line["cpu_baseline"] = cpu_baseline(inp, wl, pairs)
     print(json.dumps(line), flush=True)
 
