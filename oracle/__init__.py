@@ -39,8 +39,9 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
+        # Build when missing or older than its source.
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
         lib = ctypes.CDLL(_LIB)
         i32p = ctypes.POINTER(ctypes.c_int)
         i64p = ctypes.POINTER(ctypes.c_int64)
@@ -60,8 +61,15 @@ def _load():
         lib.lfo_attention_ex.restype = ctypes.c_int
         lib.lfo_attention_ex.argtypes = [f32p, f32p, f32p, f32p, f32p, f32p, f64p,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_int, i32p, i32p, i32p, ctypes.c_int,
-                                         ctypes.c_double, i64p, ctypes.c_int64, ctypes.c_int]
+                                         ctypes.c_int, i32p, ctypes.c_int, i32p, i32p,
+                                         ctypes.c_int, ctypes.c_double, i64p, ctypes.c_int64,
+                                         ctypes.c_int]
+        lib.lfo_allowed_set_ex.restype = ctypes.c_int64
+        lib.lfo_allowed_set_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, i32p, ctypes.c_int, ctypes.c_int, i32p]
+        lib.lfo_count_pairs_ex.restype = ctypes.c_int64
+        lib.lfo_count_pairs_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, i32p, ctypes.c_int, i32p, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -73,29 +81,32 @@ def _i32(a):
     return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
 
 
-def allowed_set(n: int, window: int, dilation: int, glob, i: int) -> np.ndarray:
-    """Sorted key positions row i scores (one head)."""
+def allowed_set(n: int, window: int, dilation: int, glob, i: int,
+                causal: bool = False) -> np.ndarray:
+    """Sorted key positions row i scores (one head).  causal: the band's left
+    half and the row itself (no global tokens)."""
     lib = _load()
     g, gp = _i32(list(glob))
     keys = np.empty(n + len(g) + 1, dtype=np.int32)
-    cnt = lib.lfo_allowed_set(n, window, dilation, gp, len(g), i,
-                              keys.ctypes.data_as(ctypes.POINTER(ctypes.c_int)))
+    cnt = lib.lfo_allowed_set_ex(n, window, dilation, int(causal), gp, len(g), i,
+                                 keys.ctypes.data_as(ctypes.POINTER(ctypes.c_int)))
     if cnt < 0:
         raise ValueError("oracle: invalid arguments (code %d)" % cnt)
     return keys[:cnt].copy()
 
 
 def count_pairs(B: int, H: int, n: int, window: int, dilation=None, glob=(),
-                batch_glob=None) -> int:
+                batch_glob=None, causal: bool = False) -> int:
     """Total scored pairs over B x H x n rows, by explicit set construction.
     batch_glob: B lists, one global set per batch element (glob ignored)."""
     if batch_glob is not None:
         assert len(batch_glob) == B
-        return sum(count_pairs(1, H, n, window, dilation, list(g)) for g in batch_glob)
+        return sum(count_pairs(1, H, n, window, dilation, list(g), causal=causal)
+                   for g in batch_glob)
     lib = _load()
     g, gp = _i32(list(glob))
     d, dp = _i32(dilation)
-    cnt = lib.lfo_count_pairs(B, H, n, window, dp, gp, len(g))
+    cnt = lib.lfo_count_pairs_ex(B, H, n, window, dp, int(causal), gp, len(g))
     if cnt < 0:
         raise ValueError("oracle: invalid arguments (code %d)" % cnt)
     return int(cnt)
@@ -103,7 +114,7 @@ def count_pairs(B: int, H: int, n: int, window: int, dilation=None, glob=(),
 
 def attention(q, k, v, window: int, dilation=None, glob=(), scale: float = 0.0,
               rows=None, nthreads: int | None = None, qg=None, kg=None, vg=None,
-              batch_glob=None) -> np.ndarray:
+              batch_glob=None, causal: bool = False) -> np.ndarray:
     """Oracle attention output in float64.
 
     q, k, v: float32 arrays [B, H, N, D] (bf16 data already widened).
@@ -111,7 +122,8 @@ def attention(q, k, v, window: int, dilation=None, glob=(), scale: float = 0.0,
     (b*H + h)*N + i (returns [len(rows), D]).
     qg, kg, vg: the global rows' own projections (same shape), or None for q,
     k, v.  batch_glob: B lists, one global set per batch element (then glob is
-    ignored), or None for glob shared by all.
+    ignored), or None for glob shared by all.  causal: the band's left half
+    and the row itself (no global tokens).
     """
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.float32)
@@ -155,8 +167,8 @@ def attention(q, k, v, window: int, dilation=None, glob=(), scale: float = 0.0,
     st = lib.lfo_attention_ex(q.ctypes.data_as(f32p), k.ctypes.data_as(f32p),
                               v.ctypes.data_as(f32p), pp[0], pp[1], pp[2],
                               out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                              B, H, N, D, window, dp, gp, gop, len(g), float(scale), rp, n_rows,
-                              int(nthreads))
+                              B, H, N, D, window, dp, int(causal), gp, gop, len(g),
+                              float(scale), rp, n_rows, int(nthreads))
     if st != 0:
         raise ValueError("oracle: attention failed (code %d)" % st)
     return out

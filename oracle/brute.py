@@ -97,3 +97,33 @@ def attention_ex(q, k, v, window: int, dilation=None, batch_glob=None, qg=None, 
                 wg = np.exp(zg)
                 out[b, h][gset] = (wg @ vg[b, h]) / wg.sum(axis=1, keepdims=True)
     return out
+
+
+def causal_band_mask(n: int, window: int, dilation: int = 1) -> np.ndarray:
+    """Boolean [n, n] mask of the causal band: key j <= i with (i - j) a
+    multiple of d and i - j <= d * (window // 2) (the symmetric band's lower
+    triangle, diagonal included)."""
+    pos = np.arange(n, dtype=np.int64)
+    diff = pos[:, None] - pos[None, :]
+    hw = window // 2
+    return (diff >= 0) & (diff <= dilation * hw) & (diff % dilation == 0)
+
+
+def attention_causal(q, k, v, window: int, dilation=None, scale: float | None = None):
+    """Masked softmax attention over the causal band, float64 [B, H, N, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, D = q.shape
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, H, N, D), dtype=np.float64)
+    for h in range(H):
+        d = 1 if dilation is None else int(dilation[h])
+        additive = np.where(causal_band_mask(N, window, d), 0.0, -np.inf)
+        for b in range(B):
+            z = scale * (q[b, h] @ k[b, h].T) + additive
+            z = z - z.max(axis=1, keepdims=True)
+            w = np.exp(z)
+            out[b, h] = (w @ v[b, h]) / w.sum(axis=1, keepdims=True)
+    return out

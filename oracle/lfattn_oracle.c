@@ -21,6 +21,9 @@
  *       z_j = scale * sum_c Qg[i,c] * Kg[j,c],  O_i = sum_j softmax(z)_j Vg_j
  *     over all N keys, while every other row keeps Q, K, V, for its band and
  *     for the global keys alike.
+ * A causal variant keeps only the band's left half and the row itself,
+ *   S_i = { i + d*k : -hw <= k <= 0, i + d*k >= 0 }
+ * (no global tokens).
  * Sources:
  *   - attention itself, softmax(Q K^T / sqrt(d_k)) V: "Unlimiformer:
  *     Long-Range Transformers with Unlimited Length Input", section 2.3, Eq. (1);
@@ -47,6 +50,10 @@
  *   - one global set per batch element: the page's closing paragraph (the
  *     Hugging Face implementation takes the global tokens as a
  *     global_attention_mask input, one mask row per sequence of the batch).
+ *   - causal band: the dilated-window bullet's use case, a character-level
+ *     language model, predicts each character from the ones before it; the
+ *     page gives no causal rule, and the reading taken keeps the same offsets
+ *     restricted to k <= 0.
  *   - memory tokens: "GMAT: Global Memory Augmentation for Transformers",
  *     section "Global Memory": M memory tokens are prefixed; they attend to all
  *     M+L positions, and main tokens attend to all memory tokens plus a sparse
@@ -94,11 +101,12 @@ static int check_globals(int N, const int* glob, int n_glob) {
  * sliding-window, dilated-window and global-attention bullets and its mask
  * sample; the GMAT page's "Global Memory" section (see the file header).
  */
-int64_t lfo_allowed_set(int N, int window, int dilation, const int* glob,
-                        int n_glob, int i, int* keys) {
+int64_t lfo_allowed_set_ex(int N, int window, int dilation, int causal, const int* glob,
+                           int n_glob, int i, int* keys) {
   if (N <= 0 || window < 0 || dilation < 1 || i < 0 || i >= N || keys == NULL)
     return LFO_EINVAL;
   if (!check_globals(N, glob, n_glob)) return LFO_EINVAL;
+  if (causal && n_glob > 0) return LFO_EINVAL; /* the causal band has no global tokens */
 
   if (is_global(glob, n_glob, i)) {
     /* A global row attends to every position. */
@@ -115,6 +123,7 @@ int64_t lfo_allowed_set(int N, int window, int dilation, const int* glob,
   int64_t k_hi = ((int64_t)(N - 1) - i) / d;
   if (k_lo < -hw) k_lo = -hw;
   if (k_hi > hw) k_hi = hw;
+  if (causal && k_hi > 0) k_hi = 0; /* causal: the row and the keys before it */
   for (int64_t k = k_lo; k <= k_hi; ++k) {
     int64_t j = (int64_t)i + d * k;
     if (j >= 0 && j < N) keys[n++] = (int)j;
@@ -130,14 +139,20 @@ int64_t lfo_allowed_set(int N, int window, int dilation, const int* glob,
   return u;
 }
 
+/* The symmetric band (see lfo_allowed_set_ex). */
+int64_t lfo_allowed_set(int N, int window, int dilation, const int* glob, int n_glob, int i,
+                        int* keys) {
+  return lfo_allowed_set_ex(N, window, dilation, 0, glob, n_glob, i, keys);
+}
+
 /*
  * Total number of scored (query, key) pairs, summed over B batches, H heads
  * and N rows, by building every S_i explicitly.  dilation: H entries, or NULL
  * for all 1.  This is the quantity the Longformer glossary page counts with
  * mask.sum() in its sample.  Returns the count, or LFO_EINVAL / LFO_ENOMEM.
  */
-int64_t lfo_count_pairs(int B, int H, int N, int window, const int* dilation,
-                        const int* glob, int n_glob) {
+int64_t lfo_count_pairs_ex(int B, int H, int N, int window, const int* dilation, int causal,
+                           const int* glob, int n_glob) {
   if (B <= 0 || H <= 0 || N <= 0 || window < 0) return LFO_EINVAL;
   if (!check_globals(N, glob, n_glob)) return LFO_EINVAL;
   int* keys = (int*)malloc(sizeof(int) * ((size_t)N + (size_t)n_glob + 1));
@@ -148,7 +163,7 @@ int64_t lfo_count_pairs(int B, int H, int N, int window, const int* dilation,
     if (d < 1) { free(keys); return LFO_EINVAL; }
     int64_t per_head = 0;
     for (int i = 0; i < N; ++i) {
-      int64_t n = lfo_allowed_set(N, window, d, glob, n_glob, i, keys);
+      int64_t n = lfo_allowed_set_ex(N, window, d, causal, glob, n_glob, i, keys);
       if (n < 0) { free(keys); return n; }
       per_head += n;
     }
@@ -158,13 +173,18 @@ int64_t lfo_count_pairs(int B, int H, int N, int window, const int* dilation,
   return total;
 }
 
+int64_t lfo_count_pairs(int B, int H, int N, int window, const int* dilation, const int* glob,
+                        int n_glob) {
+  return lfo_count_pairs_ex(B, H, N, window, dilation, 0, glob, n_glob);
+}
+
 /* ---- attention values ---------------------------------------------------- */
 
 typedef struct {
   const float *Q, *K, *V;
   const float *Qg, *Kg, *Vg; /* the global rows' projections (= Q, K, V if none) */
   double* O;
-  int B, H, N, D, window, n_glob;
+  int B, H, N, D, window, n_glob, causal;
   const int* dilation;
   const int* glob;
   const int* goff; /* per-batch lists: G_b = glob[goff[b] .. goff[b+1]), or NULL */
@@ -197,7 +217,7 @@ static int one_row(const lfo_job* jb, int64_t flat, int* keys, double* z,
   const float* Kbh = (grow ? jb->Kg : jb->K) + (size_t)bh * N * D;
   const float* Vbh = (grow ? jb->Vg : jb->V) + (size_t)bh * N * D;
 
-  int64_t n = lfo_allowed_set(N, jb->window, d, gl, ng, i, keys);
+  int64_t n = lfo_allowed_set_ex(N, jb->window, d, jb->causal, gl, ng, i, keys);
   if (n <= 0) return LFO_EINVAL; /* never empty: k = 0 gives j = i */
 
   double zmax = -INFINITY;
@@ -252,7 +272,7 @@ static void* worker(void* arg) {
  */
 int lfo_attention_ex(const float* Q, const float* K, const float* V,
                      const float* Qg, const float* Kg, const float* Vg, double* O,
-                     int B, int H, int N, int D, int window, const int* dilation,
+                     int B, int H, int N, int D, int window, const int* dilation, int causal,
                      const int* glob, const int* goff, int n_glob, double scale,
                      const int64_t* rows, int64_t n_rows, int nthreads) {
   if (!Q || !K || !V || !O || B <= 0 || H <= 0 || N <= 0 || D <= 0 ||
@@ -264,6 +284,7 @@ int lfo_attention_ex(const float* Q, const float* K, const float* V,
       if (goff[b + 1] < goff[b]) return LFO_EINVAL;
   }
   if (!check_globals(N, glob, n_glob)) return LFO_EINVAL;
+  if (causal && n_glob > 0) return LFO_EINVAL;
   if (dilation)
     for (int h = 0; h < H; ++h)
       if (dilation[h] < 1) return LFO_EINVAL;
@@ -286,6 +307,7 @@ int lfo_attention_ex(const float* Q, const float* K, const float* V,
     jb->Qg = Qg ? Qg : Q; jb->Kg = Kg ? Kg : K; jb->Vg = Vg ? Vg : V;
     jb->B = B; jb->H = H; jb->N = N; jb->D = D; jb->window = window;
     jb->dilation = dilation; jb->glob = glob; jb->n_glob = n_glob; jb->goff = goff;
+    jb->causal = causal;
     jb->scale = scale; jb->rows = rows; jb->n_rows = n_rows;
     jb->first = n_rows * t / nthreads;
     jb->last = n_rows * (t + 1) / nthreads;
@@ -312,6 +334,6 @@ int lfo_attention(const float* Q, const float* K, const float* V, double* O,
                   int B, int H, int N, int D, int window, const int* dilation,
                   const int* glob, int n_glob, double scale,
                   const int64_t* rows, int64_t n_rows, int nthreads) {
-  return lfo_attention_ex(Q, K, V, NULL, NULL, NULL, O, B, H, N, D, window, dilation, glob,
+  return lfo_attention_ex(Q, K, V, NULL, NULL, NULL, O, B, H, N, D, window, dilation, 0, glob,
                           NULL, n_glob, scale, rows, n_rows, nthreads);
 }
