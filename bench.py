@@ -38,11 +38,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--workload", default="longformer_base_n4096")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--variant", default="plain", choices=["plain", "global_proj", "two_sequences"],
+    p.add_argument("--variant", default="plain",
+                   choices=["plain", "global_proj", "two_sequences", "causal"],
                    help="global_proj: the global rows take their own projections (a second "
                         "seeded Q, K, V); two_sequences: B = 2 with a different global set per "
                         "sequence ([CLS] + 10 seeded positions for the second), and own "
-                        "projections")
+                        "projections; causal: the causal band (workloads without global "
+                        "tokens, e.g. dilated_charlm_n8192)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -173,6 +175,10 @@ def main():
     import numpy as np
 
     wl = W.BY_NAME[args.workload]
+    if args.variant == "causal" and (wl.glob or wl.n_random_glob):
+        print(f"bench.py: --variant causal needs a workload without global tokens; "
+              f"{wl.name} has some.", file=sys.stderr)
+        sys.exit(2)
     if args.variant == "two_sequences":
         wl = dataclasses.replace(wl, B=2)
     inp = W.generate(wl)
@@ -195,10 +201,13 @@ def main():
             mask[b, st] = 1
         h = L.lfattn_create_masked(wl.B, wl.H, wl.N, wl.D, dtype, wl.window,
                                    list(inp.dilation), mask)
+    elif args.variant == "causal":
+        h = L.lfattn_create_causal(wl.B, wl.H, wl.N, wl.D, dtype, wl.window,
+                                   list(inp.dilation))
     else:
         h = L.lfattn_create(wl.B, wl.H, wl.N, wl.D, dtype, wl.window, list(inp.dilation),
                             list(inp.glob))
-    if args.variant == "plain":
+    if args.variant in ("plain", "causal"):
         def forward():
             L.lfattn_forward(h, q, k, v, o, stream)
     else:

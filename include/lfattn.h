@@ -33,6 +33,12 @@
  *
  * while every other row keeps Q, K, V for its band and for the global keys.
  *
+ * A causal variant (lfattn_create_causal) keeps the band's left half and the
+ * row itself, S_i = { i + d_h*k : -hw <= k <= 0, i + d_h*k >= 0 }, with no
+ * global tokens: the dilated-window bullet's use case is a character-level
+ * language model, which predicts each character from the ones before it (the
+ * page states no causal rule; this is the reading taken).
+ *
  * Layouts.  Q, K, V, O: contiguous [B, H, N, D] arrays in device memory, D
  * fastest, 16-byte aligned, element type set at create (float, or bfloat16
  * stored as 16-bit words).  Accumulation is always fp32; bf16 outputs are
@@ -118,6 +124,14 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
 lfattn_status lfattn_create_masked(lfattn_t* out, int B, int H, int N, int D,
                                    lfattn_dtype dtype, int window, const int* dilation,
                                    const unsigned char* global_mask, float scale);
+
+/*
+ * As lfattn_create for the causal band (see the operation above): no global
+ * tokens, every row scores itself and the hw keys of its band before it.
+ */
+lfattn_status lfattn_create_causal(lfattn_t* out, int B, int H, int N, int D,
+                                   lfattn_dtype dtype, int window, const int* dilation,
+                                   float scale);
 
 /*
  * Enqueue one forward pass on `stream` (NULL: the null stream).

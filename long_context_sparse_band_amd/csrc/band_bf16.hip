@@ -227,7 +227,10 @@ void band32_kernel(BandArgs a) {
   const bool gi = w.dil == 0;
   const int d = gi ? 1 : w.dil;
   const int r = gi ? 0 : w.r, t0 = gi ? 0 : w.t0, N = a.N;
-  const int hw = gi ? (1 << 29) : a.hw;
+  // A row u scores the keys u - hl .. u + hr of its subsequence (hl = hr =
+  // the half-width; causal: hr = 0).
+  const int hl = gi ? (1 << 29) : a.hw;
+  const int hr = gi ? (1 << 29) : a.hr;
   const int Lr = d == 1 ? N - r : (N - r + d - 1) / d;
   const size_t base = (size_t)w.bh * N * D;
   // A global-row item reads the global rows' own projections.
@@ -254,8 +257,8 @@ void band32_kernel(BandArgs a) {
   const int ua = (gi ? ROWS * w.r : t0) + 32 * qblk;
   const int ub = min(ua + 31, n_rows - 1);
   const bool live = ua < n_rows;
-  const int s_lo = gi ? w.t0 * a.chunk_keys : max(0, t0 - hw);
-  const int s_hi = gi ? min(N, s_lo + a.chunk_keys) - 1 : min(Lr - 1, t0 + ROWS - 1 + hw);
+  const int s_lo = gi ? w.t0 * a.chunk_keys : max(0, t0 - hl);
+  const int s_hi = gi ? min(N, s_lo + a.chunk_keys) - 1 : min(Lr - 1, t0 + ROWS - 1 + hr);
   const int u = ua + l32;
   const bool row_ok = u < n_rows;
 
@@ -277,7 +280,7 @@ void band32_kernel(BandArgs a) {
     }
   }
   // A key at position k is in the band of the lane's row u when
-  // |k - u| <= hw and k <= s_hi (keys below 0 never occur: tiles start at
+  // -hl <= k - u <= hr and k <= s_hi (keys below 0 never occur: tiles start at
   // s_lo >= 0).  Rows past the end are never stored, so they need no mask.
 
   const int n_band = (s_hi - s_lo) / TK + 1;
@@ -381,8 +384,8 @@ void band32_kernel(BandArgs a) {
   // global tiles need the per-pair dedupe test).
   bool gdup = false;
   if (live) {
-    const int lo_w = ua - hw;
-    const unsigned span_w = (unsigned)(ub - ua + 2 * hw);
+    const int lo_w = ua - hl;
+    const unsigned span_w = (unsigned)(ub - ua + hl + hr);
     for (int x = lane; x < n_glob; x += 64) gdup |= (unsigned)(sm.gsp[x] - lo_w) <= span_w;
   }
   gdup = __any(gdup);
@@ -406,8 +409,8 @@ void band32_kernel(BandArgs a) {
     if (live && x < n_steps && tt < n_tiles) {
       if (tt < n_band) {
         const int k0 = s_lo + TK * tt, k1 = min(k0 + TK - 1, s_hi);
-        fa = (k0 <= ub + hw) & (k1 >= ua - hw);
-        ff = fa & (k1 == k0 + TK - 1) & (k1 - ua <= hw) & (ub - k0 <= hw);
+        fa = (k0 <= ub + hr) & (k1 >= ua - hl);
+        ff = fa & (k1 == k0 + TK - 1) & (k1 - ua <= hr) & (ub - k0 <= hl);
       } else {
         fa = true;
       }
@@ -451,7 +454,7 @@ void band32_kernel(BandArgs a) {
     if (!fast) {
       if (band) {
         const int k0 = s_lo + TK * t, k1 = min(k0 + TK - 1, s_hi);
-        edge = !((k1 == k0 + TK - 1) & (k1 - ua <= hw) & (ub - k0 <= hw));
+        edge = !((k1 == k0 + TK - 1) & (k1 - ua <= hr) & (ub - k0 <= hl));
       } else {
         bool act;
         const int ln = lane_id(), lh = ln >> 5, lu = ua + (ln & 31);
@@ -466,14 +469,14 @@ void band32_kernel(BandArgs a) {
           // Keep a valid slot unless its key lies in the row's band (then the
           // band already scored it).  One group of 4 slots at a time, so that
           // this rare path stays small in registers.
-          const unsigned span = 2u * (unsigned)hw;
+          const unsigned span = (unsigned)hl + (unsigned)hr;
 #pragma unroll 1
           for (int g4 = 0; g4 < 4; ++g4) {
             const int kk0 = 8 * g4 + 4 * lh;
             const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsp[min(g0 + kk0, kGlobCap - 4)];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const bool k = (kk0 + c < nvalid) & (lu < n_rows) & ((unsigned)(sp[c] - lu + hw) > span);
+              const bool k = (kk0 + c < nvalid) & (lu < n_rows) & ((unsigned)(sp[c] - lu + hl) > span);
               keep |= (unsigned)k << (4 * g4 + c);
             }
           }
@@ -513,9 +516,10 @@ void band32_kernel(BandArgs a) {
       if (edge) {
         if (band) {
           const int s0 = s_lo + TK * t;
-          const unsigned span = 2u * (unsigned)hw;
+          const unsigned span = (unsigned)hl + (unsigned)hr;
           const int ln = lane_id(), lh = ln >> 5;
-          const int e = s0 + 4 * lh - (ua + (ln & 31)) + hw;  // |key - u| <= hw  <=>  e + br <= 2hw
+          // -hl <= key - u <= hr  <=>  0 <= e + br <= hl + hr
+          const int e = s0 + 4 * lh - (ua + (ln & 31)) + hl;
           if (s0 + TK - 1 <= s_hi) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)

@@ -38,6 +38,7 @@ constexpr long long kMaxN = 1LL << 29;
 
 struct lfattn_ctx {
   int B = 0, H = 0, N = 0, D = 0, dtype = 0, window = 0, hw = 0;
+  bool causal = false;  // the band's left half and the row itself
   float scale = 0.0f;
   std::vector<int> dil;
   // Global lists, sorted and without repeats: gl[0] for every batch element
@@ -92,9 +93,9 @@ void free_ctx(lfattn_ctx* c) {
 }
 
 // Scored pairs of one head with dilation d: every row's band (keys i + d*k,
-// |k| <= hw, inside [0, N)), plus the global keys outside that band; global
-// rows score all N keys.
-long long head_pairs(int N, long long hw, int d, const std::vector<int>& glob,
+// |k| <= hw, inside [0, N); causal: -hw <= k <= 0), plus the global keys
+// outside that band; global rows score all N keys.
+long long head_pairs(int N, long long hw, int d, bool causal, const std::vector<int>& glob,
                      const std::vector<unsigned char>& isg) {
   long long total = 0;
   for (long long i = 0; i < N; ++i) {
@@ -102,7 +103,7 @@ long long head_pairs(int N, long long hw, int d, const std::vector<int>& glob,
       total += N;
       continue;
     }
-    long long left = std::min(i / d, hw), right = std::min((N - 1 - i) / d, hw);
+    long long left = std::min(i / d, hw), right = causal ? 0 : std::min((N - 1 - i) / d, hw);
     long long n = 1 + left + right;
     for (int g : glob) {
       long long off = g - i;
@@ -160,10 +161,12 @@ lfattn_status check_support(int B, int H, int N, int D) {
 // (shared) or one per batch element.
 lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtype dtype,
                           int window, const int* dilation,
-                          std::vector<std::vector<int>>&& gl, bool shared, float scale) {
+                          std::vector<std::vector<int>>&& gl, bool shared, bool causal,
+                          float scale) {
   lfattn_ctx* c = new (std::nothrow) lfattn_ctx;
   if (!c) return LFATTN_ENOMEM;
   c->B = B; c->H = H; c->N = N; c->D = D; c->dtype = (int)dtype; c->window = window;
+  c->causal = causal;
   c->hw = (int)std::min<long long>(window / 2, N);  // a wider half-width changes nothing
   c->scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
   c->dil.assign(H, 1);
@@ -194,7 +197,7 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
                                            isg.begin() + (size_t)(t + 1) * N);
       long long total = 0;
       for (int d : ds) {
-        long long per = head_pairs(N, window / 2, d, c->gl[t], row);
+        long long per = head_pairs(N, window / 2, d, causal, c->gl[t], row);
         total += per * (long long)std::count(c->dil.begin(), c->dil.end(), d);
       }
       c->pairs += total * (shared ? B : 1);
@@ -402,7 +405,20 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   gl[0].assign(global_idx, global_idx + n_global);
   std::sort(gl[0].begin(), gl[0].end());
   gl[0].erase(std::unique(gl[0].begin(), gl[0].end()), gl[0].end());
-  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), true, scale);
+  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), true, false,
+                     scale);
+}
+
+lfattn_status lfattn_create_causal(lfattn_t* out, int B, int H, int N, int D,
+                                   lfattn_dtype dtype, int window, const int* dilation,
+                                   float scale) {
+  if (!out) return LFATTN_EINVAL;
+  *out = nullptr;
+  lfattn_status st = check_shape(B, H, N, D, dtype, window, dilation, scale);
+  if (st != LFATTN_OK) return st;
+  if ((st = check_support(B, H, N, D)) != LFATTN_OK) return st;
+  std::vector<std::vector<int>> gl(1);
+  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), true, true, scale);
 }
 
 lfattn_status lfattn_create_masked(lfattn_t* out, int B, int H, int N, int D,
@@ -423,7 +439,8 @@ lfattn_status lfattn_create_masked(lfattn_t* out, int B, int H, int N, int D,
   bool shared = true;
   for (int b = 1; b < B && shared; ++b) shared = gl[b] == gl[0];
   if (shared) gl.resize(1);
-  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), shared, scale);
+  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), shared, false,
+                     scale);
 }
 
 lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const void* V, void* O,
@@ -480,6 +497,7 @@ lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* 
   a.work = c->d_work; a.glob = c->d_glob; a.is_glob = c->d_isglob;
   a.isg_stride = c->shared ? 0 : c->N;
   a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
+  a.hr = c->causal ? 0 : c->hw;
   a.rows_per_wg = c->band_rows;
   a.part = c->glob_items ? c->d_part : nullptr;
   a.n_sets = c->n_sets; a.n_chunks = c->n_chunks; a.chunk_keys = c->chunk_keys;

@@ -53,6 +53,7 @@ struct BandArgs {
   const unsigned char* is_glob;  // [B or 1][N]: 1 where the position is global
   long long isg_stride;        // N (one row per batch element) or 0 (one shared row)
   int H, N, hw, n_glob;        // n_glob: the longest global list
+  int hr;                      // keys a row scores after itself: hw, or 0 (causal)
   float sl2;                   // softmax scale times log2(e)
   int rows_per_wg;             // rows per band workgroup (bf16: 64 or 128)
   // Global-row items (dil 0): partial records laid out as GlobArgs::part

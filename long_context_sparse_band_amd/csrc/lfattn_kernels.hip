@@ -236,7 +236,9 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   const int wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
   const BandWork w = a.work[blockIdx.x];
   const int d = w.dil;
-  const int r = w.r, t0 = w.t0, hw = a.hw, N = a.N;
+  // A row u scores the keys u - hl .. u + hr of its subsequence (hl = hr =
+  // the half-width; causal: hr = 0).
+  const int r = w.r, t0 = w.t0, hl = a.hw, hr = a.hr, N = a.N;
   // The global list of this item's batch element.
   const int* gl = a.glob + w.g0;
   const int n_glob = w.ng;
@@ -257,8 +259,8 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   st.load_q(Qp, qrow, hi);
 
   // Key range of the workgroup's band, in subsequence positions.
-  const int s_lo = max(0, t0 - hw);
-  const int s_hi = min(Lr - 1, t0 + kBandRows - 1 + hw);
+  const int s_lo = max(0, t0 - hl);
+  const int s_hi = min(Lr - 1, t0 + kBandRows - 1 + hr);
   const int n_band = (s_hi - s_lo) / TK + 1;
   const int n_glob_tiles = (n_glob + TK - 1) / TK;
   const int n_tiles = n_band + n_glob_tiles;
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   // Keys a row may score inside a band tile form the interval [lo, hi] of
   // subsequence positions.  Rows past the end of the subsequence get an empty
   // interval.
-  int lo = max(u - hw, 0), hi_key = min(u + hw, s_hi);
+  int lo = max(u - hl, 0), hi_key = min(u + hr, s_hi);
   if (u >= Lr || hi_key < lo) {
     lo = 0x3fffffff;
     hi_key = lo;
@@ -309,9 +311,9 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
       if (tt < n_band) {
         const int s0 = s_lo + TK * tt;
         const int kb_ = min(s0 + TK - 1, s_hi);  // last real key of the tile
-        const bool any = s0 <= ub + hw && kb_ >= ua - hw;
+        const bool any = s0 <= ub + hr && kb_ >= ua - hl;
         if (any) {
-          const bool full = (kb_ == s0 + TK - 1) && (s0 + TK - 1 - ua <= hw) && (ub - s0 <= hw);
+          const bool full = (kb_ == s0 + TK - 1) && (s0 + TK - 1 - ua <= hr) && (ub - s0 <= hl);
           st.scores(tile, lane, s);
           if (!full) {
             const int base = s0 + 4 * hi - lo;
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
       } else {
         // Global keys, minus those already inside this row's band.
         const int nvalid = min(TK, n_glob - TK * (tt - n_band));
-        const unsigned span = 2u * (unsigned)hw;
+        const unsigned span = (unsigned)hl + (unsigned)hr;
         bool any = false;
         unsigned keep = 0;  // bit 16*kb + i
 #pragma unroll
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const bool k = (kk0 + c < nvalid) && u < Lr &&
-                             (unsigned)(spv[c] - u + hw) > span;
+                             (unsigned)(spv[c] - u + hl) > span;
               keep |= (unsigned)k << (16 * kb + 4 * g + c);
               any |= k;
             }

@@ -24,7 +24,7 @@ LFATTN_F32 = 0
 LFATTN_BF16 = 1
 
 # Every entry point include/lfattn.h declares.
-EXPORTS = ("lfattn_create", "lfattn_create_masked", "lfattn_forward",
+EXPORTS = ("lfattn_create", "lfattn_create_masked", "lfattn_create_causal", "lfattn_forward",
            "lfattn_forward_global_proj", "lfattn_destroy", "lfattn_status_string",
            "lfattn_scored_pairs", "lfattn_band_launch_pairs", "lfattn_band_rows",
            "lfattn_global_list", "lfattn_global_list_batch",
@@ -58,6 +58,10 @@ def load():
     lib.lfattn_create_masked.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          i32p, ctypes.POINTER(ctypes.c_ubyte), ctypes.c_float]
+    lib.lfattn_create_causal.restype = ctypes.c_int
+    lib.lfattn_create_causal.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         i32p, ctypes.c_float]
     lib.lfattn_forward.restype = ctypes.c_int
     lib.lfattn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.lfattn_forward_global_proj.restype = ctypes.c_int
@@ -128,6 +132,17 @@ def lfattn_create_masked(B: int, H: int, N: int, D: int, dtype: int, window: int
     st = lib.lfattn_create_masked(ctypes.byref(handle), B, H, N, D, dtype, window,
                                   _int_array(dilation), mp, float(scale))
     _check(st, "lfattn_create_masked")
+    return handle.value
+
+
+def lfattn_create_causal(B: int, H: int, N: int, D: int, dtype: int, window: int,
+                         dilation=None, scale: float = 0.0) -> int:
+    """As lfattn_create for the causal band (no global tokens)."""
+    lib = load()
+    handle = ctypes.c_void_p()
+    st = lib.lfattn_create_causal(ctypes.byref(handle), B, H, N, D, dtype, window,
+                                  _int_array(dilation), float(scale))
+    _check(st, "lfattn_create_causal")
     return handle.value
 
 

@@ -123,6 +123,16 @@ def test_create_masked_unsupported_head_dim(lib):
         L.LFATTN_EUNSUPPORTED
 
 
+def test_create_causal_rejects_invalid(lib):
+    h = ctypes.c_void_p(1234)
+    assert lib.lfattn_create_causal(None, 1, 1, 16, 64, 1, 4, None, 0.0) == L.LFATTN_EINVAL
+    assert lib.lfattn_create_causal(ctypes.byref(h), 1, 1, 16, 64, 1, -2, None, 0.0) == \
+        L.LFATTN_EINVAL
+    assert h.value is None
+    assert lib.lfattn_create_causal(ctypes.byref(h), 1, 1, 16, 96, 1, 4, None, 0.0) == \
+        L.LFATTN_EUNSUPPORTED
+
+
 def test_new_entry_points_reject_null_handle(lib):
     assert lib.lfattn_forward_global_proj(None, 16, 16, 16, None, None, None, 16, None) == \
         L.LFATTN_EINVAL
