@@ -67,6 +67,15 @@ def _load():
         lib.lfo_allowed_set_ex.restype = ctypes.c_int64
         lib.lfo_allowed_set_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, i32p, ctypes.c_int, ctypes.c_int, i32p]
+        lib.lfo_allowed_set_chunked.restype = ctypes.c_int64
+        lib.lfo_allowed_set_chunked.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, i32p]
+        lib.lfo_attention_chunked.restype = ctypes.c_int
+        lib.lfo_attention_chunked.argtypes = [f32p, f32p, f32p, f32p, f32p, f32p, f64p,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_double, i64p, ctypes.c_int64,
+                                              ctypes.c_int]
         lib.lfo_count_pairs_ex.restype = ctypes.c_int64
         lib.lfo_count_pairs_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, i32p, ctypes.c_int, i32p, ctypes.c_int]
@@ -171,4 +180,54 @@ def attention(q, k, v, window: int, dilation=None, glob=(), scale: float = 0.0,
                               float(scale), rp, n_rows, int(nthreads))
     if st != 0:
         raise ValueError("oracle: attention failed (code %d)" % st)
+    return out
+
+
+def allowed_set_chunked(n: int, chunk: int, n_memory: int, i: int) -> np.ndarray:
+    """Sorted key positions row i scores under C x k chunked attention with
+    n_memory memory tokens at positions 0..n_memory-1 (chunks start after)."""
+    lib = _load()
+    keys = np.empty(n + 1, dtype=np.int32)
+    cnt = lib.lfo_allowed_set_chunked(n, chunk, n_memory, i,
+                                      keys.ctypes.data_as(ctypes.POINTER(ctypes.c_int)))
+    if cnt < 0:
+        raise ValueError("oracle: invalid arguments (code %d)" % cnt)
+    return keys[:cnt].copy()
+
+
+def count_pairs_chunked(B: int, H: int, n: int, chunk: int, n_memory: int) -> int:
+    """Total scored pairs under chunked attention, by explicit set construction."""
+    return B * H * sum(len(allowed_set_chunked(n, chunk, n_memory, i)) for i in range(n))
+
+
+def attention_chunked(q, k, v, chunk: int, n_memory: int, scale: float = 0.0, rows=None,
+                      nthreads: int | None = None, qg=None, kg=None, vg=None) -> np.ndarray:
+    """Oracle output under GMAT's C x k chunked attention with n_memory memory
+    tokens (the memory rows take qg, kg, vg when given).  Shapes as attention()."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    B, H, N, D = q.shape
+    proj = [None if x is None else np.ascontiguousarray(x, dtype=np.float32)
+            for x in (qg, kg, vg)]
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    if rows is None:
+        n_rows, rp = B * H * N, None
+        out = np.empty((B, H, N, D), dtype=np.float64)
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n_rows = len(r)
+        rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        out = np.empty((n_rows, D), dtype=np.float64)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    pp = [None if x is None else x.ctypes.data_as(f32p) for x in proj]
+    st = lib.lfo_attention_chunked(q.ctypes.data_as(f32p), k.ctypes.data_as(f32p),
+                                   v.ctypes.data_as(f32p), pp[0], pp[1], pp[2],
+                                   out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                   B, H, N, D, chunk, n_memory, float(scale), rp, n_rows,
+                                   int(nthreads))
+    if st != 0:
+        raise ValueError("oracle: chunked attention failed (code %d)" % st)
     return out

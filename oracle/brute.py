@@ -127,3 +127,44 @@ def attention_causal(q, k, v, window: int, dilation=None, scale: float | None = 
             w = np.exp(z)
             out[b, h] = (w @ v[b, h]) / w.sum(axis=1, keepdims=True)
     return out
+
+
+def chunked_mask(n: int, chunk: int, n_memory: int) -> np.ndarray:
+    """Boolean [n, n] mask of GMAT's C x k chunked attention with n_memory
+    memory tokens prefixed: block-diagonal chunks of the main sequence (which
+    starts at n_memory), plus the memory rows and columns set to True."""
+    pos = np.arange(n, dtype=np.int64)
+    blk = np.where(pos >= n_memory, (pos - n_memory) // chunk, -1)
+    mask = (blk[:, None] == blk[None, :]) & (blk[:, None] >= 0)
+    mask[:n_memory, :] = True
+    mask[:, :n_memory] = True
+    return mask
+
+
+def attention_chunked(q, k, v, chunk: int, n_memory: int, qg=None, kg=None, vg=None,
+                      scale: float | None = None):
+    """Masked softmax attention over the chunked pattern, float64; the memory
+    rows take qg, kg, vg when given."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    qg = q if qg is None else np.asarray(qg, dtype=np.float64)
+    kg = k if kg is None else np.asarray(kg, dtype=np.float64)
+    vg = v if vg is None else np.asarray(vg, dtype=np.float64)
+    B, H, N, D = q.shape
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(D)
+    additive = np.where(chunked_mask(N, chunk, n_memory), 0.0, -np.inf)
+    out = np.empty((B, H, N, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            z = scale * (q[b, h] @ k[b, h].T) + additive
+            z = z - z.max(axis=1, keepdims=True)
+            w = np.exp(z)
+            out[b, h] = (w @ v[b, h]) / w.sum(axis=1, keepdims=True)
+            if n_memory:
+                zg = scale * (qg[b, h][:n_memory] @ kg[b, h].T)
+                zg = zg - zg.max(axis=1, keepdims=True)
+                wg = np.exp(zg)
+                out[b, h][:n_memory] = (wg @ vg[b, h]) / wg.sum(axis=1, keepdims=True)
+    return out

@@ -23,7 +23,11 @@
  *     for the global keys alike.
  * A causal variant keeps only the band's left half and the row itself,
  *   S_i = { i + d*k : -hw <= k <= 0, i + d*k >= 0 }
- * (no global tokens).
+ * (no global tokens).  The chunked variant (GMAT's C x k chunked
+ * self-attention with M memory tokens) replaces the band by the row's chunk:
+ *   S_i = { 0, ..., N-1 }                                      if i < M
+ *   S_i = { 0, ..., M-1 }  u  { c0, ..., min(c0 + C, N) - 1 }    otherwise,
+ *   c0 = M + C * floor((i - M) / C).
  * Sources:
  *   - attention itself, softmax(Q K^T / sqrt(d_k)) V: "Unlimiformer:
  *     Long-Range Transformers with Unlimited Length Input", section 2.3, Eq. (1);
@@ -54,6 +58,12 @@
  *     language model, predicts each character from the ones before it; the
  *     page gives no causal rule, and the reading taken keeps the same offsets
  *     restricted to k <= 0.
+ *   - chunked self-attention: "GMAT: Global Memory Augmentation for
+ *     Transformers", section "Chunked self-attention": the main sequence is cut
+ *     into contiguous chunks of length C, each token attends to the tokens of
+ *     its chunk and to the memory, not to other chunks (the last chunk may be
+ *     shorter when the length is not a multiple of C: a reading, the page
+ *     takes length C*k).
  *   - memory tokens: "GMAT: Global Memory Augmentation for Transformers",
  *     section "Global Memory": M memory tokens are prefixed; they attend to all
  *     M+L positions, and main tokens attend to all memory tokens plus a sparse
@@ -139,6 +149,29 @@ int64_t lfo_allowed_set_ex(int N, int window, int dilation, int causal, const in
   return u;
 }
 
+/*
+ * The allowed key set of row i under C x k chunked attention with M memory
+ * tokens (positions 0..M-1; the chunks start at M), in increasing order.
+ * Returns |S_i| or LFO_EINVAL.  Source: the GMAT page, sections "Global
+ * Memory" and "Chunked self-attention" (see the file header).
+ */
+int64_t lfo_allowed_set_chunked(int N, int chunk, int n_memory, int i, int* keys) {
+  if (N <= 0 || chunk < 1 || n_memory < 0 || n_memory > N || i < 0 || i >= N || !keys)
+    return LFO_EINVAL;
+  int64_t n = 0;
+  if (i < n_memory) {
+    /* A memory token attends to all M + L positions. */
+    for (int j = 0; j < N; ++j) keys[n++] = j;
+    return n;
+  }
+  /* The memory first (all of it), then the row's chunk. */
+  for (int j = 0; j < n_memory; ++j) keys[n++] = j;
+  const int64_t c0 = n_memory + (int64_t)chunk * ((i - n_memory) / chunk);
+  const int64_t c1 = c0 + chunk < N ? c0 + chunk : N;
+  for (int64_t j = c0; j < c1; ++j) keys[n++] = (int)j;
+  return n;
+}
+
 /* The symmetric band (see lfo_allowed_set_ex). */
 int64_t lfo_allowed_set(int N, int window, int dilation, const int* glob, int n_glob, int i,
                         int* keys) {
@@ -185,6 +218,7 @@ typedef struct {
   const float *Qg, *Kg, *Vg; /* the global rows' projections (= Q, K, V if none) */
   double* O;
   int B, H, N, D, window, n_glob, causal;
+  int chunk, n_memory; /* chunk > 0: chunked attention (window, glob unused) */
   const int* dilation;
   const int* glob;
   const int* goff; /* per-batch lists: G_b = glob[goff[b] .. goff[b+1]), or NULL */
@@ -212,12 +246,13 @@ static int one_row(const lfo_job* jb, int64_t flat, int* keys, double* z,
   const int* gl = jb->goff ? jb->glob + jb->goff[b] : jb->glob;
   const int ng = jb->goff ? jb->goff[b + 1] - jb->goff[b] : jb->n_glob;
   /* A global row takes its own projections. */
-  const int grow = is_global(gl, ng, i);
+  const int grow = jb->chunk > 0 ? i < jb->n_memory : is_global(gl, ng, i);
   const float* q = (grow ? jb->Qg : jb->Q) + (size_t)flat * D;
   const float* Kbh = (grow ? jb->Kg : jb->K) + (size_t)bh * N * D;
   const float* Vbh = (grow ? jb->Vg : jb->V) + (size_t)bh * N * D;
 
-  int64_t n = lfo_allowed_set_ex(N, jb->window, d, jb->causal, gl, ng, i, keys);
+  int64_t n = jb->chunk > 0 ? lfo_allowed_set_chunked(N, jb->chunk, jb->n_memory, i, keys)
+                            : lfo_allowed_set_ex(N, jb->window, d, jb->causal, gl, ng, i, keys);
   if (n <= 0) return LFO_EINVAL; /* never empty: k = 0 gives j = i */
 
   double zmax = -INFINITY;
@@ -259,6 +294,8 @@ static void* worker(void* arg) {
   return NULL;
 }
 
+static int run_jobs(const lfo_job* base, int nthreads);
+
 /*
  * Attention output for a list of rows, general form.  Q, K, V: [B, H, N, D]
  * row-major floats; Qg, Kg, Vg: the same shape, the global rows' projections,
@@ -294,24 +331,31 @@ int lfo_attention_ex(const float* Q, const float* K, const float* V,
     for (int64_t r = 0; r < n_rows; ++r)
       if (rows[r] < 0 || rows[r] >= total) return LFO_EINVAL;
   if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  lfo_job base;
+  memset(&base, 0, sizeof(base));
+  base.Q = Q; base.K = K; base.V = V; base.O = O;
+  base.Qg = Qg ? Qg : Q; base.Kg = Kg ? Kg : K; base.Vg = Vg ? Vg : V;
+  base.B = B; base.H = H; base.N = N; base.D = D; base.window = window;
+  base.dilation = dilation; base.glob = glob; base.n_glob = n_glob; base.goff = goff;
+  base.causal = causal;
+  base.scale = scale; base.rows = rows; base.n_rows = n_rows;
+  return run_jobs(&base, nthreads);
+}
+
+/* Split the row list of `base` over nthreads workers and run them. */
+static int run_jobs(const lfo_job* base, int nthreads) {
+  const int64_t n_rows = base->n_rows;
   if (nthreads < 1) nthreads = 1;
   if (n_rows == 0) return LFO_OK;
   if ((int64_t)nthreads > n_rows) nthreads = (int)n_rows;
-
   lfo_job* jobs = (lfo_job*)calloc((size_t)nthreads, sizeof(lfo_job));
   pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
   if (!jobs || !tids) { free(jobs); free(tids); return LFO_ENOMEM; }
   for (int t = 0; t < nthreads; ++t) {
-    lfo_job* jb = &jobs[t];
-    jb->Q = Q; jb->K = K; jb->V = V; jb->O = O;
-    jb->Qg = Qg ? Qg : Q; jb->Kg = Kg ? Kg : K; jb->Vg = Vg ? Vg : V;
-    jb->B = B; jb->H = H; jb->N = N; jb->D = D; jb->window = window;
-    jb->dilation = dilation; jb->glob = glob; jb->n_glob = n_glob; jb->goff = goff;
-    jb->causal = causal;
-    jb->scale = scale; jb->rows = rows; jb->n_rows = n_rows;
-    jb->first = n_rows * t / nthreads;
-    jb->last = n_rows * (t + 1) / nthreads;
-    jb->status = LFO_OK;
+    jobs[t] = *base;
+    jobs[t].first = n_rows * t / nthreads;
+    jobs[t].last = n_rows * (t + 1) / nthreads;
+    jobs[t].status = LFO_OK;
   }
   char* created = (char*)calloc((size_t)nthreads, 1);
   if (!created) { free(jobs); free(tids); return LFO_ENOMEM; }
@@ -336,4 +380,32 @@ int lfo_attention(const float* Q, const float* K, const float* V, double* O,
                   const int64_t* rows, int64_t n_rows, int nthreads) {
   return lfo_attention_ex(Q, K, V, NULL, NULL, NULL, O, B, H, N, D, window, dilation, 0, glob,
                           NULL, n_glob, scale, rows, n_rows, nthreads);
+}
+
+/*
+ * Attention output under C x k chunked attention with M memory tokens (the
+ * memory rows use Qg, Kg, Vg when given, as global rows).  Arguments as
+ * lfo_attention_ex; chunk >= 1, 0 <= n_memory <= N.
+ */
+int lfo_attention_chunked(const float* Q, const float* K, const float* V,
+                          const float* Qg, const float* Kg, const float* Vg, double* O,
+                          int B, int H, int N, int D, int chunk, int n_memory, double scale,
+                          const int64_t* rows, int64_t n_rows, int nthreads) {
+  if (!Q || !K || !V || !O || B <= 0 || H <= 0 || N <= 0 || D <= 0 || chunk < 1 ||
+      n_memory < 0 || n_memory > N || n_rows < 0)
+    return LFO_EINVAL;
+  const int64_t total = (int64_t)B * H * N;
+  if (!rows && n_rows != total) return LFO_EINVAL;
+  if (rows)
+    for (int64_t r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= total) return LFO_EINVAL;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  lfo_job base;
+  memset(&base, 0, sizeof(base));
+  base.Q = Q; base.K = K; base.V = V; base.O = O;
+  base.Qg = Qg ? Qg : Q; base.Kg = Kg ? Kg : K; base.Vg = Vg ? Vg : V;
+  base.B = B; base.H = H; base.N = N; base.D = D;
+  base.chunk = chunk; base.n_memory = n_memory;
+  base.scale = scale; base.rows = rows; base.n_rows = n_rows;
+  return run_jobs(&base, nthreads);
 }
