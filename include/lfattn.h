@@ -39,6 +39,15 @@
  * language model, which predicts each character from the ones before it (the
  * page states no causal rule; this is the reading taken).
  *
+ * A chunked variant (lfattn_create_chunked) is GMAT's C x k chunked
+ * self-attention with M memory tokens ("GMAT: Global Memory Augmentation for
+ * Transformers", sections "Global Memory" and "Chunked self-attention"): the
+ * memory is positions 0 .. M-1 (G = {0, ..., M-1}); the main sequence after it
+ * is cut into contiguous chunks of C positions (the last one shorter when
+ * N - M is not a multiple of C), and a main row scores its own chunk and the
+ * memory, S_i = {0, ..., M-1} u {c0, ..., min(c0 + C, N) - 1} with
+ * c0 = M + C * floor((i - M) / C).  Memory rows score all N keys.
+ *
  * Layouts.  Q, K, V, O: contiguous [B, H, N, D] arrays in device memory, D
  * fastest, 16-byte aligned, element type set at create (float, or bfloat16
  * stored as 16-bit words).  Accumulation is always fp32; bf16 outputs are
@@ -132,6 +141,15 @@ lfattn_status lfattn_create_masked(lfattn_t* out, int B, int H, int N, int D,
 lfattn_status lfattn_create_causal(lfattn_t* out, int B, int H, int N, int D,
                                    lfattn_dtype dtype, int window, const int* dilation,
                                    float scale);
+
+/*
+ * As lfattn_create for GMAT's chunked attention (see the operation above):
+ * chunk >= 1 keys per chunk, 0 <= n_memory <= N memory positions at the start
+ * (bf16: n_memory <= 512).  Dilation is 1.  lfattn_forward_global_proj gives
+ * the memory rows their own projections, as for any global rows.
+ */
+lfattn_status lfattn_create_chunked(lfattn_t* out, int B, int H, int N, int D,
+                                    lfattn_dtype dtype, int chunk, int n_memory, float scale);
 
 /*
  * Enqueue one forward pass on `stream` (NULL: the null stream).

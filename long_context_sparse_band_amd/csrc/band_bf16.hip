@@ -1,4 +1,4 @@
-// bf16 band kernel for gfx950 (MI355X): band32_kernel<D, KS>, D = 64 or 128.
+// bf16 band kernel for gfx950 (MI355X): band32_kernel<D, KS, CHUNK>, D = 64 or 128.
 //
 // A workgroup of 4 wavefronts takes 32*4/KS consecutive query rows of one
 // (batch, head, dilation residue) and walks the 32-key tiles of their band,
@@ -204,7 +204,9 @@ struct B32 {
   };
 };
 
-template <int D, int KS_>
+// CHUNK: GMAT chunked attention (a.chunk > 0) instead of a band; a separate
+// instantiation, so that the band kernels carry none of its arithmetic.
+template <int D, int KS_, bool CHUNK>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(B32<D, KS_>::WPE, B32<D, KS_>::WPE)))
 void band32_kernel(BandArgs a) {
@@ -231,6 +233,16 @@ void band32_kernel(BandArgs a) {
   // the half-width; causal: hr = 0).
   const int hl = gi ? (1 << 29) : a.hw;
   const int hr = gi ? (1 << 29) : a.hr;
+  // Chunked attention (band items, d = 1): row u scores its chunk instead,
+  // positions c0 .. c0 + C - 1 with c0 = cb + C * floor((u - cb) / C); rows
+  // before cb are the memory (global rows, whose band output is not kept).
+  const int cC = (!CHUNK || gi) ? 0 : a.chunk, cb = a.cbase;
+  auto lo_of = [&](int uu) -> int {
+    return cC == 0 ? uu - hl : (uu < cb ? uu : cb + (uu - cb) / cC * cC);
+  };
+  auto hi_of = [&](int uu) -> int {
+    return cC == 0 ? uu + hr : (uu < cb ? uu : cb + (uu - cb) / cC * cC + cC - 1);
+  };
   const int Lr = d == 1 ? N - r : (N - r + d - 1) / d;
   const size_t base = (size_t)w.bh * N * D;
   // A global-row item reads the global rows' own projections.
@@ -257,8 +269,12 @@ void band32_kernel(BandArgs a) {
   const int ua = (gi ? ROWS * w.r : t0) + 32 * qblk;
   const int ub = min(ua + 31, n_rows - 1);
   const bool live = ua < n_rows;
-  const int s_lo = gi ? w.t0 * a.chunk_keys : max(0, t0 - hl);
-  const int s_hi = gi ? min(N, s_lo + a.chunk_keys) - 1 : min(Lr - 1, t0 + ROWS - 1 + hr);
+  const int s_lo = gi ? w.t0 * a.chunk_keys : max(0, lo_of(t0));
+  const int s_hi = gi ? min(N, s_lo + a.chunk_keys) - 1 : min(Lr - 1, hi_of(t0 + ROWS - 1));
+  // Keys of this wave's first and last rows (both ends are non-decreasing in
+  // the row): a tile reaches some row when k0 <= hi_b and k1 >= lo_a, and
+  // every row wholly when k0 >= lo_b and k1 <= hi_a.
+  const int lo_a = lo_of(ua), hi_a = hi_of(ua), lo_b = lo_of(ub), hi_b = hi_of(ub);
   const int u = ua + l32;
   const bool row_ok = u < n_rows;
 
@@ -384,8 +400,8 @@ void band32_kernel(BandArgs a) {
   // global tiles need the per-pair dedupe test).
   bool gdup = false;
   if (live) {
-    const int lo_w = ua - hl;
-    const unsigned span_w = (unsigned)(ub - ua + hl + hr);
+    const int lo_w = lo_a;
+    const unsigned span_w = (unsigned)(hi_b - lo_a);
     for (int x = lane; x < n_glob; x += 64) gdup |= (unsigned)(sm.gsp[x] - lo_w) <= span_w;
   }
   gdup = __any(gdup);
@@ -409,8 +425,8 @@ void band32_kernel(BandArgs a) {
     if (live && x < n_steps && tt < n_tiles) {
       if (tt < n_band) {
         const int k0 = s_lo + TK * tt, k1 = min(k0 + TK - 1, s_hi);
-        fa = (k0 <= ub + hr) & (k1 >= ua - hl);
-        ff = fa & (k1 == k0 + TK - 1) & (k1 - ua <= hr) & (ub - k0 <= hl);
+        fa = (k0 <= hi_b) & (k1 >= lo_a);
+        ff = fa & (k1 == k0 + TK - 1) & (k1 <= hi_a) & (k0 >= lo_b);
       } else {
         fa = true;
       }
@@ -454,7 +470,7 @@ void band32_kernel(BandArgs a) {
     if (!fast) {
       if (band) {
         const int k0 = s_lo + TK * t, k1 = min(k0 + TK - 1, s_hi);
-        edge = !((k1 == k0 + TK - 1) & (k1 - ua <= hr) & (ub - k0 <= hl));
+        edge = !((k1 == k0 + TK - 1) & (k1 <= hi_a) & (k0 >= lo_b));
       } else {
         bool act;
         const int ln = lane_id(), lh = ln >> 5, lu = ua + (ln & 31);
@@ -469,14 +485,15 @@ void band32_kernel(BandArgs a) {
           // Keep a valid slot unless its key lies in the row's band (then the
           // band already scored it).  One group of 4 slots at a time, so that
           // this rare path stays small in registers.
-          const unsigned span = (unsigned)hl + (unsigned)hr;
+          const int lo_u = lo_of(lu);
+          const unsigned span = (unsigned)(hi_of(lu) - lo_u);
 #pragma unroll 1
           for (int g4 = 0; g4 < 4; ++g4) {
             const int kk0 = 8 * g4 + 4 * lh;
             const i32x4 sp = *(const LDS_AS i32x4*)&sm.gsp[min(g0 + kk0, kGlobCap - 4)];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const bool k = (kk0 + c < nvalid) & (lu < n_rows) & ((unsigned)(sp[c] - lu + hl) > span);
+              const bool k = (kk0 + c < nvalid) & (lu < n_rows) & ((unsigned)(sp[c] - lo_u) > span);
               keep |= (unsigned)k << (4 * g4 + c);
             }
           }
@@ -516,10 +533,11 @@ void band32_kernel(BandArgs a) {
       if (edge) {
         if (band) {
           const int s0 = s_lo + TK * t;
-          const unsigned span = (unsigned)hl + (unsigned)hr;
-          const int ln = lane_id(), lh = ln >> 5;
-          // -hl <= key - u <= hr  <=>  0 <= e + br <= hl + hr
-          const int e = s0 + 4 * lh - (ua + (ln & 31)) + hl;
+          const int ln = lane_id(), lh = ln >> 5, lu = ua + (ln & 31);
+          // lo(u) <= key <= hi(u)  <=>  0 <= e + br <= hi(u) - lo(u)
+          const int lo_u = lo_of(lu);
+          const unsigned span = (unsigned)(hi_of(lu) - lo_u);
+          const int e = s0 + 4 * lh - lo_u;
           if (s0 + TK - 1 <= s_hi) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
@@ -758,8 +776,21 @@ hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, c
   const dim3 grid(n_wg), block(256);
   const bool wide = a.rows_per_wg == 128;  // one tile stream for four row blocks
   if (!wide && a.rows_per_wg != 64) return hipErrorInvalidValue;
-  if (D == 64) return launch_kernel(wide ? band32_kernel<64, 1> : band32_kernel<64, 2>, grid, block, s, a, t);
-  if (D == 128) return launch_kernel(wide ? band32_kernel<128, 1> : band32_kernel<128, 2>, grid, block, s, a, t);
+  if (a.chunk > 0) {
+    if (D == 64)
+      return launch_kernel(wide ? band32_kernel<64, 1, true> : band32_kernel<64, 2, true>, grid,
+                           block, s, a, t);
+    if (D == 128)
+      return launch_kernel(wide ? band32_kernel<128, 1, true> : band32_kernel<128, 2, true>,
+                           grid, block, s, a, t);
+    return hipErrorInvalidValue;
+  }
+  if (D == 64)
+    return launch_kernel(wide ? band32_kernel<64, 1, false> : band32_kernel<64, 2, false>, grid,
+                         block, s, a, t);
+  if (D == 128)
+    return launch_kernel(wide ? band32_kernel<128, 1, false> : band32_kernel<128, 2, false>,
+                         grid, block, s, a, t);
   return hipErrorInvalidValue;
 }
 

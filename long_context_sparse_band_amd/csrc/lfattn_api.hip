@@ -39,6 +39,8 @@ constexpr long long kMaxN = 1LL << 29;
 struct lfattn_ctx {
   int B = 0, H = 0, N = 0, D = 0, dtype = 0, window = 0, hw = 0;
   bool causal = false;  // the band's left half and the row itself
+  int chunk = 0;        // > 0: chunked attention with chunks of this length
+  int n_memory = 0;     // chunked: memory positions 0 .. n_memory - 1 (the global rows)
   float scale = 0.0f;
   std::vector<int> dil;
   // Global lists, sorted and without repeats: gl[0] for every batch element
@@ -94,13 +96,19 @@ void free_ctx(lfattn_ctx* c) {
 
 // Scored pairs of one head with dilation d: every row's band (keys i + d*k,
 // |k| <= hw, inside [0, N); causal: -hw <= k <= 0), plus the global keys
-// outside that band; global rows score all N keys.
-long long head_pairs(int N, long long hw, int d, bool causal, const std::vector<int>& glob,
-                     const std::vector<unsigned char>& isg) {
+// outside that band; global rows score all N keys.  chunk > 0: a row past the
+// memory scores its chunk and the memory.
+long long head_pairs(int N, long long hw, int d, bool causal, int chunk, int n_memory,
+                     const std::vector<int>& glob, const std::vector<unsigned char>& isg) {
   long long total = 0;
   for (long long i = 0; i < N; ++i) {
     if (isg[i]) {
       total += N;
+      continue;
+    }
+    if (chunk > 0) {
+      const long long c0 = n_memory + (i - n_memory) / chunk * chunk;
+      total += std::min<long long>(c0 + chunk, N) - c0 + n_memory;
       continue;
     }
     long long left = std::min(i / d, hw), right = causal ? 0 : std::min((N - 1 - i) / d, hw);
@@ -162,11 +170,13 @@ lfattn_status check_support(int B, int H, int N, int D) {
 lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtype dtype,
                           int window, const int* dilation,
                           std::vector<std::vector<int>>&& gl, bool shared, bool causal,
-                          float scale) {
+                          int chunk, float scale) {
   lfattn_ctx* c = new (std::nothrow) lfattn_ctx;
   if (!c) return LFATTN_ENOMEM;
   c->B = B; c->H = H; c->N = N; c->D = D; c->dtype = (int)dtype; c->window = window;
   c->causal = causal;
+  c->chunk = chunk;
+  c->n_memory = chunk > 0 ? (int)gl[0].size() : 0;  // chunked: G = {0 .. M-1}
   c->hw = (int)std::min<long long>(window / 2, N);  // a wider half-width changes nothing
   c->scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
   c->dil.assign(H, 1);
@@ -197,7 +207,8 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
                                            isg.begin() + (size_t)(t + 1) * N);
       long long total = 0;
       for (int d : ds) {
-        long long per = head_pairs(N, window / 2, d, causal, c->gl[t], row);
+        long long per =
+            head_pairs(N, window / 2, d, causal, chunk, c->n_memory, c->gl[t], row);
         total += per * (long long)std::count(c->dil.begin(), c->dil.end(), d);
       }
       c->pairs += total * (shared ? B : 1);
@@ -405,7 +416,22 @@ lfattn_status lfattn_create(lfattn_t* out, int B, int H, int N, int D, lfattn_dt
   gl[0].assign(global_idx, global_idx + n_global);
   std::sort(gl[0].begin(), gl[0].end());
   gl[0].erase(std::unique(gl[0].begin(), gl[0].end()), gl[0].end());
-  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), true, false,
+  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), true, false, 0,
+                     scale);
+}
+
+lfattn_status lfattn_create_chunked(lfattn_t* out, int B, int H, int N, int D,
+                                    lfattn_dtype dtype, int chunk, int n_memory, float scale) {
+  if (!out) return LFATTN_EINVAL;
+  *out = nullptr;
+  lfattn_status st = check_shape(B, H, N, D, dtype, 0, nullptr, scale);
+  if (st != LFATTN_OK) return st;
+  if (chunk < 1 || n_memory < 0 || n_memory > N) return LFATTN_EINVAL;
+  if ((st = check_support(B, H, N, D)) != LFATTN_OK) return st;
+  // The memory tokens are the global positions 0 .. M-1.
+  std::vector<std::vector<int>> gl(1);
+  for (int m = 0; m < n_memory; ++m) gl[0].push_back(m);
+  return create_impl(out, B, H, N, D, dtype, 0, nullptr, std::move(gl), true, false, chunk,
                      scale);
 }
 
@@ -418,7 +444,8 @@ lfattn_status lfattn_create_causal(lfattn_t* out, int B, int H, int N, int D,
   if (st != LFATTN_OK) return st;
   if ((st = check_support(B, H, N, D)) != LFATTN_OK) return st;
   std::vector<std::vector<int>> gl(1);
-  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), true, true, scale);
+  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), true, true, 0,
+                     scale);
 }
 
 lfattn_status lfattn_create_masked(lfattn_t* out, int B, int H, int N, int D,
@@ -439,7 +466,7 @@ lfattn_status lfattn_create_masked(lfattn_t* out, int B, int H, int N, int D,
   bool shared = true;
   for (int b = 1; b < B && shared; ++b) shared = gl[b] == gl[0];
   if (shared) gl.resize(1);
-  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), shared, false,
+  return create_impl(out, B, H, N, D, dtype, window, dilation, std::move(gl), shared, false, 0,
                      scale);
 }
 
@@ -498,6 +525,8 @@ lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* 
   a.isg_stride = c->shared ? 0 : c->N;
   a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
   a.hr = c->causal ? 0 : c->hw;
+  a.chunk = c->chunk;
+  a.cbase = c->n_memory;
   a.rows_per_wg = c->band_rows;
   a.part = c->glob_items ? c->d_part : nullptr;
   a.n_sets = c->n_sets; a.n_chunks = c->n_chunks; a.chunk_keys = c->chunk_keys;

@@ -54,6 +54,8 @@ struct BandArgs {
   long long isg_stride;        // N (one row per batch element) or 0 (one shared row)
   int H, N, hw, n_glob;        // n_glob: the longest global list
   int hr;                      // keys a row scores after itself: hw, or 0 (causal)
+  int chunk;                   // > 0: chunked attention, chunks of this many keys
+  int cbase;                   // first position of the chunked main sequence
   float sl2;                   // softmax scale times log2(e)
   int rows_per_wg;             // rows per band workgroup (bf16: 64 or 128)
   // Global-row items (dil 0): partial records laid out as GlobArgs::part

@@ -239,6 +239,15 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   // A row u scores the keys u - hl .. u + hr of its subsequence (hl = hr =
   // the half-width; causal: hr = 0).
   const int r = w.r, t0 = w.t0, hl = a.hw, hr = a.hr, N = a.N;
+  // Chunked attention (d = 1): row u scores its chunk c0 .. c0 + C - 1,
+  // c0 = cb + C * floor((u - cb) / C), instead; rows before cb are the memory.
+  const int cC = a.chunk, cb = a.cbase;
+  auto lo_of = [&](int uu) -> int {
+    return cC == 0 ? uu - hl : (uu < cb ? uu : cb + (uu - cb) / cC * cC);
+  };
+  auto hi_of = [&](int uu) -> int {
+    return cC == 0 ? uu + hr : (uu < cb ? uu : cb + (uu - cb) / cC * cC + cC - 1);
+  };
   // The global list of this item's batch element.
   const int* gl = a.glob + w.g0;
   const int n_glob = w.ng;
@@ -259,8 +268,9 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   st.load_q(Qp, qrow, hi);
 
   // Key range of the workgroup's band, in subsequence positions.
-  const int s_lo = max(0, t0 - hl);
-  const int s_hi = min(Lr - 1, t0 + kBandRows - 1 + hr);
+  const int s_lo = max(0, lo_of(t0));
+  const int s_hi = min(Lr - 1, hi_of(t0 + kBandRows - 1));
+  const int lo_a = lo_of(ua), hi_a = hi_of(ua), lo_b = lo_of(ub), hi_b = hi_of(ub);
   const int n_band = (s_hi - s_lo) / TK + 1;
   const int n_glob_tiles = (n_glob + TK - 1) / TK;
   const int n_tiles = n_band + n_glob_tiles;
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
   // Keys a row may score inside a band tile form the interval [lo, hi] of
   // subsequence positions.  Rows past the end of the subsequence get an empty
   // interval.
-  int lo = max(u - hl, 0), hi_key = min(u + hr, s_hi);
+  int lo = max(lo_of(u), 0), hi_key = min(hi_of(u), s_hi);
   if (u >= Lr || hi_key < lo) {
     lo = 0x3fffffff;
     hi_key = lo;
@@ -311,9 +321,9 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
       if (tt < n_band) {
         const int s0 = s_lo + TK * tt;
         const int kb_ = min(s0 + TK - 1, s_hi);  // last real key of the tile
-        const bool any = s0 <= ub + hr && kb_ >= ua - hl;
+        const bool any = s0 <= hi_b && kb_ >= lo_a;
         if (any) {
-          const bool full = (kb_ == s0 + TK - 1) && (s0 + TK - 1 - ua <= hr) && (ub - s0 <= hl);
+          const bool full = (kb_ == s0 + TK - 1) && (s0 + TK - 1 <= hi_a) && (s0 >= lo_b);
           st.scores(tile, lane, s);
           if (!full) {
             const int base = s0 + 4 * hi - lo;
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
       } else {
         // Global keys, minus those already inside this row's band.
         const int nvalid = min(TK, n_glob - TK * (tt - n_band));
-        const unsigned span = (unsigned)hl + (unsigned)hr;
+
         bool any = false;
         unsigned keep = 0;  // bit 16*kb + i
 #pragma unroll
@@ -343,7 +353,7 @@ __global__ __launch_bounds__(kBandWaves * 64) void band_kernel(BandArgs a) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const bool k = (kk0 + c < nvalid) && u < Lr &&
-                             (unsigned)(spv[c] - u + hl) > span;
+                             (unsigned)(spv[c] - lo) > rng;
               keep |= (unsigned)k << (16 * kb + 4 * g + c);
               any |= k;
             }

@@ -24,7 +24,8 @@ LFATTN_F32 = 0
 LFATTN_BF16 = 1
 
 # Every entry point include/lfattn.h declares.
-EXPORTS = ("lfattn_create", "lfattn_create_masked", "lfattn_create_causal", "lfattn_forward",
+EXPORTS = ("lfattn_create", "lfattn_create_masked", "lfattn_create_causal",
+           "lfattn_create_chunked", "lfattn_forward",
            "lfattn_forward_global_proj", "lfattn_destroy", "lfattn_status_string",
            "lfattn_scored_pairs", "lfattn_band_launch_pairs", "lfattn_band_rows",
            "lfattn_global_list", "lfattn_global_list_batch",
@@ -62,6 +63,10 @@ def load():
     lib.lfattn_create_causal.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          i32p, ctypes.c_float]
+    lib.lfattn_create_chunked.restype = ctypes.c_int
+    lib.lfattn_create_chunked.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_float]
     lib.lfattn_forward.restype = ctypes.c_int
     lib.lfattn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.lfattn_forward_global_proj.restype = ctypes.c_int
@@ -143,6 +148,18 @@ def lfattn_create_causal(B: int, H: int, N: int, D: int, dtype: int, window: int
     st = lib.lfattn_create_causal(ctypes.byref(handle), B, H, N, D, dtype, window,
                                   _int_array(dilation), float(scale))
     _check(st, "lfattn_create_causal")
+    return handle.value
+
+
+def lfattn_create_chunked(B: int, H: int, N: int, D: int, dtype: int, chunk: int,
+                          n_memory: int, scale: float = 0.0) -> int:
+    """GMAT chunked attention: chunks of `chunk` keys after n_memory memory
+    positions (the global rows)."""
+    lib = load()
+    handle = ctypes.c_void_p()
+    st = lib.lfattn_create_chunked(ctypes.byref(handle), B, H, N, D, dtype, chunk, n_memory,
+                                   float(scale))
+    _check(st, "lfattn_create_chunked")
     return handle.value
 
 

@@ -133,6 +133,17 @@ def test_create_causal_rejects_invalid(lib):
         L.LFATTN_EUNSUPPORTED
 
 
+def test_create_chunked_rejects_invalid(lib):
+    h = ctypes.c_void_p(1234)
+    assert lib.lfattn_create_chunked(None, 1, 1, 16, 64, 1, 4, 2, 0.0) == L.LFATTN_EINVAL
+    for chunk, mem in [(0, 2), (-1, 2), (4, -1), (4, 17)]:
+        assert lib.lfattn_create_chunked(ctypes.byref(h), 1, 1, 16, 64, 1, chunk, mem, 0.0) == \
+            L.LFATTN_EINVAL
+        assert h.value is None
+    assert lib.lfattn_create_chunked(ctypes.byref(h), 1, 1, 16, 96, 1, 4, 2, 0.0) == \
+        L.LFATTN_EUNSUPPORTED
+
+
 def test_new_entry_points_reject_null_handle(lib):
     assert lib.lfattn_forward_global_proj(None, 16, 16, 16, None, None, None, 16, None) == \
         L.LFATTN_EINVAL
