@@ -39,12 +39,15 @@ def parse():
     p.add_argument("--workload", default="longformer_base_n4096")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--variant", default="plain",
-                   choices=["plain", "global_proj", "two_sequences", "causal"],
+                   choices=["plain", "global_proj", "two_sequences", "causal", "chunked"],
                    help="global_proj: the global rows take their own projections (a second "
                         "seeded Q, K, V); two_sequences: B = 2 with a different global set per "
                         "sequence ([CLS] + 10 seeded positions for the second), and own "
                         "projections; causal: the causal band (workloads without global "
-                        "tokens, e.g. dilated_charlm_n8192)")
+                        "tokens, e.g. dilated_charlm_n8192); chunked: GMAT chunked attention, "
+                        "chunks of --chunk keys after the workload's memory tokens "
+                        "(gmat_memory_m64_l16384: (512 x 32, 64))")
+    p.add_argument("--chunk", type=int, default=512, help="chunk length of --variant chunked")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -179,6 +182,10 @@ def main():
         print(f"bench.py: --variant causal needs a workload without global tokens; "
               f"{wl.name} has some.", file=sys.stderr)
         sys.exit(2)
+    if args.variant == "chunked" and tuple(wl.glob) != tuple(range(len(wl.glob))):
+        print(f"bench.py: --variant chunked needs memory tokens at 0..M-1; {wl.name} has "
+              f"other global positions.", file=sys.stderr)
+        sys.exit(2)
     if args.variant == "two_sequences":
         wl = dataclasses.replace(wl, B=2)
     inp = W.generate(wl)
@@ -201,13 +208,15 @@ def main():
             mask[b, st] = 1
         h = L.lfattn_create_masked(wl.B, wl.H, wl.N, wl.D, dtype, wl.window,
                                    list(inp.dilation), mask)
+    elif args.variant == "chunked":
+        h = L.lfattn_create_chunked(wl.B, wl.H, wl.N, wl.D, dtype, args.chunk, len(wl.glob))
     elif args.variant == "causal":
         h = L.lfattn_create_causal(wl.B, wl.H, wl.N, wl.D, dtype, wl.window,
                                    list(inp.dilation))
     else:
         h = L.lfattn_create(wl.B, wl.H, wl.N, wl.D, dtype, wl.window, list(inp.dilation),
                             list(inp.glob))
-    if args.variant in ("plain", "causal"):
+    if args.variant in ("plain", "causal", "chunked"):
         def forward():
             L.lfattn_forward(h, q, k, v, o, stream)
     else:
@@ -302,8 +311,11 @@ def main():
         "data": "synthetic (seeded i.i.d. Gaussian Q, K, V)",
         "inputs": input_record(inp),
         "config": {"workload": wl.name, "variant": args.variant,
+                   **({"chunk": args.chunk, "n_memory": len(wl.glob)}
+                      if args.variant == "chunked" else {}),
                    "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
-                   "window": wl.window, "dilation": [int(x) for x in inp.dilation],
+                   "window": None if args.variant == "chunked" else wl.window,
+                   "dilation": [int(x) for x in inp.dilation],
                    "n_global": n_g, "scored_pairs": pairs, "parallelism": "single GPU"},
         "whole_forward_tflops": pairs * flops_per_pair / (ms * 1e-3) / 1e12,
         "whole_forward_mfma_frac": pairs * flops_per_pair / (ms * 1e-3) / 1e12 / peak,
