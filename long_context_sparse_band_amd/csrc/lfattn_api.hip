@@ -32,6 +32,13 @@ constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
 // path), longer ones otherwise (fewer items, less per-item overhead).
 constexpr int kGlobItemKeysShort = 256, kGlobItemKeysLong = 512;
 constexpr int kWideRounds = 2;
+// From this many rounds of band items per round of workgroup slots on, the
+// global-row items are spread evenly among the band items instead of
+// following them: in a long launch they would otherwise form a last phase of
+// their own, bound by their memory traffic, while spread out they overlap the
+// band items' arithmetic.  (In a launch of one or two rounds, dispatching them
+// last measured faster.)
+constexpr int kSpreadRounds = 4;
 constexpr long long kMaxN = 1LL << 29;
 
 }  // namespace
@@ -287,8 +294,9 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
 
   // Global rows: sets of rows (a workgroup's share of the global rows) times
   // key chunks.  bf16: each (b, h, row set, 256- or 512-key chunk) is one more
-  // item at the end of the band launch, so that those workgroups are
-  // dispatched last and fill the slots the band items leave free.  fp32: a
+  // item of the band launch, after the band items, so that those workgroups
+  // are dispatched last and fill the slots the band items leave free (in a
+  // launch of many rounds, spread among them: kSpreadRounds).  fp32: a
   // separate kernel (below).
   // (Sets are counted per batch element; records are laid out for the
   // longest list.)
@@ -307,8 +315,7 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
     c->n_chunks = (N + keys - 1) / keys;
     // Each global item goes to the XCD of the residue-0 band item whose rows
     // start nearest its chunk (that XCD's L2 holds the chunk's K and V rows):
-    // items are queued per XCD and dealt to block indices congruent to it,
-    // falling back to another queue when one runs dry.
+    // items are queued per XCD.
     std::vector<std::vector<BandWork>> q(kXcds);
     std::vector<int> first_item(B * H, -1);
     for (int k = 0; k < n_items; ++k)
@@ -327,13 +334,32 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
               BandWork{bh, set, ch, 0, gsel[b].x, gsel[b].y, b, 0});
         }
     }
+    // Per XCD, the order of its items: the band items then the global items,
+    // or (long launches) each global item at its proportional place.
+    std::vector<std::vector<BandWork>> ml(kXcds);
+    const bool spread = (long long)n_items >= kSpreadRounds * slots;
+    {
+      std::vector<std::vector<BandWork>> bl(kXcds);
+      for (int bid = 0; bid < n_items; ++bid) bl[bid % kXcds].push_back(table[bid]);
+      for (int x = 0; x < kXcds; ++x) {
+        const size_t nb = bl[x].size(), ng = q[x].size(), tot = nb + ng;
+        size_t ib = 0, ig = 0;
+        for (size_t k2 = 0; k2 < tot; ++k2) {
+          const bool take_g = ig < ng && (ib >= nb || (spread && k2 * ng >= (2 * ig + 1) * tot / 2));
+          ml[x].push_back(take_g ? q[x][ig++] : bl[x][ib++]);
+        }
+      }
+    }
+    // Block indices congruent to x (mod 8) run on XCD x: deal each list to
+    // them in order, falling back to another list when one runs dry.
+    table.clear();
     size_t left = 0;
-    for (auto& v : q) left += v.size();
+    for (auto& v : ml) left += v.size();
     std::vector<size_t> pos(kXcds, 0);
     while (left > 0) {
       int x = (int)(table.size() % kXcds);
-      for (int t = 0; t < kXcds && pos[x] >= q[x].size(); ++t) x = (x + 1) % kXcds;
-      table.push_back(q[x][pos[x]++]);
+      for (int t = 0; t < kXcds && pos[x] >= ml[x].size(); ++t) x = (x + 1) % kXcds;
+      table.push_back(ml[x][pos[x]++]);
       --left;
     }
   } else if (n_g > 0) {
