@@ -31,6 +31,9 @@ constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
 // launch fits one round of workgroup slots (they then set the critical
 // path), longer ones otherwise (fewer items, less per-item overhead).
 constexpr int kGlobItemKeysShort = 256, kGlobItemKeysLong = 512;
+// ... and longer still when they are spread among the band items of a long
+// launch (kSpreadRounds): fewer items, partial records and merge reads.
+constexpr int kGlobItemKeysSpread = 1024;
 constexpr int kWideRounds = 2;
 // From this many rounds of band items per round of workgroup slots on, the
 // global-row items are spread evenly among the band items instead of
@@ -310,7 +313,9 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
       set_count += (long long)H * ((gsel[b].y + c->g_rows - 1) / c->g_rows);
     const long long short_items =
         set_count * ((N + kGlobItemKeysShort - 1) / kGlobItemKeysShort);
-    const int keys = n_items + short_items <= slots ? kGlobItemKeysShort : kGlobItemKeysLong;
+    const int keys = n_items + short_items <= slots ? kGlobItemKeysShort
+                     : (long long)n_items >= kSpreadRounds * slots ? kGlobItemKeysSpread
+                                                                   : kGlobItemKeysLong;
     c->chunk_keys = keys;
     c->n_chunks = (N + keys - 1) / keys;
     // Each global item goes to the XCD of the residue-0 band item whose rows
