@@ -76,6 +76,12 @@ def _load():
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_double, i64p, ctypes.c_int64,
                                               ctypes.c_int]
+        lib.lfo_attention_grad.restype = ctypes.c_int
+        lib.lfo_attention_grad.argtypes = [f32p, f32p, f32p, f32p, f64p, f64p, f64p,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int,
+                                           i32p, i32p, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_double, ctypes.c_int]
         lib.lfo_count_pairs_ex.restype = ctypes.c_int64
         lib.lfo_count_pairs_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, i32p, ctypes.c_int, i32p, ctypes.c_int]
@@ -231,3 +237,37 @@ def attention_chunked(q, k, v, chunk: int, n_memory: int, scale: float = 0.0, ro
     if st != 0:
         raise ValueError("oracle: chunked attention failed (code %d)" % st)
     return out
+
+
+def attention_grad(q, k, v, do, window: int = 0, dilation=None, glob=(), batch_glob=None,
+                   causal: bool = False, chunk: int = 0, n_memory: int = 0, scale: float = 0.0,
+                   nthreads: int | None = None):
+    """Gradients (dq, dk, dv), float64 [B, H, N, D], of the attention output
+    for the upstream gradient do, under the same patterns as attention() and
+    attention_chunked() (chunk > 0), with the ordinary projections."""
+    lib = _load()
+    q, k, v, do = (np.ascontiguousarray(x, dtype=np.float32) for x in (q, k, v, do))
+    B, H, N, D = q.shape
+    if batch_glob is not None:
+        flat = [int(x) for lst in batch_glob for x in lst]
+        offs = np.cumsum([0] + [len(lst) for lst in batch_glob]).astype(np.int32)
+        g, gp = _i32(flat)
+        go, gop = _i32(offs)
+    else:
+        g, gp = _i32(list(glob))
+        go, gop = None, None
+    d, dp = _i32(dilation)
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    out = [np.empty((B, H, N, D), dtype=np.float64) for _ in range(3)]
+    f32p = ctypes.POINTER(ctypes.c_float)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    st = lib.lfo_attention_grad(q.ctypes.data_as(f32p), k.ctypes.data_as(f32p),
+                                v.ctypes.data_as(f32p), do.ctypes.data_as(f32p),
+                                out[0].ctypes.data_as(f64p), out[1].ctypes.data_as(f64p),
+                                out[2].ctypes.data_as(f64p), B, H, N, D, window, dp,
+                                int(causal), gp, gop, len(g), int(chunk), int(n_memory),
+                                float(scale), int(nthreads))
+    if st != 0:
+        raise ValueError("oracle: gradient failed (code %d)" % st)
+    return tuple(out)

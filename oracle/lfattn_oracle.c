@@ -409,3 +409,153 @@ int lfo_attention_chunked(const float* Q, const float* K, const float* V,
   base.scale = scale; base.rows = rows; base.n_rows = n_rows;
   return run_jobs(&base, nthreads);
 }
+
+/* ---- gradients ----------------------------------------------------------- */
+
+/*
+ * Gradients of the attention above with respect to Q, K and V, for an upstream
+ * gradient dO (all [B, H, N, D]; outputs in double).  Pattern arguments as
+ * lfo_attention_ex (ordinary projections only) and chunk/n_memory as
+ * lfo_attention_chunked (chunk > 0 selects the chunked pattern).  For each row
+ * i with key set S_i, P = softmax over S_i of z_j = scale * Q_i . K_j, and by
+ * the chain rule through that softmax (Eq. (1) of the Unlimiformer page):
+ *   dP_j   = dO_i . V_j
+ *   Delta  = sum_{j in S_i} P_j dP_j            (= dO_i . O_i)
+ *   dS_j   = P_j (dP_j - Delta)
+ *   dQ_i  += scale * sum_j dS_j K_j
+ *   dK_j  += scale * dS_j Q_i
+ *   dV_j  += P_j dO_i
+ * One worker per (batch, head) pair, so the K and V gradients need no locks.
+ */
+typedef struct {
+  const float *Q, *K, *V, *dO;
+  double *dQ, *dK, *dV;
+  int B, H, N, D, window, causal, chunk, n_memory, n_glob;
+  const int* dilation;
+  const int* glob;
+  const int* goff;
+  double scale;
+  int64_t first_bh, last_bh;
+  int status;
+} lfo_grad_job;
+
+static void* grad_worker(void* arg) {
+  lfo_grad_job* jb = (lfo_grad_job*)arg;
+  const int N = jb->N, D = jb->D;
+  int* keys = (int*)malloc(sizeof(int) * ((size_t)N + (size_t)jb->n_glob + 1));
+  double* p = (double*)malloc(sizeof(double) * ((size_t)N + (size_t)jb->n_glob + 1));
+  double* dp = (double*)malloc(sizeof(double) * ((size_t)N + (size_t)jb->n_glob + 1));
+  if (!keys || !p || !dp) {
+    jb->status = LFO_ENOMEM;
+    free(keys); free(p); free(dp);
+    return NULL;
+  }
+  for (int64_t bh = jb->first_bh; bh < jb->last_bh && jb->status == LFO_OK; ++bh) {
+    const int h = (int)(bh % jb->H), b = (int)(bh / jb->H);
+    const int d = jb->dilation ? jb->dilation[h] : 1;
+    const int* gl = jb->goff ? jb->glob + jb->goff[b] : jb->glob;
+    const int ng = jb->goff ? jb->goff[b + 1] - jb->goff[b] : jb->n_glob;
+    const size_t off = (size_t)bh * N * D;
+    const float *Qh = jb->Q + off, *Kh = jb->K + off, *Vh = jb->V + off, *dOh = jb->dO + off;
+    double *dQh = jb->dQ + off, *dKh = jb->dK + off, *dVh = jb->dV + off;
+    for (int i = 0; i < N; ++i) {
+      int64_t n = jb->chunk > 0 ? lfo_allowed_set_chunked(N, jb->chunk, jb->n_memory, i, keys)
+                                : lfo_allowed_set_ex(N, jb->window, d, jb->causal, gl, ng, i, keys);
+      if (n <= 0) { jb->status = LFO_EINVAL; break; }
+      const float* q = Qh + (size_t)i * D;
+      const float* g = dOh + (size_t)i * D;
+      /* Softmax over S_i (max subtracted first). */
+      double zmax = -INFINITY;
+      for (int64_t t = 0; t < n; ++t) {
+        const float* kr = Kh + (size_t)keys[t] * D;
+        double s = 0.0;
+        for (int c = 0; c < D; ++c) s += (double)q[c] * (double)kr[c];
+        p[t] = jb->scale * s;
+        if (p[t] > zmax) zmax = p[t];
+      }
+      double den = 0.0;
+      for (int64_t t = 0; t < n; ++t) { p[t] = exp(p[t] - zmax); den += p[t]; }
+      double delta = 0.0;
+      for (int64_t t = 0; t < n; ++t) {
+        p[t] /= den;
+        const float* vr = Vh + (size_t)keys[t] * D;
+        double s = 0.0;
+        for (int c = 0; c < D; ++c) s += (double)g[c] * (double)vr[c];
+        dp[t] = s;
+        delta += p[t] * s;
+      }
+      for (int64_t t = 0; t < n; ++t) {
+        const int j = keys[t];
+        const double ds = p[t] * (dp[t] - delta);
+        const float* kr = Kh + (size_t)j * D;
+        for (int c = 0; c < D; ++c) {
+          dQh[(size_t)i * D + c] += jb->scale * ds * (double)kr[c];
+          dKh[(size_t)j * D + c] += jb->scale * ds * (double)q[c];
+          dVh[(size_t)j * D + c] += p[t] * (double)g[c];
+        }
+      }
+    }
+  }
+  free(keys); free(p); free(dp);
+  return NULL;
+}
+
+/*
+ * Gradients dQ, dK, dV (doubles, [B, H, N, D], overwritten) for the upstream
+ * gradient dO.  window, dilation, causal, glob/goff/n_glob as
+ * lfo_attention_ex; chunk > 0 selects chunked attention with n_memory memory
+ * tokens instead.  Returns LFO_OK or a negative error.
+ */
+int lfo_attention_grad(const float* Q, const float* K, const float* V, const float* dO,
+                       double* dQ, double* dK, double* dV, int B, int H, int N, int D,
+                       int window, const int* dilation, int causal, const int* glob,
+                       const int* goff, int n_glob, int chunk, int n_memory, double scale,
+                       int nthreads) {
+  if (!Q || !K || !V || !dO || !dQ || !dK || !dV || B <= 0 || H <= 0 || N <= 0 || D <= 0 ||
+      window < 0 || chunk < 0 || n_memory < 0 || n_memory > N)
+    return LFO_EINVAL;
+  if (goff) {
+    if (goff[0] != 0 || goff[B] != n_glob) return LFO_EINVAL;
+    for (int b = 0; b < B; ++b)
+      if (goff[b + 1] < goff[b]) return LFO_EINVAL;
+  }
+  if (!check_globals(N, glob, n_glob)) return LFO_EINVAL;
+  if (causal && n_glob > 0) return LFO_EINVAL;
+  if (dilation)
+    for (int h = 0; h < H; ++h)
+      if (dilation[h] < 1) return LFO_EINVAL;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  const size_t total = (size_t)B * H * N * D;
+  memset(dQ, 0, total * sizeof(double));
+  memset(dK, 0, total * sizeof(double));
+  memset(dV, 0, total * sizeof(double));
+  const int64_t n_bh = (int64_t)B * H;
+  if (nthreads < 1) nthreads = 1;
+  if ((int64_t)nthreads > n_bh) nthreads = (int)n_bh;
+  lfo_grad_job* jobs = (lfo_grad_job*)calloc((size_t)nthreads, sizeof(lfo_grad_job));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  char* created = (char*)calloc((size_t)nthreads, 1);
+  if (!jobs || !tids || !created) { free(jobs); free(tids); free(created); return LFO_ENOMEM; }
+  for (int t = 0; t < nthreads; ++t) {
+    lfo_grad_job* jb = &jobs[t];
+    jb->Q = Q; jb->K = K; jb->V = V; jb->dO = dO; jb->dQ = dQ; jb->dK = dK; jb->dV = dV;
+    jb->B = B; jb->H = H; jb->N = N; jb->D = D; jb->window = window; jb->causal = causal;
+    jb->chunk = chunk; jb->n_memory = n_memory; jb->n_glob = n_glob;
+    jb->dilation = dilation; jb->glob = glob; jb->goff = goff; jb->scale = scale;
+    jb->first_bh = n_bh * t / nthreads;
+    jb->last_bh = n_bh * (t + 1) / nthreads;
+    jb->status = LFO_OK;
+  }
+  for (int t = 1; t < nthreads; ++t)
+    created[t] = (char)(pthread_create(&tids[t], NULL, grad_worker, &jobs[t]) == 0);
+  grad_worker(&jobs[0]);
+  for (int t = 1; t < nthreads; ++t) {
+    if (created[t]) pthread_join(tids[t], NULL);
+    else grad_worker(&jobs[t]);
+  }
+  int st = LFO_OK;
+  for (int t = 0; t < nthreads; ++t)
+    if (jobs[t].status != LFO_OK) st = jobs[t].status;
+  free(jobs); free(tids); free(created);
+  return st;
+}
