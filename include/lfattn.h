@@ -174,6 +174,15 @@ lfattn_status lfattn_forward_global_proj(lfattn_t ctx, const void* Q, const void
                                          const void* V, const void* Qg, const void* Kg,
                                          const void* Vg, void* O, hipStream_t stream);
 
+/*
+ * As lfattn_forward, also writing LSE[b, h, i] = log sum_{j in S_i}
+ * exp(scale * Q_i . K_j) (natural log, fp32, [B, H, N] device array that must
+ * overlap no other argument), the per-row statistic a backward pass needs.
+ * bf16 handles only (EUNSUPPORTED otherwise).
+ */
+lfattn_status lfattn_forward_lse(lfattn_t ctx, const void* Q, const void* K, const void* V,
+                                 void* O, float* LSE, hipStream_t stream);
+
 /* Release the handle and its device memory (waits for the device first).
  * NULL is accepted and ignored. */
 lfattn_status lfattn_destroy(lfattn_t ctx);

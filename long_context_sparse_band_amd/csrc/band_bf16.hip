@@ -749,6 +749,9 @@ void band32_kernel(BandArgs a) {
   }
   const int row = r + d * eu;
   if (sm.rowg[32 * qblk + el32]) return;
+  // Natural log-sum-exp of the row's scaled scores (m and the weights are in
+  // base 2 of scores times scale * log2(e)).
+  if (a.lse && ehi == 0) a.lse[(size_t)w.bh * N + row] = (m + __log2f(lt)) * 0.6931471805599453f;
   const float inv = 1.0f / lt;
   unsigned short* Op = (unsigned short*)a.O + base + (size_t)row * D;
 #pragma unroll

@@ -133,9 +133,19 @@ long long head_pairs(int N, long long hw, int d, bool causal, int chunk, int n_m
   return total;
 }
 
+lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void* V,
+                           const void* Qg, const void* Kg, const void* Vg, void* O, float* lse,
+                           hipStream_t stream);
+
 bool overlaps(const void* a, const void* b, size_t bytes) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + bytes && y < x + bytes;
+}
+
+// Whether [a, a + abytes) and [b, b + bbytes) share a byte.
+bool overlaps2(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bbytes && y < x + abytes;
 }
 
 }  // namespace
@@ -509,6 +519,23 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
 lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* K,
                                          const void* V, const void* Qg, const void* Kg,
                                          const void* Vg, void* O, hipStream_t stream) {
+  return forward_impl(c, Q, K, V, Qg, Kg, Vg, O, nullptr, stream);
+}
+
+lfattn_status lfattn_forward_lse(lfattn_t c, const void* Q, const void* K, const void* V,
+                                 void* O, float* LSE, hipStream_t stream) {
+  if (!c || !LSE) return LFATTN_EINVAL;
+  if (c->dtype != LFATTN_BF16) return LFATTN_EUNSUPPORTED;
+  return forward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, LSE, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void* V,
+                           const void* Qg, const void* Kg, const void* Vg, void* O, float* lse,
+                           hipStream_t stream) {
   if (!c || !Q || !K || !V || !O) return LFATTN_EINVAL;
   if (!Qg) Qg = Q;
   if (!Kg) Kg = K;
@@ -519,6 +546,12 @@ lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* 
   const size_t bytes = (size_t)c->B * c->H * c->N * c->D * (c->dtype == LFATTN_BF16 ? 2 : 4);
   for (const void* in : {Q, K, V, Qg, Kg, Vg})
     if (overlaps(O, in, bytes)) return LFATTN_EINVAL;
+  if (lse) {
+    const size_t lbytes = (size_t)c->B * c->H * c->N * sizeof(float);
+    if ((uintptr_t)lse & 3u) return LFATTN_EINVAL;
+    for (const void* in : {Q, K, V, (const void*)O})
+      if (overlaps2(lse, lbytes, in, bytes)) return LFATTN_EINVAL;
+  }
 
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess || cur != c->device) return LFATTN_EINVAL;
@@ -544,6 +577,7 @@ lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* 
     g.rows_per_set = c->g_rows;
     g.n_sets = c->n_sets; g.n_chunks = c->n_chunks; g.chunk_keys = c->chunk_keys;
     g.sl2 = sl2;
+    g.lse = lse;
     if (!c->glob_items &&
         lfattn::launch_glob(c->dtype, c->D, c->g_waves, g, c->n_glob_wg, stream, t_part) != hipSuccess)
       return LFATTN_EHIP;
@@ -557,6 +591,7 @@ lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* 
   a.H = c->H; a.N = c->N; a.hw = c->hw; a.n_glob = n_g; a.sl2 = sl2;
   a.hr = c->causal ? 0 : c->hw;
   a.chunk = c->chunk;
+  a.lse = lse;
   a.cbase = c->n_memory;
   a.rows_per_wg = c->band_rows;
   a.part = c->glob_items ? c->d_part : nullptr;
@@ -570,6 +605,10 @@ lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* 
   if (timed) ++c->n_timed;
   return LFATTN_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 lfattn_status lfattn_destroy(lfattn_t c) {
   if (!c) return LFATTN_OK;

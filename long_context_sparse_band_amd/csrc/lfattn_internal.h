@@ -56,6 +56,7 @@ struct BandArgs {
   int hr;                      // keys a row scores after itself: hw, or 0 (causal)
   int chunk;                   // > 0: chunked attention, chunks of this many keys
   int cbase;                   // first position of the chunked main sequence
+  float* lse;                  // [B, H, N] log-sum-exp of the band rows' scores, or null
   float sl2;                   // softmax scale times log2(e)
   int rows_per_wg;             // rows per band workgroup (bf16: 64 or 128)
   // Global-row items (dil 0): partial records laid out as GlobArgs::part
@@ -79,6 +80,7 @@ struct GlobArgs {
   int n_chunks;                // key chunks per (bh, set)
   int chunk_keys;              // keys per chunk, a multiple of kTileKeys
   float sl2;
+  float* lse;                  // [B, H, N] log-sum-exp of the global rows' scores, or null
 };
 
 // Optional events around one launch: start and stop take the kernel's own

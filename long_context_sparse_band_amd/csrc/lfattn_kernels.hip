@@ -537,7 +537,10 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
     }
   }
   const float inv = 1.0f / lt;
-  E* Orow = (E*)a.O + (size_t)bh * a.N * D + (size_t)a.glob[gs.x + slot] * D;
+  const int orow = a.glob[gs.x + slot];
+  if (a.lse && q0 == 0)
+    a.lse[(size_t)bh * a.N + orow] = (mt + __log2f(lt)) * 0.6931471805599453f;
+  E* Orow = (E*)a.O + (size_t)bh * a.N * D + (size_t)orow * D;
 #pragma unroll
   for (int t = 0; t < QPT; ++t) {
     E* Op = Orow + 4 * (q0 + 16 * t);

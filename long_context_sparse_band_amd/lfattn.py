@@ -25,7 +25,7 @@ LFATTN_BF16 = 1
 
 # Every entry point include/lfattn.h declares.
 EXPORTS = ("lfattn_create", "lfattn_create_masked", "lfattn_create_causal",
-           "lfattn_create_chunked", "lfattn_forward",
+           "lfattn_create_chunked", "lfattn_forward", "lfattn_forward_lse",
            "lfattn_forward_global_proj", "lfattn_destroy", "lfattn_status_string",
            "lfattn_scored_pairs", "lfattn_band_launch_pairs", "lfattn_band_rows",
            "lfattn_global_list", "lfattn_global_list_batch",
@@ -69,6 +69,8 @@ def load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_float]
     lib.lfattn_forward.restype = ctypes.c_int
     lib.lfattn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.lfattn_forward_lse.restype = ctypes.c_int
+    lib.lfattn_forward_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.lfattn_forward_global_proj.restype = ctypes.c_int
     lib.lfattn_forward_global_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.lfattn_destroy.restype = ctypes.c_int
@@ -183,6 +185,14 @@ def lfattn_forward(handle: int, Q, K, V, O, stream=None) -> None:
     lib = load()
     _check(lib.lfattn_forward(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _stream(stream)),
            "lfattn_forward")
+
+
+def lfattn_forward_lse(handle: int, Q, K, V, O, LSE, stream=None) -> None:
+    """Forward that also writes the natural log-sum-exp of each row's scaled
+    scores into LSE (a float32 device tensor [B, H, N]); bf16 handles."""
+    lib = load()
+    _check(lib.lfattn_forward_lse(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE),
+                                  _stream(stream)), "lfattn_forward_lse")
 
 
 def lfattn_forward_global_proj(handle: int, Q, K, V, Qg, Kg, Vg, O, stream=None) -> None:

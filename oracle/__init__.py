@@ -82,6 +82,10 @@ def _load():
                                            ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int,
                                            i32p, i32p, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_double, ctypes.c_int]
+        lib.lfo_row_lse.restype = ctypes.c_int
+        lib.lfo_row_lse.argtypes = [f32p, f32p, f64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, i32p, i32p,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         lib.lfo_count_pairs_ex.restype = ctypes.c_int64
         lib.lfo_count_pairs_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, i32p, ctypes.c_int, i32p, ctypes.c_int]
@@ -271,3 +275,30 @@ def attention_grad(q, k, v, do, window: int = 0, dilation=None, glob=(), batch_g
     if st != 0:
         raise ValueError("oracle: gradient failed (code %d)" % st)
     return tuple(out)
+
+
+def row_lse(q, k, window: int = 0, dilation=None, glob=(), batch_glob=None, causal: bool = False,
+            chunk: int = 0, n_memory: int = 0, scale: float = 0.0) -> np.ndarray:
+    """Natural log-sum-exp of each row's scaled scores over its key set,
+    float64 [B, H, N]; patterns as attention_grad()."""
+    lib = _load()
+    q, k = (np.ascontiguousarray(x, dtype=np.float32) for x in (q, k))
+    B, H, N, D = q.shape
+    if batch_glob is not None:
+        flat = [int(x) for lst in batch_glob for x in lst]
+        offs = np.cumsum([0] + [len(lst) for lst in batch_glob]).astype(np.int32)
+        g, gp = _i32(flat)
+        go, gop = _i32(offs)
+    else:
+        g, gp = _i32(list(glob))
+        go, gop = None, None
+    d, dp = _i32(dilation)
+    out = np.empty((B, H, N), dtype=np.float64)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    st = lib.lfo_row_lse(q.ctypes.data_as(f32p), k.ctypes.data_as(f32p),
+                         out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), B, H, N, D,
+                         window, dp, int(causal), gp, gop, len(g), int(chunk), int(n_memory),
+                         float(scale))
+    if st != 0:
+        raise ValueError("oracle: row_lse failed (code %d)" % st)
+    return out

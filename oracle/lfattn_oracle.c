@@ -559,3 +559,47 @@ int lfo_attention_grad(const float* Q, const float* K, const float* V, const flo
   free(jobs); free(tids); free(created);
   return st;
 }
+
+/*
+ * Per-row log-sum-exp of the scaled scores, lse_i = log sum_{j in S_i}
+ * exp(scale * Q_i . K_j) (natural log, the max taken out first), for every
+ * row, [B, H, N] doubles.  Pattern arguments as lfo_attention_grad.
+ */
+int lfo_row_lse(const float* Q, const float* K, double* lse, int B, int H, int N, int D,
+                int window, const int* dilation, int causal, const int* glob, const int* goff,
+                int n_glob, int chunk, int n_memory, double scale) {
+  if (!Q || !K || !lse || B <= 0 || H <= 0 || N <= 0 || D <= 0 || window < 0 || chunk < 0 ||
+      n_memory < 0 || n_memory > N)
+    return LFO_EINVAL;
+  if (!check_globals(N, glob, n_glob)) return LFO_EINVAL;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  int* keys = (int*)malloc(sizeof(int) * ((size_t)N + (size_t)n_glob + 1));
+  double* z = (double*)malloc(sizeof(double) * ((size_t)N + (size_t)n_glob + 1));
+  if (!keys || !z) { free(keys); free(z); return LFO_ENOMEM; }
+  int st = LFO_OK;
+  for (int64_t bh = 0; bh < (int64_t)B * H && st == LFO_OK; ++bh) {
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const int d = dilation ? dilation[h] : 1;
+    const int* gl = goff ? glob + goff[b] : glob;
+    const int ng = goff ? goff[b + 1] - goff[b] : n_glob;
+    for (int i = 0; i < N; ++i) {
+      int64_t n = chunk > 0 ? lfo_allowed_set_chunked(N, chunk, n_memory, i, keys)
+                            : lfo_allowed_set_ex(N, window, d, causal, gl, ng, i, keys);
+      if (n <= 0) { st = LFO_EINVAL; break; }
+      const float* q = Q + ((size_t)bh * N + i) * D;
+      double zmax = -INFINITY;
+      for (int64_t t = 0; t < n; ++t) {
+        const float* kr = K + ((size_t)bh * N + keys[t]) * D;
+        double s = 0.0;
+        for (int c = 0; c < D; ++c) s += (double)q[c] * (double)kr[c];
+        z[t] = scale * s;
+        if (z[t] > zmax) zmax = z[t];
+      }
+      double sum = 0.0;
+      for (int64_t t = 0; t < n; ++t) sum += exp(z[t] - zmax);
+      lse[(size_t)bh * N + i] = zmax + log(sum);
+    }
+  }
+  free(keys); free(z);
+  return st;
+}

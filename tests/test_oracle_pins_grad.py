@@ -129,3 +129,18 @@ def test_gradient_sums(kw):
     np.testing.assert_allclose(dv.sum(axis=2), do.astype(np.float64).sum(axis=2), rtol=1e-10,
                                atol=1e-10)
     np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-10)
+
+
+def test_row_lse_matches_torch_logsumexp():
+    """Library routine: torch.logsumexp (float64) of the masked scores."""
+    rng = np.random.default_rng(54)
+    for t in range(16):
+        B, H, N, D, masks, kw = _case(rng, t)
+        a = W.small_case(B, H, N, D, "f32", 0, seed=950 + t)
+        got = oracle.row_lse(a.q, a.k, **kw)
+        for b in range(B):
+            for h in range(H):
+                z = torch.from_numpy(a.q[b, h]).double() @ torch.from_numpy(a.k[b, h]).double().T
+                z = z / np.sqrt(D) + torch.from_numpy(np.where(masks[b][h], 0.0, -np.inf))
+                np.testing.assert_allclose(got[b, h], torch.logsumexp(z, dim=1).numpy(),
+                                           rtol=1e-12, atol=1e-12)
