@@ -39,14 +39,17 @@ def parse():
     p.add_argument("--workload", default="longformer_base_n4096")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--variant", default="plain",
-                   choices=["plain", "global_proj", "two_sequences", "causal", "chunked"],
+                   choices=["plain", "global_proj", "two_sequences", "causal", "chunked",
+                            "backward"],
                    help="global_proj: the global rows take their own projections (a second "
                         "seeded Q, K, V); two_sequences: B = 2 with a different global set per "
                         "sequence ([CLS] + 10 seeded positions for the second), and own "
                         "projections; causal: the causal band (workloads without global "
                         "tokens, e.g. dilated_charlm_n8192); chunked: GMAT chunked attention, "
                         "chunks of --chunk keys after the workload's memory tokens "
-                        "(gmat_memory_m64_l16384: (512 x 32, 64))")
+                        "(gmat_memory_m64_l16384: (512 x 32, 64)); backward: one step is "
+                        "lfattn_backward (dQ, dK, dV from a seeded upstream gradient, bf16 "
+                        "D 64 workloads) after one untimed lfattn_forward_lse")
     p.add_argument("--chunk", type=int, default=512, help="chunk length of --variant chunked")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
@@ -158,6 +161,78 @@ def cpu_baseline(inp, wl, pairs_per_head_total):
             "cpu_model": cpu_model()}
 
 
+def bench_backward(args, wl, inp, L, torch):
+    """One step: lfattn_backward over the workload.  Algorithmic work: five
+    products of 2D flops per scored pair (scores, dP = dO V^T, dV, dQ, dK);
+    the key-side kernel itself does four (scores, dP, dK, dV) and the
+    query-side kernel three (scores, dP, dQ)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+
+    def upload(x):
+        return torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
+
+    q, k, v = (upload(a) for a in (inp.q, inp.k, inp.v))
+    rng = np.random.default_rng(wl.seed + 7)
+    g = upload(rng.standard_normal(inp.q.shape).astype(np.float32))
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty((wl.B, wl.H, wl.N, wl.D), dtype=torch.float32, device=dev)
+                  for _ in range(3))
+    h = L.lfattn_create(wl.B, wl.H, wl.N, wl.D, L.LFATTN_BF16, wl.window, list(inp.dilation),
+                        list(inp.glob))
+    stream = torch.cuda.current_stream()
+    L.lfattn_forward_lse(h, q, k, v, o, lse, stream)
+
+    def step():
+        L.lfattn_backward(h, q, k, v, o, g, lse, dq, dk, dv, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    L.lfattn_set_timing(h, True)
+    for _ in range(args.steps):
+        step()
+    prep, rows, keys, n = L.lfattn_read_backward_timing(h)
+    L.lfattn_set_timing(h, False)
+    prep, rows, keys = (x / max(n, 1) for x in (prep, rows, keys))
+    pairs = L.lfattn_scored_pairs(h)
+    L.lfattn_destroy(h)
+    peak = PEAK_TFLOPS["bf16"]
+    D = wl.D
+    keys_tf = pairs * 8 * D / (keys * 1e-3) / 1e12
+    rows_tf = pairs * 6 * D / (rows * 1e-3) / 1e12
+    line = {
+        "metric": "backward scored-pairs/sec (dQ, dK, dV)",
+        "value": pairs / (ms * 1e-3),
+        "unit": "scored pairs/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. Gaussian Q, K, V and upstream gradient)",
+        "inputs": input_record(inp),
+        "config": {"workload": wl.name, "variant": "backward", "B": wl.B, "H": wl.H,
+                   "N": wl.N, "D": D, "window": wl.window,
+                   "dilation": [int(x) for x in inp.dilation], "n_global": len(inp.glob),
+                   "scored_pairs": pairs, "parallelism": "single GPU"},
+        "whole_backward_tflops": pairs * 10 * D / (ms * 1e-3) / 1e12,
+        "whole_backward_mfma_frac": pairs * 10 * D / (ms * 1e-3) / 1e12 / peak,
+        "kernels_ms": {"prep": prep, "rows_dq": rows, "keys_dkdv": keys},
+        "rows_kernel": {"achieved": rows_tf, "frac": rows_tf / peak,
+                        "flops_per_launch": pairs * 6 * D},
+        "roofline": {"kernel": "bwd_keys_kernel", "bound": "mfma", "achieved": keys_tf,
+                     "peak": peak, "unit": "TFLOP/s", "frac": keys_tf / peak, "traffic": None,
+                     "algorithmic_flops_per_launch": pairs * 8 * D},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -186,9 +261,16 @@ def main():
         print(f"bench.py: --variant chunked needs memory tokens at 0..M-1; {wl.name} has "
               f"other global positions.", file=sys.stderr)
         sys.exit(2)
+    if args.variant == "backward" and (wl.dtype != "bf16" or wl.D != 64):
+        print(f"bench.py: --variant backward runs on bf16 workloads with D 64; {wl.name} "
+              f"is {wl.dtype} with D {wl.D}.", file=sys.stderr)
+        sys.exit(2)
     if args.variant == "two_sequences":
         wl = dataclasses.replace(wl, B=2)
     inp = W.generate(wl)
+    if args.variant == "backward":
+        bench_backward(args, wl, inp, L, torch)
+        return
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 

@@ -183,6 +183,24 @@ lfattn_status lfattn_forward_global_proj(lfattn_t ctx, const void* Q, const void
 lfattn_status lfattn_forward_lse(lfattn_t ctx, const void* Q, const void* K, const void* V,
                                  void* O, float* LSE, hipStream_t stream);
 
+/*
+ * Backward pass: gradients of the forward (lfattn_forward / lfattn_forward_lse,
+ * the ordinary projections) for the upstream gradient dO.  Q, K, V: the
+ * forward's inputs; O and LSE: its output and log-sum-exp (from
+ * lfattn_forward_lse); dO: [B, H, N, D] like O.  Writes dQ, dK, dV: fp32
+ * [B, H, N, D] device arrays, fully overwritten, overlapping no input and
+ * each other.  With P the forward's weights over each row's key set S_i (the
+ * chain rule through the row softmax of Eq. (1) of the Unlimiformer page):
+ *   dS_ij = P_ij (dO_i . V_j - dO_i . O_i),   dQ_i = scale sum_j dS_ij K_j,
+ *   dK_j = scale sum_i dS_ij Q_i,            dV_j = sum_i P_ij dO_i.
+ * bf16 handles with D = 64 only (EUNSUPPORTED otherwise), every pattern.
+ * Allocates nothing; the handle's workspace holds dO . O per row.  Sums over
+ * global rows and keys use atomics, so their last bits vary between runs.
+ */
+lfattn_status lfattn_backward(lfattn_t ctx, const void* Q, const void* K, const void* V,
+                              const void* O, const void* dO, const float* LSE, float* dQ,
+                              float* dK, float* dV, hipStream_t stream);
+
 /* Release the handle and its device memory (waits for the device first).
  * NULL is accepted and ignored. */
 lfattn_status lfattn_destroy(lfattn_t ctx);
@@ -238,6 +256,16 @@ lfattn_status lfattn_global_list_batch(lfattn_t ctx, int b, int* out, int capaci
 lfattn_status lfattn_set_timing(lfattn_t ctx, int enable);
 lfattn_status lfattn_read_timing(lfattn_t ctx, double* band_ms, double* global_ms,
                                  int* n_forwards);
+
+/*
+ * The same for lfattn_backward calls while timing is enabled (at most 1024
+ * recorded): the milliseconds, summed over the recorded calls, of the
+ * preparation kernel (row terms Delta, clearing of the global rows'
+ * gradients), of the query-side kernel (dQ) and of the key-side kernel
+ * (dK, dV); the number of calls recorded; then clears that record.
+ */
+lfattn_status lfattn_read_backward_timing(lfattn_t ctx, double* prep_ms, double* rows_ms,
+                                          double* keys_ms, int* n_backwards);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,9 @@ constexpr int kMaxTimedForwards = 4096;
 // Timing events per forward: band start/stop, global partials start/stop,
 // merge start/stop.
 constexpr int kEvPerForward = 6;
+// ... and per backward: prep, rows and keys kernels, start/stop each.
+constexpr int kMaxTimedBackwards = 1024;
+constexpr int kEvPerBackward = 6;
 constexpr int kXcds = 8;           // MI355X: workgroups go round-robin over 8 XCDs
 constexpr int kMaxChunks = lfattn::kMergeBatch;  // key chunks per global row set
 constexpr int kGlobTarget = 1024;  // aim for this many global-row workgroups
@@ -42,6 +45,9 @@ constexpr int kWideRounds = 2;
 // band items' arithmetic.  (In a launch of one or two rounds, dispatching them
 // last measured faster.)
 constexpr int kSpreadRounds = 4;
+// Backward work items: rows or keys per item, and the key or row chunk of a
+// global item.
+constexpr int kBwdRows = 128, kBwdChunk = 512;
 constexpr long long kMaxN = 1LL << 29;
 
 }  // namespace
@@ -64,6 +70,10 @@ struct lfattn_ctx {
   int device = 0;
 
   BandWork* d_work = nullptr;
+  // Backward pass (bf16, D = 64): its work table and the per-row Delta.
+  BandWork* d_bwork = nullptr;
+  int n_bwork = 0;
+  float* d_delta = nullptr;
   int n_band_wg = 0;
   int* d_glob = nullptr;           // the distinct lists, one after another
   int2* d_gsel = nullptr;          // [B]: (offset, length) of each batch element's list
@@ -77,6 +87,8 @@ struct lfattn_ctx {
   bool timing = false;
   int n_timed = 0;
   std::vector<hipEvent_t> ev;  // kEvPerForward per timed forward
+  int n_btimed = 0;
+  std::vector<hipEvent_t> bev;  // kEvPerBackward per timed backward
 };
 
 namespace {
@@ -100,7 +112,10 @@ void free_ctx(lfattn_ctx* c) {
   (void)hipFree(c->d_gsel);
   (void)hipFree(c->d_isglob);
   (void)hipFree(c->d_part);
+  (void)hipFree(c->d_bwork);
+  (void)hipFree(c->d_delta);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->bev) (void)hipEventDestroy(e);
   delete c;
 }
 
@@ -398,6 +413,31 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   if (table.size() > (size_t)INT32_MAX) { free_ctx(c); return LFATTN_EUNSUPPORTED; }
   c->n_band_wg = (int)table.size();
 
+  // Backward work (bf16, D = 64): band items of kBwdRows rows (row side) or
+  // keys (key side) per (b, h, residue), then items of kBwdRows global
+  // positions against a chunk of kBwdChunk keys (row side) or rows (key side).
+  std::vector<BandWork> btable;
+  const bool has_bwd = dtype == LFATTN_BF16 && D == 64;
+  if (has_bwd) {
+    for (int bh = 0; bh < B * H; ++bh) {
+      const int d = c->dil[bh % H], b = bh / H;
+      for (int r = 0; r < d && r < N; ++r) {
+        const int Lr = (N - r + d - 1) / d;
+        for (int t0 = 0; t0 < Lr; t0 += kBwdRows)
+          btable.push_back(BandWork{bh, r, t0, d, gsel[b].x, gsel[b].y, b, 0});
+      }
+    }
+    for (int bh = 0; bh < B * H; ++bh) {
+      const int b = bh / H;
+      const int sets_b = (gsel[b].y + kBwdRows - 1) / kBwdRows;
+      for (int set = 0; set < sets_b; ++set)
+        for (int ch = 0; ch < (N + kBwdChunk - 1) / kBwdChunk; ++ch)
+          btable.push_back(BandWork{bh, set, ch, 0, gsel[b].x, gsel[b].y, b, 0});
+    }
+    if (btable.size() > (size_t)INT32_MAX) { free_ctx(c); return LFATTN_EUNSUPPORTED; }
+    c->n_bwork = (int)btable.size();
+  }
+
   // ---- device state ----
   lfattn_status st = LFATTN_OK;
   if (hipGetDevice(&c->device) != hipSuccess) { free_ctx(c); return LFATTN_EHIP; }
@@ -405,6 +445,11 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
       (st = dev_alloc(&c->d_isglob, isg.size())) != LFATTN_OK ||
       (st = dev_alloc(&c->d_glob, (size_t)std::max(goff[n_lists], 1))) != LFATTN_OK ||
       (st = dev_alloc(&c->d_gsel, (size_t)B)) != LFATTN_OK) {
+    free_ctx(c);
+    return st;
+  }
+  if (has_bwd && ((st = dev_alloc(&c->d_bwork, btable.size())) != LFATTN_OK ||
+                   (st = dev_alloc(&c->d_delta, (size_t)B * H * N)) != LFATTN_OK)) {
     free_ctx(c);
     return st;
   }
@@ -419,6 +464,9 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   bool ok = hipMemcpy(c->d_work, table.data(), table.size() * sizeof(BandWork),
                       hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(c->d_isglob, isg.data(), isg.size(), hipMemcpyHostToDevice) == hipSuccess;
+  if (has_bwd)
+    ok = ok && hipMemcpy(c->d_bwork, btable.data(), btable.size() * sizeof(BandWork),
+                         hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(c->d_gsel, gsel.data(), B * sizeof(int2), hipMemcpyHostToDevice) == hipSuccess;
   if (goff[n_lists] > 0) {
     std::vector<int> flat;
@@ -610,6 +658,46 @@ lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void*
 
 extern "C" {
 
+lfattn_status lfattn_backward(lfattn_t c, const void* Q, const void* K, const void* V,
+                              const void* O, const void* dO, const float* LSE, float* dQ,
+                              float* dK, float* dV, hipStream_t stream) {
+  if (!c || !Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return LFATTN_EINVAL;
+  if (c->dtype != LFATTN_BF16 || c->D != 64) return LFATTN_EUNSUPPORTED;
+  const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O |
+                         (uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK | (uintptr_t)dV) & 15u;
+  if (mis || ((uintptr_t)LSE & 3u)) return LFATTN_EINVAL;
+  const size_t n_el = (size_t)c->B * c->H * c->N * c->D;
+  const size_t in_b = n_el * 2, out_b = n_el * 4, lse_b = (size_t)c->B * c->H * c->N * 4;
+  // The outputs overlap no input and no other output.
+  const void* outs[3] = {dQ, dK, dV};
+  for (int x = 0; x < 3; ++x) {
+    for (const void* in : {Q, K, V, O, dO})
+      if (overlaps2(outs[x], out_b, in, in_b)) return LFATTN_EINVAL;
+    if (overlaps2(outs[x], out_b, LSE, lse_b)) return LFATTN_EINVAL;
+    for (int y = x + 1; y < 3; ++y)
+      if (overlaps2(outs[x], out_b, outs[y], out_b)) return LFATTN_EINVAL;
+  }
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != c->device) return LFATTN_EINVAL;
+
+  lfattn::BwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.lse = LSE; a.delta = c->d_delta;
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.work = c->d_bwork; a.glob = c->d_glob; a.is_glob = c->d_isglob;
+  a.isg_stride = c->shared ? 0 : c->N;
+  a.H = c->H; a.N = c->N; a.D = c->D; a.n_bh = c->B * c->H;
+  a.hw = c->hw; a.hr = c->causal ? 0 : c->hw; a.chunk = c->chunk; a.cbase = c->n_memory;
+  a.chunk_keys = kBwdChunk; a.n_glob = c->n_gmax;
+  a.scale = c->scale; a.sl2 = c->scale * 1.4426950408889634f;
+  lfattn::Timing t[3];
+  if (c->timing && c->n_btimed < kMaxTimedBackwards) {
+    hipEvent_t* e = &c->bev[kEvPerBackward * c->n_btimed++];
+    for (int x = 0; x < 3; ++x) t[x] = {e[2 * x], e[2 * x + 1]};
+  }
+  if (lfattn::launch_backward_bf16(a, c->n_bwork, stream, t) != hipSuccess) return LFATTN_EHIP;
+  return LFATTN_OK;
+}
+
 lfattn_status lfattn_destroy(lfattn_t c) {
   if (!c) return LFATTN_OK;
   (void)hipDeviceSynchronize();
@@ -652,19 +740,25 @@ lfattn_status lfattn_global_list_batch(lfattn_t c, int b, int* out, int capacity
 
 lfattn_status lfattn_set_timing(lfattn_t c, int enable) {
   if (!c) return LFATTN_EINVAL;
-  if (enable && c->ev.empty()) {
-    c->ev.resize(kEvPerForward * kMaxTimedForwards, nullptr);
-    for (auto& e : c->ev)
+  auto make = [](std::vector<hipEvent_t>& v, size_t n) {
+    if (!v.empty()) return true;
+    v.resize(n, nullptr);
+    for (auto& e : v)
       if (hipEventCreate(&e) != hipSuccess) {
         (void)hipGetLastError();
-        for (auto& x : c->ev)
+        for (auto& x : v)
           if (x) (void)hipEventDestroy(x);
-        c->ev.clear();
-        return LFATTN_EHIP;
+        v.clear();
+        return false;
       }
-  }
+    return true;
+  };
+  if (enable && (!make(c->ev, (size_t)kEvPerForward * kMaxTimedForwards) ||
+                 !make(c->bev, (size_t)kEvPerBackward * kMaxTimedBackwards)))
+    return LFATTN_EHIP;
   c->timing = enable != 0;
   c->n_timed = 0;
+  c->n_btimed = 0;
   return LFATTN_OK;
 }
 
@@ -690,6 +784,31 @@ lfattn_status lfattn_read_timing(lfattn_t c, double* band_ms, double* global_ms,
   *global_ms = g;
   *n_forwards = c->n_timed;
   c->n_timed = 0;
+  return LFATTN_OK;
+}
+
+lfattn_status lfattn_read_backward_timing(lfattn_t c, double* prep_ms, double* rows_ms,
+                                          double* keys_ms, int* n_backwards) {
+  if (!c || !prep_ms || !rows_ms || !keys_ms || !n_backwards) return LFATTN_EINVAL;
+  double sum[3] = {0.0, 0.0, 0.0};
+  if (c->n_btimed > 0 &&
+      hipEventSynchronize(c->bev[kEvPerBackward * c->n_btimed - 1]) != hipSuccess)
+    return LFATTN_EHIP;
+  for (int t = 0; t < c->n_btimed; ++t) {
+    hipEvent_t* e = &c->bev[kEvPerBackward * t];
+    for (int x = 0; x < 3; ++x) {
+      float ms = 0.0f;
+      // A launch with no work items records no rows/keys events.
+      if (x > 0 && c->n_bwork <= 0) continue;
+      if (hipEventElapsedTime(&ms, e[2 * x], e[2 * x + 1]) != hipSuccess) return LFATTN_EHIP;
+      sum[x] += ms;
+    }
+  }
+  *prep_ms = sum[0];
+  *rows_ms = sum[1];
+  *keys_ms = sum[2];
+  *n_backwards = c->n_btimed;
+  c->n_btimed = 0;
   return LFATTN_OK;
 }
 

@@ -83,6 +83,29 @@ struct GlobArgs {
   float* lse;                  // [B, H, N] log-sum-exp of the global rows' scores, or null
 };
 
+// Backward pass (bf16, D = 64): gradients of the band + global attention.
+// The work table holds band items of 128 rows (row side) or keys (key side)
+// and global items of 128 global positions against a chunk of chunk_keys
+// keys (row side) or rows (key side).
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* lse;            // [B, H, N] natural log-sum-exp from the forward
+  float* delta;                // [B, H, N] workspace: dO . O per row
+  float* dQ;                   // [B, H, N, D] fp32 outputs
+  float* dK;
+  float* dV;
+  const BandWork* work;
+  const int* glob;
+  const unsigned char* is_glob;
+  long long isg_stride;
+  int H, N, D, n_bh, hw, hr, chunk, cbase, chunk_keys, n_glob;
+  float sl2, scale;
+};
+
 // Optional events around one launch: start and stop take the kernel's own
 // begin and end timestamps (hipExtLaunchKernel), so their elapsed time is the
 // kernel's duration without the stream's marker overhead.  Null: untimed.
@@ -110,5 +133,7 @@ int band_workgroups_per_cu(int dtype, int D);
 hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s,
                        const Timing& t);
 hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s, const Timing& t);
+// t: events around the prep, rows and keys kernels (null events: untimed).
+hipError_t launch_backward_bf16(const BwdArgs& a, int n_wg, hipStream_t s, const Timing t[3]);
 
 }  // namespace lfattn

@@ -25,11 +25,11 @@ LFATTN_BF16 = 1
 
 # Every entry point include/lfattn.h declares.
 EXPORTS = ("lfattn_create", "lfattn_create_masked", "lfattn_create_causal",
-           "lfattn_create_chunked", "lfattn_forward", "lfattn_forward_lse",
+           "lfattn_create_chunked", "lfattn_forward", "lfattn_forward_lse", "lfattn_backward",
            "lfattn_forward_global_proj", "lfattn_destroy", "lfattn_status_string",
            "lfattn_scored_pairs", "lfattn_band_launch_pairs", "lfattn_band_rows",
            "lfattn_global_list", "lfattn_global_list_batch",
-           "lfattn_set_timing", "lfattn_read_timing")
+           "lfattn_set_timing", "lfattn_read_timing", "lfattn_read_backward_timing")
 
 _lib = None
 
@@ -69,6 +69,8 @@ def load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_float]
     lib.lfattn_forward.restype = ctypes.c_int
     lib.lfattn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.lfattn_backward.restype = ctypes.c_int
+    lib.lfattn_backward.argtypes = [vp] * 10 + [vp]
     lib.lfattn_forward_lse.restype = ctypes.c_int
     lib.lfattn_forward_lse.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.lfattn_forward_global_proj.restype = ctypes.c_int
@@ -92,6 +94,8 @@ def load():
     lib.lfattn_read_timing.restype = ctypes.c_int
     lib.lfattn_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_double), i32p]
+    lib.lfattn_read_backward_timing.restype = ctypes.c_int
+    lib.lfattn_read_backward_timing.argtypes = [vp] + [ctypes.POINTER(ctypes.c_double)] * 3 + [i32p]
     _lib = lib
     return lib
 
@@ -195,6 +199,15 @@ def lfattn_forward_lse(handle: int, Q, K, V, O, LSE, stream=None) -> None:
                                   _stream(stream)), "lfattn_forward_lse")
 
 
+def lfattn_backward(handle: int, Q, K, V, O, dO, LSE, dQ, dK, dV, stream=None) -> None:
+    """Gradients dQ, dK, dV (float32 device tensors [B, H, N, D]) of the forward
+    for the upstream gradient dO; LSE from lfattn_forward_lse.  bf16, D = 64."""
+    lib = load()
+    _check(lib.lfattn_backward(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE),
+                               _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)),
+           "lfattn_backward")
+
+
 def lfattn_forward_global_proj(handle: int, Q, K, V, Qg, Kg, Vg, O, stream=None) -> None:
     """Enqueue one forward in which the global rows take Qg, Kg, Vg (each may be
     None for Q, K, V)."""
@@ -256,6 +269,16 @@ def lfattn_read_timing(handle: int):
     _check(load().lfattn_read_timing(handle, ctypes.byref(b), ctypes.byref(g), ctypes.byref(n)),
            "lfattn_read_timing")
     return b.value, g.value, n.value
+
+
+def lfattn_read_backward_timing(handle: int):
+    """(prep_ms_total, rows_ms_total, keys_ms_total, n_backwards) of the
+    backward calls since timing was enabled/read."""
+    t = [ctypes.c_double() for _ in range(3)]
+    n = ctypes.c_int()
+    _check(load().lfattn_read_backward_timing(handle, *(ctypes.byref(x) for x in t),
+                                              ctypes.byref(n)), "lfattn_read_backward_timing")
+    return t[0].value, t[1].value, t[2].value, n.value
 
 
 class LFAttention:

@@ -144,6 +144,11 @@ def test_create_chunked_rejects_invalid(lib):
         L.LFATTN_EUNSUPPORTED
 
 
+def test_backward_rejects_null_handle(lib):
+    assert lib.lfattn_backward(None, 16, 16, 16, 16, 16, 16, 16, 16, 16, None) == \
+        L.LFATTN_EINVAL
+
+
 def test_new_entry_points_reject_null_handle(lib):
     assert lib.lfattn_forward_global_proj(None, 16, 16, 16, None, None, None, 16, None) == \
         L.LFATTN_EINVAL

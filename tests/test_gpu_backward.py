@@ -1,0 +1,158 @@
+"""GPU parity of the backward pass (lfattn_backward, bf16, D = 64): dQ, dK, dV
+against the oracle's double-precision gradients on the same bf16-valued
+inputs, every pattern, both forward band kernels feeding the log-sum-exp."""
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_sparse_band_amd import lfattn as L
+from long_context_sparse_band_amd import workloads as W
+from gpu_util import say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+
+
+def _bf16(x):
+    return W.bf16_bits_to_f32(W.bf16_round_bits(x)).reshape(x.shape)
+
+
+# Gradient tolerances relative to the reference's largest magnitude: the
+# weights P and dS enter the MFMAs rounded to bf16 (relative error 2^-9, a
+# few such roundings summed over a row's keys) and Delta is taken from the
+# bf16 output O.  Measured: max about 4e-3, mean about 2.5e-4 of that scale.
+REL_MAX, REL_MEAN = 1e-2, 1e-3
+
+
+def check(got, want, what):
+    ref = max(1e-6, float(np.abs(want).max()))
+    err = np.abs(got - want)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    assert err.max() <= REL_MAX * ref, f"{what}: max-abs {err.max():.3g} (ref max {ref:.3g})"
+    assert err.mean() <= REL_MEAN * ref, f"{what}: mean-abs {err.mean():.3g} (ref max {ref:.3g})"
+    return err.max() / ref, err.mean() / ref
+
+
+CASES = [
+    ("band", dict(B=1, H=2, N=300, window=64, dil=[1, 2], glob=[0, 150])),
+    ("band", dict(B=2, H=1, N=700, window=256, dil=[1], glob=list(range(0, 700, 23)))),
+    ("band", dict(B=1, H=2, N=129, window=1000, dil=[1, 3], glob=[])),
+    ("masked", dict(B=2, H=2, N=400, window=40, dil=[1, 2], sets=[[3, 200, 399], []])),
+    ("causal", dict(B=1, H=2, N=500, window=100, dil=[1, 2])),
+    ("chunked", dict(B=1, H=2, N=20 + 64 * 3 + 7, chunk=64, M=20)),
+    ("band", dict(B=1, H=1, N=1, window=8, dil=[1], glob=[])),
+    ("band", dict(B=1, H=1, N=65, window=16, dil=[3], glob=[64])),
+    ("causal", dict(B=2, H=1, N=1, window=4, dil=[1])),
+]
+
+
+@pytest.mark.parametrize("rows_mode", [64, 128])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0] + "_N%d" % c[1]["N"])
+def test_backward_every_element(case, rows_mode, monkeypatch):
+    import torch
+    monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows_mode))
+    kind, p = case
+    B, H, N, D = p["B"], p["H"], p["N"], 64
+    a = W.small_case(B, H, N, D, "bf16", p.get("window", 0), dilation=p.get("dil"), seed=88)
+    rng = np.random.default_rng(89)
+    do = _bf16(rng.standard_normal((B, H, N, D)).astype(np.float32))
+    if kind == "band":
+        h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, p["window"], p["dil"], p["glob"])
+        kw = dict(window=p["window"], dilation=p["dil"], glob=p["glob"])
+    elif kind == "masked":
+        mask = np.zeros((B, N), dtype=np.uint8)
+        for b, s in enumerate(p["sets"]):
+            mask[b, s] = 1
+        h = L.lfattn_create_masked(B, H, N, D, L.LFATTN_BF16, p["window"], p["dil"], mask)
+        kw = dict(window=p["window"], dilation=p["dil"], batch_glob=p["sets"])
+    elif kind == "causal":
+        h = L.lfattn_create_causal(B, H, N, D, L.LFATTN_BF16, p["window"], p["dil"])
+        kw = dict(window=p["window"], dilation=p["dil"], causal=True)
+    else:
+        h = L.lfattn_create_chunked(B, H, N, D, L.LFATTN_BF16, p["chunk"], p["M"])
+        kw = dict(chunk=p["chunk"], n_memory=p["M"])
+    try:
+        q, k, v = to_device(a)
+        g = torch.from_numpy(do).to("cuda:0").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        dq, dk, dv = (torch.full((B, H, N, D), float("nan"), dtype=torch.float32,
+                                 device=q.device) for _ in range(3))
+        say(f"backward {kind} {p} rows {rows_mode}")
+        L.lfattn_forward_lse(h, q, k, v, o, lse)
+        L.lfattn_backward(h, q, k, v, o, g, lse, dq, dk, dv)
+        torch.cuda.synchronize()
+    finally:
+        L.lfattn_destroy(h)
+    want = oracle.attention_grad(a.q, a.k, a.v, do, **kw)
+    errs = [check(x.cpu().numpy().astype(np.float64), w, f"{kind} {n}")
+            for x, w, n in zip((dq, dk, dv), want, ("dq", "dk", "dv"))]
+    say(f"  relative max/mean errors dq dk dv: {errs}")
+
+
+FULL = ["longformer_base_n4096", "dilated_charlm_n8192", "gmat_memory_m64_l16384"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_backward_full_size_sampled_heads(name):
+    """At the full sizes: the whole launch over every head, checked element
+    by element on the first and last heads (heads are independent)."""
+    import torch
+    wl = W.BY_NAME[name]
+    a = W.generate(wl)
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    rng = np.random.default_rng(wl.seed + 7)
+    do = _bf16(rng.standard_normal((B, H, N, D)).astype(np.float32))
+    h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, wl.window, list(a.dilation), list(a.glob))
+    try:
+        q, k, v = to_device(a)
+        g = torch.from_numpy(do).to("cuda:0").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        dq, dk, dv = (torch.full((B, H, N, D), float("nan"), dtype=torch.float32,
+                                 device=q.device) for _ in range(3))
+        say(f"backward full size {name}")
+        L.lfattn_forward_lse(h, q, k, v, o, lse)
+        L.lfattn_backward(h, q, k, v, o, g, lse, dq, dk, dv)
+        torch.cuda.synchronize()
+    finally:
+        L.lfattn_destroy(h)
+    hs = [0, H - 1]
+    want = oracle.attention_grad(a.q[:, hs], a.k[:, hs], a.v[:, hs], do[:, hs],
+                                 window=wl.window, dilation=[int(a.dilation[x]) for x in hs],
+                                 glob=list(a.glob))
+    for x, w, n in zip((dq, dk, dv), want, ("dq", "dk", "dv")):
+        assert np.all(np.isfinite(x.cpu().numpy())), f"{name} {n}: non-finite"
+        say(f"  {n}: {check(x[:, hs].cpu().numpy().astype(np.float64), w, f'{name} {n}')}")
+
+
+def test_backward_timing_records_each_call():
+    import torch
+    B, H, N, D = 1, 2, 512, 64
+    a = W.small_case(B, H, N, D, "bf16", 128, seed=5)
+    h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, 128, [1, 1], [0])
+    try:
+        q, k, v = to_device(a)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        dq, dk, dv = (torch.empty((B, H, N, D), dtype=torch.float32, device=q.device)
+                      for _ in range(3))
+        say("backward timing")
+        L.lfattn_forward_lse(h, q, k, v, o, lse)
+        L.lfattn_set_timing(h, True)
+        for _ in range(3):
+            L.lfattn_backward(h, q, k, v, o, q, lse, dq, dk, dv)
+        prep, rows, keys, n = L.lfattn_read_backward_timing(h)
+        assert n == 3 and prep > 0 and rows > 0 and keys > 0
+        assert L.lfattn_read_backward_timing(h)[3] == 0
+        L.lfattn_set_timing(h, False)
+    finally:
+        L.lfattn_destroy(h)
