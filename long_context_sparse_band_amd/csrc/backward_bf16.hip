@@ -76,9 +76,10 @@ __device__ __forceinline__ void tr_wait(s16x4& a0, s16x4& a1, s16x4& a2, s16x4& 
 struct BwdSmem {
   unsigned char x[2][kTileB];  // row side: K tiles; key side: Q tiles
   unsigned char y[2][kTileB];  // row side: V tiles; key side: dO tiles
-  float lse2[2][32];           // key side: the tile rows' log-sum-exp (base 2 units)
-  float dlt[2][32];            // key side: the tile rows' Delta
-  int ok[2][32];               // key side: the tile row takes part
+  // Key side: the tile rows' log-sum-exp in base-2 units (+inf for a row
+  // that takes no part: its weights are exp2(-inf) = 0) and their Delta.
+  float lse2[2][32];
+  float dlt[2][32];
   int gpos[kGCap];             // the batch element's global positions
   int gsp[kGCap];              // their place in the residue's subsequence
 };
@@ -302,36 +303,54 @@ void bwd_rows_kernel(BwdArgs a) {
   for (int t = 0; t < n_tiles; ++t) {
     const int st = t & 1;
     if (t + 1 < n_tiles) load(t + 1);
-    // Tiles none of this wave's rows score are skipped (a wave-uniform test).
-    bool act = ua < n_rows;
-    if (act && !gi && t < n_band) {
-      const int k0 = s_lo + 32 * t, k1 = min(k0 + 31, s_hi);
-      act = (k0 <= pat.hi(min(ua + 31, n_rows - 1))) && (k1 >= pat.lo(ua));
+    // Tiles none of this wave's rows score are skipped, and a tile every
+    // row of the wave scores completely needs no mask (wave-uniform tests;
+    // lo and hi are non-decreasing in the row).  Lanes of rows past the end
+    // or of global rows compute values that are never stored.
+    bool act = ua < n_rows, full = false;
+    if (act) {
+      if (gi) {
+        full = c0 + 32 * t + 31 < c1;
+      } else if (t < n_band) {
+        const int k0 = s_lo + 32 * t, k1 = min(k0 + 31, s_hi);
+        const int ul = min(ua + 31, n_rows - 1);
+        act = (k0 <= pat.hi(ul)) && (k1 >= pat.lo(ua));
+        full = (k0 + 31 <= s_hi) && (k0 >= pat.lo(ul)) && (k0 + 31 <= pat.hi(ua));
+      }
     }
     if (act) {
       const f32x16 s = rows_mfma(sm.x[st], l32, hi, q);
       const f32x16 dp = rows_mfma(sm.y[st], l32, hi, g);
       unsigned dsw[8];
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float ds2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int kk = brow(i + e, hi);
-          bool ok = row_ok;
-          if (gi) {
-            ok &= c0 + 32 * t + kk < c1;
-          } else if (t < n_band) {
-            const int k = s_lo + 32 * t + kk;
-            ok &= (k <= s_hi) & ((unsigned)(k - lo_u) <= span_u);
-          } else {
-            const int slot = 32 * (t - n_band) + kk;
-            ok &= (slot < ng) && ((unsigned)(sm.gsp[min(slot, kGCap - 1)] - lo_u) > span_u);
-          }
-          const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[i + e], a.sl2, -lse2)) : 0.0f;
-          ds2[e] = p * (dp[i + e] - dlt);
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i], a.sl2, -lse2));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], a.sl2, -lse2));
+          dsw[i / 2] = pack2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
         }
-        dsw[i / 2] = pack2(ds2[0], ds2[1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          float ds2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int kk = brow(i + e, hi);
+            bool ok = row_ok;
+            if (gi) {
+              ok &= c0 + 32 * t + kk < c1;
+            } else if (t < n_band) {
+              const int k = s_lo + 32 * t + kk;
+              ok &= (k <= s_hi) & ((unsigned)(k - lo_u) <= span_u);
+            } else {
+              const int slot = 32 * (t - n_band) + kk;
+              ok &= (slot < ng) && ((unsigned)(sm.gsp[min(slot, kGCap - 1)] - lo_u) > span_u);
+            }
+            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[i + e], a.sl2, -lse2)) : 0.0f;
+            ds2[e] = p * (dp[i + e] - dlt);
+          }
+          dsw[i / 2] = pack2(ds2[0], ds2[1]);
+        }
       }
       const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st];
       tr_mfma(xb, ta, dsw, acc);
@@ -396,7 +415,8 @@ void bwd_keys_kernel(BwdArgs a) {
   const int k = ka + l32;
   const bool key_ok = k < n_keys;
   const int pos_k = !key_ok ? 0 : (gk ? sm.gpos[k] : r + d * k);
-  // A global key (band item) is left to the global-key items.
+  // A global key (band item) is left to the global-key items: its lane's
+  // sums are computed but not stored.
   const bool key_band = key_ok && (gk || !isg[pos_k]);
   const int rlo_k = gk ? 0 : pat.rlo(k);
   const unsigned rspan_k = gk ? 0u : (unsigned)(pat.rhi(k) - rlo_k);
@@ -446,7 +466,6 @@ void bwd_keys_kernel(BwdArgs a) {
   const int ld_row = tid >> 3, ld_c = tid & 7;
   bf16x8 xv, yv;
   float m_lse = 0.0f, m_dlt = 0.0f;
-  int m_ok = 0;
   auto load = [&](int t) {
     bool part;
     const int p = row_pos(t, ld_row, part);
@@ -457,8 +476,7 @@ void bwd_keys_kernel(BwdArgs a) {
       yv = *(const bf16x8*)(dOp + (size_t)p * kBD + 8 * ld_c);
     }
     if (ld_c == 0) {
-      m_ok = p >= 0 && part;
-      m_lse = p >= 0 ? lsep[p] * kLog2e : 0.0f;
+      m_lse = (p >= 0 && part) ? lsep[p] * kLog2e : __builtin_inff();
       m_dlt = p >= 0 ? dlp[p] : 0.0f;
     }
   };
@@ -469,7 +487,6 @@ void bwd_keys_kernel(BwdArgs a) {
     if (ld_c == 0) {
       sm.lse2[st][ld_row] = m_lse;
       sm.dlt[st][ld_row] = m_dlt;
-      sm.ok[st][ld_row] = m_ok;
     }
   };
 
@@ -485,29 +502,43 @@ void bwd_keys_kernel(BwdArgs a) {
   for (int t = 0; t < n_tiles; ++t) {
     const int st = t & 1;
     if (t + 1 < n_tiles) load(t + 1);
-    bool act = ka < n_keys;
+    // The tile's rows reach one of this wave's keys; a band tile whose rows
+    // all score all of them needs no mask (rlo and rhi are non-decreasing;
+    // rows taking no part carry lse +inf, gathered global rows score every
+    // key, and keys before the first chunk are global: their lanes are not
+    // stored).
+    bool act = ka < n_keys, full = true;
     if (!gk && t < n_band) {
-      // The tile's rows reach one of this wave's keys.
       const int u0 = q_lo + 32 * t, u1 = min(u0 + 31, q_hi);
-      const int kb = min(ka + 31, n_keys - 1);
-      act = act && (u0 <= pat.rhi(kb)) && (u1 >= pat.rlo(ka > kfirst ? ka : kfirst));
+      const int kb = min(ka + 31, n_keys - 1), kf = ka > kfirst ? ka : kfirst;
+      act = act && (u0 <= pat.rhi(kb)) && (u1 >= pat.rlo(kf));
+      full = (u0 >= pat.rlo(kb)) && (u1 <= pat.rhi(kf));
     }
     if (act) {
       const f32x16 s = rows_mfma(sm.x[st], l32, hi, kr);
       const f32x16 dp = rows_mfma(sm.y[st], l32, hi, vr);
+      // Rows 8j + 4hi .. +3 of the result block sit in registers 4j .. 4j+3.
+      float4 l4[4], d4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l4[j] = *(const float4*)&sm.lse2[st][8 * j + 4 * hi];
+        d4[j] = *(const float4*)&sm.dlt[st][8 * j + 4 * hi];
+      }
+      const float* lv = (const float*)l4;
+      const float* dv4 = (const float*)d4;
       unsigned pw[8], dsw[8];
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         float p2[2], ds2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int qq = brow(i + e, hi);
-          bool ok = key_band && sm.ok[st][qq];
-          if (!gk && t < n_band) ok &= (unsigned)(q_lo + 32 * t + qq - rlo_k) <= rspan_k;
-          const float p =
-              ok ? __builtin_amdgcn_exp2f(fmaf(s[i + e], a.sl2, -sm.lse2[st][qq])) : 0.0f;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[i + e], a.sl2, -lv[i + e]));
+          if (!full) {
+            const int qq = brow(i + e, hi);
+            p = (unsigned)(q_lo + 32 * t + qq - rlo_k) <= rspan_k ? p : 0.0f;
+          }
           p2[e] = p;
-          ds2[e] = p * (dp[i + e] - sm.dlt[st][qq]);
+          ds2[e] = p * (dp[i + e] - dv4[i + e]);
         }
         pw[i / 2] = pack2(p2[0], p2[1]);
         dsw[i / 2] = pack2(ds2[0], ds2[1]);
