@@ -73,13 +73,27 @@ __device__ __forceinline__ void tr_wait(s16x4& a0, s16x4& a1, s16x4& a2, s16x4& 
                : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4), "+v"(a5), "+v"(a6), "+v"(a7));
 }
 
+// 16-byte direct global -> LDS load: lane i's 16 bytes land at LDS byte
+// address M0 + 16 i (M0 = the wave-uniform lds).  Inline assembly, so the
+// compiler does not drain outstanding loads before every LDS read; the
+// ring's explicit wait orders the accesses.
+__device__ __forceinline__ void dma16(const void* gaddr, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(gaddr)
+               : "memory", "m0");
+}
+// s_waitcnt vmcnt(0) (gfx9-family encoding; expcnt and lgkmcnt left open).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 struct BwdSmem {
   unsigned char x[2][kTileB];  // row side: K tiles; key side: Q tiles
   unsigned char y[2][kTileB];  // row side: V tiles; key side: dO tiles
-  // Key side: the tile rows' log-sum-exp in base-2 units (+inf for a row
-  // that takes no part: its weights are exp2(-inf) = 0) and their Delta.
-  float lse2[2][32];
-  float dlt[2][32];
+  // Key side: per tile row, -lse / scale (-inf for a row that takes no
+  // part: its weights are exp2(-inf) = 0) and -Delta, the initial values of
+  // the score and dP accumulators.
+  float nls[2][32];
+  float ndl[2][32];
   int gpos[kGCap];             // the batch element's global positions
   int gsp[kGCap];              // their place in the residue's subsequence
 };
@@ -145,11 +159,10 @@ __device__ __forceinline__ void tr_mfma(unsigned base, const TrAddr& ta, const u
   }
 }
 
-// sum_ks A_ks . B_ks with A from the 32 rows of the tile at LDS pointer t
+// s + sum_ks A_ks . B_ks with A from the 32 rows of the tile at LDS pointer t
 // (lane: row L%32, columns 16ks + 8(L/32) .. +7) and B in registers.
 __device__ __forceinline__ f32x16 rows_mfma(const unsigned char* t, int l32, int hi,
-                                            const bf16x8* bop) {
-  f32x16 s = {};
+                                            const bf16x8* bop, f32x16 s = f32x16{}) {
 #pragma unroll
   for (int ks = 0; ks < kBD / 16; ++ks) {
     const bf16x8 a = *(const LDS_AS bf16x8*)(const LDS_AS unsigned char*)
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Row side: dQ.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void bwd_rows_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) BwdSmem sm;
   const int tid = threadIdx.x;
@@ -262,43 +275,33 @@ void bwd_rows_kernel(BwdArgs a) {
   const float lse2 = a.lse[(size_t)w.bh * N + pos_u] * kLog2e;
   const float dlt = a.delta[(size_t)w.bh * N + pos_u];
 
-  // Key position of row rr of tile t, or -1.
+  // Key position of row rr of tile t; a row past the end of the tile's keys
+  // takes the last one (its weights are masked).
   auto key_pos = [&](int t, int rr) -> int {
-    if (gi) {
-      const int k = c0 + 32 * t + rr;
-      return k < c1 ? k : -1;
-    }
-    if (t < n_band) {
-      const int k = s_lo + 32 * t + rr;
-      return k <= s_hi ? r + d * k : -1;
-    }
-    const int slot = 32 * (t - n_band) + rr;
-    return slot < ng ? sm.gpos[slot] : -1;
+    if (gi) return min(c0 + 32 * t + rr, c1 - 1);
+    if (t < n_band) return r + d * min(s_lo + 32 * t + rr, s_hi);
+    return sm.gpos[min(32 * (t - n_band) + rr, ng - 1)];
   };
-  // One thread's share of tile t's loads: row tid/8, 16-byte chunk tid%8.
-  const int ld_row = tid >> 3, ld_c = tid & 7;
-  bf16x8 xv, yv;
+  // One thread's share of tile t's loads: tile row tid/8, physical 16-byte
+  // chunk tid%8 (wave w fills bytes 1024 w .. 1024 w + 1023 of the tile).
+  const int ld_row = tid >> 3, ld_c = swz(ld_row, tid & 7);
+  const unsigned xl = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(LDS_AS void*)sm.x[0] + 1024u * wave);
+  const unsigned yl = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(LDS_AS void*)sm.y[0] + 1024u * wave);
   auto load = [&](int t) {
-    const int p = key_pos(t, ld_row);
-    xv = bf16x8{};
-    yv = bf16x8{};
-    if (p >= 0) {
-      xv = *(const bf16x8*)(Kp + (size_t)p * kBD + 8 * ld_c);
-      yv = *(const bf16x8*)(Vp + (size_t)p * kBD + 8 * ld_c);
-    }
-  };
-  auto store = [&](int st) {
-    const int o = ld_row * kRB + 16 * swz(ld_row, ld_c);
-    *(bf16x8*)(sm.x[st] + o) = xv;
-    *(bf16x8*)(sm.y[st] + o) = yv;
+    const size_t p = (size_t)key_pos(t, ld_row);
+    const unsigned so = (unsigned)(t & 1) * kTileB;
+    dma16(Kp + p * kBD + 8 * ld_c, xl + so);
+    dma16(Vp + p * kBD + 8 * ld_c, yl + so);
   };
 
   TrAddr ta;
   ta.init(lane);
   f32x16 acc[2] = {f32x16{}, f32x16{}};
 
-  load(0);
-  store(0);
+  if (n_tiles > 0) load(0);
+  wait_vm0();
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int st = t & 1;
@@ -355,7 +358,7 @@ void bwd_rows_kernel(BwdArgs a) {
       const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st];
       tr_mfma(xb, ta, dsw, acc);
     }
-    if (t + 1 < n_tiles) store(1 - st);
+    wait_vm0();
     __syncthreads();
   }
 
@@ -383,7 +386,7 @@ void bwd_rows_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Key side: dK, dV.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void bwd_keys_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) BwdSmem sm;
   const int tid = threadIdx.x;
@@ -441,52 +444,49 @@ void bwd_keys_kernel(BwdArgs a) {
     vr[ks] = *(const bf16x8*)(Vp + (size_t)pos_k * kBD + 16 * ks + 8 * hi);
   }
 
-  // Query position of row rr of tile t (or -1) and whether it takes part
-  // (a global row of a band tile is left to the gathered global rows).
+  // Query position of row rr of tile t and whether it takes part (a global
+  // row of a band tile is left to the gathered global rows; a row past the
+  // end of the tile's rows takes the last one and no part).
   auto row_pos = [&](int t, int rr, bool& part) -> int {
-    part = false;
     if (gk) {
       const int p = c0 + 32 * t + rr;
-      if (p >= c1) return -1;
-      part = true;
-      return p;
+      part = p < c1;
+      return min(p, c1 - 1);
     }
     if (t < n_band) {
       const int uq = q_lo + 32 * t + rr;
-      if (uq > q_hi) return -1;
-      const int p = r + d * uq;
-      part = !isg[p];
+      const int p = r + d * min(uq, q_hi);
+      part = uq <= q_hi && !isg[p];
       return p;
     }
     const int slot = 32 * (t - n_band) + rr;
-    if (slot >= ng) return -1;
-    part = true;
-    return sm.gpos[slot];
+    part = slot < ng;
+    return sm.gpos[min(slot, ng - 1)];
   };
-  const int ld_row = tid >> 3, ld_c = tid & 7;
-  bf16x8 xv, yv;
+  // Tile loads as on the row side; the thread of chunk 0 of a row also
+  // fetches the row's -lse / scale and -Delta.
+  const int ld_row = tid >> 3, ld_c = swz(ld_row, tid & 7);
+  const bool ld_meta = (tid & 7) == 0;
+  const unsigned xl = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(LDS_AS void*)sm.x[0] + 1024u * wave);
+  const unsigned yl = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(LDS_AS void*)sm.y[0] + 1024u * wave);
   float m_lse = 0.0f, m_dlt = 0.0f;
   auto load = [&](int t) {
     bool part;
     const int p = row_pos(t, ld_row, part);
-    xv = bf16x8{};
-    yv = bf16x8{};
-    if (p >= 0) {
-      xv = *(const bf16x8*)(Qp + (size_t)p * kBD + 8 * ld_c);
-      yv = *(const bf16x8*)(dOp + (size_t)p * kBD + 8 * ld_c);
-    }
-    if (ld_c == 0) {
-      m_lse = (p >= 0 && part) ? lsep[p] * kLog2e : __builtin_inff();
-      m_dlt = p >= 0 ? dlp[p] : 0.0f;
+    const unsigned so = (unsigned)(t & 1) * kTileB;
+    dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so);
+    dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so);
+    if (ld_meta) {
+      m_lse = part ? -lsep[p] / a.scale : -__builtin_inff();
+      m_dlt = -dlp[p];
     }
   };
-  auto store = [&](int st) {
-    const int o = ld_row * kRB + 16 * swz(ld_row, ld_c);
-    *(bf16x8*)(sm.x[st] + o) = xv;
-    *(bf16x8*)(sm.y[st] + o) = yv;
-    if (ld_c == 0) {
-      sm.lse2[st][ld_row] = m_lse;
-      sm.dlt[st][ld_row] = m_dlt;
+  auto store_meta = [&](int st) {
+    if (ld_meta) {
+      sm.nls[st][ld_row] = m_lse;
+      sm.ndl[st][ld_row] = m_dlt;
     }
   };
 
@@ -496,8 +496,9 @@ void bwd_keys_kernel(BwdArgs a) {
 
   if (n_tiles > 0) {
     load(0);
-    store(0);
+    store_meta(0);
   }
+  wait_vm0();
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int st = t & 1;
@@ -515,30 +516,32 @@ void bwd_keys_kernel(BwdArgs a) {
       full = (u0 >= pat.rlo(kb)) && (u1 <= pat.rhi(kf));
     }
     if (act) {
-      const f32x16 s = rows_mfma(sm.x[st], l32, hi, kr);
-      const f32x16 dp = rows_mfma(sm.y[st], l32, hi, vr);
-      // Rows 8j + 4hi .. +3 of the result block sit in registers 4j .. 4j+3.
-      float4 l4[4], d4[4];
+      // Rows 8j + 4hi .. +3 of a result block sit in registers 4j .. 4j+3:
+      // the accumulators start at -lse / scale and -Delta of their rows, so
+      // s = q.k - lse / scale and dp = dO.v - Delta.
+      f32x16 s0, d0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        l4[j] = *(const float4*)&sm.lse2[st][8 * j + 4 * hi];
-        d4[j] = *(const float4*)&sm.dlt[st][8 * j + 4 * hi];
+        const float4 l4 = *(const float4*)&sm.nls[st][8 * j + 4 * hi];
+        const float4 d4 = *(const float4*)&sm.ndl[st][8 * j + 4 * hi];
+        s0[4 * j] = l4.x; s0[4 * j + 1] = l4.y; s0[4 * j + 2] = l4.z; s0[4 * j + 3] = l4.w;
+        d0[4 * j] = d4.x; d0[4 * j + 1] = d4.y; d0[4 * j + 2] = d4.z; d0[4 * j + 3] = d4.w;
       }
-      const float* lv = (const float*)l4;
-      const float* dv4 = (const float*)d4;
+      const f32x16 s = rows_mfma(sm.x[st], l32, hi, kr, s0);
+      const f32x16 dp = rows_mfma(sm.y[st], l32, hi, vr, d0);
       unsigned pw[8], dsw[8];
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         float p2[2], ds2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          float p = __builtin_amdgcn_exp2f(fmaf(s[i + e], a.sl2, -lv[i + e]));
+          float p = __builtin_amdgcn_exp2f(s[i + e] * a.sl2);
           if (!full) {
             const int qq = brow(i + e, hi);
             p = (unsigned)(q_lo + 32 * t + qq - rlo_k) <= rspan_k ? p : 0.0f;
           }
           p2[e] = p;
-          ds2[e] = p * (dp[i + e] - dv4[i + e]);
+          ds2[e] = p * dp[i + e];
         }
         pw[i / 2] = pack2(p2[0], p2[1]);
         dsw[i / 2] = pack2(ds2[0], ds2[1]);
@@ -548,7 +551,8 @@ void bwd_keys_kernel(BwdArgs a) {
       tr_mfma(yb, ta, pw, accV);   // dV^T += dO^T P
       tr_mfma(xb, ta, dsw, accK);  // dK^T += Q^T dS
     }
-    if (t + 1 < n_tiles) store(1 - st);
+    if (t + 1 < n_tiles) store_meta(1 - st);
+    wait_vm0();
     __syncthreads();
   }
 

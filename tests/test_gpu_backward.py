@@ -33,7 +33,10 @@ REL_MAX, REL_MEAN = 1e-2, 1e-3
 
 
 def check(got, want, what):
-    ref = max(1e-6, float(np.abs(want).max()))
+    # Floor of the scale: where the exact gradient cancels to zero (one key
+    # per row: dS = P (dP - Delta) = 0) fp32 leaves residues of about 1e-7
+    # of the O(1..10) terms that cancel.
+    ref = max(1e-3, float(np.abs(want).max()))
     err = np.abs(got - want)
     assert np.all(np.isfinite(got)), f"{what}: non-finite"
     assert err.max() <= REL_MAX * ref, f"{what}: max-abs {err.max():.3g} (ref max {ref:.3g})"
