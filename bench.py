@@ -200,9 +200,9 @@ def bench_backward(args, wl, inp, L, torch):
     L.lfattn_set_timing(h, True)
     for _ in range(args.steps):
         step()
-    prep, rows, keys, n = L.lfattn_read_backward_timing(h)
+    rows, keys, merge, n = L.lfattn_read_backward_timing(h)
     L.lfattn_set_timing(h, False)
-    prep, rows, keys = (x / max(n, 1) for x in (prep, rows, keys))
+    rows, keys, merge = (x / max(n, 1) for x in (rows, keys, merge))
     pairs = L.lfattn_scored_pairs(h)
     L.lfattn_destroy(h)
     peak = PEAK_TFLOPS["bf16"]
@@ -223,7 +223,7 @@ def bench_backward(args, wl, inp, L, torch):
                    "scored_pairs": pairs, "parallelism": "single GPU"},
         "whole_backward_tflops": pairs * 10 * D / (ms * 1e-3) / 1e12,
         "whole_backward_mfma_frac": pairs * 10 * D / (ms * 1e-3) / 1e12 / peak,
-        "kernels_ms": {"prep": prep, "rows_dq": rows, "keys_dkdv": keys},
+        "kernels_ms": {"rows_dq": rows, "keys_dkdv": keys, "merge": merge},
         "rows_kernel": {"achieved": rows_tf, "frac": rows_tf / peak,
                         "flops_per_launch": pairs * 6 * D},
         "roofline": {"kernel": "bwd_keys_kernel", "bound": "mfma", "achieved": keys_tf,

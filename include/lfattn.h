@@ -260,12 +260,13 @@ lfattn_status lfattn_read_timing(lfattn_t ctx, double* band_ms, double* global_m
 /*
  * The same for lfattn_backward calls while timing is enabled (at most 1024
  * recorded): the milliseconds, summed over the recorded calls, of the
- * preparation kernel (row terms Delta, clearing of the global rows'
- * gradients), of the query-side kernel (dQ) and of the key-side kernel
- * (dK, dV); the number of calls recorded; then clears that record.
+ * query-side kernel (dQ and the row terms Delta), of the key-side kernel
+ * (dK, dV) and of the merge of the global rows' and keys' partial gradients
+ * (0 without global positions); the number of calls recorded; then clears
+ * that record.
  */
-lfattn_status lfattn_read_backward_timing(lfattn_t ctx, double* prep_ms, double* rows_ms,
-                                          double* keys_ms, int* n_backwards);
+lfattn_status lfattn_read_backward_timing(lfattn_t ctx, double* rows_ms, double* keys_ms,
+                                          double* merge_ms, int* n_backwards);
 
 #ifdef __cplusplus
 }

@@ -10,19 +10,20 @@
 //   dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij Q_i,  dV_j = sum_i P_ij dO_i.
 //
 // Three launches:
-//  - bwd_prep_kernel: Delta for every row; zeroes dQ at the global rows and dK,
-//    dV at the global keys (which receive atomic sums below).
 //  - bwd_rows_kernel (row side, like the forward): a workgroup takes 128 rows
 //    of one (batch, head, residue) and walks the 32-key tiles of their band,
-//    then the gathered global keys: S^T = K Q^T and dP^T = V dO^T on MFMA,
+//    then the gathered global keys (and Delta = dO . O of its rows, written
+//    for the key side): S^T = K Q^T and dP^T = V dO^T on MFMA,
 //    dS on the vector unit, dQ^T += K^T dS^T on MFMA (K^T read from the
-//    row-major tile with ds_read_b64_tr_b16).  Global-row items (128 global
-//    rows against a 512-key chunk) add their dQ with atomics.
+//    row-major tile with ds_read_b64_tr_b16).  Global-row items (a set of
+//    global rows against a chunk of keys) write partial dQ per chunk.
 //  - bwd_keys_kernel (key side, the roles of queries and keys swapped): a
 //    workgroup takes 128 keys and walks the 32-row tiles of the rows whose
 //    band holds them, then the gathered global rows: S = Q K^T, dP = dO V^T,
-//    dV^T += dO^T P and dK^T += Q^T dS.  Global-key items (128 global keys
-//    against a 512-row chunk) add dK, dV with atomics.
+//    dV^T += dO^T P and dK^T += Q^T dS.  Global-key items (a set of global
+//    keys against a chunk of rows) write partial dK, dV per chunk.
+//  - bwd_merge_kernel: the global rows' dQ and the global keys' dK, dV as
+//    the sums of their chunks' partials (no atomics: deterministic).
 // Tiles go global -> registers -> LDS through a two-stage ring, one barrier
 // per step; the same 16-byte-chunk swizzle as the forward keeps the MFMA
 // operand reads free of bank conflicts.
@@ -41,7 +42,6 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 constexpr int kBD = 64;          // head dimension
 constexpr int kRB = 2 * kBD;     // bytes per row
 constexpr int kTileB = 32 * kRB; // bytes per 32-row tile
-constexpr int kItemRows = 128;   // rows (row side) or keys (key side) per workgroup
 constexpr int kGCap = kMaxGlobalBf16;
 constexpr int kOutOfClass = 0x40000000;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -86,14 +86,16 @@ __device__ __forceinline__ void dma16(const void* gaddr, unsigned lds) {
 // s_waitcnt vmcnt(0) (gfx9-family encoding; expcnt and lgkmcnt left open).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// The tile ring: two stages of up to two tiles (one per key split); after
+// the loop its first 32 KB hold the key splits' partial sums.
 struct BwdSmem {
-  unsigned char x[2][kTileB];  // row side: K tiles; key side: Q tiles
-  unsigned char y[2][kTileB];  // row side: V tiles; key side: dO tiles
+  unsigned char x[2][2][kTileB];  // row side: K tiles; key side: Q tiles
+  unsigned char y[2][2][kTileB];  // row side: V tiles; key side: dO tiles
   // Key side: per tile row, -lse / scale (-inf for a row that takes no
   // part: its weights are exp2(-inf) = 0) and -Delta, the initial values of
   // the score and dP accumulators.
-  float nls[2][32];
-  float ndl[2][32];
+  float nls[2][2][32];
+  float ndl[2][2][32];
   int gpos[kGCap];             // the batch element's global positions
   int gsp[kGCap];              // their place in the residue's subsequence
 };
@@ -189,44 +191,20 @@ __device__ __forceinline__ void stage_globals(BwdSmem& sm, const int* gl, int ng
 }
 
 // ---------------------------------------------------------------------------
-// Delta and zeroing.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-  const long long row = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long n_rows = (long long)a.n_bh * a.N;
-  if (row >= n_rows) return;
-  const int bh = (int)(row / a.N), pos = (int)(row % a.N), b = bh / a.H;
-  const unsigned short* o = (const unsigned short*)a.O + row * kBD;
-  const unsigned short* g = (const unsigned short*)a.dO + row * kBD;
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < kBD; c += 8) {
-    const bf16x8 ov = *(const bf16x8*)(o + c), gv = *(const bf16x8*)(g + c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s += (float)ov[e] * (float)gv[e];
-  }
-  a.delta[row] = s;
-  if (a.is_glob[(long long)b * a.isg_stride + pos]) {
-    float4* q = (float4*)(a.dQ + row * kBD);
-    float4* k = (float4*)(a.dK + row * kBD);
-    float4* v = (float4*)(a.dV + row * kBD);
-#pragma unroll
-    for (int c = 0; c < kBD / 4; ++c) {
-      q[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      k[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Row side: dQ.
 // ---------------------------------------------------------------------------
+// KS = 1: four waves of 32 rows (128 per workgroup) share one stream of key
+// tiles.  KS = 2: two waves of 32 rows (64 per workgroup) take the even
+// tiles, the other two the odd ones, and the two partial dQ add up through
+// LDS at the end (twice the workgroups, half the tiles per wave).
+template <int KS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void bwd_rows_kernel(BwdArgs a) {
+  constexpr int RB = 4 / KS, IR = 32 * RB;  // row blocks, rows per item
   __shared__ __attribute__((aligned(16))) BwdSmem sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = wave % RB, kq = wave / RB;
   const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
   const BandWork w = a.work[blockIdx.x];
   const bool gi = w.dil == 0;
@@ -237,6 +215,7 @@ void bwd_rows_kernel(BwdArgs a) {
   const unsigned short* Kp = (const unsigned short*)a.K + base;
   const unsigned short* Vp = (const unsigned short*)a.V + base;
   const unsigned short* dOp = (const unsigned short*)a.dO + base;
+  const unsigned short* Op = (const unsigned short*)a.O + base;
   const int* gl = a.glob + w.g0;
   const int ng = w.ng;
   const unsigned char* isg = a.is_glob + (long long)w.b * a.isg_stride;
@@ -248,7 +227,7 @@ void bwd_rows_kernel(BwdArgs a) {
   // This wave's rows: band item, subsequence positions u = ua + l32 (< Lr);
   // global-row item, slots of the global list.
   const int n_rows = gi ? ng : Lr;
-  const int ua = (gi ? kItemRows * w.r : w.t0) + 32 * wave;
+  const int ua = (gi ? IR * w.r : w.t0) + 32 * rb;
   const int u = ua + l32;
   const bool row_ok = u < n_rows;
   const int pos_u = !row_ok ? 0 : (gi ? sm.gpos[u] : r + d * u);
@@ -260,7 +239,7 @@ void bwd_rows_kernel(BwdArgs a) {
   const int t0 = w.t0;
   const int c0 = gi ? t0 * a.chunk_keys : 0, c1 = gi ? min(N, c0 + a.chunk_keys) : 0;
   const int s_lo = gi ? 0 : max(0, pat.lo(t0));
-  const int s_hi = gi ? -1 : min(Lr - 1, pat.hi(min(t0 + kItemRows - 1, Lr - 1)));
+  const int s_hi = gi ? -1 : min(Lr - 1, pat.hi(min(t0 + IR - 1, Lr - 1)));
   const int n_band = gi ? (c1 - c0 + 31) / 32 : (s_hi - s_lo) / 32 + 1;
   const int n_tiles = n_band + (gi ? 0 : (ng + 31) / 32);
 
@@ -273,7 +252,17 @@ void bwd_rows_kernel(BwdArgs a) {
     g[ks] = *(const bf16x8*)(dOp + (size_t)pos_u * kBD + 16 * ks + 8 * hi);
   }
   const float lse2 = a.lse[(size_t)w.bh * N + pos_u] * kLog2e;
-  const float dlt = a.delta[(size_t)w.bh * N + pos_u];
+  // Delta = dO . O of the row (each lane half holds 32 of its columns); the
+  // band items write it for the key side, which runs after this kernel.
+  float dlt = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < kBD / 16; ++ks) {
+    const bf16x8 o8 = *(const bf16x8*)(Op + (size_t)pos_u * kBD + 16 * ks + 8 * hi);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dlt = fmaf((float)g[ks][e], (float)o8[e], dlt);
+  }
+  dlt += __shfl_xor(dlt, 32);
+  if (!gi && row_ok && hi == 0) a.delta[(size_t)w.bh * N + pos_u] = dlt;
 
   // Key position of row rr of tile t; a row past the end of the tile's keys
   // takes the last one (its weights are masked).
@@ -282,35 +271,43 @@ void bwd_rows_kernel(BwdArgs a) {
     if (t < n_band) return r + d * min(s_lo + 32 * t + rr, s_hi);
     return sm.gpos[min(32 * (t - n_band) + rr, ng - 1)];
   };
-  // One thread's share of tile t's loads: tile row tid/8, physical 16-byte
+  // One thread's share of a tile's loads: tile row tid/8, physical 16-byte
   // chunk tid%8 (wave w fills bytes 1024 w .. 1024 w + 1023 of the tile).
+  // Step j holds tiles KS j .. KS j + KS - 1 in stage j % 2.
   const int ld_row = tid >> 3, ld_c = swz(ld_row, tid & 7);
   const unsigned xl = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(LDS_AS void*)sm.x[0] + 1024u * wave);
+      (unsigned)(uintptr_t)(LDS_AS void*)&sm.x[0][0][0] + 1024u * wave);
   const unsigned yl = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(LDS_AS void*)sm.y[0] + 1024u * wave);
-  auto load = [&](int t) {
-    const size_t p = (size_t)key_pos(t, ld_row);
-    const unsigned so = (unsigned)(t & 1) * kTileB;
-    dma16(Kp + p * kBD + 8 * ld_c, xl + so);
-    dma16(Vp + p * kBD + 8 * ld_c, yl + so);
+      (unsigned)(uintptr_t)(LDS_AS void*)&sm.y[0][0][0] + 1024u * wave);
+  const int n_steps = (n_tiles + KS - 1) / KS;
+  auto load = [&](int j) {
+#pragma unroll
+    for (int q2 = 0; q2 < KS; ++q2) {
+      const int t = KS * j + q2;
+      if (t < n_tiles) {
+        const size_t p = (size_t)key_pos(t, ld_row);
+        const unsigned so = (unsigned)((j & 1) * 2 + q2) * kTileB;
+        dma16(Kp + p * kBD + 8 * ld_c, xl + so);
+        dma16(Vp + p * kBD + 8 * ld_c, yl + so);
+      }
+    }
   };
 
   TrAddr ta;
   ta.init(lane);
   f32x16 acc[2] = {f32x16{}, f32x16{}};
 
-  if (n_tiles > 0) load(0);
+  if (n_steps > 0) load(0);
   wait_vm0();
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < n_tiles) load(t + 1);
+  for (int j = 0; j < n_steps; ++j) {
+    const int st = j & 1, t = KS * j + kq;
+    if (j + 1 < n_steps) load(j + 1);
     // Tiles none of this wave's rows score are skipped, and a tile every
     // row of the wave scores completely needs no mask (wave-uniform tests;
     // lo and hi are non-decreasing in the row).  Lanes of rows past the end
     // or of global rows compute values that are never stored.
-    bool act = ua < n_rows, full = false;
+    bool act = ua < n_rows && t < n_tiles, full = false;
     if (act) {
       if (gi) {
         full = c0 + 32 * t + 31 < c1;
@@ -322,8 +319,8 @@ void bwd_rows_kernel(BwdArgs a) {
       }
     }
     if (act) {
-      const f32x16 s = rows_mfma(sm.x[st], l32, hi, q);
-      const f32x16 dp = rows_mfma(sm.y[st], l32, hi, g);
+      const f32x16 s = rows_mfma(sm.x[st][kq], l32, hi, q);
+      const f32x16 dp = rows_mfma(sm.y[st][kq], l32, hi, g);
       unsigned dsw[8];
       if (full) {
 #pragma unroll
@@ -355,42 +352,52 @@ void bwd_rows_kernel(BwdArgs a) {
           dsw[i / 2] = pack2(ds2[0], ds2[1]);
         }
       }
-      const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st];
+      const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
       tr_mfma(xb, ta, dsw, acc);
     }
     wait_vm0();
     __syncthreads();
   }
+  if (KS == 2) {
+    // The odd-tile waves hand their sums to the even-tile waves of the
+    // same rows (element e of lane L at float (32 rb + e) * 64 + L).
+    float* red = (float*)&sm.x[0][0][0];
+    if (kq == 1)
+#pragma unroll
+      for (int e = 0; e < 32; ++e) red[(32 * rb + e) * 64 + lane] = acc[e >> 4][e & 15];
+    __syncthreads();
+    if (kq == 1) return;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) acc[e >> 4][e & 15] += red[(32 * rb + e) * 64 + lane];
+  }
 
   if (!row_ok) return;
   if (!gi && isg[pos_u]) return;  // a global row: its dQ comes from the global-row items
-  float* dq = a.dQ + base + (size_t)pos_u * kBD;
+  // Band row: its dQ.  Global-row item: the chunk's partial dQ of slot u.
+  float* dq = gi ? a.gpart + (((size_t)w.bh * a.n_gch + t0) * a.n_glob + u) * kBD
+                 : a.dQ + base + (size_t)pos_u * kBD;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float* p = dq + 32 * b + 8 * g4 + 4 * hi;
-      const float v0 = a.scale * acc[b][4 * g4], v1 = a.scale * acc[b][4 * g4 + 1];
-      const float v2 = a.scale * acc[b][4 * g4 + 2], v3 = a.scale * acc[b][4 * g4 + 3];
-      if (gi) {
-        unsafeAtomicAdd(p, v0);
-        unsafeAtomicAdd(p + 1, v1);
-        unsafeAtomicAdd(p + 2, v2);
-        unsafeAtomicAdd(p + 3, v3);
-      } else {
-        *(float4*)p = make_float4(v0, v1, v2, v3);
-      }
-    }
+    for (int g4 = 0; g4 < 4; ++g4)
+      *(float4*)(dq + 32 * b + 8 * g4 + 4 * hi) =
+          make_float4(a.scale * acc[b][4 * g4], a.scale * acc[b][4 * g4 + 1],
+                      a.scale * acc[b][4 * g4 + 2], a.scale * acc[b][4 * g4 + 3]);
 }
 
 // ---------------------------------------------------------------------------
 // Key side: dK, dV.
 // ---------------------------------------------------------------------------
+// KS as on the row side: 32 (KS = 2) or 128 (KS = 1) keys per workgroup, and
+// with KS = 2 the even and odd row tiles split between two pairs of waves.
+template <int KS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void bwd_keys_kernel(BwdArgs a) {
+  constexpr int RB = 4 / KS, IK = 32 * RB;  // key blocks, keys per item
   __shared__ __attribute__((aligned(16))) BwdSmem sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = wave % RB, kq = wave / RB;
   const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
   const BandWork w = a.work[blockIdx.x];
   const bool gk = w.dil == 0;
@@ -414,7 +421,7 @@ void bwd_keys_kernel(BwdArgs a) {
   // This wave's keys: band item, subsequence positions k = ka + l32 (< Lr);
   // global-key item, slots of the global list.
   const int n_keys = gk ? ng : Lr;
-  const int ka = (gk ? kItemRows * w.r : w.t0) + 32 * wave;
+  const int ka = (gk ? IK * w.r : w.t0) + 32 * rb;
   const int k = ka + l32;
   const bool key_ok = k < n_keys;
   const int pos_k = !key_ok ? 0 : (gk ? sm.gpos[k] : r + d * k);
@@ -430,7 +437,7 @@ void bwd_keys_kernel(BwdArgs a) {
   const int t0 = w.t0;
   const int c0 = gk ? t0 * a.chunk_keys : 0, c1 = gk ? min(N, c0 + a.chunk_keys) : 0;
   const int kfirst = (a.chunk > 0) ? max(t0, a.cbase) : t0;
-  const int klast = min(t0 + kItemRows - 1, Lr - 1);
+  const int klast = min(t0 + IK - 1, Lr - 1);
   const int q_lo = gk ? 0 : max(0, pat.rlo(kfirst));
   const int q_hi = gk ? -1 : min(Lr - 1, pat.rhi(klast));
   const int n_band = gk ? (c1 - c0 + 31) / 32 : (q_hi >= q_lo ? (q_hi - q_lo) / 32 + 1 : 0);
@@ -468,47 +475,56 @@ void bwd_keys_kernel(BwdArgs a) {
   const int ld_row = tid >> 3, ld_c = swz(ld_row, tid & 7);
   const bool ld_meta = (tid & 7) == 0;
   const unsigned xl = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(LDS_AS void*)sm.x[0] + 1024u * wave);
+      (unsigned)(uintptr_t)(LDS_AS void*)&sm.x[0][0][0] + 1024u * wave);
   const unsigned yl = __builtin_amdgcn_readfirstlane(
-      (unsigned)(uintptr_t)(LDS_AS void*)sm.y[0] + 1024u * wave);
-  float m_lse = 0.0f, m_dlt = 0.0f;
-  auto load = [&](int t) {
-    bool part;
-    const int p = row_pos(t, ld_row, part);
-    const unsigned so = (unsigned)(t & 1) * kTileB;
-    dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so);
-    dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so);
-    if (ld_meta) {
-      m_lse = part ? -lsep[p] / a.scale : -__builtin_inff();
-      m_dlt = -dlp[p];
+      (unsigned)(uintptr_t)(LDS_AS void*)&sm.y[0][0][0] + 1024u * wave);
+  const int n_steps = (n_tiles + KS - 1) / KS;
+  float m_lse[KS], m_dlt[KS];
+  auto load = [&](int j) {
+#pragma unroll
+    for (int q2 = 0; q2 < KS; ++q2) {
+      const int t = KS * j + q2;
+      if (t < n_tiles) {
+        bool part;
+        const int p = row_pos(t, ld_row, part);
+        const unsigned so = (unsigned)((j & 1) * 2 + q2) * kTileB;
+        dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so);
+        dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so);
+        if (ld_meta) {
+          m_lse[q2] = part ? -lsep[p] / a.scale : -__builtin_inff();
+          m_dlt[q2] = -dlp[p];
+        }
+      }
     }
   };
-  auto store_meta = [&](int st) {
-    if (ld_meta) {
-      sm.nls[st][ld_row] = m_lse;
-      sm.ndl[st][ld_row] = m_dlt;
-    }
+  auto store_meta = [&](int j) {
+#pragma unroll
+    for (int q2 = 0; q2 < KS; ++q2)
+      if (ld_meta && KS * j + q2 < n_tiles) {
+        sm.nls[j & 1][q2][ld_row] = m_lse[q2];
+        sm.ndl[j & 1][q2][ld_row] = m_dlt[q2];
+      }
   };
 
   TrAddr ta;
   ta.init(lane);
   f32x16 accK[2] = {f32x16{}, f32x16{}}, accV[2] = {f32x16{}, f32x16{}};
 
-  if (n_tiles > 0) {
+  if (n_steps > 0) {
     load(0);
     store_meta(0);
   }
   wait_vm0();
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < n_tiles) load(t + 1);
+  for (int j = 0; j < n_steps; ++j) {
+    const int st = j & 1, t = KS * j + kq;
+    if (j + 1 < n_steps) load(j + 1);
     // The tile's rows reach one of this wave's keys; a band tile whose rows
     // all score all of them needs no mask (rlo and rhi are non-decreasing;
     // rows taking no part carry lse +inf, gathered global rows score every
     // key, and keys before the first chunk are global: their lanes are not
     // stored).
-    bool act = ka < n_keys, full = true;
+    bool act = ka < n_keys && t < n_tiles, full = true;
     if (!gk && t < n_band) {
       const int u0 = q_lo + 32 * t, u1 = min(u0 + 31, q_hi);
       const int kb = min(ka + 31, n_keys - 1), kf = ka > kfirst ? ka : kfirst;
@@ -521,14 +537,14 @@ void bwd_keys_kernel(BwdArgs a) {
       // s = q.k - lse / scale and dp = dO.v - Delta.
       f32x16 s0, d0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 l4 = *(const float4*)&sm.nls[st][8 * j + 4 * hi];
-        const float4 d4 = *(const float4*)&sm.ndl[st][8 * j + 4 * hi];
-        s0[4 * j] = l4.x; s0[4 * j + 1] = l4.y; s0[4 * j + 2] = l4.z; s0[4 * j + 3] = l4.w;
-        d0[4 * j] = d4.x; d0[4 * j + 1] = d4.y; d0[4 * j + 2] = d4.z; d0[4 * j + 3] = d4.w;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 l4 = *(const float4*)&sm.nls[st][kq][8 * i4 + 4 * hi];
+        const float4 d4 = *(const float4*)&sm.ndl[st][kq][8 * i4 + 4 * hi];
+        s0[4 * i4] = l4.x; s0[4 * i4 + 1] = l4.y; s0[4 * i4 + 2] = l4.z; s0[4 * i4 + 3] = l4.w;
+        d0[4 * i4] = d4.x; d0[4 * i4 + 1] = d4.y; d0[4 * i4 + 2] = d4.z; d0[4 * i4 + 3] = d4.w;
       }
-      const f32x16 s = rows_mfma(sm.x[st], l32, hi, kr, s0);
-      const f32x16 dp = rows_mfma(sm.y[st], l32, hi, vr, d0);
+      const f32x16 s = rows_mfma(sm.x[st][kq], l32, hi, kr, s0);
+      const f32x16 dp = rows_mfma(sm.y[st][kq], l32, hi, vr, d0);
       unsigned pw[8], dsw[8];
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
@@ -546,19 +562,40 @@ void bwd_keys_kernel(BwdArgs a) {
         pw[i / 2] = pack2(p2[0], p2[1]);
         dsw[i / 2] = pack2(ds2[0], ds2[1]);
       }
-      const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st];
-      const unsigned yb = (unsigned)(uintptr_t)(LDS_AS void*)sm.y[st];
+      const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
+      const unsigned yb = (unsigned)(uintptr_t)(LDS_AS void*)sm.y[st][kq];
       tr_mfma(yb, ta, pw, accV);   // dV^T += dO^T P
       tr_mfma(xb, ta, dsw, accK);  // dK^T += Q^T dS
     }
-    if (t + 1 < n_tiles) store_meta(1 - st);
+    if (j + 1 < n_steps) store_meta(j + 1);
     wait_vm0();
     __syncthreads();
   }
+  if (KS == 2) {
+    // As on the row side, for dK (in the x half of the ring) and dV (y).
+    float* rk = (float*)&sm.x[0][0][0];
+    float* rv = (float*)&sm.y[0][0][0];
+    if (kq == 1)
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        rk[(32 * rb + e) * 64 + lane] = accK[e >> 4][e & 15];
+        rv[(32 * rb + e) * 64 + lane] = accV[e >> 4][e & 15];
+      }
+    __syncthreads();
+    if (kq == 1) return;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      accK[e >> 4][e & 15] += rk[(32 * rb + e) * 64 + lane];
+      accV[e >> 4][e & 15] += rv[(32 * rb + e) * 64 + lane];
+    }
+  }
 
   if (!key_band) return;
-  float* dk = a.dK + base + (size_t)pos_k * kBD;
-  float* dv = a.dV + base + (size_t)pos_k * kBD;
+  // Band key: its dK, dV.  Global-key item: the chunk's partials of slot k.
+  const size_t plane = (size_t)a.n_bh * a.n_gch * a.n_glob * kBD;
+  float* dk = gk ? a.gpart + plane + (((size_t)w.bh * a.n_gch + t0) * a.n_glob + k) * kBD
+                 : a.dK + base + (size_t)pos_k * kBD;
+  float* dv = gk ? dk + plane : a.dV + base + (size_t)pos_k * kBD;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -568,34 +605,45 @@ void bwd_keys_kernel(BwdArgs a) {
                                     a.scale * accK[b][4 * g4 + 2], a.scale * accK[b][4 * g4 + 3]);
       const float4 vv = make_float4(accV[b][4 * g4], accV[b][4 * g4 + 1], accV[b][4 * g4 + 2],
                                     accV[b][4 * g4 + 3]);
-      if (gk) {
-        unsafeAtomicAdd(dk + c, kv.x);
-        unsafeAtomicAdd(dk + c + 1, kv.y);
-        unsafeAtomicAdd(dk + c + 2, kv.z);
-        unsafeAtomicAdd(dk + c + 3, kv.w);
-        unsafeAtomicAdd(dv + c, vv.x);
-        unsafeAtomicAdd(dv + c + 1, vv.y);
-        unsafeAtomicAdd(dv + c + 2, vv.z);
-        unsafeAtomicAdd(dv + c + 3, vv.w);
-      } else {
-        *(float4*)(dk + c) = kv;
-        *(float4*)(dv + c) = vv;
-      }
+      *(float4*)(dk + c) = kv;
+      *(float4*)(dv + c) = vv;
     }
 }
 
 }  // namespace
 
-hipError_t launch_backward_bf16(const BwdArgs& a, int n_wg, hipStream_t s, const Timing* t) {
-  if (a.D != kBD) return hipErrorInvalidValue;
-  if (a.n_glob > kGCap) return hipErrorInvalidValue;
-  const long long n_rows = (long long)a.n_bh * a.N;
-  hipError_t e = launch_kernel(bwd_prep_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256),
-                               s, a, t[0]);
-  if (e != hipSuccess || n_wg <= 0) return e;
-  e = launch_kernel(bwd_rows_kernel, dim3(n_wg), dim3(256), s, a, t[1]);
+// ---------------------------------------------------------------------------
+// Global rows and keys: the sums of the chunks' partial gradients.
+// ---------------------------------------------------------------------------
+// One workgroup per (b*h, global slot), 192 threads: plane (dQ, dK, dV) and
+// column; each adds the slot's partials over the chunks and writes the row.
+__global__ __launch_bounds__(192) void bwd_merge_kernel(BwdArgs a) {
+  const int bh = blockIdx.x / a.n_glob, g = blockIdx.x % a.n_glob;
+  const int2 gs = a.gsel[bh / a.H];
+  if (g >= gs.y) return;
+  const int pl = threadIdx.x >> 6, col = threadIdx.x & 63;
+  const size_t plane = (size_t)a.n_bh * a.n_gch * a.n_glob * kBD;
+  const float* src = a.gpart + pl * plane + ((size_t)bh * a.n_gch * a.n_glob + g) * kBD + col;
+  float sum = 0.0f;
+#pragma unroll 8
+  for (int ch = 0; ch < a.n_gch; ++ch) sum += src[(size_t)ch * a.n_glob * kBD];
+  float* dst = pl == 0 ? a.dQ : (pl == 1 ? a.dK : a.dV);
+  dst[((size_t)bh * a.N + a.glob[gs.x + g]) * kBD + col] = sum;
+}
+
+hipError_t launch_backward_bf16(const BwdArgs& rows, const BwdArgs& keys, int n_rows_wg,
+                                int n_keys_wg, hipStream_t s, const Timing* t) {
+  for (const BwdArgs* a : {&rows, &keys})
+    if (a->D != kBD || a->n_glob > kGCap || (a->ks != 1 && a->ks != 2)) return hipErrorInvalidValue;
+  if (n_rows_wg <= 0 || n_keys_wg <= 0) return hipSuccess;
+  hipError_t e = launch_kernel(rows.ks == 2 ? bwd_rows_kernel<2> : bwd_rows_kernel<1>,
+                               dim3(n_rows_wg), dim3(256), s, rows, t[0]);
   if (e != hipSuccess) return e;
-  return launch_kernel(bwd_keys_kernel, dim3(n_wg), dim3(256), s, a, t[2]);
+  e = launch_kernel(keys.ks == 2 ? bwd_keys_kernel<2> : bwd_keys_kernel<1>, dim3(n_keys_wg),
+                    dim3(256), s, keys, t[1]);
+  if (e != hipSuccess || keys.n_glob <= 0) return e;
+  return launch_kernel(bwd_merge_kernel, dim3((unsigned)(keys.n_bh * keys.n_glob)), dim3(192), s,
+                       keys, t[2]);
 }
 
 }  // namespace lfattn

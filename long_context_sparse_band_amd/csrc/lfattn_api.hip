@@ -24,7 +24,7 @@ constexpr int kMaxTimedForwards = 4096;
 // Timing events per forward: band start/stop, global partials start/stop,
 // merge start/stop.
 constexpr int kEvPerForward = 6;
-// ... and per backward: prep, rows and keys kernels, start/stop each.
+// ... and per backward: rows, keys and merge kernels, start/stop each.
 constexpr int kMaxTimedBackwards = 1024;
 constexpr int kEvPerBackward = 6;
 constexpr int kXcds = 8;           // MI355X: workgroups go round-robin over 8 XCDs
@@ -47,7 +47,10 @@ constexpr int kWideRounds = 2;
 constexpr int kSpreadRounds = 4;
 // Backward work items: rows or keys per item, and the key or row chunk of a
 // global item.
-constexpr int kBwdRows = 128, kBwdChunk = 512;
+constexpr int kBwdChunk = 512;
+// At most this many chunks per global set (longer chunks past 32768 keys),
+// bounding the partial-gradient workspace.
+constexpr int kBwdMaxChunks = 64;
 constexpr long long kMaxN = 1LL << 29;
 
 }  // namespace
@@ -71,9 +74,11 @@ struct lfattn_ctx {
 
   BandWork* d_work = nullptr;
   // Backward pass (bf16, D = 64): its work table and the per-row Delta.
-  BandWork* d_bwork = nullptr;
-  int n_bwork = 0;
+  BandWork* d_bwork = nullptr;  // backward tables: row side, then key side
+  int n_bwork[2] = {0, 0};
   float* d_delta = nullptr;
+  float* d_gpart = nullptr;  // backward: global items' partial gradients
+  int n_gch = 0;             // backward: key (row) chunks of a global item
   int n_band_wg = 0;
   int* d_glob = nullptr;           // the distinct lists, one after another
   int2* d_gsel = nullptr;          // [B]: (offset, length) of each batch element's list
@@ -81,6 +86,8 @@ struct lfattn_ctx {
 
   float* d_part = nullptr;
   int band_rows = 0;  // rows per band workgroup
+  int bwd_rows[2] = {0, 0};  // rows (keys) per backward item, row / key side: 64 or 128
+  int bwd_chunk = 0;  // keys (rows) per chunk of a backward global item
   int g_waves = 0, g_rows = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
   bool glob_items = false;  // global-row partials run as items of the band launch
 
@@ -114,6 +121,7 @@ void free_ctx(lfattn_ctx* c) {
   (void)hipFree(c->d_part);
   (void)hipFree(c->d_bwork);
   (void)hipFree(c->d_delta);
+  (void)hipFree(c->d_gpart);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->bev) (void)hipEventDestroy(e);
   delete c;
@@ -293,6 +301,20 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   }
   c->band_rows = band_rows;
 
+  // Rows (keys) per backward item: the row side takes 64 (each workgroup's
+  // key tiles split between two pairs of wavefronts), the key side 128 (one
+  // row-tile stream shared by four 32-key blocks), the faster choice of each
+  // on the bf16 workloads measured; LFATTN_BWD_ROWS=64 or 128 sets both (both
+  // give the same results; this lets the tests run every kernel).
+  if (dtype == LFATTN_BF16 && D == 64) {
+    c->bwd_rows[0] = 64;
+    c->bwd_rows[1] = 128;
+    if (const char* e = std::getenv("LFATTN_BWD_ROWS")) {
+      if (std::strcmp(e, "64") == 0) c->bwd_rows[0] = c->bwd_rows[1] = 64;
+      if (std::strcmp(e, "128") == 0) c->bwd_rows[0] = c->bwd_rows[1] = 128;
+    }
+  }
+
   // Band work: one item per workgroup's rows of each (b, h, residue r)
   // subsequence, laid out so that the items the hardware sends to one XCD
   // (blockIdx congruent mod 8) are consecutive query blocks of the same head,
@@ -413,29 +435,36 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   if (table.size() > (size_t)INT32_MAX) { free_ctx(c); return LFATTN_EUNSUPPORTED; }
   c->n_band_wg = (int)table.size();
 
-  // Backward work (bf16, D = 64): band items of kBwdRows rows (row side) or
-  // keys (key side) per (b, h, residue), then items of kBwdRows global
-  // positions against a chunk of kBwdChunk keys (row side) or rows (key side).
+  // Backward work (bf16, D = 64), one table per side: band items of
+  // bwd_rows rows (row side) or keys (key side) per (b, h, residue), then
+  // items of bwd_rows global positions against a chunk of bwd_chunk keys
+  // (row side) or rows (key side).
   std::vector<BandWork> btable;
   const bool has_bwd = dtype == LFATTN_BF16 && D == 64;
   if (has_bwd) {
-    for (int bh = 0; bh < B * H; ++bh) {
-      const int d = c->dil[bh % H], b = bh / H;
-      for (int r = 0; r < d && r < N; ++r) {
-        const int Lr = (N - r + d - 1) / d;
-        for (int t0 = 0; t0 < Lr; t0 += kBwdRows)
-          btable.push_back(BandWork{bh, r, t0, d, gsel[b].x, gsel[b].y, b, 0});
+    c->bwd_chunk = std::max(kBwdChunk, (N + kBwdMaxChunks * 32 - 1) / (kBwdMaxChunks * 32) * 32);
+    c->n_gch = (N + c->bwd_chunk - 1) / c->bwd_chunk;
+    for (int side = 0; side < 2; ++side) {
+      const int rows = c->bwd_rows[side];
+      const size_t start = btable.size();
+      for (int bh = 0; bh < B * H; ++bh) {
+        const int d = c->dil[bh % H], b = bh / H;
+        for (int r = 0; r < d && r < N; ++r) {
+          const int Lr = (N - r + d - 1) / d;
+          for (int t0 = 0; t0 < Lr; t0 += rows)
+            btable.push_back(BandWork{bh, r, t0, d, gsel[b].x, gsel[b].y, b, 0});
+        }
       }
+      for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H;
+        const int sets_b = (gsel[b].y + rows - 1) / rows;
+        for (int set = 0; set < sets_b; ++set)
+          for (int ch = 0; ch < c->n_gch; ++ch)
+            btable.push_back(BandWork{bh, set, ch, 0, gsel[b].x, gsel[b].y, b, 0});
+      }
+      if (btable.size() - start > (size_t)INT32_MAX) { free_ctx(c); return LFATTN_EUNSUPPORTED; }
+      c->n_bwork[side] = (int)(btable.size() - start);
     }
-    for (int bh = 0; bh < B * H; ++bh) {
-      const int b = bh / H;
-      const int sets_b = (gsel[b].y + kBwdRows - 1) / kBwdRows;
-      for (int set = 0; set < sets_b; ++set)
-        for (int ch = 0; ch < (N + kBwdChunk - 1) / kBwdChunk; ++ch)
-          btable.push_back(BandWork{bh, set, ch, 0, gsel[b].x, gsel[b].y, b, 0});
-    }
-    if (btable.size() > (size_t)INT32_MAX) { free_ctx(c); return LFATTN_EUNSUPPORTED; }
-    c->n_bwork = (int)btable.size();
   }
 
   // ---- device state ----
@@ -449,7 +478,10 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
     return st;
   }
   if (has_bwd && ((st = dev_alloc(&c->d_bwork, btable.size())) != LFATTN_OK ||
-                   (st = dev_alloc(&c->d_delta, (size_t)B * H * N)) != LFATTN_OK)) {
+                   (st = dev_alloc(&c->d_delta, (size_t)B * H * N)) != LFATTN_OK ||
+                   (n_g > 0 &&
+                    (st = dev_alloc(&c->d_gpart, (size_t)3 * B * H * c->n_gch * n_g * D)) !=
+                        LFATTN_OK))) {
     free_ctx(c);
     return st;
   }
@@ -683,18 +715,26 @@ lfattn_status lfattn_backward(lfattn_t c, const void* Q, const void* K, const vo
   lfattn::BwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.lse = LSE; a.delta = c->d_delta;
   a.dQ = dQ; a.dK = dK; a.dV = dV;
-  a.work = c->d_bwork; a.glob = c->d_glob; a.is_glob = c->d_isglob;
+  a.glob = c->d_glob; a.is_glob = c->d_isglob;
   a.isg_stride = c->shared ? 0 : c->N;
   a.H = c->H; a.N = c->N; a.D = c->D; a.n_bh = c->B * c->H;
   a.hw = c->hw; a.hr = c->causal ? 0 : c->hw; a.chunk = c->chunk; a.cbase = c->n_memory;
-  a.chunk_keys = kBwdChunk; a.n_glob = c->n_gmax;
+  a.chunk_keys = c->bwd_chunk; a.n_glob = c->n_gmax;
+  a.gpart = c->d_gpart; a.n_gch = c->n_gch; a.gsel = c->d_gsel;
   a.scale = c->scale; a.sl2 = c->scale * 1.4426950408889634f;
+  // The key side: the same arguments with its own table and item size.
+  lfattn::BwdArgs ak = a;
+  a.work = c->d_bwork;
+  a.ks = c->bwd_rows[0] == 64 ? 2 : 1;
+  ak.work = c->d_bwork + c->n_bwork[0];
+  ak.ks = c->bwd_rows[1] == 64 ? 2 : 1;
   lfattn::Timing t[3];
   if (c->timing && c->n_btimed < kMaxTimedBackwards) {
     hipEvent_t* e = &c->bev[kEvPerBackward * c->n_btimed++];
     for (int x = 0; x < 3; ++x) t[x] = {e[2 * x], e[2 * x + 1]};
   }
-  if (lfattn::launch_backward_bf16(a, c->n_bwork, stream, t) != hipSuccess) return LFATTN_EHIP;
+  if (lfattn::launch_backward_bf16(a, ak, c->n_bwork[0], c->n_bwork[1], stream, t) != hipSuccess)
+    return LFATTN_EHIP;
   return LFATTN_OK;
 }
 
@@ -787,26 +827,29 @@ lfattn_status lfattn_read_timing(lfattn_t c, double* band_ms, double* global_ms,
   return LFATTN_OK;
 }
 
-lfattn_status lfattn_read_backward_timing(lfattn_t c, double* prep_ms, double* rows_ms,
-                                          double* keys_ms, int* n_backwards) {
-  if (!c || !prep_ms || !rows_ms || !keys_ms || !n_backwards) return LFATTN_EINVAL;
+lfattn_status lfattn_read_backward_timing(lfattn_t c, double* rows_ms, double* keys_ms,
+                                          double* merge_ms, int* n_backwards) {
+  if (!c || !rows_ms || !keys_ms || !merge_ms || !n_backwards) return LFATTN_EINVAL;
   double sum[3] = {0.0, 0.0, 0.0};
-  if (c->n_btimed > 0 &&
-      hipEventSynchronize(c->bev[kEvPerBackward * c->n_btimed - 1]) != hipSuccess)
+  // Kernels that a call does not launch record no events: none without work
+  // items (an empty problem), the merge without global positions.
+  const bool run = c->n_bwork[0] > 0 && c->n_bwork[1] > 0;
+  const int n_k = !run ? 0 : (c->n_gmax > 0 ? 3 : 2);
+  if (c->n_btimed > 0 && n_k > 0 &&
+      hipEventSynchronize(c->bev[kEvPerBackward * (c->n_btimed - 1) + 2 * n_k - 1]) !=
+          hipSuccess)
     return LFATTN_EHIP;
   for (int t = 0; t < c->n_btimed; ++t) {
     hipEvent_t* e = &c->bev[kEvPerBackward * t];
-    for (int x = 0; x < 3; ++x) {
+    for (int x = 0; x < n_k; ++x) {
       float ms = 0.0f;
-      // A launch with no work items records no rows/keys events.
-      if (x > 0 && c->n_bwork <= 0) continue;
       if (hipEventElapsedTime(&ms, e[2 * x], e[2 * x + 1]) != hipSuccess) return LFATTN_EHIP;
       sum[x] += ms;
     }
   }
-  *prep_ms = sum[0];
-  *rows_ms = sum[1];
-  *keys_ms = sum[2];
+  *rows_ms = sum[0];
+  *keys_ms = sum[1];
+  *merge_ms = sum[2];
   *n_backwards = c->n_btimed;
   c->n_btimed = 0;
   return LFATTN_OK;

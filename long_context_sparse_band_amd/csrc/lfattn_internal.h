@@ -94,7 +94,7 @@ struct BwdArgs {
   const void* O;
   const void* dO;
   const float* lse;            // [B, H, N] natural log-sum-exp from the forward
-  float* delta;                // [B, H, N] workspace: dO . O per row
+  float* delta;                // [B, H, N] workspace: dO . O per row (row side writes it)
   float* dQ;                   // [B, H, N, D] fp32 outputs
   float* dK;
   float* dV;
@@ -103,7 +103,14 @@ struct BwdArgs {
   const unsigned char* is_glob;
   long long isg_stride;
   int H, N, D, n_bh, hw, hr, chunk, cbase, chunk_keys, n_glob;
+  int ks;                      // 1: 128 rows (keys) per item; 2: 64, tiles split in two
   float sl2, scale;
+  // Global items' partial gradients, three planes (dQ, dK, dV) of
+  // [B*H][n_gch chunks][n_glob][D] fp32, summed by the merge kernel; gsel:
+  // (offset, length) of each batch element's global list.
+  float* gpart;
+  int n_gch;
+  const int2* gsel;
 };
 
 // Optional events around one launch: start and stop take the kernel's own
@@ -133,7 +140,10 @@ int band_workgroups_per_cu(int dtype, int D);
 hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s,
                        const Timing& t);
 hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s, const Timing& t);
-// t: events around the prep, rows and keys kernels (null events: untimed).
-hipError_t launch_backward_bf16(const BwdArgs& a, int n_wg, hipStream_t s, const Timing t[3]);
+// The row-side and key-side launches take their own work tables (rows.work,
+// keys.work; n_*_wg items); t: events around the rows, keys and merge
+// kernels (null events: untimed).
+hipError_t launch_backward_bf16(const BwdArgs& rows, const BwdArgs& keys, int n_rows_wg,
+                                int n_keys_wg, hipStream_t s, const Timing t[3]);
 
 }  // namespace lfattn

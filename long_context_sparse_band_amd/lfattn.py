@@ -272,7 +272,7 @@ def lfattn_read_timing(handle: int):
 
 
 def lfattn_read_backward_timing(handle: int):
-    """(prep_ms_total, rows_ms_total, keys_ms_total, n_backwards) of the
+    """(rows_ms_total, keys_ms_total, merge_ms_total, n_backwards) of the
     backward calls since timing was enabled/read."""
     t = [ctypes.c_double() for _ in range(3)]
     n = ctypes.c_int()

@@ -61,7 +61,10 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0] + "_N%d" % c[1]["N"])
 def test_backward_every_element(case, rows_mode, monkeypatch):
     import torch
+    # Both forward band kernels (the log-sum-exp) and both backward item
+    # sizes (64 rows with split tiles, 128 rows with one tile stream).
     monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows_mode))
+    monkeypatch.setenv("LFATTN_BWD_ROWS", str(rows_mode))
     kind, p = case
     B, H, N, D = p["B"], p["H"], p["N"], 64
     a = W.small_case(B, H, N, D, "bf16", p.get("window", 0), dilation=p.get("dil"), seed=88)
@@ -104,11 +107,13 @@ def test_backward_every_element(case, rows_mode, monkeypatch):
 FULL = ["longformer_base_n4096", "dilated_charlm_n8192", "gmat_memory_m64_l16384"]
 
 
+@pytest.mark.parametrize("bwd_rows", [64, 128])
 @pytest.mark.parametrize("name", FULL)
-def test_backward_full_size_sampled_heads(name):
+def test_backward_full_size_sampled_heads(name, bwd_rows, monkeypatch):
     """At the full sizes: the whole launch over every head, checked element
     by element on the first and last heads (heads are independent)."""
     import torch
+    monkeypatch.setenv("LFATTN_BWD_ROWS", str(bwd_rows))
     wl = W.BY_NAME[name]
     a = W.generate(wl)
     B, H, N, D = wl.B, wl.H, wl.N, wl.D
@@ -153,8 +158,8 @@ def test_backward_timing_records_each_call():
         L.lfattn_set_timing(h, True)
         for _ in range(3):
             L.lfattn_backward(h, q, k, v, o, q, lse, dq, dk, dv)
-        prep, rows, keys, n = L.lfattn_read_backward_timing(h)
-        assert n == 3 and prep > 0 and rows > 0 and keys > 0
+        rows, keys, merge, n = L.lfattn_read_backward_timing(h)
+        assert n == 3 and rows > 0 and keys > 0 and merge > 0
         assert L.lfattn_read_backward_timing(h)[3] == 0
         L.lfattn_set_timing(h, False)
     finally:
