@@ -66,6 +66,27 @@ def band_source_hash():
         return hashlib.sha256(f.read()).hexdigest()
 
 
+BWD_SOURCE = os.path.join(ROOT, "long_context_sparse_band_amd", "csrc", "backward_bf16.hip")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_backward.json")
+
+
+def recorded_backward_traffic(workload):
+    """HBM bytes per key-side backward launch from the recorded counter runs,
+    or None when they were taken on a different kernel source."""
+    import hashlib
+    try:
+        with open(BWD_TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(BWD_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry or rec.get("source_sha256") != sha:
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
 def recorded_traffic(workload):
     """HBM bytes per band-kernel launch from the recorded FETCH_SIZE/WRITE_SIZE
     counter runs, or None when they were taken on a different kernel source."""
@@ -227,8 +248,10 @@ def bench_backward(args, wl, inp, L, torch):
         "rows_kernel": {"achieved": rows_tf, "frac": rows_tf / peak,
                         "flops_per_launch": pairs * 6 * D},
         "roofline": {"kernel": "bwd_keys_kernel", "bound": "mfma", "achieved": keys_tf,
-                     "peak": peak, "unit": "TFLOP/s", "frac": keys_tf / peak, "traffic": None,
-                     "algorithmic_flops_per_launch": pairs * 8 * D},
+                     "peak": peak, "unit": "TFLOP/s", "frac": keys_tf / peak,
+                     "traffic": recorded_backward_traffic(wl.name),
+                     "algorithmic_flops_per_launch": pairs * 8 * D,
+                     "ideal_bytes_per_launch": wl.B * wl.H * wl.N * 16 * D},
     }
     print(json.dumps(line), flush=True)
 
