@@ -253,7 +253,28 @@ def bench_backward(args, wl, inp, L, torch):
                      "algorithmic_flops_per_launch": pairs * 8 * D,
                      "ideal_bytes_per_launch": wl.B * wl.H * wl.N * 16 * D},
     }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_backward(inp, wl, g.float().cpu().numpy(), pairs)
     print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_backward(inp, wl, do, pairs):
+    """The gradient oracle as it stands, on this host's cores, over the whole
+    workload (repeated until at least 5 s have passed)."""
+    import oracle
+    threads = os.cpu_count() or 1
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention_grad(inp.q, inp.k, inp.v, do, window=wl.window,
+                              dilation=list(inp.dilation), glob=list(inp.glob), nthreads=threads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= 5.0:
+            break
+    return {"value": pairs * passes / el, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "sample": f"the gradients of the whole {wl.name} workload, {passes} pass(es) in "
+                      f"{el:.2f} s, double precision, {threads} threads",
+            "cpu_model": cpu_model()}
 
 
 def main():

@@ -164,3 +164,43 @@ def test_backward_timing_records_each_call():
         L.lfattn_set_timing(h, False)
     finally:
         L.lfattn_destroy(h)
+
+
+def test_backward_rejects_bad_arguments():
+    """Error paths, all taken before any kernel launch: handles the backward
+    does not support, misaligned pointers, outputs overlapping an input or
+    each other."""
+    import torch
+    dev = "cuda:0"
+    B, H, N = 1, 1, 64
+    for dtype, D in ((L.LFATTN_F32, 64), (L.LFATTN_BF16, 128)):
+        h = L.lfattn_create(B, H, N, D, dtype, 8, None, [0])
+        try:
+            t = torch.zeros((B, H, N, D), dtype=torch.float32, device=dev)
+            lse = torch.zeros((B, H, N), dtype=torch.float32, device=dev)
+            g = [torch.zeros_like(t) for _ in range(3)]
+            with pytest.raises(L.LfattnError) as e:
+                L.lfattn_backward(h, t, t, t, t, t, lse, *g)
+            assert e.value.status == L.LFATTN_EUNSUPPORTED
+        finally:
+            L.lfattn_destroy(h)
+    D = 64
+    h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, 8, None, [0])
+    try:
+        x = torch.zeros((B, H, N, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.zeros((B, H, N), dtype=torch.float32, device=dev)
+        outs = [torch.zeros((B, H, N, D), dtype=torch.float32, device=dev) for _ in range(3)]
+        buf = torch.zeros(B * H * N * D + 8, dtype=torch.bfloat16, device=dev)
+        say("backward argument checks")
+        cases = [
+            ("misaligned input", (buf.data_ptr() + 2, x, x, x, x, lse, *outs)),
+            ("dQ overlaps dK", (x, x, x, x, x, lse, outs[0], outs[0], outs[2])),
+            ("dV overlaps the log-sum-exp", (x, x, x, x, x, outs[2], outs[0], outs[1], outs[2])),
+            ("null dK", (x, x, x, x, x, lse, outs[0], None, outs[2])),
+        ]
+        for what, args in cases:
+            with pytest.raises(L.LfattnError) as e:
+                L.lfattn_backward(h, *args)
+            assert e.value.status == L.LFATTN_EINVAL, what
+    finally:
+        L.lfattn_destroy(h)
