@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 from long_context_sparse_band_amd import lfattn as L
@@ -161,3 +162,16 @@ def test_binding_raises_on_missing_library(tmp_path, monkeypatch):
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(FileNotFoundError):
         L.load()
+
+
+def test_bf16_global_limit_checked_before_any_hip_call():
+    """bf16 handles take at most 512 distinct global positions; one more is
+    refused with LFATTN_EUNSUPPORTED before the library touches the GPU."""
+    with pytest.raises(L.LfattnError) as e:
+        L.lfattn_create(1, 1, 1000, 64, L.LFATTN_BF16, 16, None, list(range(513)))
+    assert e.value.status == L.LFATTN_EUNSUPPORTED
+    mask = np.zeros((2, 1000), dtype=np.uint8)
+    mask[1, :513] = 1
+    with pytest.raises(L.LfattnError) as e:
+        L.lfattn_create_masked(2, 1, 1000, 64, L.LFATTN_BF16, 16, None, mask)
+    assert e.value.status == L.LFATTN_EUNSUPPORTED

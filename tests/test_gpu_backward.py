@@ -204,3 +204,38 @@ def test_backward_rejects_bad_arguments():
             assert e.value.status == L.LFATTN_EINVAL, what
     finally:
         L.lfattn_destroy(h)
+
+
+@pytest.mark.parametrize("rows_mode", [64, 128])
+def test_forward_and_backward_at_the_global_limit(rows_mode, monkeypatch):
+    """512 distinct global positions (the bf16 maximum), seeded and spread
+    over a 1200-token sequence with dilation: forward output and all three
+    gradients element by element."""
+    import torch
+    monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows_mode))
+    monkeypatch.setenv("LFATTN_BWD_ROWS", str(rows_mode))
+    B, H, N, D, window, dil = 1, 2, 1200, 64, 48, [1, 3]
+    rng = np.random.default_rng(90)
+    glob = sorted(rng.choice(N, size=512, replace=False).tolist())
+    a = W.small_case(B, H, N, D, "bf16", window, dilation=dil, glob=glob, seed=91)
+    do = _bf16(rng.standard_normal((B, H, N, D)).astype(np.float32))
+    h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, window, dil, glob)
+    try:
+        q, k, v = to_device(a)
+        g = torch.from_numpy(do).to("cuda:0").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        dq, dk, dv = (torch.full((B, H, N, D), float("nan"), dtype=torch.float32,
+                                 device=q.device) for _ in range(3))
+        say(f"forward + backward with 512 global positions, rows {rows_mode}")
+        L.lfattn_forward_lse(h, q, k, v, o, lse)
+        L.lfattn_backward(h, q, k, v, o, g, lse, dq, dk, dv)
+        torch.cuda.synchronize()
+    finally:
+        L.lfattn_destroy(h)
+    want_o = oracle.attention(a.q, a.k, a.v, window, dil, glob)
+    err = np.abs(o.float().cpu().numpy().astype(np.float64) - want_o)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+    want = oracle.attention_grad(a.q, a.k, a.v, do, window=window, dilation=dil, glob=glob)
+    for x, w, n in zip((dq, dk, dv), want, ("dq", "dk", "dv")):
+        check(x.cpu().numpy().astype(np.float64), w, f"512 globals {n}")
