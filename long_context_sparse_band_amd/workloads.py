@@ -2,7 +2,7 @@
 
 This module only makes inputs: shapes, seeds, random Q/K/V and the pattern
 parameters (window, per-head dilation, global positions).  It holds none of the
-attention arithmetic, imports neither the GPU library nor the CPU checker, and
+attention arithmetic, imports neither the GPU library nor the CPU oracle, and
 serves both.
 
 The shapes stand in for the pages' workloads, whose datasets and trained
