@@ -194,8 +194,10 @@ lfattn_status lfattn_forward_lse(lfattn_t ctx, const void* Q, const void* K, con
  *   dS_ij = P_ij (dO_i . V_j - dO_i . O_i),   dQ_i = scale sum_j dS_ij K_j,
  *   dK_j = scale sum_i dS_ij Q_i,            dV_j = sum_i P_ij dO_i.
  * bf16 handles with D = 64 only (EUNSUPPORTED otherwise), every pattern.
- * Allocates nothing; the handle's workspace holds dO . O per row.  Sums over
- * global rows and keys use atomics, so their last bits vary between runs.
+ * Allocates nothing; the handle's workspace holds dO . O per row and the
+ * global rows' and keys' partial gradients per key (row) chunk, summed in a
+ * fixed order: results are the same bits on every run.  Launches kernels
+ * only, so the call may be captured into a HIP graph.
  */
 lfattn_status lfattn_backward(lfattn_t ctx, const void* Q, const void* K, const void* V,
                               const void* O, const void* dO, const float* LSE, float* dQ,

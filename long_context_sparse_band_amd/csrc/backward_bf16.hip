@@ -10,23 +10,24 @@
 //   dQ_i = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij Q_i,  dV_j = sum_i P_ij dO_i.
 //
 // Three launches:
-//  - bwd_rows_kernel (row side, like the forward): a workgroup takes 128 rows
-//    of one (batch, head, residue) and walks the 32-key tiles of their band,
+//  - bwd_rows_kernel (row side, like the forward): a workgroup takes 128 (or
+//    64) rows of one (batch, head, residue) and walks the 32-key tiles of
+//    their band,
 //    then the gathered global keys (and Delta = dO . O of its rows, written
 //    for the key side): S^T = K Q^T and dP^T = V dO^T on MFMA,
 //    dS on the vector unit, dQ^T += K^T dS^T on MFMA (K^T read from the
 //    row-major tile with ds_read_b64_tr_b16).  Global-row items (a set of
 //    global rows against a chunk of keys) write partial dQ per chunk.
 //  - bwd_keys_kernel (key side, the roles of queries and keys swapped): a
-//    workgroup takes 128 keys and walks the 32-row tiles of the rows whose
+//    workgroup takes 128 (or 64) keys and walks the 32-row tiles of the rows whose
 //    band holds them, then the gathered global rows: S = Q K^T, dP = dO V^T,
 //    dV^T += dO^T P and dK^T += Q^T dS.  Global-key items (a set of global
 //    keys against a chunk of rows) write partial dK, dV per chunk.
 //  - bwd_merge_kernel: the global rows' dQ and the global keys' dK, dV as
 //    the sums of their chunks' partials (no atomics: deterministic).
-// Tiles go global -> registers -> LDS through a two-stage ring, one barrier
-// per step; the same 16-byte-chunk swizzle as the forward keeps the MFMA
-// operand reads free of bank conflicts.
+// Tiles go global -> LDS directly (global_load_lds_dwordx4) through a
+// two-stage ring, one barrier per step; the same 16-byte-chunk swizzle as
+// the forward keeps the MFMA operand reads free of bank conflicts.
 #include "lfattn_internal.h"
 
 namespace lfattn {

@@ -84,9 +84,9 @@ struct GlobArgs {
 };
 
 // Backward pass (bf16, D = 64): gradients of the band + global attention.
-// The work table holds band items of 128 rows (row side) or keys (key side)
-// and global items of 128 global positions against a chunk of chunk_keys
-// keys (row side) or rows (key side).
+// Each side's work table holds band items of 64 or 128 rows (row side) or
+// keys (key side), ks = 2 or 1, and global items of as many global positions
+// against a chunk of chunk_keys keys (row side) or rows (key side).
 struct BwdArgs {
   const void* Q;
   const void* K;
