@@ -297,6 +297,16 @@ class LFAttention:
             lfattn_forward_global_proj(self.handle, Q, K, V, Qg, Kg, Vg, O, stream)
         return O
 
+    def forward_lse(self, Q, K, V, O, LSE, stream=None):
+        """Forward that also writes each row's log-sum-exp (bf16 handles)."""
+        lfattn_forward_lse(self.handle, Q, K, V, O, LSE, stream)
+        return O, LSE
+
+    def backward(self, Q, K, V, O, dO, LSE, dQ, dK, dV, stream=None):
+        """Gradients into the caller's fp32 dQ, dK, dV (bf16, D = 64 handles)."""
+        lfattn_backward(self.handle, Q, K, V, O, dO, LSE, dQ, dK, dV, stream)
+        return dQ, dK, dV
+
     @property
     def scored_pairs(self) -> int:
         return lfattn_scored_pairs(self.handle)

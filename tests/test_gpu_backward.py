@@ -239,3 +239,26 @@ def test_forward_and_backward_at_the_global_limit(rows_mode, monkeypatch):
     want = oracle.attention_grad(a.q, a.k, a.v, do, window=window, dilation=dil, glob=glob)
     for x, w, n in zip((dq, dk, dv), want, ("dq", "dk", "dv")):
         check(x.cpu().numpy().astype(np.float64), w, f"512 globals {n}")
+
+
+def test_handle_class_forward_lse_and_backward():
+    """The LFAttention class runs the same calls as the functions."""
+    import torch
+    B, H, N, D = 1, 1, 300, 64
+    a = W.small_case(B, H, N, D, "bf16", 64, seed=95)
+    q, k, v = to_device(a)
+    g = q.flip(2).contiguous()
+    f32 = dict(dtype=torch.float32, device=q.device)
+    outs = []
+    with L.LFAttention(B, H, N, D, L.LFATTN_BF16, 64, None, [0, 7]) as att:
+        for _ in range(2):
+            o, lse = att.forward_lse(q, k, v, torch.empty_like(q), torch.empty((B, H, N), **f32))
+            grads = att.backward(q, k, v, o, g, lse,
+                                 *(torch.empty((B, H, N, D), **f32) for _ in range(3)))
+            outs.append((o, lse, *grads))
+    torch.cuda.synchronize()
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+    want = oracle.attention_grad(a.q, a.k, a.v, g.float().cpu().numpy(), window=64, glob=[0, 7])
+    for x, w, n in zip(outs[0][2:], want, ("dq", "dk", "dv")):
+        check(x.cpu().numpy().astype(np.float64), w, f"class {n}")
