@@ -262,3 +262,43 @@ def test_handle_class_forward_lse_and_backward():
     want = oracle.attention_grad(a.q, a.k, a.v, g.float().cpu().numpy(), window=64, glob=[0, 7])
     for x, w, n in zip(outs[0][2:], want, ("dq", "dk", "dv")):
         check(x.cpu().numpy().astype(np.float64), w, f"class {n}")
+
+
+@pytest.mark.parametrize("form", ["causal_dilated_charlm_n8192", "chunked_gmat_m64_l16384"])
+def test_backward_general_forms_full_size_sampled_heads(form):
+    """The causal band at the dilated character-LM shape and GMAT chunked
+    attention ((512 x 32, 64)) at the 16K shape: every head runs, the first
+    and last are checked element by element."""
+    import torch
+    if form.startswith("causal"):
+        wl = W.BY_NAME["dilated_charlm_n8192"]
+    else:
+        wl = W.BY_NAME["gmat_memory_m64_l16384"]
+    a = W.generate(wl)
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    rng = np.random.default_rng(wl.seed + 8)
+    do = _bf16(rng.standard_normal((B, H, N, D)).astype(np.float32))
+    hs = [0, H - 1]
+    if form.startswith("causal"):
+        h = L.lfattn_create_causal(B, H, N, D, L.LFATTN_BF16, wl.window, list(a.dilation))
+        kw = dict(window=wl.window, dilation=[int(a.dilation[x]) for x in hs], causal=True)
+    else:
+        h = L.lfattn_create_chunked(B, H, N, D, L.LFATTN_BF16, 512, len(wl.glob))
+        kw = dict(chunk=512, n_memory=len(wl.glob))
+    try:
+        q, k, v = to_device(a)
+        g = torch.from_numpy(do).to("cuda:0").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        dq, dk, dv = (torch.full((B, H, N, D), float("nan"), dtype=torch.float32,
+                                 device=q.device) for _ in range(3))
+        say(f"backward full size, {form}")
+        L.lfattn_forward_lse(h, q, k, v, o, lse)
+        L.lfattn_backward(h, q, k, v, o, g, lse, dq, dk, dv)
+        torch.cuda.synchronize()
+    finally:
+        L.lfattn_destroy(h)
+    want = oracle.attention_grad(a.q[:, hs], a.k[:, hs], a.v[:, hs], do[:, hs], **kw)
+    for x, w, n in zip((dq, dk, dv), want, ("dq", "dk", "dv")):
+        assert np.all(np.isfinite(x.cpu().numpy())), f"{form} {n}: non-finite"
+        say(f"  {n}: {check(x[:, hs].cpu().numpy().astype(np.float64), w, f'{form} {n}')}")
