@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--variant", default="plain",
                    choices=["plain", "global_proj", "two_sequences", "causal", "chunked",
-                            "backward"],
+                            "backward", "backward_causal", "backward_chunked"],
                    help="global_proj: the global rows take their own projections (a second "
                         "seeded Q, K, V); two_sequences: B = 2 with a different global set per "
                         "sequence ([CLS] + 10 seeded positions for the second), and own "
@@ -49,7 +49,9 @@ def parse():
                         "chunks of --chunk keys after the workload's memory tokens "
                         "(gmat_memory_m64_l16384: (512 x 32, 64)); backward: one step is "
                         "lfattn_backward (dQ, dK, dV from a seeded upstream gradient, bf16 "
-                        "D 64 workloads) after one untimed lfattn_forward_lse")
+                        "D 64 workloads) after one untimed lfattn_forward_lse; backward_causal, "
+                        "backward_chunked: the same for the causal band and chunked attention "
+                        "(same workload conditions as causal and chunked)")
     p.add_argument("--chunk", type=int, default=512, help="chunk length of --variant chunked")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
@@ -200,8 +202,16 @@ def bench_backward(args, wl, inp, L, torch):
     lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.empty((wl.B, wl.H, wl.N, wl.D), dtype=torch.float32, device=dev)
                   for _ in range(3))
-    h = L.lfattn_create(wl.B, wl.H, wl.N, wl.D, L.LFATTN_BF16, wl.window, list(inp.dilation),
-                        list(inp.glob))
+    form = args.variant[len("backward_"):] if args.variant != "backward" else "plain"
+    if form == "causal":
+        h = L.lfattn_create_causal(wl.B, wl.H, wl.N, wl.D, L.LFATTN_BF16, wl.window,
+                                   list(inp.dilation))
+    elif form == "chunked":
+        h = L.lfattn_create_chunked(wl.B, wl.H, wl.N, wl.D, L.LFATTN_BF16, args.chunk,
+                                    len(wl.glob))
+    else:
+        h = L.lfattn_create(wl.B, wl.H, wl.N, wl.D, L.LFATTN_BF16, wl.window,
+                            list(inp.dilation), list(inp.glob))
     stream = torch.cuda.current_stream()
     L.lfattn_forward_lse(h, q, k, v, o, lse, stream)
 
@@ -238,8 +248,9 @@ def bench_backward(args, wl, inp, L, torch):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded i.i.d. Gaussian Q, K, V and upstream gradient)",
         "inputs": input_record(inp),
-        "config": {"workload": wl.name, "variant": "backward", "B": wl.B, "H": wl.H,
-                   "N": wl.N, "D": D, "window": wl.window,
+        "config": {"workload": wl.name, "variant": args.variant, "B": wl.B, "H": wl.H,
+                   "N": wl.N, "D": D, "window": None if form == "chunked" else wl.window,
+                   **({"chunk": args.chunk, "n_memory": len(wl.glob)} if form == "chunked" else {}),
                    "dilation": [int(x) for x in inp.dilation], "n_global": len(inp.glob),
                    "scored_pairs": pairs, "parallelism": "single GPU"},
         "whole_backward_tflops": pairs * 10 * D / (ms * 1e-3) / 1e12,
@@ -249,11 +260,11 @@ def bench_backward(args, wl, inp, L, torch):
                         "flops_per_launch": pairs * 6 * D},
         "roofline": {"kernel": "bwd_keys_kernel", "bound": "mfma", "achieved": keys_tf,
                      "peak": peak, "unit": "TFLOP/s", "frac": keys_tf / peak,
-                     "traffic": recorded_backward_traffic(wl.name),
+                     "traffic": recorded_backward_traffic(wl.name) if form == "plain" else None,
                      "algorithmic_flops_per_launch": pairs * 8 * D,
                      "ideal_bytes_per_launch": wl.B * wl.H * wl.N * 16 * D},
     }
-    if not args.no_cpu:
+    if not args.no_cpu and form == "plain":
         line["cpu_baseline"] = cpu_baseline_backward(inp, wl, g.float().cpu().numpy(), pairs)
     print(json.dumps(line), flush=True)
 
@@ -297,22 +308,23 @@ def main():
     import numpy as np
 
     wl = W.BY_NAME[args.workload]
-    if args.variant == "causal" and (wl.glob or wl.n_random_glob):
+    if args.variant in ("causal", "backward_causal") and (wl.glob or wl.n_random_glob):
         print(f"bench.py: --variant causal needs a workload without global tokens; "
               f"{wl.name} has some.", file=sys.stderr)
         sys.exit(2)
-    if args.variant == "chunked" and tuple(wl.glob) != tuple(range(len(wl.glob))):
+    if (args.variant in ("chunked", "backward_chunked")
+            and tuple(wl.glob) != tuple(range(len(wl.glob)))):
         print(f"bench.py: --variant chunked needs memory tokens at 0..M-1; {wl.name} has "
               f"other global positions.", file=sys.stderr)
         sys.exit(2)
-    if args.variant == "backward" and (wl.dtype != "bf16" or wl.D != 64):
+    if args.variant.startswith("backward") and (wl.dtype != "bf16" or wl.D != 64):
         print(f"bench.py: --variant backward runs on bf16 workloads with D 64; {wl.name} "
               f"is {wl.dtype} with D {wl.D}.", file=sys.stderr)
         sys.exit(2)
     if args.variant == "two_sequences":
         wl = dataclasses.replace(wl, B=2)
     inp = W.generate(wl)
-    if args.variant == "backward":
+    if args.variant.startswith("backward"):
         bench_backward(args, wl, inp, L, torch)
         return
     dev = torch.device("cuda:0")
