@@ -72,7 +72,10 @@
  * 32-row blocks), chosen at lfattn_create from the number of row blocks and
  * the device's compute units.  The environment variable LFATTN_BAND_ROWS,
  * set to 64 or 128 when lfattn_create runs, overrides that choice; results
- * are the same either way up to floating-point summation order.
+ * are the same either way up to floating-point summation order.  The
+ * backward (bf16, D = 64) takes 64-row items with split key tiles on its
+ * query side and 128-key items on its key side; LFATTN_BWD_ROWS, 64 or 128
+ * when lfattn_create runs, sets both sides to that size.
  *
  * Errors.  Every entry point returns a status synchronously.  Arguments are
  * checked before any HIP call is made, so invalid arguments never touch the
