@@ -60,3 +60,69 @@ def compare(got, want, dtype, what=""):
     assert mx <= tol["max_abs"], f"{what}: max-abs {mx:.3g} > {tol['max_abs']}"
     assert mean <= tol["mean_abs"], f"{what}: mean-abs {mean:.3g} > {tol['mean_abs']}"
     return mx, mean
+
+
+# --------------------------------------------------------------------------
+# Mask readout: recover each row's allowed key set from the production
+# kernels.  With Q = K = 0 every scored pair weighs 1/|S_i|; V holds one-hot
+# rows for a chunk of D keys, so O[i, c] != 0 exactly when key c0 + c is in
+# S_i, and a key scored twice would show as a doubled entry.  The expected
+# (row, key) pairs come from the oracle's explicit sets, kept per pattern in
+# key-major order so that each chunk is compared on its own (no table of
+# every pair of a long sequence is held at once).
+# --------------------------------------------------------------------------
+
+class KeyMajorSets:
+    """Rows scoring each key, from allowed(i) -> sorted keys of row i."""
+
+    def __init__(self, N, allowed):
+        rows, keys = [], []
+        for i in range(N):
+            k = np.asarray(allowed(i), dtype=np.int64)
+            keys.append(k)
+            rows.append(np.full(len(k), i, dtype=np.int64))
+        keys = np.concatenate(keys) if keys else np.zeros(0, np.int64)
+        rows = np.concatenate(rows) if rows else np.zeros(0, np.int64)
+        order = np.lexsort((rows, keys))
+        self.N = N
+        self.keys, self.rows = keys[order], rows[order]
+        self.indptr = np.searchsorted(self.keys, np.arange(N + 1))
+
+    def codes(self, bh, c0, c1):
+        """((bh * N + row) * N + key) of the pairs with key in [c0, c1)."""
+        s = slice(self.indptr[c0], self.indptr[c1])
+        return (bh * self.N + self.rows[s]) * self.N + self.keys[s]
+
+
+def readout_compare(forward, B, H, N, D, tdt, sets_of, chunks=None, what=""):
+    """Run forward(q, k, v, o) with Q = K = 0 and one-hot V per chunk of D keys
+    and compare every (b, h, row, key) pair with the oracle's sets, chunk by
+    chunk.  sets_of(b, h) -> KeyMajorSets of that (batch, head).  Returns the
+    number of pairs compared."""
+    import torch
+    q = torch.zeros((B, H, N, D), dtype=tdt, device="cuda:0")
+    v = torch.zeros_like(q)
+    o = torch.empty_like(q)
+    starts = list(range(0, N, D)) if chunks is None else list(chunks)
+    total = 0
+    for n_done, c0 in enumerate(starts):
+        if n_done % 64 == 0:
+            say(f"{what}: readout chunk {n_done} of {len(starts)}")
+        v.zero_()
+        n = min(D, N - c0)
+        v[:, :, c0:c0 + n, :n] = torch.eye(n, dtype=tdt, device=v.device)
+        forward(q, q, v, o)
+        torch.cuda.synchronize()
+        of = o.float()
+        nz = of > 0
+        rowmax = of.amax(dim=3, keepdim=True)
+        assert bool(((of == rowmax) | ~nz).all()), f"{what}: unequal weights in chunk {c0}"
+        idx = torch.nonzero(nz)
+        bh = idx[:, 0] * H + idx[:, 1]
+        got = np.sort(((bh * N + idx[:, 2]) * N + (c0 + idx[:, 3])).cpu().numpy())
+        want = np.sort(np.concatenate([sets_of(b, h).codes(b * H + h, c0, c0 + n)
+                                       for b in range(B) for h in range(H)]))
+        assert len(got) == len(want), f"{what}: chunk {c0}: {len(got)} pairs, oracle {len(want)}"
+        assert np.array_equal(got, want), f"{what}: chunk {c0}: key sets differ"
+        total += len(want)
+    return total

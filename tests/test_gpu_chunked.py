@@ -39,15 +39,17 @@ def _case_ids(c):
     return "B%dH%dD%d_%s_C%dk%dM%d+%d" % c[:8]
 
 
+# bf16 runs both band kernels besides the host's own choice; fp32 has one.
+ROW_CASES = [pytest.param(c, r, id=_case_ids(c) + "-rows%s" % r)
+             for c in CASES for r in ([None, 64, 128] if c[3] == "bf16" else [None])]
+
+
 @pytest.mark.parametrize("proj", [False, True])
-@pytest.mark.parametrize("rows_mode", [None, 64, 128])
-@pytest.mark.parametrize("case", CASES, ids=_case_ids)
+@pytest.mark.parametrize("case,rows_mode", ROW_CASES)
 def test_chunked_every_element(case, rows_mode, proj, monkeypatch):
     import torch
     B, H, D, dt, C, k, M, extra, seed = case
     if rows_mode is not None:
-        if dt != "bf16":
-            pytest.skip("the band-rows choice applies to bf16")
         monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows_mode))
     N = M + C * k + extra
     a = W.small_case(B, H, N, D, dt, 0, seed=seed)
