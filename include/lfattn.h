@@ -99,7 +99,9 @@ typedef enum {
   LFATTN_EUNSUPPORTED = 2, /* valid but not implemented: D not 64 or 128, N >= 2^29,
                              or more than 512 distinct global positions with bf16 */
   LFATTN_ENOMEM = 3,      /* device or host allocation failed */
-  LFATTN_EHIP = 4         /* a HIP runtime call or kernel launch failed */
+  LFATTN_EHIP = 4,        /* a HIP runtime call or kernel launch failed */
+  LFATTN_ESCRATCH = 5     /* lfattn_forward_noalloc: the handle's global-row partials
+                             need more than the library's static scratch array */
 } lfattn_status;
 
 typedef enum { LFATTN_F32 = 0, LFATTN_BF16 = 1 } lfattn_dtype;
@@ -162,6 +164,25 @@ lfattn_status lfattn_create_chunked(lfattn_t* out, int B, int H, int N, int D,
  */
 lfattn_status lfattn_forward(lfattn_t ctx, const void* Q, const void* K, const void* V,
                              void* O, hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as lfattn_forward, with the global rows' per-chunk partial records
+ * kept in the library's static device array (32 MiB per GPU, held until the
+ * process ends) instead of the handle's workspace.  Allocates nothing and
+ * calls no allocating routine; launches kernels only.  Every call on one GPU
+ * shares that GPU's array: two calls that may overlap on one GPU (any
+ * streams, any handles) race and must not be made.  Each call writes every
+ * record it reads, so the array needs no clearing between calls.  Returns
+ * ESCRATCH when the handle's records exceed the array (B * H * ceil(|G| /
+ * rows per set) * key chunks * rows per set * (D + 4) * 4 bytes; the
+ * 65536-token, 64-global workload needs about 69 MB), EHIP when the array's
+ * device address could not be obtained at lfattn_create, otherwise errors as
+ * lfattn_forward.
+ */
+lfattn_status lfattn_forward_noalloc(lfattn_t ctx, const void* Q, const void* K, const void* V,
+                                     void* O, hipStream_t stream);
 
 /*
  * Forward pass in which the global rows take their own projections (the

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -53,6 +54,40 @@ constexpr int kBwdChunk = 512;
 constexpr int kBwdMaxChunks = 64;
 constexpr long long kMaxN = 1LL << 29;
 
+// Static scratch of lfattn_forward_noalloc: the global-row partial records
+// of calls that may not allocate.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` only names the symbol:
+// kernels take the per-device address from scratch_ptr(), never the name.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` per device ordinal, looked up once per device
+// (hipGetSymbolAddress with that device current) by the first lfattn_create
+// on it; nullptr until then or when the lookup failed.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_tried[kMaxDevices] = {};
+
+void scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_tried[dev]) return;
+  g_scratch_tried[dev] = true;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr) {
+    g_scratch_ptr[dev] = p;
+  } else {
+    (void)hipGetLastError();
+  }
+}
+
+void* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 struct lfattn_ctx {
@@ -85,6 +120,7 @@ struct lfattn_ctx {
   unsigned char* d_isglob = nullptr;  // [1 or B][N]
 
   float* d_part = nullptr;
+  size_t part_bytes = 0;  // bytes of the global-row partial records
   int band_rows = 0;  // rows per band workgroup
   int bwd_rows[2] = {0, 0};  // rows (keys) per backward item, row / key side: 64 or 128
   int bwd_chunk = 0;  // keys (rows) per chunk of a backward global item
@@ -158,7 +194,7 @@ long long head_pairs(int N, long long hw, int d, bool causal, int chunk, int n_m
 
 lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void* V,
                            const void* Qg, const void* Kg, const void* Vg, void* O, float* lse,
-                           hipStream_t stream);
+                           hipStream_t stream, float* part);
 
 bool overlaps(const void* a, const void* b, size_t bytes) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -182,6 +218,7 @@ const char* lfattn_status_string(lfattn_status s) {
     case LFATTN_EUNSUPPORTED: return "unsupported configuration";
     case LFATTN_ENOMEM: return "out of memory";
     case LFATTN_EHIP: return "HIP runtime error";
+    case LFATTN_ESCRATCH: return "needs more than the static scratch array";
   }
   return "unknown status";
 }
@@ -488,11 +525,13 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   if (n_g > 0) {
     const size_t rec = (size_t)D + 4;
     const size_t n_part = (size_t)B * H * c->n_sets * c->n_chunks * c->g_rows * rec;
+    c->part_bytes = n_part * sizeof(float);
     if ((st = dev_alloc(&c->d_part, n_part)) != LFATTN_OK) {
       free_ctx(c);
       return st;
     }
   }
+  scratch_setup(c->device);
   bool ok = hipMemcpy(c->d_work, table.data(), table.size() * sizeof(BandWork),
                       hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(c->d_isglob, isg.data(), isg.size(), hipMemcpyHostToDevice) == hipSuccess;
@@ -599,23 +638,37 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
 lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* K,
                                          const void* V, const void* Qg, const void* Kg,
                                          const void* Vg, void* O, hipStream_t stream) {
-  return forward_impl(c, Q, K, V, Qg, Kg, Vg, O, nullptr, stream);
+  return forward_impl(c, Q, K, V, Qg, Kg, Vg, O, nullptr, stream, c ? c->d_part : nullptr);
+}
+
+lfattn_status lfattn_forward_noalloc(lfattn_t c, const void* Q, const void* K, const void* V,
+                                     void* O, hipStream_t stream) {
+  if (!c) return LFATTN_EINVAL;
+  if (c->part_bytes > kScratchBytes) return LFATTN_ESCRATCH;
+  float* part = nullptr;
+  if (c->part_bytes > 0) {
+    part = (float*)scratch_ptr(c->device);
+    if (!part) return LFATTN_EHIP;
+  }
+  return forward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, nullptr, stream, part);
 }
 
 lfattn_status lfattn_forward_lse(lfattn_t c, const void* Q, const void* K, const void* V,
                                  void* O, float* LSE, hipStream_t stream) {
   if (!c || !LSE) return LFATTN_EINVAL;
   if (c->dtype != LFATTN_BF16) return LFATTN_EUNSUPPORTED;
-  return forward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, LSE, stream);
+  return forward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, LSE, stream, c->d_part);
 }
 
 }  // extern "C"
 
 namespace {
 
+// part: where the global rows' partial records go (the handle's workspace,
+// or the static scratch for lfattn_forward_noalloc).
 lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void* V,
                            const void* Qg, const void* Kg, const void* Vg, void* O, float* lse,
-                           hipStream_t stream) {
+                           hipStream_t stream, float* part) {
   if (!c || !Q || !K || !V || !O) return LFATTN_EINVAL;
   if (!Qg) Qg = Q;
   if (!Kg) Kg = K;
@@ -652,7 +705,7 @@ lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void*
   lfattn::GlobArgs g;
   if (n_g > 0) {
     g.Q = Qg; g.K = Kg; g.V = Vg; g.O = O;
-    g.glob = c->d_glob; g.gsel = c->d_gsel; g.part = c->d_part;
+    g.glob = c->d_glob; g.gsel = c->d_gsel; g.part = part;
     g.H = c->H; g.N = c->N; g.n_glob = n_g; g.n_bh = c->B * c->H;
     g.rows_per_set = c->g_rows;
     g.n_sets = c->n_sets; g.n_chunks = c->n_chunks; g.chunk_keys = c->chunk_keys;
@@ -674,7 +727,7 @@ lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void*
   a.lse = lse;
   a.cbase = c->n_memory;
   a.rows_per_wg = c->band_rows;
-  a.part = c->glob_items ? c->d_part : nullptr;
+  a.part = c->glob_items ? part : nullptr;
   a.n_sets = c->n_sets; a.n_chunks = c->n_chunks; a.chunk_keys = c->chunk_keys;
   if (lfattn::launch_band(c->dtype, c->D, a, c->n_band_wg, stream, t_band) != hipSuccess)
     return LFATTN_EHIP;

@@ -19,13 +19,14 @@ LFATTN_EINVAL = 1
 LFATTN_EUNSUPPORTED = 2
 LFATTN_ENOMEM = 3
 LFATTN_EHIP = 4
+LFATTN_ESCRATCH = 5
 
 LFATTN_F32 = 0
 LFATTN_BF16 = 1
 
 # Every entry point include/lfattn.h declares.
 EXPORTS = ("lfattn_create", "lfattn_create_masked", "lfattn_create_causal",
-           "lfattn_create_chunked", "lfattn_forward", "lfattn_forward_lse", "lfattn_backward",
+           "lfattn_create_chunked", "lfattn_forward", "lfattn_forward_noalloc", "lfattn_forward_lse", "lfattn_backward",
            "lfattn_forward_global_proj", "lfattn_destroy", "lfattn_status_string",
            "lfattn_scored_pairs", "lfattn_band_launch_pairs", "lfattn_band_rows",
            "lfattn_global_list", "lfattn_global_list_batch",
@@ -69,6 +70,8 @@ def load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_float]
     lib.lfattn_forward.restype = ctypes.c_int
     lib.lfattn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.lfattn_forward_noalloc.restype = ctypes.c_int
+    lib.lfattn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.lfattn_backward.restype = ctypes.c_int
     lib.lfattn_backward.argtypes = [vp] * 10 + [vp]
     lib.lfattn_forward_lse.restype = ctypes.c_int
@@ -189,6 +192,15 @@ def lfattn_forward(handle: int, Q, K, V, O, stream=None) -> None:
     lib = load()
     _check(lib.lfattn_forward(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _stream(stream)),
            "lfattn_forward")
+
+
+def lfattn_forward_noalloc(handle: int, Q, K, V, O, stream=None) -> None:
+    """lfattn_forward with the global rows' partial records in the library's
+    static device scratch (allocates nothing; calls that may overlap on one
+    GPU race)."""
+    lib = load()
+    _check(lib.lfattn_forward_noalloc(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                      _stream(stream)), "lfattn_forward_noalloc")
 
 
 def lfattn_forward_lse(handle: int, Q, K, V, O, LSE, stream=None) -> None:
