@@ -227,7 +227,13 @@ lfattn_status lfattn_backward(lfattn_t ctx, const void* Q, const void* K, const 
                               const void* O, const void* dO, const float* LSE, float* dQ,
                               float* dK, float* dV, hipStream_t stream);
 
-/* Release the handle and its device memory (waits for the device first).
+/* Release the handle and its device memory.  The memory is returned with
+ * stream-ordered frees behind the work enqueued so far on the stream of the
+ * handle's latest call, which must still exist; the host waits for neither
+ * that work nor other streams' (on a device without memory pools, the
+ * runtime's hipFree waits for the device).  Work that used the handle on
+ * other streams must be complete, or ordered before that stream's current
+ * point, and every HIP graph that replays captured calls must have finished.
  * NULL is accepted and ignored. */
 lfattn_status lfattn_destroy(lfattn_t ctx);
 

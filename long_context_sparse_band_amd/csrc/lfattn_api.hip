@@ -127,6 +127,16 @@ struct lfattn_ctx {
   int g_waves = 0, g_rows = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
   bool glob_items = false;  // global-row partials run as items of the band launch
 
+  // Device memory comes from the stream-ordered allocator on this private
+  // stream (async_mem), so that lfattn_destroy can release it behind the
+  // stream of the handle's latest call (`last`, an event recorded there at
+  // destroy) without waiting for the whole device.
+  hipStream_t mem_stream = nullptr;
+  bool async_mem = false;
+  hipEvent_t done = nullptr;
+  hipStream_t last = nullptr;
+  bool used = false;
+
   bool timing = false;
   int n_timed = 0;
   std::vector<hipEvent_t> ev;  // kEvPerForward per timed forward
@@ -137,10 +147,12 @@ struct lfattn_ctx {
 namespace {
 
 template <typename T>
-lfattn_status dev_alloc(T** p, size_t count) {
+lfattn_status dev_alloc(lfattn_ctx* c, T** p, size_t count) {
   *p = nullptr;
   if (count == 0) return LFATTN_OK;
-  if (hipMalloc((void**)p, count * sizeof(T)) != hipSuccess) {
+  const hipError_t e = c->async_mem ? hipMallocAsync((void**)p, count * sizeof(T), c->mem_stream)
+                                    : hipMalloc((void**)p, count * sizeof(T));
+  if (e != hipSuccess) {
     *p = nullptr;
     (void)hipGetLastError();
     return LFATTN_ENOMEM;
@@ -148,20 +160,47 @@ lfattn_status dev_alloc(T** p, size_t count) {
   return LFATTN_OK;
 }
 
+// Whether work enqueued on `stream` is being captured into a graph.
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
+// Release a handle: its device memory goes back behind the work enqueued so
+// far on the stream of its latest call (stream-ordered frees after an event
+// recorded there), without a device-wide wait.  Where that cannot be ordered
+// (the event cannot be recorded), the device is waited for first.  With the
+// plain allocator (no memory pools) hipFree itself waits for the device.
 void free_ctx(lfattn_ctx* c) {
   if (!c) return;
-  (void)hipFree(c->d_work);
-  (void)hipFree(c->d_glob);
-  (void)hipFree(c->d_gsel);
-  (void)hipFree(c->d_isglob);
-  (void)hipFree(c->d_part);
-  (void)hipFree(c->d_bwork);
-  (void)hipFree(c->d_delta);
-  (void)hipFree(c->d_gpart);
+  void* ptrs[] = {c->d_work, c->d_glob, c->d_gsel, c->d_isglob, c->d_part, c->d_bwork,
+                  c->d_delta, c->d_gpart};
+  if (c->async_mem) {
+    if (c->used && !capturing(c->last)) {
+      if (hipEventRecord(c->done, c->last) != hipSuccess ||
+          hipStreamWaitEvent(c->mem_stream, c->done, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipDeviceSynchronize();
+      }
+    }
+    for (void* p : ptrs)
+      if (p) (void)hipFreeAsync(p, c->mem_stream);
+  } else {
+    for (void* p : ptrs)
+      if (p) (void)hipFree(p);
+  }
+  if (c->done) (void)hipEventDestroy(c->done);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->bev) (void)hipEventDestroy(e);
+  if (c->mem_stream) (void)hipStreamDestroy(c->mem_stream);
+  (void)hipGetLastError();
   delete c;
 }
+
 
 // Scored pairs of one head with dilation d: every row's band (keys i + d*k,
 // |k| <= hw, inside [0, N); causal: -hw <= k <= 0), plus the global keys
@@ -507,17 +546,29 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   // ---- device state ----
   lfattn_status st = LFATTN_OK;
   if (hipGetDevice(&c->device) != hipSuccess) { free_ctx(c); return LFATTN_EHIP; }
-  if ((st = dev_alloc(&c->d_work, table.size())) != LFATTN_OK ||
-      (st = dev_alloc(&c->d_isglob, isg.size())) != LFATTN_OK ||
-      (st = dev_alloc(&c->d_glob, (size_t)std::max(goff[n_lists], 1))) != LFATTN_OK ||
-      (st = dev_alloc(&c->d_gsel, (size_t)B)) != LFATTN_OK) {
+  if (hipStreamCreateWithFlags(&c->mem_stream, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&c->done, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    free_ctx(c);
+    return LFATTN_EHIP;
+  }
+  {
+    int pools = 0;
+    c->async_mem = hipDeviceGetAttribute(&pools, hipDeviceAttributeMemoryPoolsSupported,
+                                         c->device) == hipSuccess && pools != 0;
+    (void)hipGetLastError();
+  }
+  if ((st = dev_alloc(c, &c->d_work, table.size())) != LFATTN_OK ||
+      (st = dev_alloc(c, &c->d_isglob, isg.size())) != LFATTN_OK ||
+      (st = dev_alloc(c, &c->d_glob, (size_t)std::max(goff[n_lists], 1))) != LFATTN_OK ||
+      (st = dev_alloc(c, &c->d_gsel, (size_t)B)) != LFATTN_OK) {
     free_ctx(c);
     return st;
   }
-  if (has_bwd && ((st = dev_alloc(&c->d_bwork, btable.size())) != LFATTN_OK ||
-                   (st = dev_alloc(&c->d_delta, (size_t)B * H * N)) != LFATTN_OK ||
+  if (has_bwd && ((st = dev_alloc(c, &c->d_bwork, btable.size())) != LFATTN_OK ||
+                   (st = dev_alloc(c, &c->d_delta, (size_t)B * H * N)) != LFATTN_OK ||
                    (n_g > 0 &&
-                    (st = dev_alloc(&c->d_gpart, (size_t)3 * B * H * c->n_gch * n_g * D)) !=
+                    (st = dev_alloc(c, &c->d_gpart, (size_t)3 * B * H * c->n_gch * n_g * D)) !=
                         LFATTN_OK))) {
     free_ctx(c);
     return st;
@@ -526,25 +577,25 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
     const size_t rec = (size_t)D + 4;
     const size_t n_part = (size_t)B * H * c->n_sets * c->n_chunks * c->g_rows * rec;
     c->part_bytes = n_part * sizeof(float);
-    if ((st = dev_alloc(&c->d_part, n_part)) != LFATTN_OK) {
+    if ((st = dev_alloc(c, &c->d_part, n_part)) != LFATTN_OK) {
       free_ctx(c);
       return st;
     }
   }
   scratch_setup(c->device);
-  bool ok = hipMemcpy(c->d_work, table.data(), table.size() * sizeof(BandWork),
-                      hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(c->d_isglob, isg.data(), isg.size(), hipMemcpyHostToDevice) == hipSuccess;
-  if (has_bwd)
-    ok = ok && hipMemcpy(c->d_bwork, btable.data(), btable.size() * sizeof(BandWork),
-                         hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(c->d_gsel, gsel.data(), B * sizeof(int2), hipMemcpyHostToDevice) == hipSuccess;
-  if (goff[n_lists] > 0) {
-    std::vector<int> flat;
-    for (const auto& v : c->gl) flat.insert(flat.end(), v.begin(), v.end());
-    ok = ok && hipMemcpy(c->d_glob, flat.data(), flat.size() * sizeof(int),
-                         hipMemcpyHostToDevice) == hipSuccess;
-  }
+  std::vector<int> flat;
+  for (const auto& v : c->gl) flat.insert(flat.end(), v.begin(), v.end());
+  auto up = [&](void* dst, const void* src, size_t bytes) {
+    return bytes == 0 ||
+           hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, c->mem_stream) == hipSuccess;
+  };
+  bool ok = up(c->d_work, table.data(), table.size() * sizeof(BandWork));
+  ok = ok && up(c->d_isglob, isg.data(), isg.size());
+  if (has_bwd) ok = ok && up(c->d_bwork, btable.data(), btable.size() * sizeof(BandWork));
+  ok = ok && up(c->d_gsel, gsel.data(), B * sizeof(int2));
+  ok = ok && up(c->d_glob, flat.data(), flat.size() * sizeof(int));
+  // The tables are in place (and the host vectors may go) before any call.
+  ok = ok && hipStreamSynchronize(c->mem_stream) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
     free_ctx(c);
@@ -698,6 +749,8 @@ lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void*
     t_part = {ev[2], ev[3]};
     t_merge = {ev[4], ev[5]};
   }
+  c->last = stream;
+  c->used = true;
 
   // Global rows: partials first, then the band kernel, then the merge (which
   // reads the partials after the kernel boundary made them visible).
@@ -782,10 +835,13 @@ lfattn_status lfattn_backward(lfattn_t c, const void* Q, const void* K, const vo
   ak.work = c->d_bwork + c->n_bwork[0];
   ak.ks = c->bwd_rows[1] == 64 ? 2 : 1;
   lfattn::Timing t[3];
-  if (c->timing && c->n_btimed < kMaxTimedBackwards) {
+  const bool timed = c->timing && c->n_btimed < kMaxTimedBackwards;
+  if (timed) {
     hipEvent_t* e = &c->bev[kEvPerBackward * c->n_btimed++];
     for (int x = 0; x < 3; ++x) t[x] = {e[2 * x], e[2 * x + 1]};
   }
+  c->last = stream;
+  c->used = true;
   if (lfattn::launch_backward_bf16(a, ak, c->n_bwork[0], c->n_bwork[1], stream, t) != hipSuccess)
     return LFATTN_EHIP;
   return LFATTN_OK;
@@ -793,7 +849,6 @@ lfattn_status lfattn_backward(lfattn_t c, const void* Q, const void* K, const vo
 
 lfattn_status lfattn_destroy(lfattn_t c) {
   if (!c) return LFATTN_OK;
-  (void)hipDeviceSynchronize();
   free_ctx(c);
   return LFATTN_OK;
 }

@@ -39,10 +39,15 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        # Build when missing or older than its source.
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        # LFATTN_ORACLE_LIB names another build of the same source (the
+        # sanitizer build of the CPU tests); otherwise build when missing or
+        # older than its source.
+        path = os.environ.get("LFATTN_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+        lib = ctypes.CDLL(path)
         i32p = ctypes.POINTER(ctypes.c_int)
         i64p = ctypes.POINTER(ctypes.c_int64)
         f32p = ctypes.POINTER(ctypes.c_float)

@@ -370,3 +370,37 @@ def test_band_launch_pairs(dtype, D, with_glob_rows):
         L.lfattn_destroy(h)
     assert total == oracle.count_pairs(B, H, N, 256, None, glob)
     assert band == (total if with_glob_rows else total - B * H * len(glob) * N)
+
+
+def test_destroy_waits_only_for_its_own_work():
+    """lfattn_destroy right after an enqueued forward: the forward still
+    completes correctly (its memory is released only after it), and the call
+    does not wait for unrelated work queued on another stream."""
+    import time
+    import torch
+    inp = W.small_case(1, 2, 2000, 64, "bf16", 256, glob=[0, 999], seed=44)
+    ref, _ = run(inp)
+    q, k, v = to_device(inp)
+    o = torch.full_like(q, float("nan"))
+    busy = torch.cuda.Stream()
+    a = torch.randn(4096, 4096, device="cuda:0")
+    torch.cuda.synchronize()
+    say("destroy while another stream is busy")
+    with torch.cuda.stream(busy):
+        t0 = time.perf_counter()
+        for _ in range(40):
+            a = a @ a
+            a = a / a.norm()
+    h = L.lfattn_create(1, 2, 2000, 64, L.LFATTN_BF16, 256, None, [0, 999])
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        L.lfattn_forward(h, q, k, v, o, side)
+    t1 = time.perf_counter()
+    L.lfattn_destroy(h)
+    t_destroy = time.perf_counter() - t1
+    busy.synchronize()
+    t_busy = time.perf_counter() - t0
+    side.synchronize()
+    assert np.array_equal(o.float().cpu().numpy().astype(np.float64), ref)
+    say(f"destroy {1e3 * t_destroy:.2f} ms, other stream's work {1e3 * t_busy:.2f} ms")
+    assert t_destroy < 0.5 * t_busy
