@@ -119,6 +119,22 @@ __device__ __forceinline__ int lane_id() {
   return l;
 }
 
+// Partial records of the global rows are exchanged between workgroups that
+// may run on different XCDs (whose L2 caches are not coherent with each
+// other): they are written and read with agent-scope atomic accesses
+// (coherent at the device level without flushing the whole L2), 8 bytes at a
+// time.
+__device__ __forceinline__ void store_agent(float* p, float x, float y) {
+  const unsigned long long v =
+      (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
+  __hip_atomic_store((unsigned long long*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_agent(const float* p) {
+  const unsigned long long v = __hip_atomic_load((const unsigned long long*)p, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
+}
+
 // Key of register i (0..15) of a 32x32 MFMA result block for lane half hi.
 __device__ __forceinline__ constexpr int block_row(int i, int hi) {
   return 8 * (i >> 2) + 4 * hi + (i & 3);
@@ -196,33 +212,100 @@ struct B32 {
       return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
     }
   }
-  struct Smem {
-    unsigned char st[NS][KS][2 * MAT];
-    int gpos[kGlobCap];
-    int gsp[kGlobCap];
-    unsigned char rowg[ROWS];  // band rows that are global positions
-  };
 };
 
-// CHUNK: GMAT chunked attention (a.chunk > 0) instead of a band; a separate
-// instantiation, so that the band kernels carry none of its arithmetic.
-template <int D, int KS_, bool CHUNK>
-__global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(B32<D, KS_>::WPE, B32<D, KS_>::WPE)))
-void band32_kernel(BandArgs a) {
+// Global-row items of D = 64 launches run in the key-split layout (two
+// 32-row blocks of global rows, even and odd tiles on two wavefront pairs),
+// whatever the launch's band layout: all four wavefronts score.
+template <int D, int KS>
+constexpr int global_ks() { return D == 64 ? 2 : KS; }
+
+// LDS of one band workgroup: the tile ring (sized for the wider of the
+// launch's band and global-row layouts), the staged global positions, the
+// band rows that are global positions, and a flag.
+template <int D, int KS>
+struct BandSmem {
+  static constexpr int KSMAX = KS > global_ks<D, KS>() ? KS : global_ks<D, KS>();
+  unsigned char st[B32<D, KS>::NS * KSMAX * 2 * B32<D, KS>::MAT];
+  int gpos[kGlobCap];
+  int gsp[kGlobCap];
+  unsigned char rowg[128];   // band rows that are global positions
+  int last;                  // global-row item: this workgroup merges the set
+};
+
+// The merge of one set of global rows (slots ROWS*set .. of the batch
+// element's list) from its n_chunks (at most kFuseChunks) partial records:
+// each thread takes one row and 8 output columns, loads that row's records in
+// rounds of 4 chunks of independent loads, combines the chunks' (max, sum,
+// acc) with the log-sum-exp rule, and writes 16 bytes of the row (bf16) and,
+// where asked, its log-sum-exp.
+template <int D, int ROWS>
+__device__ __forceinline__ void merge_global_set(const BandArgs& a, const BandWork& w,
+                                                 const float* set_part, int tid) {
+  constexpr int TPR = D / 8;          // threads per row
+  constexpr int RPP = 256 / TPR;      // rows per pass
+  constexpr int REC = D + 4;
+  constexpr int CB = 4;               // chunks loaded per round
+  const int n_rows = min(ROWS, w.ng - ROWS * w.r);
+  const int cg = tid % TPR;
+  const int* gl = a.glob + w.g0;
+  for (int r = tid / TPR; r < n_rows; r += RPP) {
+    float m = kNegInit, l = 0.0f;
+    float o[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) o[x] = 0.0f;
+    for (int c0 = 0; c0 < a.n_chunks; c0 += CB) {
+      float2 ml[CB], v[CB][4];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const int c = min(c0 + u, a.n_chunks - 1);
+        const float* rec = set_part + ((size_t)c * ROWS + r) * REC;
+        ml[u] = load_agent(rec);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[u][x] = load_agent(rec + 4 + 8 * cg + 2 * x);
+      }
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        if (c0 + u >= a.n_chunks) break;
+        const float mn = fmaxf(m, ml[u].x);
+        const float a0 = fast_exp2(m - mn), a1 = fast_exp2(ml[u].x - mn);
+        l = l * a0 + ml[u].y * a1;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          o[2 * x] = o[2 * x] * a0 + v[u][x].x * a1;
+          o[2 * x + 1] = o[2 * x + 1] * a0 + v[u][x].y * a1;
+        }
+        m = mn;
+      }
+    }
+    const int orow = gl[ROWS * w.r + r];
+    if (a.lse && cg == 0) a.lse[(size_t)w.bh * a.N + orow] = (m + __log2f(l)) * 0.6931471805599453f;
+    const float inv = 1.0f / l;
+    bf16x8 ob;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) ob[x] = (__bf16)(o[x] * inv);
+    *(bf16x8*)((unsigned short*)a.O + (size_t)w.bh * a.N * D + (size_t)orow * D + 8 * cg) = ob;
+  }
+}
+
+// One work item of the band launch in the layout KS_ (a band item, or a
+// global-row item when w.dil == 0).  CHUNK: GMAT chunked attention
+// (a.chunk > 0) instead of a band; a separate instantiation, so that the band
+// kernels carry none of its arithmetic.
+template <int D, int KS_, bool CHUNK, class SM>
+__device__ __forceinline__ void band_item(const BandArgs& a, const BandWork& w, SM& sm) {
   using C = B32<D, KS_>;
   constexpr int TK = C::TK, RB = C::RB, CPR = C::CPR, RPI = C::RPI, MAT = C::MAT;
   constexpr int NE = C::NE, KS = C::KS, NS = C::NS, ROWS = C::ROWS, QBLKS = C::QBLKS;
   constexpr int RPW = C::RPW;
   static_assert(QBLKS * NE * RPI == TK, "the wavefronts of a key half load its 32-row tiles");
-  __shared__ __attribute__((aligned(16))) typename C::Smem sm;
+  static_assert(sizeof(sm.st) >= (size_t)NS * KS * 2 * MAT, "tile ring");
   auto swz = [](int row, int c) { return C::swz(row, c); };
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
   const int qblk = wave % QBLKS, kh = wave / QBLKS;
-  const BandWork w = a.work[blockIdx.x];
   // A global-row item is the band problem over plain key positions (d = 1),
   // with a half-width no key reaches past and its rows taken from the global
   // list, restricted to one key chunk.
@@ -308,7 +391,7 @@ void band32_kernel(BandArgs a) {
   // RPW*qblk + RPI*e + lane/CPR (e < NE): 2*NE loads each (tiles past the end
   // load a real row so that every wavefront issues the same count).
   const int rbase = RPW * qblk;
-  const unsigned st_base = (unsigned)(uintptr_t)(LDS_AS void*)sm.st[0][kh];
+  const unsigned st_base = (unsigned)(uintptr_t)(LDS_AS void*)(sm.st + kh * 2 * MAT);
   constexpr unsigned kStageBytes = KS * 2 * MAT;
   const int rlane = rbase + lane / CPR;
   // LDS destination of load e of K within a stage (V: + MAT).
@@ -701,7 +784,7 @@ void band32_kernel(BandArgs a) {
     constexpr int PER = 2 + D / 2;
     static_assert((size_t)2 * 64 * PER * 4 <= sizeof(sm.st), "merge area");
     __syncthreads();
-    float* mine = (float*)&sm.st[0][0][0] + ((size_t)qblk * 64 + lane) * PER;
+    float* mine = (float*)sm.st + ((size_t)qblk * 64 + lane) * PER;
     if (kh == 1 && live) {
       mine[0] = m;
       mine[1] = l;
@@ -711,7 +794,9 @@ void band32_kernel(BandArgs a) {
         for (int i = 0; i < 16; ++i) mine[2 + 16 * b + i] = acc[b][i];
     }
     __syncthreads();
-    if (kh == 1 || !live) return;
+    // (Every wave of a global-row item goes on to the arrival count below.)
+    if (!gi && (kh == 1 || !live)) return;
+    if (kh == 0 && live) {
     const float m1 = mine[0], l1 = mine[1];
     const float mn = fmaxf(m, m1);
     const float a0 = fast_exp2(m - mn), a1 = fast_exp2(m1 - mn);
@@ -721,6 +806,7 @@ void band32_kernel(BandArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[b][i] = acc[b][i] * a0 + mine[2 + 16 * b + i] * a1;
     m = mn;
+    }
   }
 
   const float lt = pair_sum(l);
@@ -730,23 +816,60 @@ void band32_kernel(BandArgs a) {
   const int lid = lane_id();
   const int ehi = lid >> 5, el32 = lid & 31;
   const int eu = ua + el32;
-  if (eu >= n_rows) return;
   if (gi) {
-    // Partial record of this global row for this key chunk.
-    float* rec = a.part + ((((size_t)w.bh * a.n_sets + w.r) * a.n_chunks + w.t0) * ROWS +
-                           32 * qblk + el32) * (D + 4);
-    if (ehi == 0) {
-      rec[0] = m;
-      rec[1] = lt;
+    // Partial record of this global row for this key chunk (the waves that
+    // hold a merged state for live rows).
+    float* const set_part = a.part + ((size_t)w.bh * a.n_sets + w.r) * a.n_chunks * ROWS * (D + 4);
+    const bool fuse = a.gcount != nullptr;
+    if (live && (KS == 1 || kh == 0) && eu < n_rows) {
+      float* rec = set_part + ((size_t)w.t0 * ROWS + 32 * qblk + el32) * (D + 4);
+      if (fuse) {
+        if (ehi == 0) store_agent(rec, m, lt);
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float* p = rec + 4 + 32 * b + 8 * g4 + 4 * ehi;
+            store_agent(p, acc[b][4 * g4], acc[b][4 * g4 + 1]);
+            store_agent(p + 2, acc[b][4 * g4 + 2], acc[b][4 * g4 + 3]);
+          }
+      } else {
+        // A separate merge kernel reads these after the launch ends.
+        if (ehi == 0) {
+          rec[0] = m;
+          rec[1] = lt;
+        }
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *(float4*)(rec + 4 + 32 * b + 8 * g4 + 4 * ehi) = make_float4(
+                acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2], acc[b][4 * g4 + 3]);
+      }
     }
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *(float4*)(rec + 4 + 32 * b + 8 * g4 + 4 * ehi) =
-            make_float4(acc[b][4 * g4], acc[b][4 * g4 + 1], acc[b][4 * g4 + 2], acc[b][4 * g4 + 3]);
+    if (!fuse) return;
+    // Arrival: once every wave's records are complete at the device level,
+    // one thread counts this chunk in; the workgroup that brings the count
+    // to the number of chunks merges the set's records into O (and resets
+    // the count for the next call).
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wait_vm_lgkm0<0>();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (tid == 0) {
+      unsigned* cnt = a.gcount + (size_t)w.bh * a.n_sets + w.r;
+      const unsigned before =
+          __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = before + 1 == (unsigned)a.n_chunks;
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.last = last;
+    }
+    __syncthreads();
+    if (!sm.last) return;
+    merge_global_set<D, ROWS>(a, w, set_part, tid);
     return;
   }
+  if (eu >= n_rows) return;
   const int row = r + d * eu;
   if (sm.rowg[32 * qblk + el32]) return;
   // Natural log-sum-exp of the row's scaled scores (m and the weights are in
@@ -765,7 +888,27 @@ void band32_kernel(BandArgs a) {
     }
 }
 
+// The band launch: one work item per workgroup.
+template <int D, int KS, bool CHUNK>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(B32<D, KS>::WPE, B32<D, KS>::WPE)))
+void band32_kernel(BandArgs a) {
+  __shared__ __attribute__((aligned(16))) BandSmem<D, KS> sm;
+  const BandWork w = a.work[blockIdx.x];
+  if constexpr (global_ks<D, KS>() != KS) {
+    if (w.dil == 0) {
+      band_item<D, global_ks<D, KS>(), CHUNK>(a, w, sm);
+      return;
+    }
+  }
+  band_item<D, KS, CHUNK>(a, w, sm);
+}
+
 }  // namespace
+
+// Rows per set of the global-row items of a bf16 launch with the given band
+// rows per workgroup.
+int global_set_rows(int D, int band_rows) { return D == 64 ? 64 : band_rows; }
 
 int band_workgroups_per_cu(int dtype, int D) {
   return dtype == 1 ? (D == 64 ? B32<64, 2>::WPE : B32<128, 2>::WPE) : 2;

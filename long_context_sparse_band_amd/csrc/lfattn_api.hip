@@ -60,6 +60,10 @@ constexpr long long kMaxN = 1LL << 29;
 // kernels take the per-device address from scratch_ptr(), never the name.
 constexpr size_t kScratchBytes = size_t(32) << 20;
 __device__ __align__(256) unsigned char scratch[kScratchBytes];
+// Its layout: the global-row sets' arrival counts (zero between calls),
+// then the partial records.
+constexpr size_t kScratchCounts = 65536;
+constexpr size_t kScratchPartOffset = kScratchCounts * sizeof(unsigned);
 
 // Device address of `scratch` per device ordinal, looked up once per device
 // (hipGetSymbolAddress with that device current) by the first lfattn_create
@@ -75,7 +79,9 @@ void scratch_setup(int dev) {
   if (g_scratch_tried[dev]) return;
   g_scratch_tried[dev] = true;
   void* p = nullptr;
-  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr) {
+  // The arrival counts start at zero (each call leaves them at zero).
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr &&
+      hipMemset(p, 0, kScratchPartOffset) == hipSuccess) {
     g_scratch_ptr[dev] = p;
   } else {
     (void)hipGetLastError();
@@ -121,11 +127,14 @@ struct lfattn_ctx {
 
   float* d_part = nullptr;
   size_t part_bytes = 0;  // bytes of the global-row partial records
+  unsigned* d_gcount = nullptr;  // arrival count per (b*H + h, set) of the fused merge
+  size_t n_gcount = 0;
   int band_rows = 0;  // rows per band workgroup
   int bwd_rows[2] = {0, 0};  // rows (keys) per backward item, row / key side: 64 or 128
   int bwd_chunk = 0;  // keys (rows) per chunk of a backward global item
   int g_waves = 0, g_rows = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
   bool glob_items = false;  // global-row partials run as items of the band launch
+  bool fuse_merge = false;  // ... and the band launch merges them too
 
   // Device memory comes from the stream-ordered allocator on this private
   // stream (async_mem), so that lfattn_destroy can release it behind the
@@ -178,7 +187,7 @@ bool capturing(hipStream_t stream) {
 void free_ctx(lfattn_ctx* c) {
   if (!c) return;
   void* ptrs[] = {c->d_work, c->d_glob, c->d_gsel, c->d_isglob, c->d_part, c->d_bwork,
-                  c->d_delta, c->d_gpart};
+                  c->d_delta, c->d_gpart, c->d_gcount};
   if (c->async_mem) {
     if (c->used && !capturing(c->last)) {
       if (hipEventRecord(c->done, c->last) != hipSuccess ||
@@ -233,7 +242,7 @@ long long head_pairs(int N, long long hw, int d, bool causal, int chunk, int n_m
 
 lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void* V,
                            const void* Qg, const void* Kg, const void* Vg, void* O, float* lse,
-                           hipStream_t stream, float* part);
+                           hipStream_t stream, float* part, unsigned* counts);
 
 bool overlaps(const void* a, const void* b, size_t bytes) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -429,16 +438,28 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   const int n_g = c->n_gmax;
   c->glob_items = n_g > 0 && lfattn::band_takes_global_items(dtype, D);
   if (c->glob_items) {
-    c->g_rows = band_rows;  // a global item's rows: one workgroup's rows of G
+    c->g_rows = lfattn::global_set_rows(D, band_rows);  // rows of G per global item
     c->n_sets = (n_g + c->g_rows - 1) / c->g_rows;
     long long set_count = 0;  // sum over (b, h) of the row sets
     for (int b = 0; b < B; ++b)
       set_count += (long long)H * ((gsel[b].y + c->g_rows - 1) / c->g_rows);
     const long long short_items =
         set_count * ((N + kGlobItemKeysShort - 1) / kGlobItemKeysShort);
-    const int keys = n_items + short_items <= slots ? kGlobItemKeysShort
-                     : (long long)n_items >= kSpreadRounds * slots ? kGlobItemKeysSpread
-                                                                   : kGlobItemKeysLong;
+    int keys = n_items + short_items <= slots ? kGlobItemKeysShort
+               : (long long)n_items >= kSpreadRounds * slots ? kGlobItemKeysSpread
+                                                             : kGlobItemKeysLong;
+    // The band launch can merge the global rows itself (the last chunk item
+    // of a set to finish merges it; chunks long enough that a set has at most
+    // kFuseChunks of them).  It measured slower than the separate merge
+    // launch on these workloads (the records cross XCDs through device-
+    // coherent accesses, 3 us to write and 1.5 us per round of reads), so it
+    // is taken only when LFATTN_FUSE_MERGE=1 at create.
+    c->fuse_merge = false;
+    if (const char* e = std::getenv("LFATTN_FUSE_MERGE")) c->fuse_merge = std::strcmp(e, "1") == 0;
+    if (c->fuse_merge) {
+      const int min_keys = (N + lfattn::kFuseChunks - 1) / lfattn::kFuseChunks;
+      keys = std::max(keys, (min_keys + 31) / 32 * 32);
+    }
     c->chunk_keys = keys;
     c->n_chunks = (N + keys - 1) / keys;
     // Each global item goes to the XCD of the residue-0 band item whose rows
@@ -581,6 +602,19 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
       free_ctx(c);
       return st;
     }
+    if (c->fuse_merge) {
+      c->n_gcount = (size_t)B * H * c->n_sets;
+      if ((st = dev_alloc(c, &c->d_gcount, c->n_gcount)) != LFATTN_OK) {
+        free_ctx(c);
+        return st;
+      }
+      if (hipMemsetAsync(c->d_gcount, 0, c->n_gcount * sizeof(unsigned), c->mem_stream) !=
+          hipSuccess) {
+        (void)hipGetLastError();
+        free_ctx(c);
+        return LFATTN_EHIP;
+      }
+    }
   }
   scratch_setup(c->device);
   std::vector<int> flat;
@@ -689,37 +723,44 @@ lfattn_status lfattn_forward(lfattn_t c, const void* Q, const void* K, const voi
 lfattn_status lfattn_forward_global_proj(lfattn_t c, const void* Q, const void* K,
                                          const void* V, const void* Qg, const void* Kg,
                                          const void* Vg, void* O, hipStream_t stream) {
-  return forward_impl(c, Q, K, V, Qg, Kg, Vg, O, nullptr, stream, c ? c->d_part : nullptr);
+  return forward_impl(c, Q, K, V, Qg, Kg, Vg, O, nullptr, stream, c ? c->d_part : nullptr,
+                      c ? c->d_gcount : nullptr);
 }
 
 lfattn_status lfattn_forward_noalloc(lfattn_t c, const void* Q, const void* K, const void* V,
                                      void* O, hipStream_t stream) {
   if (!c) return LFATTN_EINVAL;
-  if (c->part_bytes > kScratchBytes) return LFATTN_ESCRATCH;
+  if (c->part_bytes > kScratchBytes - kScratchPartOffset || c->n_gcount > kScratchCounts)
+    return LFATTN_ESCRATCH;
   float* part = nullptr;
+  unsigned* counts = nullptr;
   if (c->part_bytes > 0) {
-    part = (float*)scratch_ptr(c->device);
-    if (!part) return LFATTN_EHIP;
+    unsigned char* base = (unsigned char*)scratch_ptr(c->device);
+    if (!base) return LFATTN_EHIP;
+    counts = (unsigned*)base;
+    part = (float*)(base + kScratchPartOffset);
   }
-  return forward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, nullptr, stream, part);
+  return forward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, nullptr, stream, part, counts);
 }
 
 lfattn_status lfattn_forward_lse(lfattn_t c, const void* Q, const void* K, const void* V,
                                  void* O, float* LSE, hipStream_t stream) {
   if (!c || !LSE) return LFATTN_EINVAL;
   if (c->dtype != LFATTN_BF16) return LFATTN_EUNSUPPORTED;
-  return forward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, LSE, stream, c->d_part);
+  return forward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, LSE, stream, c->d_part,
+                      c->d_gcount);
 }
 
 }  // extern "C"
 
 namespace {
 
-// part: where the global rows' partial records go (the handle's workspace,
-// or the static scratch for lfattn_forward_noalloc).
+// part, counts: where the global rows' partial records and the sets'
+// arrival counts go (the handle's workspace, or the static scratch for
+// lfattn_forward_noalloc).
 lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void* V,
                            const void* Qg, const void* Kg, const void* Vg, void* O, float* lse,
-                           hipStream_t stream, float* part) {
+                           hipStream_t stream, float* part, unsigned* counts) {
   if (!c || !Q || !K || !V || !O) return LFATTN_EINVAL;
   if (!Qg) Qg = Q;
   if (!Kg) Kg = K;
@@ -781,11 +822,15 @@ lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void*
   a.cbase = c->n_memory;
   a.rows_per_wg = c->band_rows;
   a.part = c->glob_items ? part : nullptr;
+  a.gcount = c->fuse_merge ? counts : nullptr;
   a.n_sets = c->n_sets; a.n_chunks = c->n_chunks; a.chunk_keys = c->chunk_keys;
   if (lfattn::launch_band(c->dtype, c->D, a, c->n_band_wg, stream, t_band) != hipSuccess)
     return LFATTN_EHIP;
 
-  if (n_g > 0 && lfattn::launch_glob_merge(c->dtype, c->D, g, stream, t_merge) != hipSuccess)
+  // A separate kernel merges the global rows' partials unless the band launch
+  // does (fp32, and bf16 launches of several rounds of workgroup slots).
+  if (n_g > 0 && !c->fuse_merge &&
+      lfattn::launch_glob_merge(c->dtype, c->D, g, stream, t_merge) != hipSuccess)
     return LFATTN_EHIP;
 
   if (timed) ++c->n_timed;
@@ -913,7 +958,9 @@ lfattn_status lfattn_set_timing(lfattn_t c, int enable) {
 lfattn_status lfattn_read_timing(lfattn_t c, double* band_ms, double* global_ms, int* n_forwards) {
   if (!c || !band_ms || !global_ms || !n_forwards) return LFATTN_EINVAL;
   double b = 0.0, g = 0.0;
-  const bool has_glob = c->n_gmax > 0;
+  // Global-row kernels besides the band launch: the partials (fp32) and the
+  // merge (unless the band launch merges).
+  const bool has_glob = c->n_gmax > 0 && !c->fuse_merge;
   if (c->n_timed > 0) {
     hipEvent_t* last = &c->ev[kEvPerForward * (c->n_timed - 1)];
     if (hipEventSynchronize(last[has_glob ? 5 : 1]) != hipSuccess) return LFATTN_EHIP;

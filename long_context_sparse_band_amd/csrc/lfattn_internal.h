@@ -19,6 +19,10 @@ constexpr int kMaxGlobalBf16 = 512;
 // Key chunks of the global rows are merged from one batch of loads; the
 // chunk count per row set is at most this.
 constexpr int kMergeBatch = 16;
+// The band launch merges a set of global rows itself (the last of its chunk
+// items to finish, from one round of loads) when the set has at most this
+// many key chunks; otherwise a separate merge kernel does.
+constexpr int kFuseChunks = 16;
 
 // One band workgroup's work: batch-head bh, dilation residue r, and the first
 // position t0 (in the residue's subsequence r, r+d, r+2d, ...) of its rows.
@@ -60,8 +64,11 @@ struct BandArgs {
   float sl2;                   // softmax scale times log2(e)
   int rows_per_wg;             // rows per band workgroup (bf16: 64 or 128)
   // Global-row items (dil 0): partial records laid out as GlobArgs::part
-  // with rows_per_wg rows per set, and the chunking of the keys.
+  // with rows_per_wg rows per set, and the chunking of the keys; gcount:
+  // one arrival count per (b*H + h, set), zero between calls (the workgroup
+  // that merges a set resets it), or null when a separate kernel merges.
   float* part;
+  unsigned* gcount;
   int n_sets, n_chunks, chunk_keys;
 };
 
@@ -137,6 +144,9 @@ hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, c
 bool band_takes_global_items(int dtype, int D);
 // Band workgroups one compute unit holds at once (registers and LDS).
 int band_workgroups_per_cu(int dtype, int D);
+// Rows per set of the global-row items of a bf16 band launch (D = 64: sets
+// of 64 rows in every launch; D = 128: the band workgroup's rows).
+int global_set_rows(int D, int band_rows);
 hipError_t launch_glob(int dtype, int D, int waves, const GlobArgs& a, int n_wg, hipStream_t s,
                        const Timing& t);
 hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s, const Timing& t);

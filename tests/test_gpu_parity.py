@@ -336,7 +336,7 @@ def test_forward_rejects_bad_pointers():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_timing_records_both_kernels(dtype):
+def test_timing_records_the_kernels(dtype):
     import torch
     inp = W.small_case(1, 2, 2048, 64, dtype, 512, glob=[0, 1, 2], seed=43)
     q, k, v = to_device(inp)
@@ -348,6 +348,8 @@ def test_timing_records_both_kernels(dtype):
         for _ in range(5):
             L.lfattn_forward(h, q, k, v, o)
         band, glob_ms, n = L.lfattn_read_timing(h)
+        # The global rows' merge (and, fp32, their partials) run as separate
+        # kernels.
         assert n == 5 and band > 0 and glob_ms > 0
         L.lfattn_set_timing(h, False)
     finally:
@@ -404,3 +406,38 @@ def test_destroy_waits_only_for_its_own_work():
     assert np.array_equal(o.float().cpu().numpy().astype(np.float64), ref)
     say(f"destroy {1e3 * t_destroy:.2f} ms, other stream's work {1e3 * t_busy:.2f} ms")
     assert t_destroy < 0.5 * t_busy
+
+
+@pytest.mark.parametrize("case", [
+    (1, 12, 4096, 64, 512, None, list(range(32)), 51),
+    (2, 2, 1000, 128, 256, [1, 2], [0, 7, 999], 52),
+    (1, 3, 3000, 64, 300, [1, 2, 3], list(range(0, 3000, 40)), 53),
+], ids=["longformer_base", "d128_two_batches", "dilated_75_globals"])
+def test_fused_global_merge_every_element(case, monkeypatch):
+    """The band launch merging the global rows itself (LFATTN_FUSE_MERGE=1:
+    device-coherent partial records, the last chunk item of a set merges),
+    every element against the oracle and bit-identical to the separate merge
+    kernel's output up to summation order (tolerance as any bf16 case)."""
+    import torch
+    B, H, N, D, window, dil, glob, seed = case
+    inp = W.small_case(B, H, N, D, "bf16", window, dilation=dil, glob=glob, seed=seed)
+    monkeypatch.setenv("LFATTN_FUSE_MERGE", "1")
+    say(f"fused global-row merge {case[:6]}")
+    got, pairs = run(inp)
+    h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, window, list(inp.dilation), list(inp.glob))
+    try:
+        band, glob_ms, _ = 0.0, 0.0, 0
+        L.lfattn_set_timing(h, True)
+        q, k, v = to_device(inp)
+        o = torch.empty_like(q)
+        for _ in range(3):  # the arrival counts return to zero after each call
+            L.lfattn_forward(h, q, k, v, o)
+        band, glob_ms, n = L.lfattn_read_timing(h)
+        assert n == 3 and band > 0 and glob_ms == 0  # no merge launch
+        again = o.float().cpu().numpy().astype(np.float64)
+    finally:
+        L.lfattn_destroy(h)
+    want = oracle.attention(inp.q, inp.k, inp.v, window, list(inp.dilation), list(inp.glob))
+    compare(got, want, "bf16", "fused merge")
+    assert np.array_equal(again, got)
+    assert pairs == oracle.count_pairs(B, H, N, window, list(inp.dilation), list(inp.glob))
