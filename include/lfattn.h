@@ -73,7 +73,7 @@
  * the device's compute units.  The environment variable LFATTN_BAND_ROWS,
  * set to 64 or 128 when lfattn_create runs, overrides that choice; results
  * are the same either way up to floating-point summation order.  The
- * backward (bf16, D = 64) takes 64-row items with split key tiles on its
+ * backward (bf16) takes 64-row items with split key tiles on its
  * query side and 128-key items on its key side; LFATTN_BWD_ROWS, 64 or 128
  * when lfattn_create runs, sets both sides to that size.
  *
@@ -217,7 +217,7 @@ lfattn_status lfattn_forward_lse(lfattn_t ctx, const void* Q, const void* K, con
  * chain rule through the row softmax of Eq. (1) of the Unlimiformer page):
  *   dS_ij = P_ij (dO_i . V_j - dO_i . O_i),   dQ_i = scale sum_j dS_ij K_j,
  *   dK_j = scale sum_i dS_ij Q_i,            dV_j = sum_i P_ij dO_i.
- * bf16 handles with D = 64 only (EUNSUPPORTED otherwise), every pattern.
+ * bf16 handles (D = 64 or 128; EUNSUPPORTED for fp32), every pattern.
  * Allocates nothing; the handle's workspace holds dO . O per row and the
  * global rows' and keys' partial gradients per key (row) chunk, summed in a
  * fixed order: results are the same bits on every run.  Launches kernels

@@ -1,6 +1,7 @@
 // bf16 backward pass for gfx950 (MI355X): dQ, dK, dV of band + global
-// attention, D = 64, for every pattern the forward takes (band, dilated,
-// causal, per-batch global sets, chunked attention with a memory prefix).
+// attention, D = 64 or 128, for every pattern the forward takes (band,
+// dilated, causal, per-batch global sets, chunked attention with a memory
+// prefix).
 //
 // With P = softmax over the row's key set of z = scale * q.k (recomputed from
 // the forward's per-row log-sum-exp, no running maximum needed) and the
@@ -40,9 +41,14 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kBD = 64;          // head dimension
-constexpr int kRB = 2 * kBD;     // bytes per row
-constexpr int kTileB = 32 * kRB; // bytes per 32-row tile
+// Per head dimension D: bytes per row, bytes per 32-row tile, 16-byte
+// chunks per row.
+template <int D>
+struct BwdDim {
+  static constexpr int RB = 2 * D;
+  static constexpr int TILE = 32 * RB;
+  static constexpr int CPR = RB / 16;
+};
 constexpr int kGCap = kMaxGlobalBf16;
 constexpr int kOutOfClass = 0x40000000;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -52,13 +58,20 @@ __device__ __forceinline__ constexpr int brow(int i, int hi) {
   return 8 * (i >> 2) + 4 * hi + (i & 3);
 }
 
-// Physical 16-byte chunk of logical chunk c in row `row` of a tile with
-// 128-byte rows (the forward's swizzle for 64 LDS banks: the 16 rows a
-// row read serves at a time, and the 4 rows x 4 chunks a transposed read
-// serves, each touch distinct banks).
+// Physical 16-byte chunk of logical chunk c in row `row` of a tile (the
+// forward's swizzles for 64 LDS banks: the 16 rows a row read serves at a
+// time, and the 4 rows x 4 chunks a transposed read serves, each touch
+// distinct banks).  D = 64 (128-byte rows): a bijection of row/2 moves the
+// 4-chunk block of row pairs 2 apart; D = 128 (256-byte rows): the block bits
+// differ over any 4 consecutive rows.
+template <int D>
 __device__ __forceinline__ int swz(int row, int c) {
-  const int j = (row >> 1) & 7;
-  return c ^ (((j & 1) << 2) | ((j >> 1) & 3));
+  if constexpr (D == 64) {
+    const int j = (row >> 1) & 7;
+    return c ^ (((j & 1) << 2) | ((j >> 1) & 3));
+  } else {
+    return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  }
 }
 
 // ds_read_b64_tr_b16 at an LDS byte address (lane transpose of 4x4 blocks of
@@ -89,9 +102,10 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 // The tile ring: two stages of up to two tiles (one per key split); after
 // the loop its first 32 KB hold the key splits' partial sums.
+template <int D>
 struct BwdSmem {
-  unsigned char x[2][2][kTileB];  // row side: K tiles; key side: Q tiles
-  unsigned char y[2][2][kTileB];  // row side: V tiles; key side: dO tiles
+  unsigned char x[2][2][BwdDim<D>::TILE];  // row side: K tiles; key side: Q tiles
+  unsigned char y[2][2][BwdDim<D>::TILE];  // row side: V tiles; key side: dO tiles
   // Key side: per tile row, -lse / scale (-inf for a row that takes no
   // part: its weights are exp2(-inf) = 0) and -Delta, the initial values of
   // the score and dP accumulators.
@@ -120,56 +134,82 @@ struct Pattern {
 // k-step k2 of a 32-row tile at LDS address base: lane L gets rows
 // 16k2 + 4(L/32) + j (j < 4) and 16k2 + 8 + 4(L/32) + (j - 4) of column
 // 32b + L%32, the row order of the packed weight registers 4k2 .. 4k2+3.
+template <int D>
 struct TrAddr {
-  unsigned off[2][2];
+  unsigned off[D / 32][2];
   __device__ void init(int lane) {
     const int g16 = lane >> 4, t16 = lane & 15;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < D / 32; ++b) {
       const int dcol = 32 * b + 16 * (g16 & 1) + 4 * (t16 & 3);
       const int c = dcol >> 3, half = (dcol >> 2) & 1;
       const int row0 = 4 * (g16 >> 1) + (t16 >> 2), row1 = row0 + 8;
-      off[b][0] = row0 * kRB + 16 * swz(row0, c) + 8 * half;
-      off[b][1] = row1 * kRB + 16 * swz(row1, c) + 8 * half;
+      off[b][0] = row0 * BwdDim<D>::RB + 16 * swz<D>(row0, c) + 8 * half;
+      off[b][1] = row1 * BwdDim<D>::RB + 16 * swz<D>(row1, c) + 8 * half;
     }
   }
 };
 
 // acc[b] += (tile at base)^T . W, W = the packed weights w[0..7] (bf16 pairs),
-// over the tile's 32 rows in two k-steps.
-__device__ __forceinline__ void tr_mfma(unsigned base, const TrAddr& ta, const unsigned* w,
+// over the tile's 32 rows in two k-steps (D = 128: one k-step's eight reads
+// at a time, fewer live operands).
+template <int D>
+__device__ __forceinline__ void tr_mfma(unsigned base, const TrAddr<D>& ta, const unsigned* w,
                                         f32x16* acc) {
-  s16x4 r[2][2][2];
+  constexpr int NB = D / 32, RB = BwdDim<D>::RB;
+  if constexpr (D == 64) {
+    s16x4 r[2][2][2];
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2)
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      r[k2][b][0] = tr_read(base + ta.off[b][0] + 16 * kRB * k2);
-      r[k2][b][1] = tr_read(base + ta.off[b][1] + 16 * kRB * k2);
+      for (int b = 0; b < 2; ++b) {
+        r[k2][b][0] = tr_read(base + ta.off[b][0] + 16 * RB * k2);
+        r[k2][b][1] = tr_read(base + ta.off[b][1] + 16 * RB * k2);
+      }
+    tr_wait(r[0][0][0], r[0][0][1], r[0][1][0], r[0][1][1], r[1][0][0], r[1][0][1], r[1][1][0],
+            r[1][1][1]);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const uint4 wu = make_uint4(w[4 * k2], w[4 * k2 + 1], w[4 * k2 + 2], w[4 * k2 + 3]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(r[k2][b][0], r[k2][b][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, wu),
+                                                         acc[b], 0, 0, 0);
+      }
     }
-  tr_wait(r[0][0][0], r[0][0][1], r[0][1][0], r[0][1][1], r[1][0][0], r[1][0][1], r[1][1][0],
-          r[1][1][1]);
+  } else {
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-    const uint4 wu = make_uint4(w[4 * k2], w[4 * k2 + 1], w[4 * k2 + 2], w[4 * k2 + 3]);
+    for (int k2 = 0; k2 < 2; ++k2) {
+      s16x4 r[NB][2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, __builtin_shufflevector(r[k2][b][0], r[k2][b][1], 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, wu), acc[b],
-                                                       0, 0, 0);
+      for (int b = 0; b < NB; ++b) {
+        r[b][0] = tr_read(base + ta.off[b][0] + 16 * RB * k2);
+        r[b][1] = tr_read(base + ta.off[b][1] + 16 * RB * k2);
+      }
+      tr_wait(r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]);
+      const uint4 wu = make_uint4(w[4 * k2], w[4 * k2 + 1], w[4 * k2 + 2], w[4 * k2 + 3]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(r[b][0], r[b][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, wu),
+                                                         acc[b], 0, 0, 0);
+      }
     }
   }
 }
 
 // s + sum_ks A_ks . B_ks with A from the 32 rows of the tile at LDS pointer t
 // (lane: row L%32, columns 16ks + 8(L/32) .. +7) and B in registers.
+template <int D>
 __device__ __forceinline__ f32x16 rows_mfma(const unsigned char* t, int l32, int hi,
                                             const bf16x8* bop, f32x16 s = f32x16{}) {
 #pragma unroll
-  for (int ks = 0; ks < kBD / 16; ++ks) {
+  for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 a = *(const LDS_AS bf16x8*)(const LDS_AS unsigned char*)
-        (t + l32 * kRB + 16 * swz(l32, 2 * ks + hi));
+        (t + l32 * BwdDim<D>::RB + 16 * swz<D>(l32, 2 * ks + hi));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[ks], s, 0, 0, 0);
   }
   return s;
@@ -183,7 +223,8 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
 
 // Stage the batch element's global positions (and their subsequence
 // positions in residue r of dilation d) in LDS.
-__device__ __forceinline__ void stage_globals(BwdSmem& sm, const int* gl, int ng, int r, int d) {
+template <class SM>
+__device__ __forceinline__ void stage_globals(SM& sm, const int* gl, int ng, int r, int d) {
   for (int x = threadIdx.x; x < ng; x += blockDim.x) {
     const int g = gl[x], off = g - r;
     sm.gpos[x] = g;
@@ -198,11 +239,17 @@ __device__ __forceinline__ void stage_globals(BwdSmem& sm, const int* gl, int ng
 // tiles.  KS = 2: two waves of 32 rows (64 per workgroup) take the even
 // tiles, the other two the odd ones, and the two partial dQ add up through
 // LDS at the end (twice the workgroups, half the tiles per wave).
-template <int KS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+// Wavefronts per SIMD of the backward kernels: D = 64 fits 168 registers
+// (3), D = 128 256 (2).
+template <int D>
+constexpr int bwd_wpe() { return D == 64 ? 3 : 2; }
+
+template <int D, int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_wpe<D>(), bwd_wpe<D>())))
 void bwd_rows_kernel(BwdArgs a) {
   constexpr int RB = 4 / KS, IR = 32 * RB;  // row blocks, rows per item
-  __shared__ __attribute__((aligned(16))) BwdSmem sm;
+  constexpr int kBD = D, TILE = BwdDim<D>::TILE, CPR = BwdDim<D>::CPR;
+  __shared__ __attribute__((aligned(16))) BwdSmem<D> sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rb = wave % RB, kq = wave / RB;
@@ -272,10 +319,12 @@ void bwd_rows_kernel(BwdArgs a) {
     if (t < n_band) return r + d * min(s_lo + 32 * t + rr, s_hi);
     return sm.gpos[min(32 * (t - n_band) + rr, ng - 1)];
   };
-  // One thread's share of a tile's loads: tile row tid/8, physical 16-byte
-  // chunk tid%8 (wave w fills bytes 1024 w .. 1024 w + 1023 of the tile).
-  // Step j holds tiles KS j .. KS j + KS - 1 in stage j % 2.
-  const int ld_row = tid >> 3, ld_c = swz(ld_row, tid & 7);
+  // One thread's share of a tile's loads: tile rows tid/CPR + 256/CPR e,
+  // physical 16-byte chunk tid%CPR (the 1 KB a wave's direct load fills are
+  // bytes 1024 (w + 4e) .. of the tile).  Step j holds tiles KS j .. KS j +
+  // KS - 1 in stage j % 2.
+  constexpr int NL = TILE / 4096;  // direct loads per matrix and thread
+  const int ld_row = tid / CPR, ld_c = swz<D>(ld_row, tid % CPR);
   const unsigned xl = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(LDS_AS void*)&sm.x[0][0][0] + 1024u * wave);
   const unsigned yl = __builtin_amdgcn_readfirstlane(
@@ -286,17 +335,22 @@ void bwd_rows_kernel(BwdArgs a) {
     for (int q2 = 0; q2 < KS; ++q2) {
       const int t = KS * j + q2;
       if (t < n_tiles) {
-        const size_t p = (size_t)key_pos(t, ld_row);
-        const unsigned so = (unsigned)((j & 1) * 2 + q2) * kTileB;
-        dma16(Kp + p * kBD + 8 * ld_c, xl + so);
-        dma16(Vp + p * kBD + 8 * ld_c, yl + so);
+        const unsigned so = (unsigned)((j & 1) * 2 + q2) * TILE;
+#pragma unroll
+        for (int e = 0; e < NL; ++e) {
+          const size_t p = (size_t)key_pos(t, ld_row + (256 / CPR) * e);
+          dma16(Kp + p * kBD + 8 * ld_c, xl + so + 4096u * e);
+          dma16(Vp + p * kBD + 8 * ld_c, yl + so + 4096u * e);
+        }
       }
     }
   };
 
-  TrAddr ta;
+  TrAddr<D> ta;
   ta.init(lane);
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) acc[b] = f32x16{};
 
   if (n_steps > 0) load(0);
   wait_vm0();
@@ -320,8 +374,8 @@ void bwd_rows_kernel(BwdArgs a) {
       }
     }
     if (act) {
-      const f32x16 s = rows_mfma(sm.x[st][kq], l32, hi, q);
-      const f32x16 dp = rows_mfma(sm.y[st][kq], l32, hi, g);
+      const f32x16 s = rows_mfma<D>(sm.x[st][kq], l32, hi, q);
+      const f32x16 dp = rows_mfma<D>(sm.y[st][kq], l32, hi, g);
       unsigned dsw[8];
       if (full) {
 #pragma unroll
@@ -354,7 +408,7 @@ void bwd_rows_kernel(BwdArgs a) {
         }
       }
       const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
-      tr_mfma(xb, ta, dsw, acc);
+      tr_mfma<D>(xb, ta, dsw, acc);
     }
     wait_vm0();
     __syncthreads();
@@ -362,14 +416,16 @@ void bwd_rows_kernel(BwdArgs a) {
   if (KS == 2) {
     // The odd-tile waves hand their sums to the even-tile waves of the
     // same rows (element e of lane L at float (32 rb + e) * 64 + L).
+    constexpr int NE = D / 2;  // accumulator elements per lane
+    static_assert(2 * NE * 64 * 4 <= sizeof(sm.x), "reduction area");
     float* red = (float*)&sm.x[0][0][0];
     if (kq == 1)
 #pragma unroll
-      for (int e = 0; e < 32; ++e) red[(32 * rb + e) * 64 + lane] = acc[e >> 4][e & 15];
+      for (int e = 0; e < NE; ++e) red[(NE * rb + e) * 64 + lane] = acc[e >> 4][e & 15];
     __syncthreads();
     if (kq == 1) return;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) acc[e >> 4][e & 15] += red[(32 * rb + e) * 64 + lane];
+    for (int e = 0; e < NE; ++e) acc[e >> 4][e & 15] += red[(NE * rb + e) * 64 + lane];
   }
 
   if (!row_ok) return;
@@ -378,7 +434,7 @@ void bwd_rows_kernel(BwdArgs a) {
   float* dq = gi ? a.gpart + (((size_t)w.bh * a.n_gch + t0) * a.n_glob + u) * kBD
                  : a.dQ + base + (size_t)pos_u * kBD;
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4)
       *(float4*)(dq + 32 * b + 8 * g4 + 4 * hi) =
@@ -391,11 +447,12 @@ void bwd_rows_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // KS as on the row side: 32 (KS = 2) or 128 (KS = 1) keys per workgroup, and
 // with KS = 2 the even and odd row tiles split between two pairs of waves.
-template <int KS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+template <int D, int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_wpe<D>(), bwd_wpe<D>())))
 void bwd_keys_kernel(BwdArgs a) {
   constexpr int RB = 4 / KS, IK = 32 * RB;  // key blocks, keys per item
-  __shared__ __attribute__((aligned(16))) BwdSmem sm;
+  constexpr int kBD = D, TILE = BwdDim<D>::TILE, CPR = BwdDim<D>::CPR;
+  __shared__ __attribute__((aligned(16))) BwdSmem<D> sm;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rb = wave % RB, kq = wave / RB;
@@ -473,27 +530,31 @@ void bwd_keys_kernel(BwdArgs a) {
   };
   // Tile loads as on the row side; the thread of chunk 0 of a row also
   // fetches the row's -lse / scale and -Delta.
-  const int ld_row = tid >> 3, ld_c = swz(ld_row, tid & 7);
-  const bool ld_meta = (tid & 7) == 0;
+  constexpr int NL = TILE / 4096;  // direct loads per matrix and thread
+  const int ld_row = tid / CPR, ld_c = swz<D>(ld_row, tid % CPR);
+  const bool ld_meta = (tid % CPR) == 0;
   const unsigned xl = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(LDS_AS void*)&sm.x[0][0][0] + 1024u * wave);
   const unsigned yl = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(LDS_AS void*)&sm.y[0][0][0] + 1024u * wave);
   const int n_steps = (n_tiles + KS - 1) / KS;
-  float m_lse[KS], m_dlt[KS];
+  float m_lse[KS][NL], m_dlt[KS][NL];
   auto load = [&](int j) {
 #pragma unroll
     for (int q2 = 0; q2 < KS; ++q2) {
       const int t = KS * j + q2;
       if (t < n_tiles) {
-        bool part;
-        const int p = row_pos(t, ld_row, part);
-        const unsigned so = (unsigned)((j & 1) * 2 + q2) * kTileB;
-        dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so);
-        dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so);
-        if (ld_meta) {
-          m_lse[q2] = part ? -lsep[p] / a.scale : -__builtin_inff();
-          m_dlt[q2] = -dlp[p];
+        const unsigned so = (unsigned)((j & 1) * 2 + q2) * TILE;
+#pragma unroll
+        for (int e = 0; e < NL; ++e) {
+          bool part;
+          const int p = row_pos(t, ld_row + (256 / CPR) * e, part);
+          dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so + 4096u * e);
+          dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so + 4096u * e);
+          if (ld_meta) {
+            m_lse[q2][e] = part ? -lsep[p] / a.scale : -__builtin_inff();
+            m_dlt[q2][e] = -dlp[p];
+          }
         }
       }
     }
@@ -501,15 +562,19 @@ void bwd_keys_kernel(BwdArgs a) {
   auto store_meta = [&](int j) {
 #pragma unroll
     for (int q2 = 0; q2 < KS; ++q2)
-      if (ld_meta && KS * j + q2 < n_tiles) {
-        sm.nls[j & 1][q2][ld_row] = m_lse[q2];
-        sm.ndl[j & 1][q2][ld_row] = m_dlt[q2];
-      }
+      if (ld_meta && KS * j + q2 < n_tiles)
+#pragma unroll
+        for (int e = 0; e < NL; ++e) {
+          sm.nls[j & 1][q2][ld_row + (256 / CPR) * e] = m_lse[q2][e];
+          sm.ndl[j & 1][q2][ld_row + (256 / CPR) * e] = m_dlt[q2][e];
+        }
   };
 
-  TrAddr ta;
+  TrAddr<D> ta;
   ta.init(lane);
-  f32x16 accK[2] = {f32x16{}, f32x16{}}, accV[2] = {f32x16{}, f32x16{}};
+  f32x16 accK[D / 32], accV[D / 32];
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) accK[b] = accV[b] = f32x16{};
 
   if (n_steps > 0) {
     load(0);
@@ -544,8 +609,8 @@ void bwd_keys_kernel(BwdArgs a) {
         s0[4 * i4] = l4.x; s0[4 * i4 + 1] = l4.y; s0[4 * i4 + 2] = l4.z; s0[4 * i4 + 3] = l4.w;
         d0[4 * i4] = d4.x; d0[4 * i4 + 1] = d4.y; d0[4 * i4 + 2] = d4.z; d0[4 * i4 + 3] = d4.w;
       }
-      const f32x16 s = rows_mfma(sm.x[st][kq], l32, hi, kr, s0);
-      const f32x16 dp = rows_mfma(sm.y[st][kq], l32, hi, vr, d0);
+      const f32x16 s = rows_mfma<D>(sm.x[st][kq], l32, hi, kr, s0);
+      const f32x16 dp = rows_mfma<D>(sm.y[st][kq], l32, hi, vr, d0);
       unsigned pw[8], dsw[8];
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
@@ -565,8 +630,8 @@ void bwd_keys_kernel(BwdArgs a) {
       }
       const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
       const unsigned yb = (unsigned)(uintptr_t)(LDS_AS void*)sm.y[st][kq];
-      tr_mfma(yb, ta, pw, accV);   // dV^T += dO^T P
-      tr_mfma(xb, ta, dsw, accK);  // dK^T += Q^T dS
+      tr_mfma<D>(yb, ta, pw, accV);   // dV^T += dO^T P
+      tr_mfma<D>(xb, ta, dsw, accK);  // dK^T += Q^T dS
     }
     if (j + 1 < n_steps) store_meta(j + 1);
     wait_vm0();
@@ -574,20 +639,22 @@ void bwd_keys_kernel(BwdArgs a) {
   }
   if (KS == 2) {
     // As on the row side, for dK (in the x half of the ring) and dV (y).
+    constexpr int NE = D / 2;  // accumulator elements per lane
+    static_assert(2 * NE * 64 * 4 <= sizeof(sm.x), "reduction area");
     float* rk = (float*)&sm.x[0][0][0];
     float* rv = (float*)&sm.y[0][0][0];
     if (kq == 1)
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        rk[(32 * rb + e) * 64 + lane] = accK[e >> 4][e & 15];
-        rv[(32 * rb + e) * 64 + lane] = accV[e >> 4][e & 15];
+      for (int e = 0; e < NE; ++e) {
+        rk[(NE * rb + e) * 64 + lane] = accK[e >> 4][e & 15];
+        rv[(NE * rb + e) * 64 + lane] = accV[e >> 4][e & 15];
       }
     __syncthreads();
     if (kq == 1) return;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      accK[e >> 4][e & 15] += rk[(32 * rb + e) * 64 + lane];
-      accV[e >> 4][e & 15] += rv[(32 * rb + e) * 64 + lane];
+    for (int e = 0; e < NE; ++e) {
+      accK[e >> 4][e & 15] += rk[(NE * rb + e) * 64 + lane];
+      accV[e >> 4][e & 15] += rv[(NE * rb + e) * 64 + lane];
     }
   }
 
@@ -598,7 +665,7 @@ void bwd_keys_kernel(BwdArgs a) {
                  : a.dK + base + (size_t)pos_k * kBD;
   float* dv = gk ? dk + plane : a.dV + base + (size_t)pos_k * kBD;
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int c = 32 * b + 8 * g4 + 4 * hi;
@@ -616,13 +683,15 @@ void bwd_keys_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Global rows and keys: the sums of the chunks' partial gradients.
 // ---------------------------------------------------------------------------
-// One workgroup per (b*h, global slot), 192 threads: plane (dQ, dK, dV) and
+// One workgroup per (b*h, global slot), 3 D threads: plane (dQ, dK, dV) and
 // column; each adds the slot's partials over the chunks and writes the row.
-__global__ __launch_bounds__(192) void bwd_merge_kernel(BwdArgs a) {
+template <int D>
+__global__ __launch_bounds__(3 * D) void bwd_merge_kernel(BwdArgs a) {
+  constexpr int kBD = D;
   const int bh = blockIdx.x / a.n_glob, g = blockIdx.x % a.n_glob;
   const int2 gs = a.gsel[bh / a.H];
   if (g >= gs.y) return;
-  const int pl = threadIdx.x >> 6, col = threadIdx.x & 63;
+  const int pl = threadIdx.x / D, col = threadIdx.x % D;
   const size_t plane = (size_t)a.n_bh * a.n_gch * a.n_glob * kBD;
   const float* src = a.gpart + pl * plane + ((size_t)bh * a.n_gch * a.n_glob + g) * kBD + col;
   float sum = 0.0f;
@@ -632,19 +701,28 @@ __global__ __launch_bounds__(192) void bwd_merge_kernel(BwdArgs a) {
   dst[((size_t)bh * a.N + a.glob[gs.x + g]) * kBD + col] = sum;
 }
 
+template <int D>
+static hipError_t launch_backward_d(const BwdArgs& rows, const BwdArgs& keys, int n_rows_wg,
+                                   int n_keys_wg, hipStream_t s, const Timing* t) {
+  hipError_t e = launch_kernel(rows.ks == 2 ? bwd_rows_kernel<D, 2> : bwd_rows_kernel<D, 1>,
+                               dim3(n_rows_wg), dim3(256), s, rows, t[0]);
+  if (e != hipSuccess) return e;
+  e = launch_kernel(keys.ks == 2 ? bwd_keys_kernel<D, 2> : bwd_keys_kernel<D, 1>, dim3(n_keys_wg),
+                    dim3(256), s, keys, t[1]);
+  if (e != hipSuccess || keys.n_glob <= 0) return e;
+  return launch_kernel(bwd_merge_kernel<D>, dim3((unsigned)(keys.n_bh * keys.n_glob)),
+                       dim3(3 * D), s, keys, t[2]);
+}
+
 hipError_t launch_backward_bf16(const BwdArgs& rows, const BwdArgs& keys, int n_rows_wg,
                                 int n_keys_wg, hipStream_t s, const Timing* t) {
   for (const BwdArgs* a : {&rows, &keys})
-    if (a->D != kBD || a->n_glob > kGCap || (a->ks != 1 && a->ks != 2)) return hipErrorInvalidValue;
+    if ((a->D != 64 && a->D != 128) || a->D != rows.D || a->n_glob > kGCap ||
+        (a->ks != 1 && a->ks != 2))
+      return hipErrorInvalidValue;
   if (n_rows_wg <= 0 || n_keys_wg <= 0) return hipSuccess;
-  hipError_t e = launch_kernel(rows.ks == 2 ? bwd_rows_kernel<2> : bwd_rows_kernel<1>,
-                               dim3(n_rows_wg), dim3(256), s, rows, t[0]);
-  if (e != hipSuccess) return e;
-  e = launch_kernel(keys.ks == 2 ? bwd_keys_kernel<2> : bwd_keys_kernel<1>, dim3(n_keys_wg),
-                    dim3(256), s, keys, t[1]);
-  if (e != hipSuccess || keys.n_glob <= 0) return e;
-  return launch_kernel(bwd_merge_kernel, dim3((unsigned)(keys.n_bh * keys.n_glob)), dim3(192), s,
-                       keys, t[2]);
+  return rows.D == 64 ? launch_backward_d<64>(rows, keys, n_rows_wg, n_keys_wg, s, t)
+                      : launch_backward_d<128>(rows, keys, n_rows_wg, n_keys_wg, s, t);
 }
 
 }  // namespace lfattn

@@ -391,7 +391,7 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   // row-tile stream shared by four 32-key blocks), the faster choice of each
   // on the bf16 workloads measured; LFATTN_BWD_ROWS=64 or 128 sets both (both
   // give the same results; this lets the tests run every kernel).
-  if (dtype == LFATTN_BF16 && D == 64) {
+  if (dtype == LFATTN_BF16) {
     c->bwd_rows[0] = 64;
     c->bwd_rows[1] = 128;
     if (const char* e = std::getenv("LFATTN_BWD_ROWS")) {
@@ -537,7 +537,7 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   // items of bwd_rows global positions against a chunk of bwd_chunk keys
   // (row side) or rows (key side).
   std::vector<BandWork> btable;
-  const bool has_bwd = dtype == LFATTN_BF16 && D == 64;
+  const bool has_bwd = dtype == LFATTN_BF16;
   if (has_bwd) {
     c->bwd_chunk = std::max(kBwdChunk, (N + kBwdMaxChunks * 32 - 1) / (kBwdMaxChunks * 32) * 32);
     c->n_gch = (N + c->bwd_chunk - 1) / c->bwd_chunk;
@@ -845,7 +845,7 @@ lfattn_status lfattn_backward(lfattn_t c, const void* Q, const void* K, const vo
                               const void* O, const void* dO, const float* LSE, float* dQ,
                               float* dK, float* dV, hipStream_t stream) {
   if (!c || !Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return LFATTN_EINVAL;
-  if (c->dtype != LFATTN_BF16 || c->D != 64) return LFATTN_EUNSUPPORTED;
+  if (c->dtype != LFATTN_BF16) return LFATTN_EUNSUPPORTED;
   const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O |
                          (uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK | (uintptr_t)dV) & 15u;
   if (mis || ((uintptr_t)LSE & 3u)) return LFATTN_EINVAL;

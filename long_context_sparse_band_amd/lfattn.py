@@ -213,7 +213,7 @@ def lfattn_forward_lse(handle: int, Q, K, V, O, LSE, stream=None) -> None:
 
 def lfattn_backward(handle: int, Q, K, V, O, dO, LSE, dQ, dK, dV, stream=None) -> None:
     """Gradients dQ, dK, dV (float32 device tensors [B, H, N, D]) of the forward
-    for the upstream gradient dO; LSE from lfattn_forward_lse.  bf16, D = 64."""
+    for the upstream gradient dO; LSE from lfattn_forward_lse.  bf16 handles."""
     lib = load()
     _check(lib.lfattn_backward(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE),
                                _ptr(dQ), _ptr(dK), _ptr(dV), _stream(stream)),
@@ -315,7 +315,7 @@ class LFAttention:
         return O, LSE
 
     def backward(self, Q, K, V, O, dO, LSE, dQ, dK, dV, stream=None):
-        """Gradients into the caller's fp32 dQ, dK, dV (bf16, D = 64 handles)."""
+        """Gradients into the caller's fp32 dQ, dK, dV (bf16 handles)."""
         lfattn_backward(self.handle, Q, K, V, O, dO, LSE, dQ, dK, dV, stream)
         return dQ, dK, dV
 

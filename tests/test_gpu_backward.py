@@ -1,6 +1,7 @@
-"""GPU parity of the backward pass (lfattn_backward, bf16, D = 64): dQ, dK, dV
-against the oracle's double-precision gradients on the same bf16-valued
-inputs, every pattern, both forward band kernels feeding the log-sum-exp."""
+"""GPU parity of the backward pass (lfattn_backward, bf16, D = 64 and 128): dQ,
+dK, dV against the oracle's double-precision gradients on the same
+bf16-valued inputs, every pattern, both forward band kernels feeding the
+log-sum-exp."""
 
 import numpy as np
 import pytest
@@ -57,16 +58,17 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("rows_mode", [64, 128])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0] + "_N%d" % c[1]["N"])
-def test_backward_every_element(case, rows_mode, monkeypatch):
+def test_backward_every_element(case, rows_mode, D, monkeypatch):
     import torch
     # Both forward band kernels (the log-sum-exp) and both backward item
     # sizes (64 rows with split tiles, 128 rows with one tile stream).
     monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows_mode))
     monkeypatch.setenv("LFATTN_BWD_ROWS", str(rows_mode))
     kind, p = case
-    B, H, N, D = p["B"], p["H"], p["N"], 64
+    B, H, N = p["B"], p["H"], p["N"]
     a = W.small_case(B, H, N, D, "bf16", p.get("window", 0), dilation=p.get("dil"), seed=88)
     rng = np.random.default_rng(89)
     do = _bf16(rng.standard_normal((B, H, N, D)).astype(np.float32))
@@ -92,7 +94,7 @@ def test_backward_every_element(case, rows_mode, monkeypatch):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         dq, dk, dv = (torch.full((B, H, N, D), float("nan"), dtype=torch.float32,
                                  device=q.device) for _ in range(3))
-        say(f"backward {kind} {p} rows {rows_mode}")
+        say(f"backward {kind} {p} D {D} rows {rows_mode}")
         L.lfattn_forward_lse(h, q, k, v, o, lse)
         L.lfattn_backward(h, q, k, v, o, g, lse, dq, dk, dv)
         torch.cuda.synchronize()
@@ -104,7 +106,8 @@ def test_backward_every_element(case, rows_mode, monkeypatch):
     say(f"  relative max/mean errors dq dk dv: {errs}")
 
 
-FULL = ["longformer_base_n4096", "dilated_charlm_n8192", "gmat_memory_m64_l16384"]
+FULL = ["longformer_base_n4096", "dilated_charlm_n8192", "gmat_memory_m64_l16384",
+        "long_stress_n65536_d128"]
 
 
 @pytest.mark.parametrize("bwd_rows", [64, 128])
@@ -168,12 +171,12 @@ def test_backward_timing_records_each_call():
 
 def test_backward_rejects_bad_arguments():
     """Error paths, all taken before any kernel launch: handles the backward
-    does not support, misaligned pointers, outputs overlapping an input or
-    each other."""
+    does not support (fp32), misaligned pointers, outputs overlapping an
+    input or each other."""
     import torch
     dev = "cuda:0"
     B, H, N = 1, 1, 64
-    for dtype, D in ((L.LFATTN_F32, 64), (L.LFATTN_BF16, 128)):
+    for dtype, D in ((L.LFATTN_F32, 64), (L.LFATTN_F32, 128)):
         h = L.lfattn_create(B, H, N, D, dtype, 8, None, [0])
         try:
             t = torch.zeros((B, H, N, D), dtype=torch.float32, device=dev)
