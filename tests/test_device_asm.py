@@ -88,7 +88,7 @@ def test_d64_bf16_kernels_use_no_scratch(device_asm):
     for name, text in device_asm.items():
         for fn, body in _functions(text):
             d64_band = "band32_kernel" in fn and "ILi64E" in fn
-            d64_bwd = "bwd_" in fn and "kernel" in fn
+            d64_bwd = "bwd_" in fn and "kernel" in fn and "ILi64E" in fn
             if not (d64_band or d64_bwd):
                 continue
             checked += 1
@@ -96,6 +96,6 @@ def test_d64_bf16_kernels_use_no_scratch(device_asm):
         for m in re.finditer(r"\.name:\s+(\S+)\n(?:.*\n)*?\s+\.private_segment_fixed_size:\s+(\d+)",
                              text):
             fn, size = m.group(1), int(m.group(2))
-            if ("band32_kernel" in fn and "ILi64E" in fn) or ("bwd_" in fn and "kernel" in fn):
+            if "ILi64E" in fn and ("band32_kernel" in fn or "bwd_" in fn):
                 assert size == 0, (fn, size)
     assert checked >= 4
