@@ -87,6 +87,13 @@ def _load():
                                            ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int,
                                            i32p, i32p, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_double, ctypes.c_int]
+        lib.lfo_attention_grad_ex.restype = ctypes.c_int
+        lib.lfo_attention_grad_ex.argtypes = [f32p, f32p, f32p, f32p, f32p, f32p, f32p,
+                                              f64p, f64p, f64p, f64p, f64p, f64p,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int,
+                                              i32p, i32p, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_double, ctypes.c_int]
         lib.lfo_row_lse.restype = ctypes.c_int
         lib.lfo_row_lse.argtypes = [f32p, f32p, f64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, i32p, i32p,
@@ -250,13 +257,21 @@ def attention_chunked(q, k, v, chunk: int, n_memory: int, scale: float = 0.0, ro
 
 def attention_grad(q, k, v, do, window: int = 0, dilation=None, glob=(), batch_glob=None,
                    causal: bool = False, chunk: int = 0, n_memory: int = 0, scale: float = 0.0,
-                   nthreads: int | None = None):
+                   nthreads: int | None = None, qg=None, kg=None, vg=None):
     """Gradients (dq, dk, dv), float64 [B, H, N, D], of the attention output
     for the upstream gradient do, under the same patterns as attention() and
-    attention_chunked() (chunk > 0), with the ordinary projections."""
+    attention_chunked() (chunk > 0).  With qg, kg, vg (the global rows' own
+    projections; a missing one is q, k or v) returns (dq, dk, dv, dqg, dkg,
+    dvg): the global rows' terms go to the last three."""
     lib = _load()
     q, k, v, do = (np.ascontiguousarray(x, dtype=np.float32) for x in (q, k, v, do))
     B, H, N, D = q.shape
+    proj = not (qg is None and kg is None and vg is None)
+    if proj:
+        qg, kg, vg = (np.ascontiguousarray(y if y is not None else x, dtype=np.float32)
+                      for x, y in ((q, qg), (k, kg), (v, vg)))
+        for x in (qg, kg, vg):
+            assert x.shape == q.shape
     if batch_glob is not None:
         flat = [int(x) for lst in batch_glob for x in lst]
         offs = np.cumsum([0] + [len(lst) for lst in batch_glob]).astype(np.int32)
@@ -268,15 +283,18 @@ def attention_grad(q, k, v, do, window: int = 0, dilation=None, glob=(), batch_g
     d, dp = _i32(dilation)
     if nthreads is None:
         nthreads = os.cpu_count() or 1
-    out = [np.empty((B, H, N, D), dtype=np.float64) for _ in range(3)]
+    out = [np.empty((B, H, N, D), dtype=np.float64) for _ in range(6 if proj else 3)]
     f32p = ctypes.POINTER(ctypes.c_float)
     f64p = ctypes.POINTER(ctypes.c_double)
-    st = lib.lfo_attention_grad(q.ctypes.data_as(f32p), k.ctypes.data_as(f32p),
-                                v.ctypes.data_as(f32p), do.ctypes.data_as(f32p),
-                                out[0].ctypes.data_as(f64p), out[1].ctypes.data_as(f64p),
-                                out[2].ctypes.data_as(f64p), B, H, N, D, window, dp,
-                                int(causal), gp, gop, len(g), int(chunk), int(n_memory),
-                                float(scale), int(nthreads))
+    pin = [x.ctypes.data_as(f32p) if proj else None for x in ((qg, kg, vg) if proj else (0, 0, 0))]
+    pout = [out[3 + x].ctypes.data_as(f64p) if proj else None for x in range(3)]
+    st = lib.lfo_attention_grad_ex(q.ctypes.data_as(f32p), k.ctypes.data_as(f32p),
+                                   v.ctypes.data_as(f32p), pin[0], pin[1], pin[2],
+                                   do.ctypes.data_as(f32p), out[0].ctypes.data_as(f64p),
+                                   out[1].ctypes.data_as(f64p), out[2].ctypes.data_as(f64p),
+                                   pout[0], pout[1], pout[2], B, H, N, D, window, dp,
+                                   int(causal), gp, gop, len(g), int(chunk), int(n_memory),
+                                   float(scale), int(nthreads))
     if st != 0:
         raise ValueError("oracle: gradient failed (code %d)" % st)
     return tuple(out)

@@ -426,10 +426,15 @@ int lfo_attention_chunked(const float* Q, const float* K, const float* V,
  *   dK_j  += scale * dS_j Q_i
  *   dV_j  += P_j dO_i
  * One worker per (batch, head) pair, so the K and V gradients need no locks.
+ * With separate projections for the global rows (the reading of
+ * lfo_attention_ex), a global row i takes Qg_i, Kg_j, Vg_j in place of Q_i,
+ * K_j, V_j in all of the above, and its terms go to dQg_i, dKg_j, dVg_j.
  */
 typedef struct {
   const float *Q, *K, *V, *dO;
+  const float *Qg, *Kg, *Vg;  /* NULL: the global rows share Q, K, V */
   double *dQ, *dK, *dV;
+  double *dQg, *dKg, *dVg;    /* used when Qg is not NULL */
   int B, H, N, D, window, causal, chunk, n_memory, n_glob;
   const int* dilation;
   const int* glob;
@@ -456,12 +461,18 @@ static void* grad_worker(void* arg) {
     const int* gl = jb->goff ? jb->glob + jb->goff[b] : jb->glob;
     const int ng = jb->goff ? jb->goff[b + 1] - jb->goff[b] : jb->n_glob;
     const size_t off = (size_t)bh * N * D;
-    const float *Qh = jb->Q + off, *Kh = jb->K + off, *Vh = jb->V + off, *dOh = jb->dO + off;
-    double *dQh = jb->dQ + off, *dKh = jb->dK + off, *dVh = jb->dV + off;
+    const float* dOh = jb->dO + off;
     for (int i = 0; i < N; ++i) {
       int64_t n = jb->chunk > 0 ? lfo_allowed_set_chunked(N, jb->chunk, jb->n_memory, i, keys)
                                 : lfo_allowed_set_ex(N, jb->window, d, jb->causal, gl, ng, i, keys);
       if (n <= 0) { jb->status = LFO_EINVAL; break; }
+      /* The row's projections and gradient outputs. */
+      const int own = jb->Qg != NULL &&
+                      (jb->chunk > 0 ? i < jb->n_memory : is_global(gl, ng, i));
+      const float *Qh = (own ? jb->Qg : jb->Q) + off, *Kh = (own ? jb->Kg : jb->K) + off;
+      const float* Vh = (own ? jb->Vg : jb->V) + off;
+      double *dQh = (own ? jb->dQg : jb->dQ) + off, *dKh = (own ? jb->dKg : jb->dK) + off;
+      double* dVh = (own ? jb->dVg : jb->dV) + off;
       const float* q = Qh + (size_t)i * D;
       const float* g = dOh + (size_t)i * D;
       /* Softmax over S_i (max subtracted first). */
@@ -506,11 +517,21 @@ static void* grad_worker(void* arg) {
  * lfo_attention_ex; chunk > 0 selects chunked attention with n_memory memory
  * tokens instead.  Returns LFO_OK or a negative error.
  */
-int lfo_attention_grad(const float* Q, const float* K, const float* V, const float* dO,
-                       double* dQ, double* dK, double* dV, int B, int H, int N, int D,
-                       int window, const int* dilation, int causal, const int* glob,
-                       const int* goff, int n_glob, int chunk, int n_memory, double scale,
-                       int nthreads) {
+/*
+ * As lfo_attention_grad, with separate projections Qg, Kg, Vg for the global
+ * rows (the memory rows when chunk > 0) and their gradients dQg, dKg, dVg
+ * (doubles, [B, H, N, D], overwritten).  Qg, Kg, Vg all NULL (and dQg, dKg,
+ * dVg ignored): the shared-projection gradients of lfo_attention_grad.
+ */
+int lfo_attention_grad_ex(const float* Q, const float* K, const float* V, const float* Qg,
+                          const float* Kg, const float* Vg, const float* dO, double* dQ,
+                          double* dK, double* dV, double* dQg, double* dKg, double* dVg, int B,
+                          int H, int N, int D, int window, const int* dilation, int causal,
+                          const int* glob, const int* goff, int n_glob, int chunk, int n_memory,
+                          double scale, int nthreads) {
+  const int proj = Qg != NULL;
+  if (proj && (!Kg || !Vg || !dQg || !dKg || !dVg)) return LFO_EINVAL;
+  if (!proj && (Kg || Vg)) return LFO_EINVAL;
   if (!Q || !K || !V || !dO || !dQ || !dK || !dV || B <= 0 || H <= 0 || N <= 0 || D <= 0 ||
       window < 0 || chunk < 0 || n_memory < 0 || n_memory > N)
     return LFO_EINVAL;
@@ -529,6 +550,11 @@ int lfo_attention_grad(const float* Q, const float* K, const float* V, const flo
   memset(dQ, 0, total * sizeof(double));
   memset(dK, 0, total * sizeof(double));
   memset(dV, 0, total * sizeof(double));
+  if (proj) {
+    memset(dQg, 0, total * sizeof(double));
+    memset(dKg, 0, total * sizeof(double));
+    memset(dVg, 0, total * sizeof(double));
+  }
   const int64_t n_bh = (int64_t)B * H;
   if (nthreads < 1) nthreads = 1;
   if ((int64_t)nthreads > n_bh) nthreads = (int)n_bh;
@@ -539,6 +565,8 @@ int lfo_attention_grad(const float* Q, const float* K, const float* V, const flo
   for (int t = 0; t < nthreads; ++t) {
     lfo_grad_job* jb = &jobs[t];
     jb->Q = Q; jb->K = K; jb->V = V; jb->dO = dO; jb->dQ = dQ; jb->dK = dK; jb->dV = dV;
+    jb->Qg = proj ? Qg : NULL; jb->Kg = Kg; jb->Vg = Vg;
+    jb->dQg = dQg; jb->dKg = dKg; jb->dVg = dVg;
     jb->B = B; jb->H = H; jb->N = N; jb->D = D; jb->window = window; jb->causal = causal;
     jb->chunk = chunk; jb->n_memory = n_memory; jb->n_glob = n_glob;
     jb->dilation = dilation; jb->glob = glob; jb->goff = goff; jb->scale = scale;
@@ -558,6 +586,16 @@ int lfo_attention_grad(const float* Q, const float* K, const float* V, const flo
     if (jobs[t].status != LFO_OK) st = jobs[t].status;
   free(jobs); free(tids); free(created);
   return st;
+}
+
+int lfo_attention_grad(const float* Q, const float* K, const float* V, const float* dO,
+                       double* dQ, double* dK, double* dV, int B, int H, int N, int D,
+                       int window, const int* dilation, int causal, const int* glob,
+                       const int* goff, int n_glob, int chunk, int n_memory, double scale,
+                       int nthreads) {
+  return lfo_attention_grad_ex(Q, K, V, NULL, NULL, NULL, dO, dQ, dK, dV, NULL, NULL, NULL, B, H,
+                               N, D, window, dilation, causal, glob, goff, n_glob, chunk,
+                               n_memory, scale, nthreads);
 }
 
 /*

@@ -144,3 +144,106 @@ def test_row_lse_matches_torch_logsumexp():
                 z = z / np.sqrt(D) + torch.from_numpy(np.where(masks[b][h], 0.0, -np.inf))
                 np.testing.assert_allclose(got[b, h], torch.logsumexp(z, dim=1).numpy(),
                                            rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Separate projections for the global rows (the memory rows of chunked
+# attention): a global row i attends all keys with Qg_i, Kg, Vg; every other
+# row keeps Q, K, V over its set.
+# ---------------------------------------------------------------------------
+
+def _torch_grads_proj(q, k, v, qg, kg, vg, do, masks_per_b, gsets_per_b):
+    """Autograd through the dense two-projection form in float64: a global
+    row's output is softmax(scale Qg_i Kg^T) Vg over every key, any other
+    row's the masked softmax with Q, K, V."""
+    ts = [torch.from_numpy(x).double().requires_grad_(True) for x in (q, k, v, qg, kg, vg)]
+    qt, kt, vt, qgt, kgt, vgt = ts
+    B, H, N, D = q.shape
+    outs = []
+    for b in range(B):
+        rows = []
+        isg = torch.zeros(N, dtype=torch.bool)
+        isg[list(gsets_per_b[b])] = True
+        for h in range(H):
+            add = torch.from_numpy(np.where(masks_per_b[b][h], 0.0, -np.inf))
+            ob = torch.softmax((qt[b, h] @ kt[b, h].T) / np.sqrt(D) + add, dim=1) @ vt[b, h]
+            og = torch.softmax((qgt[b, h] @ kgt[b, h].T) / np.sqrt(D), dim=1) @ vgt[b, h]
+            rows.append(torch.where(isg[:, None], og, ob))
+        outs.append(torch.stack(rows))
+    o = torch.stack(outs)
+    (o * torch.from_numpy(do).double()).sum().backward()
+    return tuple(t.grad.numpy() for t in ts)
+
+
+def _proj_case(rng, t):
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    N, D = int(rng.integers(2, 40)), int(rng.choice([1, 4, 8]))
+    kind = ["band", "batch", "chunked"][t % 3]
+    dil = [int(x) for x in rng.integers(1, 4, size=H)]
+    window = int(rng.integers(0, 2 * N + 3))
+    if kind == "chunked":
+        chunk, M = int(rng.integers(1, 12)), int(rng.integers(1, min(N, 4) + 1))
+        masks = [_mask(N, H, ("chunked", chunk, M))] * B
+        return B, H, N, D, masks, [list(range(M))] * B, dict(chunk=chunk, n_memory=M)
+    sets = []
+    for _ in range(B if kind == "batch" else 1):
+        n_g = int(rng.integers(1, min(N, 4) + 1))
+        sets.append(sorted(rng.choice(N, size=n_g, replace=False).tolist()))
+    if kind == "band":
+        sets = sets * B
+        kw = dict(window=window, dilation=dil, glob=sets[0])
+    else:
+        kw = dict(window=window, dilation=dil, batch_glob=sets)
+    masks = [_mask(N, H, ("band", window, dil, sets[b])) for b in range(B)]
+    return B, H, N, D, masks, sets, kw
+
+
+def test_gradients_with_global_projections_match_torch_autograd():
+    rng = np.random.default_rng(61)
+    for t in range(24):
+        B, H, N, D, masks, gsets, kw = _proj_case(rng, t)
+        a = W.small_case(B, H, N, D, "f32", 0, seed=900 + t)
+        g = W.small_case(B, H, N, D, "f32", 0, seed=1900 + t)
+        do = rng.standard_normal((B, H, N, D)).astype(np.float32)
+        got = oracle.attention_grad(a.q, a.k, a.v, do, qg=g.q, kg=g.k, vg=g.v, **kw)
+        want = _torch_grads_proj(a.q, a.k, a.v, g.q, g.k, g.v, do, masks, gsets)
+        for x, w, n in zip(got, want, ("dq", "dk", "dv", "dqg", "dkg", "dvg")):
+            np.testing.assert_allclose(x, w, rtol=1e-9, atol=1e-10, err_msg=f"case {t} {n}")
+
+
+def test_gradients_with_global_projections_closed_forms():
+    """Each head: the V gradients of the global rows' attention add up to their
+    dO rows and the others' to the rest; both K gradient sums vanish; rows
+    outside G have no Qg gradient and rows in G no Q gradient."""
+    rng = np.random.default_rng(62)
+    for t in range(12):
+        B, H, N, D, masks, gsets, kw = _proj_case(rng, t)
+        a = W.small_case(B, H, N, D, "f32", 0, seed=950 + t)
+        g = W.small_case(B, H, N, D, "f32", 0, seed=1950 + t)
+        do = rng.standard_normal((B, H, N, D)).astype(np.float64)
+        dq, dk, dv, dqg, dkg, dvg = oracle.attention_grad(a.q, a.k, a.v, do.astype(np.float32),
+                                                          qg=g.q, kg=g.k, vg=g.v, **kw)
+        do32 = do.astype(np.float32).astype(np.float64)
+        for b in range(B):
+            isg = np.zeros(N, dtype=bool)
+            isg[gsets[b]] = True
+            for h in range(H):
+                np.testing.assert_allclose(dvg[b, h].sum(0), do32[b, h][isg].sum(0), atol=1e-9)
+                np.testing.assert_allclose(dv[b, h].sum(0), do32[b, h][~isg].sum(0), atol=1e-9)
+                np.testing.assert_allclose(dkg[b, h].sum(0), 0.0, atol=1e-9)
+                np.testing.assert_allclose(dk[b, h].sum(0), 0.0, atol=1e-9)
+                assert np.all(dq[b, h][isg] == 0.0) and np.all(dqg[b, h][~isg] == 0.0)
+
+
+def test_gradients_with_shared_global_projections_add_up():
+    """Qg = Q, Kg = K, Vg = V: the two gradient sets add up to the shared-
+    projection gradients."""
+    rng = np.random.default_rng(63)
+    for t in range(9):
+        B, H, N, D, masks, gsets, kw = _proj_case(rng, t)
+        a = W.small_case(B, H, N, D, "f32", 0, seed=990 + t)
+        do = rng.standard_normal((B, H, N, D)).astype(np.float32)
+        six = oracle.attention_grad(a.q, a.k, a.v, do, qg=a.q, kg=a.k, vg=a.v, **kw)
+        three = oracle.attention_grad(a.q, a.k, a.v, do, **kw)
+        for x, y, w in zip(six[:3], six[3:], three):
+            np.testing.assert_allclose(x + y, w, rtol=1e-12, atol=1e-12)
