@@ -208,6 +208,16 @@ lfattn_status lfattn_forward_lse(lfattn_t ctx, const void* Q, const void* K, con
                                  void* O, float* LSE, hipStream_t stream);
 
 /*
+ * As lfattn_forward_global_proj, also writing LSE as lfattn_forward_lse does
+ * (the global rows' from their own projections): the forward whose output
+ * and log-sum-exp lfattn_backward_global_proj takes.  bf16 handles only.
+ */
+lfattn_status lfattn_forward_global_proj_lse(lfattn_t ctx, const void* Q, const void* K,
+                                             const void* V, const void* Qg, const void* Kg,
+                                             const void* Vg, void* O, float* LSE,
+                                             hipStream_t stream);
+
+/*
  * Backward pass: gradients of the forward (lfattn_forward / lfattn_forward_lse,
  * the ordinary projections) for the upstream gradient dO.  Q, K, V: the
  * forward's inputs; O and LSE: its output and log-sum-exp (from
@@ -226,6 +236,26 @@ lfattn_status lfattn_forward_lse(lfattn_t ctx, const void* Q, const void* K, con
 lfattn_status lfattn_backward(lfattn_t ctx, const void* Q, const void* K, const void* V,
                               const void* O, const void* dO, const float* LSE, float* dQ,
                               float* dK, float* dV, hipStream_t stream);
+
+/*
+ * Backward pass of the forward with separate global-row projections
+ * (lfattn_forward_global_proj_lse; Qg, Kg, Vg may each be NULL for Q, K, V):
+ * a global row i of batch element b scores every key with Qg_i, Kg, Vg, so
+ * its terms of the chain rule above go to dQg_i, dKg_j, dVg_j, while every
+ * other row's go to dQ, dK, dV as in lfattn_backward (the global-attention
+ * bullet of the Longformer glossary page: global attention has its own query,
+ * key and value projections).  All six outputs are fp32 [B, H, N, D] arrays,
+ * fully overwritten (dQ is zero on global rows and dQg on the others),
+ * overlapping no input and each other.  With Qg = Q, Kg = K and Vg = V the
+ * sums dQ + dQg, dK + dKg and dV + dVg are lfattn_backward's gradients.
+ * Errors and execution as lfattn_backward.
+ */
+lfattn_status lfattn_backward_global_proj(lfattn_t ctx, const void* Q, const void* K,
+                                          const void* V, const void* Qg, const void* Kg,
+                                          const void* Vg, const void* O, const void* dO,
+                                          const float* LSE, float* dQ, float* dK, float* dV,
+                                          float* dQg, float* dKg, float* dVg,
+                                          hipStream_t stream);
 
 /* Release the handle and its device memory.  The memory is returned with
  * stream-ordered frees behind the work enqueued so far on the stream of the

@@ -259,9 +259,10 @@ void bwd_rows_kernel(BwdArgs a) {
   const int d = gi ? 1 : w.dil, r = gi ? 0 : w.r, N = a.N;
   const int Lr = d == 1 ? N - r : (N - r + d - 1) / d;
   const size_t base = (size_t)w.bh * N * kBD;
-  const unsigned short* Qp = (const unsigned short*)a.Q + base;
-  const unsigned short* Kp = (const unsigned short*)a.K + base;
-  const unsigned short* Vp = (const unsigned short*)a.V + base;
+  // Global-row items attend with the global rows' projections.
+  const unsigned short* Qp = (const unsigned short*)(gi ? a.Qg : a.Q) + base;
+  const unsigned short* Kp = (const unsigned short*)(gi ? a.Kg : a.K) + base;
+  const unsigned short* Vp = (const unsigned short*)(gi ? a.Vg : a.V) + base;
   const unsigned short* dOp = (const unsigned short*)a.dO + base;
   const unsigned short* Op = (const unsigned short*)a.O + base;
   const int* gl = a.glob + w.g0;
@@ -429,7 +430,16 @@ void bwd_rows_kernel(BwdArgs a) {
   }
 
   if (!row_ok) return;
-  if (!gi && isg[pos_u]) return;  // a global row: its dQ comes from the global-row items
+  // With separate projections a band row has no Qg gradient.
+  if (a.proj && !gi) {
+    float* dqg = a.dQg + base + (size_t)pos_u * kBD;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(float4*)(dqg + 32 * b + 8 * g4 + 4 * hi) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (!gi && isg[pos_u]) return;  // a global row: its gradient comes from the global-row items
   // Band row: its dQ.  Global-row item: the chunk's partial dQ of slot u.
   float* dq = gi ? a.gpart + (((size_t)w.bh * a.n_gch + t0) * a.n_glob + u) * kBD
                  : a.dQ + base + (size_t)pos_u * kBD;
@@ -447,7 +457,9 @@ void bwd_rows_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // KS as on the row side: 32 (KS = 2) or 128 (KS = 1) keys per workgroup, and
 // with KS = 2 the even and odd row tiles split between two pairs of waves.
-template <int D, int KS>
+// PROJ: the global rows take their own projections (a separate
+// instantiation: a second pass over the gathered global rows).
+template <int D, int KS, bool PROJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_wpe<D>(), bwd_wpe<D>())))
 void bwd_keys_kernel(BwdArgs a) {
   constexpr int RB = 4 / KS, IK = 32 * RB;  // key blocks, keys per item
@@ -463,8 +475,6 @@ void bwd_keys_kernel(BwdArgs a) {
   const int Lr = d == 1 ? N - r : (N - r + d - 1) / d;
   const size_t base = (size_t)w.bh * N * kBD;
   const unsigned short* Qp = (const unsigned short*)a.Q + base;
-  const unsigned short* Kp = (const unsigned short*)a.K + base;
-  const unsigned short* Vp = (const unsigned short*)a.V + base;
   const unsigned short* dOp = (const unsigned short*)a.dO + base;
   const float* lsep = a.lse + (size_t)w.bh * N;
   const float* dlp = a.delta + (size_t)w.bh * N;
@@ -503,20 +513,28 @@ void bwd_keys_kernel(BwdArgs a) {
 
   // Operands of the keys: K and V rows (B of S = Q K^T and dP = dO V^T).
   bf16x8 kr[kBD / 16], vr[kBD / 16];
+  auto load_keys = [&](const void* Ksrc, const void* Vsrc) {
+    const unsigned short* Kp = (const unsigned short*)Ksrc + base;
+    const unsigned short* Vp = (const unsigned short*)Vsrc + base;
 #pragma unroll
-  for (int ks = 0; ks < kBD / 16; ++ks) {
-    kr[ks] = *(const bf16x8*)(Kp + (size_t)pos_k * kBD + 16 * ks + 8 * hi);
-    vr[ks] = *(const bf16x8*)(Vp + (size_t)pos_k * kBD + 16 * ks + 8 * hi);
-  }
+    for (int ks = 0; ks < kBD / 16; ++ks) {
+      kr[ks] = *(const bf16x8*)(Kp + (size_t)pos_k * kBD + 16 * ks + 8 * hi);
+      vr[ks] = *(const bf16x8*)(Vp + (size_t)pos_k * kBD + 16 * ks + 8 * hi);
+    }
+  };
+  load_keys(a.K, a.V);
 
   // Query position of row rr of tile t and whether it takes part (a global
-  // row of a band tile is left to the gathered global rows; a row past the
-  // end of the tile's rows takes the last one and no part).
+  // row of a band tile is left to the gathered global rows, and with separate
+  // projections a global row of a global-key item's chunk to those too; a row
+  // past the end of the tile's rows takes the last one and no part).
   auto row_pos = [&](int t, int rr, bool& part) -> int {
     if (gk) {
       const int p = c0 + 32 * t + rr;
       part = p < c1;
-      return min(p, c1 - 1);
+      const int pc = min(p, c1 - 1);
+      if (PROJ) part = part && !isg[pc];
+      return pc;
     }
     if (t < n_band) {
       const int uq = q_lo + 32 * t + rr;
@@ -537,13 +555,14 @@ void bwd_keys_kernel(BwdArgs a) {
       (unsigned)(uintptr_t)(LDS_AS void*)&sm.x[0][0][0] + 1024u * wave);
   const unsigned yl = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(LDS_AS void*)&sm.y[0][0][0] + 1024u * wave);
-  const int n_steps = (n_tiles + KS - 1) / KS;
   float m_lse[KS][NL], m_dlt[KS][NL];
+  // Tiles tb .. te-1 of this item; step j holds tiles tb + KS j .. + KS - 1.
+  int tb = 0, te = n_tiles;
   auto load = [&](int j) {
 #pragma unroll
     for (int q2 = 0; q2 < KS; ++q2) {
-      const int t = KS * j + q2;
-      if (t < n_tiles) {
+      const int t = tb + KS * j + q2;
+      if (t < te) {
         const unsigned so = (unsigned)((j & 1) * 2 + q2) * TILE;
 #pragma unroll
         for (int e = 0; e < NL; ++e) {
@@ -562,7 +581,7 @@ void bwd_keys_kernel(BwdArgs a) {
   auto store_meta = [&](int j) {
 #pragma unroll
     for (int q2 = 0; q2 < KS; ++q2)
-      if (ld_meta && KS * j + q2 < n_tiles)
+      if (ld_meta && tb + KS * j + q2 < te)
 #pragma unroll
         for (int e = 0; e < NL; ++e) {
           sm.nls[j & 1][q2][ld_row + (256 / CPR) * e] = m_lse[q2][e];
@@ -573,109 +592,137 @@ void bwd_keys_kernel(BwdArgs a) {
   TrAddr<D> ta;
   ta.init(lane);
   f32x16 accK[D / 32], accV[D / 32];
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b) accK[b] = accV[b] = f32x16{};
 
-  if (n_steps > 0) {
-    load(0);
-    store_meta(0);
-  }
-  wait_vm0();
-  __syncthreads();
-  for (int j = 0; j < n_steps; ++j) {
-    const int st = j & 1, t = KS * j + kq;
-    if (j + 1 < n_steps) load(j + 1);
-    // The tile's rows reach one of this wave's keys; a band tile whose rows
-    // all score all of them needs no mask (rlo and rhi are non-decreasing;
-    // rows taking no part carry lse +inf, gathered global rows score every
-    // key, and keys before the first chunk are global: their lanes are not
-    // stored).
-    bool act = ka < n_keys && t < n_tiles, full = true;
-    if (!gk && t < n_band) {
-      const int u0 = q_lo + 32 * t, u1 = min(u0 + 31, q_hi);
-      const int kb = min(ka + 31, n_keys - 1), kf = ka > kfirst ? ka : kfirst;
-      act = act && (u0 <= pat.rhi(kb)) && (u1 >= pat.rlo(kf));
-      full = (u0 >= pat.rlo(kb)) && (u1 <= pat.rhi(kf));
+  // The sums over tiles tb .. te-1 in accK, accV (KS = 2: in the even-tile
+  // waves, the odd-tile waves' halves added through LDS).
+  auto run = [&]() {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) accK[b] = accV[b] = f32x16{};
+    const int n_steps = (te - tb + KS - 1) / KS;
+    if (n_steps > 0) {
+      load(0);
+      store_meta(0);
     }
-    if (act) {
-      // Rows 8j + 4hi .. +3 of a result block sit in registers 4j .. 4j+3:
-      // the accumulators start at -lse / scale and -Delta of their rows, so
-      // s = q.k - lse / scale and dp = dO.v - Delta.
-      f32x16 s0, d0;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 l4 = *(const float4*)&sm.nls[st][kq][8 * i4 + 4 * hi];
-        const float4 d4 = *(const float4*)&sm.ndl[st][kq][8 * i4 + 4 * hi];
-        s0[4 * i4] = l4.x; s0[4 * i4 + 1] = l4.y; s0[4 * i4 + 2] = l4.z; s0[4 * i4 + 3] = l4.w;
-        d0[4 * i4] = d4.x; d0[4 * i4 + 1] = d4.y; d0[4 * i4 + 2] = d4.z; d0[4 * i4 + 3] = d4.w;
-      }
-      const f32x16 s = rows_mfma<D>(sm.x[st][kq], l32, hi, kr, s0);
-      const f32x16 dp = rows_mfma<D>(sm.y[st][kq], l32, hi, vr, d0);
-      unsigned pw[8], dsw[8];
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        float p2[2], ds2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          float p = __builtin_amdgcn_exp2f(s[i + e] * a.sl2);
-          if (!full) {
-            const int qq = brow(i + e, hi);
-            p = (unsigned)(q_lo + 32 * t + qq - rlo_k) <= rspan_k ? p : 0.0f;
-          }
-          p2[e] = p;
-          ds2[e] = p * dp[i + e];
-        }
-        pw[i / 2] = pack2(p2[0], p2[1]);
-        dsw[i / 2] = pack2(ds2[0], ds2[1]);
-      }
-      const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
-      const unsigned yb = (unsigned)(uintptr_t)(LDS_AS void*)sm.y[st][kq];
-      tr_mfma<D>(yb, ta, pw, accV);   // dV^T += dO^T P
-      tr_mfma<D>(xb, ta, dsw, accK);  // dK^T += Q^T dS
-    }
-    if (j + 1 < n_steps) store_meta(j + 1);
     wait_vm0();
     __syncthreads();
-  }
-  if (KS == 2) {
-    // As on the row side, for dK (in the x half of the ring) and dV (y).
-    constexpr int NE = D / 2;  // accumulator elements per lane
-    static_assert(2 * NE * 64 * 4 <= sizeof(sm.x), "reduction area");
-    float* rk = (float*)&sm.x[0][0][0];
-    float* rv = (float*)&sm.y[0][0][0];
-    if (kq == 1)
-#pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        rk[(NE * rb + e) * 64 + lane] = accK[e >> 4][e & 15];
-        rv[(NE * rb + e) * 64 + lane] = accV[e >> 4][e & 15];
+    for (int j = 0; j < n_steps; ++j) {
+      const int st = j & 1, t = tb + KS * j + kq;
+      if (j + 1 < n_steps) load(j + 1);
+      // The tile's rows reach one of this wave's keys; a band tile whose rows
+      // all score all of them needs no mask (rlo and rhi are non-decreasing;
+      // rows taking no part carry lse +inf, gathered global rows score every
+      // key, and keys before the first chunk are global: their lanes are not
+      // stored).
+      bool act = ka < n_keys && t < te, full = true;
+      if (!gk && t < n_band) {
+        const int u0 = q_lo + 32 * t, u1 = min(u0 + 31, q_hi);
+        const int kb = min(ka + 31, n_keys - 1), kf = ka > kfirst ? ka : kfirst;
+        act = act && (u0 <= pat.rhi(kb)) && (u1 >= pat.rlo(kf));
+        full = (u0 >= pat.rlo(kb)) && (u1 <= pat.rhi(kf));
       }
-    __syncthreads();
-    if (kq == 1) return;
+      if (act) {
+        // Rows 8j + 4hi .. +3 of a result block sit in registers 4j .. 4j+3:
+        // the accumulators start at -lse / scale and -Delta of their rows, so
+        // s = q.k - lse / scale and dp = dO.v - Delta.
+        f32x16 s0, d0;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      accK[e >> 4][e & 15] += rk[(NE * rb + e) * 64 + lane];
-      accV[e >> 4][e & 15] += rv[(NE * rb + e) * 64 + lane];
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const float4 l4 = *(const float4*)&sm.nls[st][kq][8 * i4 + 4 * hi];
+          const float4 d4 = *(const float4*)&sm.ndl[st][kq][8 * i4 + 4 * hi];
+          s0[4 * i4] = l4.x; s0[4 * i4 + 1] = l4.y; s0[4 * i4 + 2] = l4.z; s0[4 * i4 + 3] = l4.w;
+          d0[4 * i4] = d4.x; d0[4 * i4 + 1] = d4.y; d0[4 * i4 + 2] = d4.z; d0[4 * i4 + 3] = d4.w;
+        }
+        const f32x16 s = rows_mfma<D>(sm.x[st][kq], l32, hi, kr, s0);
+        const f32x16 dp = rows_mfma<D>(sm.y[st][kq], l32, hi, vr, d0);
+        unsigned pw[8], dsw[8];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          float p2[2], ds2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            float p = __builtin_amdgcn_exp2f(s[i + e] * a.sl2);
+            if (!full) {
+              const int qq = brow(i + e, hi);
+              p = (unsigned)(q_lo + 32 * t + qq - rlo_k) <= rspan_k ? p : 0.0f;
+            }
+            p2[e] = p;
+            ds2[e] = p * dp[i + e];
+          }
+          pw[i / 2] = pack2(p2[0], p2[1]);
+          dsw[i / 2] = pack2(ds2[0], ds2[1]);
+        }
+        const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
+        const unsigned yb = (unsigned)(uintptr_t)(LDS_AS void*)sm.y[st][kq];
+        tr_mfma<D>(yb, ta, pw, accV);   // dV^T += dO^T P
+        tr_mfma<D>(xb, ta, dsw, accK);  // dK^T += Q^T dS
+      }
+      if (j + 1 < n_steps) store_meta(j + 1);
+      wait_vm0();
+      __syncthreads();
+    }
+    if constexpr (KS == 2) {
+      // As on the row side, for dK (in the x half of the ring) and dV (y).
+      constexpr int NE = D / 2;  // accumulator elements per lane
+      static_assert(2 * NE * 64 * 4 <= sizeof(sm.x), "reduction area");
+      float* rk = (float*)&sm.x[0][0][0];
+      float* rv = (float*)&sm.y[0][0][0];
+      if (kq == 1)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          rk[(NE * rb + e) * 64 + lane] = accK[e >> 4][e & 15];
+          rv[(NE * rb + e) * 64 + lane] = accV[e >> 4][e & 15];
+        }
+      __syncthreads();
+      if (kq == 0)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          accK[e >> 4][e & 15] += rk[(NE * rb + e) * 64 + lane];
+          accV[e >> 4][e & 15] += rv[(NE * rb + e) * 64 + lane];
+        }
+      __syncthreads();  // the ring is free again
+    }
+  };
+  // Key lane's dK (scaled) and dV rows at dk and dv.
+  auto store = [&](float* dk, float* dv) {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = 32 * b + 8 * g4 + 4 * hi;
+        const float4 kv = make_float4(a.scale * accK[b][4 * g4], a.scale * accK[b][4 * g4 + 1],
+                                      a.scale * accK[b][4 * g4 + 2], a.scale * accK[b][4 * g4 + 3]);
+        const float4 vv = make_float4(accV[b][4 * g4], accV[b][4 * g4 + 1], accV[b][4 * g4 + 2],
+                                      accV[b][4 * g4 + 3]);
+        *(float4*)(dk + c) = kv;
+        *(float4*)(dv + c) = vv;
+      }
+  };
+  const bool holder = KS == 1 || kq == 0;  // holds the item's sums after run()
+
+  // Shared projections: band rows and gathered global rows together.  With
+  // separate projections: band rows first (dK, dV), then the gathered global
+  // rows with Qg and the keys' Kg, Vg (dKg, dVg of every key of the item).
+  if (PROJ && !gk) te = n_band;
+  run();
+  if (holder && key_band) {
+    // Band key: its dK, dV.  Global-key item: the chunk's partials of slot k.
+    const size_t plane = (size_t)a.n_bh * a.n_gch * a.n_glob * kBD;
+    float* dk = gk ? a.gpart + plane + (((size_t)w.bh * a.n_gch + t0) * a.n_glob + k) * kBD
+                   : a.dK + base + (size_t)pos_k * kBD;
+    float* dv = gk ? dk + plane : a.dV + base + (size_t)pos_k * kBD;
+    store(dk, dv);
+  }
+  if constexpr (PROJ) {
+    if (!gk) {
+      tb = n_band;
+      te = n_tiles;
+      Qp = (const unsigned short*)a.Qg + base;
+      load_keys(a.Kg, a.Vg);
+      run();
+      if (holder && key_ok)
+        store(a.dKg + base + (size_t)pos_k * kBD, a.dVg + base + (size_t)pos_k * kBD);
     }
   }
-
-  if (!key_band) return;
-  // Band key: its dK, dV.  Global-key item: the chunk's partials of slot k.
-  const size_t plane = (size_t)a.n_bh * a.n_gch * a.n_glob * kBD;
-  float* dk = gk ? a.gpart + plane + (((size_t)w.bh * a.n_gch + t0) * a.n_glob + k) * kBD
-                 : a.dK + base + (size_t)pos_k * kBD;
-  float* dv = gk ? dk + plane : a.dV + base + (size_t)pos_k * kBD;
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int c = 32 * b + 8 * g4 + 4 * hi;
-      const float4 kv = make_float4(a.scale * accK[b][4 * g4], a.scale * accK[b][4 * g4 + 1],
-                                    a.scale * accK[b][4 * g4 + 2], a.scale * accK[b][4 * g4 + 3]);
-      const float4 vv = make_float4(accV[b][4 * g4], accV[b][4 * g4 + 1], accV[b][4 * g4 + 2],
-                                    accV[b][4 * g4 + 3]);
-      *(float4*)(dk + c) = kv;
-      *(float4*)(dv + c) = vv;
-    }
 }
 
 }  // namespace
@@ -697,8 +744,12 @@ __global__ __launch_bounds__(3 * D) void bwd_merge_kernel(BwdArgs a) {
   float sum = 0.0f;
 #pragma unroll 8
   for (int ch = 0; ch < a.n_gch; ++ch) sum += src[(size_t)ch * a.n_glob * kBD];
-  float* dst = pl == 0 ? a.dQ : (pl == 1 ? a.dK : a.dV);
-  dst[((size_t)bh * a.N + a.glob[gs.x + g]) * kBD + col] = sum;
+  // The global rows' dQ partials: their Qg gradient with separate
+  // projections (and no Q gradient).
+  float* dst = pl == 0 ? (a.proj ? a.dQg : a.dQ) : (pl == 1 ? a.dK : a.dV);
+  const size_t at = ((size_t)bh * a.N + a.glob[gs.x + g]) * kBD + col;
+  dst[at] = sum;
+  if (pl == 0 && a.proj) a.dQ[at] = 0.0f;
 }
 
 template <int D>
@@ -707,8 +758,9 @@ static hipError_t launch_backward_d(const BwdArgs& rows, const BwdArgs& keys, in
   hipError_t e = launch_kernel(rows.ks == 2 ? bwd_rows_kernel<D, 2> : bwd_rows_kernel<D, 1>,
                                dim3(n_rows_wg), dim3(256), s, rows, t[0]);
   if (e != hipSuccess) return e;
-  e = launch_kernel(keys.ks == 2 ? bwd_keys_kernel<D, 2> : bwd_keys_kernel<D, 1>, dim3(n_keys_wg),
-                    dim3(256), s, keys, t[1]);
+  auto kk = keys.proj ? (keys.ks == 2 ? bwd_keys_kernel<D, 2, true> : bwd_keys_kernel<D, 1, true>)
+                      : (keys.ks == 2 ? bwd_keys_kernel<D, 2, false> : bwd_keys_kernel<D, 1, false>);
+  e = launch_kernel(kk, dim3(n_keys_wg), dim3(256), s, keys, t[1]);
   if (e != hipSuccess || keys.n_glob <= 0) return e;
   return launch_kernel(bwd_merge_kernel<D>, dim3((unsigned)(keys.n_bh * keys.n_glob)),
                        dim3(3 * D), s, keys, t[2]);

@@ -743,6 +743,20 @@ lfattn_status lfattn_forward_noalloc(lfattn_t c, const void* Q, const void* K, c
   return forward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, nullptr, stream, part, counts);
 }
 
+lfattn_status lfattn_forward_global_proj_lse(lfattn_t c, const void* Q, const void* K,
+                                             const void* V, const void* Qg, const void* Kg,
+                                             const void* Vg, void* O, float* LSE,
+                                             hipStream_t stream) {
+  if (!c || !LSE) return LFATTN_EINVAL;
+  if (c->dtype != LFATTN_BF16) return LFATTN_EUNSUPPORTED;
+  // The global-row projections must not overlap the log-sum-exp either.
+  const size_t bytes = (size_t)c->B * c->H * c->N * c->D * 2;
+  const size_t lbytes = (size_t)c->B * c->H * c->N * sizeof(float);
+  for (const void* in : {Qg, Kg, Vg})
+    if (in && overlaps2(LSE, lbytes, in, bytes)) return LFATTN_EINVAL;
+  return forward_impl(c, Q, K, V, Qg, Kg, Vg, O, LSE, stream, c->d_part, c->d_gcount);
+}
+
 lfattn_status lfattn_forward_lse(lfattn_t c, const void* Q, const void* K, const void* V,
                                  void* O, float* LSE, hipStream_t stream) {
   if (!c || !LSE) return LFATTN_EINVAL;
@@ -837,27 +851,33 @@ lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void*
   return LFATTN_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-lfattn_status lfattn_backward(lfattn_t c, const void* Q, const void* K, const void* V,
-                              const void* O, const void* dO, const float* LSE, float* dQ,
-                              float* dK, float* dV, hipStream_t stream) {
+// The backward pass; proj: the global rows' own projections Qg, Kg, Vg
+// (NULL: Q, K, V) with their gradients in dQg, dKg, dVg.
+lfattn_status backward_impl(lfattn_t c, const void* Q, const void* K, const void* V,
+                            const void* Qg, const void* Kg, const void* Vg, const void* O,
+                            const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                            float* dQg, float* dKg, float* dVg, bool proj, hipStream_t stream) {
   if (!c || !Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return LFATTN_EINVAL;
+  if (proj && (!dQg || !dKg || !dVg)) return LFATTN_EINVAL;
   if (c->dtype != LFATTN_BF16) return LFATTN_EUNSUPPORTED;
-  const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O |
-                         (uintptr_t)dO | (uintptr_t)dQ | (uintptr_t)dK | (uintptr_t)dV) & 15u;
+  if (!Qg) Qg = Q;
+  if (!Kg) Kg = K;
+  if (!Vg) Vg = V;
+  uintptr_t mis = ((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO |
+                   (uintptr_t)dQ | (uintptr_t)dK | (uintptr_t)dV | (uintptr_t)Qg |
+                   (uintptr_t)Kg | (uintptr_t)Vg) & 15u;
+  if (proj) mis |= ((uintptr_t)dQg | (uintptr_t)dKg | (uintptr_t)dVg) & 15u;
   if (mis || ((uintptr_t)LSE & 3u)) return LFATTN_EINVAL;
   const size_t n_el = (size_t)c->B * c->H * c->N * c->D;
   const size_t in_b = n_el * 2, out_b = n_el * 4, lse_b = (size_t)c->B * c->H * c->N * 4;
   // The outputs overlap no input and no other output.
-  const void* outs[3] = {dQ, dK, dV};
-  for (int x = 0; x < 3; ++x) {
-    for (const void* in : {Q, K, V, O, dO})
+  const void* outs[6] = {dQ, dK, dV, dQg, dKg, dVg};
+  const int n_out = proj ? 6 : 3;
+  for (int x = 0; x < n_out; ++x) {
+    for (const void* in : {Q, K, V, O, dO, Qg, Kg, Vg})
       if (overlaps2(outs[x], out_b, in, in_b)) return LFATTN_EINVAL;
     if (overlaps2(outs[x], out_b, LSE, lse_b)) return LFATTN_EINVAL;
-    for (int y = x + 1; y < 3; ++y)
+    for (int y = x + 1; y < n_out; ++y)
       if (overlaps2(outs[x], out_b, outs[y], out_b)) return LFATTN_EINVAL;
   }
   int cur = -1;
@@ -866,6 +886,9 @@ lfattn_status lfattn_backward(lfattn_t c, const void* Q, const void* K, const vo
   lfattn::BwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.lse = LSE; a.delta = c->d_delta;
   a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.Qg = Qg; a.Kg = Kg; a.Vg = Vg;
+  a.dQg = proj ? dQg : nullptr; a.dKg = proj ? dKg : nullptr; a.dVg = proj ? dVg : nullptr;
+  a.proj = proj ? 1 : 0;
   a.glob = c->d_glob; a.is_glob = c->d_isglob;
   a.isg_stride = c->shared ? 0 : c->N;
   a.H = c->H; a.N = c->N; a.D = c->D; a.n_bh = c->B * c->H;
@@ -890,6 +913,27 @@ lfattn_status lfattn_backward(lfattn_t c, const void* Q, const void* K, const vo
   if (lfattn::launch_backward_bf16(a, ak, c->n_bwork[0], c->n_bwork[1], stream, t) != hipSuccess)
     return LFATTN_EHIP;
   return LFATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lfattn_status lfattn_backward(lfattn_t c, const void* Q, const void* K, const void* V,
+                              const void* O, const void* dO, const float* LSE, float* dQ,
+                              float* dK, float* dV, hipStream_t stream) {
+  return backward_impl(c, Q, K, V, nullptr, nullptr, nullptr, O, dO, LSE, dQ, dK, dV, nullptr,
+                       nullptr, nullptr, false, stream);
+}
+
+lfattn_status lfattn_backward_global_proj(lfattn_t c, const void* Q, const void* K,
+                                          const void* V, const void* Qg, const void* Kg,
+                                          const void* Vg, const void* O, const void* dO,
+                                          const float* LSE, float* dQ, float* dK, float* dV,
+                                          float* dQg, float* dKg, float* dVg,
+                                          hipStream_t stream) {
+  return backward_impl(c, Q, K, V, Qg, Kg, Vg, O, dO, LSE, dQ, dK, dV, dQg, dKg, dVg, true,
+                       stream);
 }
 
 lfattn_status lfattn_destroy(lfattn_t c) {

@@ -105,6 +105,16 @@ struct BwdArgs {
   float* dQ;                   // [B, H, N, D] fp32 outputs
   float* dK;
   float* dV;
+  // The global rows' own projections (the same pointers as Q, K, V when the
+  // forward shared them) and, with proj set, their gradients: the global
+  // rows' terms go to dQg, dKg, dVg ([B, H, N, D] fp32) instead of dQ, dK, dV.
+  const void* Qg;
+  const void* Kg;
+  const void* Vg;
+  float* dQg;
+  float* dKg;
+  float* dVg;
+  int proj;
   const BandWork* work;
   const int* glob;
   const unsigned char* is_glob;

@@ -26,7 +26,8 @@ LFATTN_BF16 = 1
 
 # Every entry point include/lfattn.h declares.
 EXPORTS = ("lfattn_create", "lfattn_create_masked", "lfattn_create_causal",
-           "lfattn_create_chunked", "lfattn_forward", "lfattn_forward_noalloc", "lfattn_forward_lse", "lfattn_backward",
+           "lfattn_create_chunked", "lfattn_forward", "lfattn_forward_noalloc", "lfattn_forward_lse",
+           "lfattn_forward_global_proj_lse", "lfattn_backward_global_proj", "lfattn_backward",
            "lfattn_forward_global_proj", "lfattn_destroy", "lfattn_status_string",
            "lfattn_scored_pairs", "lfattn_band_launch_pairs", "lfattn_band_rows",
            "lfattn_global_list", "lfattn_global_list_batch",
@@ -70,6 +71,10 @@ def load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_float]
     lib.lfattn_forward.restype = ctypes.c_int
     lib.lfattn_forward.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.lfattn_forward_global_proj_lse.restype = ctypes.c_int
+    lib.lfattn_forward_global_proj_lse.argtypes = [vp] * 10
+    lib.lfattn_backward_global_proj.restype = ctypes.c_int
+    lib.lfattn_backward_global_proj.argtypes = [vp] * 17
     lib.lfattn_forward_noalloc.restype = ctypes.c_int
     lib.lfattn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.lfattn_backward.restype = ctypes.c_int
@@ -192,6 +197,28 @@ def lfattn_forward(handle: int, Q, K, V, O, stream=None) -> None:
     lib = load()
     _check(lib.lfattn_forward(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _stream(stream)),
            "lfattn_forward")
+
+
+def lfattn_forward_global_proj_lse(handle: int, Q, K, V, Qg, Kg, Vg, O, LSE,
+                                   stream=None) -> None:
+    """lfattn_forward_global_proj that also writes each row's log-sum-exp
+    (the global rows' from their own projections); bf16 handles."""
+    lib = load()
+    _check(lib.lfattn_forward_global_proj_lse(handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(Qg),
+                                              _ptr(Kg), _ptr(Vg), _ptr(O), _ptr(LSE),
+                                              _stream(stream)),
+           "lfattn_forward_global_proj_lse")
+
+
+def lfattn_backward_global_proj(handle: int, Q, K, V, Qg, Kg, Vg, O, dO, LSE, dQ, dK, dV,
+                                dQg, dKg, dVg, stream=None) -> None:
+    """Gradients of the forward with the global rows' own projections: the
+    global rows' terms in dQg, dKg, dVg, the other rows' in dQ, dK, dV (fp32
+    device tensors [B, H, N, D]); Qg, Kg, Vg may be None for Q, K, V."""
+    lib = load()
+    _check(lib.lfattn_backward_global_proj(
+        handle, *(_ptr(x) for x in (Q, K, V, Qg, Kg, Vg, O, dO, LSE, dQ, dK, dV, dQg, dKg, dVg)),
+        _stream(stream)), "lfattn_backward_global_proj")
 
 
 def lfattn_forward_noalloc(handle: int, Q, K, V, O, stream=None) -> None:

@@ -305,3 +305,132 @@ def test_backward_general_forms_full_size_sampled_heads(form):
     for x, w, n in zip((dq, dk, dv), want, ("dq", "dk", "dv")):
         assert np.all(np.isfinite(x.cpu().numpy())), f"{form} {n}: non-finite"
         say(f"  {n}: {check(x[:, hs].cpu().numpy().astype(np.float64), w, f'{form} {n}')}")
+
+
+# ---------------------------------------------------------------------------
+# Separate projections for the global rows: lfattn_forward_global_proj_lse +
+# lfattn_backward_global_proj against the oracle's six gradients.
+# ---------------------------------------------------------------------------
+
+PROJ_CASES = [
+    ("band", dict(B=1, H=2, N=300, window=64, dil=[1, 2], glob=[0, 150, 299])),
+    ("band", dict(B=1, H=1, N=700, window=256, dil=[1], glob=list(range(0, 700, 23)))),
+    ("band", dict(B=1, H=2, N=200, window=40, dil=[1, 3], glob=[])),
+    ("masked", dict(B=2, H=2, N=400, window=40, dil=[1, 2], sets=[[3, 200, 399], [7]])),
+    ("chunked", dict(B=1, H=2, N=20 + 64 * 3 + 7, chunk=64, M=20)),
+]
+
+
+def _proj_handle(kind, p, D):
+    B, H, N = p["B"], p["H"], p["N"]
+    if kind == "band":
+        h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, p["window"], p["dil"], p["glob"])
+        kw = dict(window=p["window"], dilation=p["dil"], glob=p["glob"])
+    elif kind == "masked":
+        mask = np.zeros((B, N), dtype=np.uint8)
+        for b, s in enumerate(p["sets"]):
+            mask[b, s] = 1
+        h = L.lfattn_create_masked(B, H, N, D, L.LFATTN_BF16, p["window"], p["dil"], mask)
+        kw = dict(window=p["window"], dilation=p["dil"], batch_glob=p["sets"])
+    else:
+        h = L.lfattn_create_chunked(B, H, N, D, L.LFATTN_BF16, p["chunk"], p["M"])
+        kw = dict(chunk=p["chunk"], n_memory=p["M"])
+    return h, kw
+
+
+def _run_proj(h, a, g, do, shape):
+    import torch
+    B, H, N, D = shape
+    q, k, v = to_device(a)
+    qg, kg, vg = to_device(g)
+    dgrad = torch.from_numpy(do).to("cuda:0").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    outs = [torch.full((B, H, N, D), float("nan"), dtype=torch.float32, device=q.device)
+            for _ in range(6)]
+    L.lfattn_forward_global_proj_lse(h, q, k, v, qg, kg, vg, o, lse)
+    L.lfattn_backward_global_proj(h, q, k, v, qg, kg, vg, o, dgrad, lse, *outs)
+    torch.cuda.synchronize()
+    return [x.cpu().numpy().astype(np.float64) for x in outs]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("rows_mode", [64, 128])
+@pytest.mark.parametrize("case", PROJ_CASES, ids=lambda c: c[0] + "_N%d" % c[1]["N"])
+def test_backward_global_proj_every_element(case, rows_mode, D, monkeypatch):
+    monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows_mode))
+    monkeypatch.setenv("LFATTN_BWD_ROWS", str(rows_mode))
+    kind, p = case
+    B, H, N = p["B"], p["H"], p["N"]
+    a = W.small_case(B, H, N, D, "bf16", p.get("window", 0), dilation=p.get("dil"), seed=188)
+    g = W.small_case(B, H, N, D, "bf16", p.get("window", 0), dilation=p.get("dil"), seed=189)
+    rng = np.random.default_rng(190)
+    do = _bf16(rng.standard_normal((B, H, N, D)).astype(np.float32))
+    h, kw = _proj_handle(kind, p, D)
+    try:
+        say(f"backward with global projections {kind} {p} D {D} rows {rows_mode}")
+        got = _run_proj(h, a, g, do, (B, H, N, D))
+    finally:
+        L.lfattn_destroy(h)
+    want = oracle.attention_grad(a.q, a.k, a.v, do, qg=g.q, kg=g.k, vg=g.v, **kw)
+    for x, w, n in zip(got, want, ("dq", "dk", "dv", "dqg", "dkg", "dvg")):
+        if not np.any(w):  # (no global rows: an all-zero gradient, exactly)
+            assert np.array_equal(x, w), f"{kind} {n}: not zero"
+        else:
+            check(x, w, f"{kind} {n}")
+
+
+def test_backward_global_proj_shared_adds_up():
+    """Qg = Q, Kg = K, Vg = V: the two gradient sets add up to lfattn_backward's."""
+    import torch
+    B, H, N, D = 1, 2, 600, 64
+    a = W.small_case(B, H, N, D, "bf16", 128, dilation=[1, 2], seed=191)
+    do = _bf16(np.random.default_rng(192).standard_normal((B, H, N, D)).astype(np.float32))
+    glob = [0, 5, 300, 599]
+    h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, 128, [1, 2], glob)
+    try:
+        say("backward with global projections = the shared ones")
+        six = _run_proj(h, a, a, do, (B, H, N, D))
+        q, k, v = to_device(a)
+        dgrad = torch.from_numpy(do).to("cuda:0").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        three = [torch.empty((B, H, N, D), dtype=torch.float32, device=q.device)
+                 for _ in range(3)]
+        L.lfattn_forward_lse(h, q, k, v, o, lse)
+        L.lfattn_backward(h, q, k, v, o, dgrad, lse, *three)
+        torch.cuda.synchronize()
+    finally:
+        L.lfattn_destroy(h)
+    for x, y, w in zip(six[:3], six[3:], three):
+        w = w.cpu().numpy().astype(np.float64)
+        check(x + y, w, "shared projections")
+
+
+def test_backward_global_proj_full_size_two_sequences():
+    """The Longformer-base shape with two sequences of different global sets
+    and their own projections: every head runs, the first and last of each
+    sequence are checked element by element."""
+    import torch
+    B, H, N, D, window = 2, 12, 4096, 64, 512
+    rng = np.random.default_rng(9)
+    sets = [list(range(32)), sorted({0} | set(rng.choice(N, size=10, replace=False).tolist()))]
+    a = W.small_case(B, H, N, D, "bf16", window, seed=20261)
+    g = W.small_case(B, H, N, D, "bf16", window, seed=21261)
+    do = _bf16(rng.standard_normal((B, H, N, D)).astype(np.float32))
+    mask = np.zeros((B, N), dtype=np.uint8)
+    for b, s in enumerate(sets):
+        mask[b, s] = 1
+    h = L.lfattn_create_masked(B, H, N, D, L.LFATTN_BF16, window, None, mask)
+    try:
+        say("backward with global projections, Longformer-base shape, two sequences")
+        got = _run_proj(h, a, g, do, (B, H, N, D))
+    finally:
+        L.lfattn_destroy(h)
+    hs = [0, H - 1]
+    want = oracle.attention_grad(a.q[:, hs], a.k[:, hs], a.v[:, hs], do[:, hs],
+                                 qg=g.q[:, hs], kg=g.k[:, hs], vg=g.v[:, hs], window=window,
+                                 batch_glob=sets)
+    for x, w, n in zip(got, want, ("dq", "dk", "dv", "dqg", "dkg", "dvg")):
+        assert np.all(np.isfinite(x)), f"{n}: non-finite"
+        check(x[:, hs], w, f"two sequences {n}")
