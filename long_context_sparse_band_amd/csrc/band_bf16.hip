@@ -547,9 +547,12 @@ __device__ __forceinline__ void band_item(const BandArgs& a, const BandWork& w, 
     const int t = tile_of(j);
     const bool band = t < n_band;
 
-    // Global tiles: which slots the rows keep.
+    // Global tiles: which slots the rows keep (with the dedupe test: one
+    // bit per register; without: the slots before glim, counted from this
+    // lane half's first key).
     bool edge = false;
     unsigned keep = 0;
+    int glim = TK;
     if (!fast) {
       if (band) {
         const int k0 = s_lo + TK * t, k1 = min(k0 + TK - 1, s_hi);
@@ -560,8 +563,7 @@ __device__ __forceinline__ void band_item(const BandArgs& a, const BandWork& w, 
         const int g0 = TK * (t - n_band);
         const int nvalid = min(TK, n_glob - g0);
         if (!gdup) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) keep |= (unsigned)(block_row(i, lh) < nvalid) << i;
+          glim = nvalid - 4 * lh;
           act = true;
           edge = nvalid < TK;
         } else {
@@ -632,6 +634,9 @@ __device__ __forceinline__ void band_item(const BandArgs& a, const BandWork& w, 
               S[i] = ((int)((unsigned)(e + block_row(i, 0)) > span) | (int)(block_row(i, 0) > last))
                          ? -INFINITY : S[i];
           }
+        } else if (!gdup) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) S[i] = block_row(i, 0) < glim ? S[i] : -INFINITY;
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) S[i] = ((keep >> i) & 1u) ? S[i] : -INFINITY;
@@ -766,10 +771,21 @@ __device__ __forceinline__ void band_item(const BandArgs& a, const BandWork& w, 
   };
 
   // Steps in pairs (stage 0 then stage 1), flags refreshed every 64 steps.
+  // In a launch whose workgroups all run at once, a wavefront's issue
+  // priority falls as its steps run out (s_setprio 3 .. 0): the hardware
+  // otherwise favours the oldest wavefronts, which finish first and leave the
+  // youngest to run on a part-empty compute unit at the end.
   for (int j0 = 0; j0 < n_steps; j0 += 64) {
     flags(j0);
     const int j1 = min(n_steps, j0 + 64);
     for (int j = j0; j < j1; j += 2) {
+      if (a.lrf) {
+        const int rem = n_steps - j;
+        if (rem > 6) __builtin_amdgcn_s_setprio(3);
+        else if (rem > 3) __builtin_amdgcn_s_setprio(2);
+        else if (rem > 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       step(j, j - j0, std::integral_constant<int, 0>{});
       if (j + 1 < j1) step(j + 1, j + 1 - j0, std::integral_constant<int, 1>{});
     }

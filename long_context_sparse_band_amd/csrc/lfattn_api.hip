@@ -135,6 +135,7 @@ struct lfattn_ctx {
   int g_waves = 0, g_rows = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
   bool glob_items = false;  // global-row partials run as items of the band launch
   bool fuse_merge = false;  // ... and the band launch merges them too
+  bool one_round = false;   // the band launch fits one round of workgroup slots
 
   // Device memory comes from the stream-ordered allocator on this private
   // stream (async_mem), so that lfattn_destroy can release it behind the
@@ -531,6 +532,7 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   }
   if (table.size() > (size_t)INT32_MAX) { free_ctx(c); return LFATTN_EUNSUPPORTED; }
   c->n_band_wg = (int)table.size();
+  c->one_round = (long long)c->n_band_wg <= slots;
 
   // Backward work (bf16, D = 64), one table per side: band items of
   // bwd_rows rows (row side) or keys (key side) per (b, h, residue), then
@@ -838,6 +840,7 @@ lfattn_status forward_impl(lfattn_t c, const void* Q, const void* K, const void*
   a.part = c->glob_items ? part : nullptr;
   a.gcount = c->fuse_merge ? counts : nullptr;
   a.n_sets = c->n_sets; a.n_chunks = c->n_chunks; a.chunk_keys = c->chunk_keys;
+  a.lrf = c->one_round ? 1 : 0;
   if (lfattn::launch_band(c->dtype, c->D, a, c->n_band_wg, stream, t_band) != hipSuccess)
     return LFATTN_EHIP;
 

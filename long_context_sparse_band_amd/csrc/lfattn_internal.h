@@ -70,6 +70,10 @@ struct BandArgs {
   float* part;
   unsigned* gcount;
   int n_sets, n_chunks, chunk_keys;
+  // Nonzero when every workgroup of the launch is resident at once: the
+  // wavefronts then take issue priority by the steps they have left (the
+  // furthest behind first), so that the workgroups finish together.
+  int lrf;
 };
 
 struct GlobArgs {
