@@ -97,6 +97,13 @@ __device__ __forceinline__ void dma16(const void* gaddr, unsigned lds) {
                : "s"(lds), "v"(gaddr)
                : "memory", "m0");
 }
+// 4-byte direct global -> LDS load: lane i's 4 bytes land at M0 + 4 i.
+__device__ __forceinline__ void dma4(const void* gaddr, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds), "v"(gaddr)
+               : "memory", "m0");
+}
 // s_waitcnt vmcnt(0) (gfx9-family encoding; expcnt and lgkmcnt left open).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -106,9 +113,10 @@ template <int D>
 struct BwdSmem {
   unsigned char x[2][2][BwdDim<D>::TILE];  // row side: K tiles; key side: Q tiles
   unsigned char y[2][2][BwdDim<D>::TILE];  // row side: V tiles; key side: dO tiles
-  // Key side: per tile row, -lse / scale (-inf for a row that takes no
-  // part: its weights are exp2(-inf) = 0) and -Delta, the initial values of
-  // the score and dP accumulators.
+  // Key side: per tile row, -lse / scale (-inf for a global row of a band
+  // tile, which takes no part there: its weights are exp2(-inf) = 0) and
+  // -Delta, the initial values of the score and dP accumulators, loaded
+  // straight from the row side's per-row terms.
   float nls[2][2][32];
   float ndl[2][2][32];
   int gpos[kGCap];             // the batch element's global positions
@@ -302,7 +310,8 @@ void bwd_rows_kernel(BwdArgs a) {
   }
   const float lse2 = a.lse[(size_t)w.bh * N + pos_u] * kLog2e;
   // Delta = dO . O of the row (each lane half holds 32 of its columns); the
-  // band items write it for the key side, which runs after this kernel.
+  // band items write it, with the row's -lse / scale, for the key side,
+  // which runs after this kernel.
   float dlt = 0.0f;
 #pragma unroll
   for (int ks = 0; ks < kBD / 16; ++ks) {
@@ -311,7 +320,7 @@ void bwd_rows_kernel(BwdArgs a) {
     for (int e = 0; e < 8; ++e) dlt = fmaf((float)g[ks][e], (float)o8[e], dlt);
   }
   dlt += __shfl_xor(dlt, 32);
-  if (!gi && row_ok && hi == 0) a.delta[(size_t)w.bh * N + pos_u] = dlt;
+  const float nls = -a.lse[(size_t)w.bh * N + pos_u] / a.scale;
 
   // Key position of row rr of tile t; a row past the end of the tile's keys
   // takes the last one (its weights are masked).
@@ -430,6 +439,17 @@ void bwd_rows_kernel(BwdArgs a) {
   }
 
   if (!row_ok) return;
+  // The key side's per-row terms (three planes of [B*H, N], written by the
+  // band items, which hold every position): -Delta, -lse / scale, and the
+  // same with -inf at global positions (band tiles leave the global rows to
+  // the gathered global tiles).
+  const bool row_glob = !gi && isg[pos_u];
+  if (!gi && hi == 0) {
+    const size_t plane = (size_t)a.n_bh * N, at = (size_t)w.bh * N + pos_u;
+    a.delta[at] = -dlt;
+    a.delta[plane + at] = nls;
+    a.delta[2 * plane + at] = row_glob ? -__builtin_inff() : nls;
+  }
   // With separate projections a band row has no Qg gradient.
   if (a.proj && !gi) {
     float* dqg = a.dQg + base + (size_t)pos_u * kBD;
@@ -439,7 +459,7 @@ void bwd_rows_kernel(BwdArgs a) {
       for (int g4 = 0; g4 < 4; ++g4)
         *(float4*)(dqg + 32 * b + 8 * g4 + 4 * hi) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (!gi && isg[pos_u]) return;  // a global row: its gradient comes from the global-row items
+  if (row_glob) return;  // a global row: its gradient comes from the global-row items
   // Band row: its dQ.  Global-row item: the chunk's partial dQ of slot u.
   float* dq = gi ? a.gpart + (((size_t)w.bh * a.n_gch + t0) * a.n_glob + u) * kBD
                  : a.dQ + base + (size_t)pos_u * kBD;
@@ -476,8 +496,9 @@ void bwd_keys_kernel(BwdArgs a) {
   const size_t base = (size_t)w.bh * N * kBD;
   const unsigned short* Qp = (const unsigned short*)a.Q + base;
   const unsigned short* dOp = (const unsigned short*)a.dO + base;
-  const float* lsep = a.lse + (size_t)w.bh * N;
-  const float* dlp = a.delta + (size_t)w.bh * N;
+  // Planes of the row side's per-row terms: -Delta, -lse / scale, and the
+  // same with -inf at global positions.
+  const size_t mplane = (size_t)a.n_bh * N;
   const int* gl = a.glob + w.g0;
   const int ng = w.ng;
   const unsigned char* isg = a.is_glob + (long long)w.b * a.isg_stride;
@@ -497,7 +518,6 @@ void bwd_keys_kernel(BwdArgs a) {
   // sums are computed but not stored.
   const bool key_band = key_ok && (gk || !isg[pos_k]);
   const int rlo_k = gk ? 0 : pat.rlo(k);
-  const unsigned rspan_k = gk ? 0u : (unsigned)(pat.rhi(k) - rlo_k);
 
   // Query rows: band item, subsequence positions q_lo .. q_hi (the rows whose
   // interval holds one of the item's keys) then the global rows; global-key
@@ -510,6 +530,9 @@ void bwd_keys_kernel(BwdArgs a) {
   const int q_hi = gk ? -1 : min(Lr - 1, pat.rhi(klast));
   const int n_band = gk ? (c1 - c0 + 31) / 32 : (q_hi >= q_lo ? (q_hi - q_lo) / 32 + 1 : 0);
   const int n_tiles = n_band + (gk ? 0 : (ng + 31) / 32);
+  // Rows of the key's interval that the item's tiles hold (rows past q_hi
+  // are padding: the last band tile repeats row q_hi).
+  const unsigned rspan_k = gk ? 0u : (unsigned)(min(pat.rhi(k), q_hi) - rlo_k);
 
   // Operands of the keys: K and V rows (B of S = Q K^T and dP = dO V^T).
   bf16x8 kr[kBD / 16], vr[kBD / 16];
@@ -546,16 +569,21 @@ void bwd_keys_kernel(BwdArgs a) {
     part = slot < ng;
     return sm.gpos[min(slot, ng - 1)];
   };
-  // Tile loads as on the row side; the thread of chunk 0 of a row also
-  // fetches the row's -lse / scale and -Delta.
+  // Tile loads as on the row side.  The rows' -lse / scale and -Delta go to
+  // LDS with direct loads too (wavefronts 0 and 1, lane L: row L%32 of the
+  // step's tile L/32, KS = 1: both lane halves the one tile, the second slot
+  // unused): band tiles take the terms with -inf at global rows, gathered
+  // global rows (and the chunks of global-key items, shared projections)
+  // the plain ones.  Padding rows repeat a real row; the masks drop them.
   constexpr int NL = TILE / 4096;  // direct loads per matrix and thread
   const int ld_row = tid / CPR, ld_c = swz<D>(ld_row, tid % CPR);
-  const bool ld_meta = (tid % CPR) == 0;
   const unsigned xl = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(LDS_AS void*)&sm.x[0][0][0] + 1024u * wave);
   const unsigned yl = __builtin_amdgcn_readfirstlane(
       (unsigned)(uintptr_t)(LDS_AS void*)&sm.y[0][0][0] + 1024u * wave);
-  float m_lse[KS][NL], m_dlt[KS][NL];
+  const unsigned ml = __builtin_amdgcn_readfirstlane(
+      wave == 0 ? (unsigned)(uintptr_t)(LDS_AS void*)&sm.nls[0][0][0]
+                : (unsigned)(uintptr_t)(LDS_AS void*)&sm.ndl[0][0][0]);
   // Tiles tb .. te-1 of this item; step j holds tiles tb + KS j .. + KS - 1.
   int tb = 0, te = n_tiles;
   auto load = [&](int j) {
@@ -570,23 +598,20 @@ void bwd_keys_kernel(BwdArgs a) {
           const int p = row_pos(t, ld_row + (256 / CPR) * e, part);
           dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so + 4096u * e);
           dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so + 4096u * e);
-          if (ld_meta) {
-            m_lse[q2][e] = part ? -lsep[p] / a.scale : -__builtin_inff();
-            m_dlt[q2][e] = -dlp[p];
-          }
         }
       }
     }
-  };
-  auto store_meta = [&](int j) {
-#pragma unroll
-    for (int q2 = 0; q2 < KS; ++q2)
-      if (ld_meta && tb + KS * j + q2 < te)
-#pragma unroll
-        for (int e = 0; e < NL; ++e) {
-          sm.nls[j & 1][q2][ld_row + (256 / CPR) * e] = m_lse[q2][e];
-          sm.ndl[j & 1][q2][ld_row + (256 / CPR) * e] = m_dlt[q2][e];
-        }
+    if (wave < 2) {
+      const int t = min(tb + KS * j + (KS == 2 ? lane >> 5 : 0), te - 1);
+      bool part;
+      const int p = row_pos(t, lane & 31, part);
+      // Plane 0 (-Delta) for wavefront 1; wavefront 0: plane 2 (-inf at
+      // global rows) or 1.  (An index rather than a choice among pointers:
+      // the compiler kept the latter in vector registers and spilled.)
+      const int pl = wave == 1 ? 0 : ((!gk && t < n_band) || (gk && PROJ) ? 2 : 1);
+      dma4(a.delta + ((size_t)pl * mplane + (size_t)w.bh * N + p),
+           ml + (unsigned)(j & 1) * (2 * 32 * 4));
+    }
   };
 
   TrAddr<D> ta;
@@ -599,10 +624,7 @@ void bwd_keys_kernel(BwdArgs a) {
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) accK[b] = accV[b] = f32x16{};
     const int n_steps = (te - tb + KS - 1) / KS;
-    if (n_steps > 0) {
-      load(0);
-      store_meta(0);
-    }
+    if (n_steps > 0) load(0);
     wait_vm0();
     __syncthreads();
     for (int j = 0; j < n_steps; ++j) {
@@ -613,12 +635,18 @@ void bwd_keys_kernel(BwdArgs a) {
       // rows taking no part carry lse +inf, gathered global rows score every
       // key, and keys before the first chunk are global: their lanes are not
       // stored).
+      // Other tiles: rows at or past glim are padding.
+      const bool band_tile = !gk && t < n_band;
       bool act = ka < n_keys && t < te, full = true;
-      if (!gk && t < n_band) {
+      int glim = 32;
+      if (band_tile) {
         const int u0 = q_lo + 32 * t, u1 = min(u0 + 31, q_hi);
         const int kb = min(ka + 31, n_keys - 1), kf = ka > kfirst ? ka : kfirst;
         act = act && (u0 <= pat.rhi(kb)) && (u1 >= pat.rlo(kf));
-        full = (u0 >= pat.rlo(kb)) && (u1 <= pat.rhi(kf));
+        full = (u0 >= pat.rlo(kb)) && (u1 <= pat.rhi(kf)) && (u0 + 31 <= q_hi);
+      } else {
+        glim = gk ? c1 - c0 - 32 * t : ng - 32 * (t - n_band);
+        full = glim >= 32;
       }
       if (act) {
         // Rows 8j + 4hi .. +3 of a result block sit in registers 4j .. 4j+3:
@@ -643,7 +671,9 @@ void bwd_keys_kernel(BwdArgs a) {
             float p = __builtin_amdgcn_exp2f(s[i + e] * a.sl2);
             if (!full) {
               const int qq = brow(i + e, hi);
-              p = (unsigned)(q_lo + 32 * t + qq - rlo_k) <= rspan_k ? p : 0.0f;
+              const bool keep = band_tile ? (unsigned)(q_lo + 32 * t + qq - rlo_k) <= rspan_k
+                                          : qq < glim;
+              p = keep ? p : 0.0f;
             }
             p2[e] = p;
             ds2[e] = p * dp[i + e];
@@ -656,7 +686,6 @@ void bwd_keys_kernel(BwdArgs a) {
         tr_mfma<D>(yb, ta, pw, accV);   // dV^T += dO^T P
         tr_mfma<D>(xb, ta, dsw, accK);  // dK^T += Q^T dS
       }
-      if (j + 1 < n_steps) store_meta(j + 1);
       wait_vm0();
       __syncthreads();
     }

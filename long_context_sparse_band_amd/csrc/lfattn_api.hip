@@ -606,7 +606,7 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
     return st;
   }
   if (has_bwd && ((st = dev_alloc(c, &c->d_bwork, btable.size())) != LFATTN_OK ||
-                   (st = dev_alloc(c, &c->d_delta, (size_t)B * H * N)) != LFATTN_OK ||
+                   (st = dev_alloc(c, &c->d_delta, (size_t)3 * B * H * N)) != LFATTN_OK ||
                    (n_g > 0 &&
                     (st = dev_alloc(c, &c->d_gpart, (size_t)3 * B * H * c->n_gch * n_g * D)) !=
                         LFATTN_OK))) {

@@ -94,7 +94,7 @@ struct GlobArgs {
   float* lse;                  // [B, H, N] log-sum-exp of the global rows' scores, or null
 };
 
-// Backward pass (bf16, D = 64): gradients of the band + global attention.
+// Backward pass (bf16, D = 64 or 128): gradients of the band + global attention.
 // Each side's work table holds band items of 64 or 128 rows (row side) or
 // keys (key side), ks = 2 or 1, and global items of as many global positions
 // against a chunk of chunk_keys keys (row side) or rows (key side).
@@ -105,7 +105,10 @@ struct BwdArgs {
   const void* O;
   const void* dO;
   const float* lse;            // [B, H, N] natural log-sum-exp from the forward
-  float* delta;                // [B, H, N] workspace: dO . O per row (row side writes it)
+  // Workspace the row side writes for the key side, three planes of
+  // [B, H, N]: -Delta (Delta = dO . O), -lse / scale, and -lse / scale with
+  // -inf at global positions.
+  float* delta;
   float* dQ;                   // [B, H, N, D] fp32 outputs
   float* dK;
   float* dV;

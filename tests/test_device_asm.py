@@ -4,7 +4,7 @@ no GPU needed):
 
 - M0 (the LDS base of the direct global -> LDS loads) is written only by the
   inline-assembly load statements, each of which sets it right before its
-  own global_load_lds_dwordx4; no compiler-generated instruction uses M0,
+  own global_load_lds_dwordx4 (or dword); no compiler-generated instruction uses M0,
   so the value a load statement sets cannot be clobbered between the two.
 - No packed fp32 VALU instruction (v_pk_fma_f32, v_pk_mul_f32,
   v_pk_add_f32) is emitted anywhere (the sources are built with the
@@ -67,7 +67,8 @@ def test_m0_only_in_direct_load_statements(device_asm):
                 if any(re.search(r"\bm0\b", b) for b in block):
                     ops = [b.split()[0] for b in block if b and not b.startswith(";")]
                     assert ops in (["s_mov_b32", "global_load_lds_dwordx4"],
-                                   ["s_add_u32", "global_load_lds_dwordx4"]), (name, block)
+                                   ["s_add_u32", "global_load_lds_dwordx4"],
+                                   ["s_mov_b32", "global_load_lds_dword"]), (name, block)
                     assert re.match(r"s_(mov_b32|add_u32)\s+m0\s*,", block[0]), (name, block)
                 in_asm = False
                 continue
