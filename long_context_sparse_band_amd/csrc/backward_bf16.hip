@@ -97,6 +97,20 @@ __device__ __forceinline__ void dma16(const void* gaddr, unsigned lds) {
                : "s"(lds), "v"(gaddr)
                : "memory", "m0");
 }
+// The same from a wave-uniform base address plus a per-lane 32-bit byte
+// offset (no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
 // 4-byte direct global -> LDS load: lane i's 4 bytes land at M0 + 4 i.
 __device__ __forceinline__ void dma4(const void* gaddr, unsigned lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
@@ -584,33 +598,57 @@ void bwd_keys_kernel(BwdArgs a) {
   const unsigned ml = __builtin_amdgcn_readfirstlane(
       wave == 0 ? (unsigned)(uintptr_t)(LDS_AS void*)&sm.nls[0][0][0]
                 : (unsigned)(uintptr_t)(LDS_AS void*)&sm.ndl[0][0][0]);
+  // A band tile whose 32 rows all lie before q_hi is loaded from its first
+  // row's address (wave-uniform) plus per-lane offsets (rows d apart).
+  unsigned boff[NL];
+#pragma unroll
+  for (int e = 0; e < NL; ++e)
+    boff[e] = (unsigned)((d * (ld_row + (256 / CPR) * e)) * kBD + 8 * ld_c) * 2u;
+  const unsigned moff = (unsigned)(d * (KS == 2 ? lane : (lane & 31))) * 4u;
   // Tiles tb .. te-1 of this item; step j holds tiles tb + KS j .. + KS - 1.
   int tb = 0, te = n_tiles;
+  auto fast_tile = [&](int t) { return !gk && t < n_band && q_lo + 32 * t + 31 <= q_hi; };
   auto load = [&](int j) {
 #pragma unroll
     for (int q2 = 0; q2 < KS; ++q2) {
       const int t = tb + KS * j + q2;
       if (t < te) {
         const unsigned so = (unsigned)((j & 1) * 2 + q2) * TILE;
+        if (fast_tile(t)) {
+          const size_t row0 = (size_t)(r + d * (q_lo + 32 * t)) * kBD;
 #pragma unroll
-        for (int e = 0; e < NL; ++e) {
-          bool part;
-          const int p = row_pos(t, ld_row + (256 / CPR) * e, part);
-          dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so + 4096u * e);
-          dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so + 4096u * e);
+          for (int e = 0; e < NL; ++e) {
+            dma16_s(Qp + row0, boff[e], xl + so + 4096u * e);
+            dma16_s(dOp + row0, boff[e], yl + so + 4096u * e);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < NL; ++e) {
+            bool part;
+            const int p = row_pos(t, ld_row + (256 / CPR) * e, part);
+            dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so + 4096u * e);
+            dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so + 4096u * e);
+          }
         }
       }
     }
     if (wave < 2) {
-      const int t = min(tb + KS * j + (KS == 2 ? lane >> 5 : 0), te - 1);
-      bool part;
-      const int p = row_pos(t, lane & 31, part);
       // Plane 0 (-Delta) for wavefront 1; wavefront 0: plane 2 (-inf at
       // global rows) or 1.  (An index rather than a choice among pointers:
       // the compiler kept the latter in vector registers and spilled.)
-      const int pl = wave == 1 ? 0 : ((!gk && t < n_band) || (gk && PROJ) ? 2 : 1);
-      dma4(a.delta + ((size_t)pl * mplane + (size_t)w.bh * N + p),
-           ml + (unsigned)(j & 1) * (2 * 32 * 4));
+      const int t0s = tb + KS * j;
+      const unsigned lds = ml + (unsigned)(j & 1) * (2 * 32 * 4);
+      if (fast_tile(t0s + KS - 1) && t0s + KS - 1 < te) {
+        const int pl = wave == 1 ? 0 : 2;
+        dma4_s(a.delta + ((size_t)pl * mplane + (size_t)w.bh * N + r + d * (q_lo + 32 * t0s)),
+               moff, lds);
+      } else {
+        const int t = min(t0s + (KS == 2 ? lane >> 5 : 0), te - 1);
+        bool part;
+        const int p = row_pos(t, lane & 31, part);
+        const int pl = wave == 1 ? 0 : ((!gk && t < n_band) || (gk && PROJ) ? 2 : 1);
+        dma4(a.delta + ((size_t)pl * mplane + (size_t)w.bh * N + p), lds);
+      }
     }
   };
 
