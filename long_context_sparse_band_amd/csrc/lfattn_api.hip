@@ -571,6 +571,7 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
             btable.push_back(BandWork{bh, r, t0, d, gsel[b].x, gsel[b].y, b, 0});
         }
       }
+      const size_t gstart = btable.size();
       for (int bh = 0; bh < B * H; ++bh) {
         const int b = bh / H;
         const int sets_b = (gsel[b].y + rows - 1) / rows;
@@ -580,6 +581,24 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
       }
       if (btable.size() - start > (size_t)INT32_MAX) { free_ctx(c); return LFATTN_EUNSUPPORTED; }
       c->n_bwork[side] = (int)(btable.size() - start);
+      // Block indices congruent to x (mod 8) run on XCD x: each XCD takes a
+      // run of consecutive band items (which share their neighbours' row or
+      // key tiles in that XCD's L2), then its share of the global items.
+      {
+        std::vector<std::vector<BandWork>> ml(kXcds);
+        for (const size_t lo0 : {start, gstart}) {
+          const size_t hi0 = lo0 == start ? gstart : btable.size(), n = hi0 - lo0;
+          for (int x = 0; x < kXcds; ++x)
+            ml[x].insert(ml[x].end(), btable.begin() + lo0 + n * x / kXcds,
+                         btable.begin() + lo0 + n * (x + 1) / kXcds);
+        }
+        std::vector<size_t> pos(kXcds, 0);
+        for (size_t bid = 0; bid < btable.size() - start; ++bid) {
+          int x = (int)(bid % kXcds);
+          for (int t = 0; t < kXcds && pos[x] >= ml[x].size(); ++t) x = (x + 1) % kXcds;
+          btable[start + bid] = ml[x][pos[x]++];
+        }
+      }
     }
   }
 
