@@ -266,7 +266,9 @@ def test_mask_readout_both_band_kernels(case, rows, monkeypatch):
 
 
 def test_mask_readout_long_stress_chunks():
-    """Full N = 65536, D = 128, window 1024 and the seeded 64 globals, on the
+    """The 65536-token workload's shape on all 16 heads (N = 65536, D = 128,
+    window 1024, the seeded 64 globals; a launch of many rounds, whose
+    global-row items of 1024 keys are spread among the band items), on the
     key chunks that hold the globals, the sequence ends and random chunks."""
     wl = W.LONG_STRESS
     glob = W.generate(W.Workload("g", B=1, H=1, N=wl.N, D=8, dtype="f32", window=0,
@@ -274,8 +276,8 @@ def test_mask_readout_long_stress_chunks():
     rng = np.random.default_rng(5)
     starts = sorted({0, wl.N - wl.D} | {g // wl.D * wl.D for g in glob[:8]} |
                     {int(x) * wl.D for x in rng.integers(0, wl.N // wl.D, size=6)})
-    say(f"mask readout long stress, {len(starts)} chunks")
-    _readout(1, 1, wl.N, wl.D, "bf16", wl.window, None, glob, starts, what="long stress")
+    say(f"mask readout long stress, {len(starts)} chunks, {wl.H} heads")
+    _readout(wl.B, wl.H, wl.N, wl.D, "bf16", wl.window, None, glob, starts, what="long stress")
 
 
 # --------------------------------------------------------------------------
