@@ -387,14 +387,14 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   }
   c->band_rows = band_rows;
 
-  // Rows (keys) per backward item: the row side takes 64 (each workgroup's
-  // key tiles split between two pairs of wavefronts), the key side 128 (one
-  // row-tile stream shared by four 32-key blocks), the faster choice of each
-  // on the bf16 workloads measured; LFATTN_BWD_ROWS=64 or 128 sets both (both
+  // Rows (keys) per backward item: 64 on both sides (each workgroup's tiles
+  // split between two pairs of wavefronts: twice the workgroups of 128-row
+  // items, whose one tile stream four 32-row blocks share), the faster choice
+  // on every bf16 workload measured; LFATTN_BWD_ROWS=64 or 128 sets both (both
   // give the same results; this lets the tests run every kernel).
   if (dtype == LFATTN_BF16) {
     c->bwd_rows[0] = 64;
-    c->bwd_rows[1] = 128;
+    c->bwd_rows[1] = 64;
     if (const char* e = std::getenv("LFATTN_BWD_ROWS")) {
       if (std::strcmp(e, "64") == 0) c->bwd_rows[0] = c->bwd_rows[1] = 64;
       if (std::strcmp(e, "128") == 0) c->bwd_rows[0] = c->bwd_rows[1] = 128;
