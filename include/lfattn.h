@@ -56,8 +56,8 @@
  * Ownership.  Q, K, V, O (and Qg, Kg, Vg) belong to the caller.  The inputs
  * are only read; O is fully overwritten and must not overlap any input.  The
  * host arrays passed to the create calls (dilation, global_idx, global_mask)
- * are copied; the caller may free them on return.  The handle owns its device tables and workspace and frees them in
- * lfattn_destroy.
+ * are copied; the caller may free them on return.  The handle owns its
+ * device tables and workspace and frees them in lfattn_destroy.
  *
  * Execution.  The forward calls allocate nothing and do not wait on the host:
  * it enqueues its kernels on the given HIP stream and returns.  Device-side
@@ -73,9 +73,12 @@
  * the device's compute units.  The environment variable LFATTN_BAND_ROWS,
  * set to 64 or 128 when lfattn_create runs, overrides that choice; results
  * are the same either way up to floating-point summation order.  The
- * backward (bf16) takes 64-row items with split key tiles on its
- * query side and 128-key items on its key side; LFATTN_BWD_ROWS, 64 or 128
- * when lfattn_create runs, sets both sides to that size.
+ * backward (bf16) takes 64-row items with split key tiles on its query side
+ * and 64-key items with split row tiles on its key side; LFATTN_BWD_ROWS, 64
+ * or 128 when lfattn_create runs, sets both sides to that size.  With
+ * LFATTN_FUSE_MERGE=1 at lfattn_create, bf16 handles merge the global rows'
+ * partial results inside the band launch instead of a separate launch (the
+ * same results; slower on the workloads measured, hence not the default).
  *
  * Errors.  Every entry point returns a status synchronously.  Arguments are
  * checked before any HIP call is made, so invalid arguments never touch the
