@@ -460,9 +460,9 @@ void bwd_rows_kernel(BwdArgs a) {
   const bool row_glob = !gi && isg[pos_u];
   if (!gi && hi == 0) {
     const size_t plane = (size_t)a.n_bh * N, at = (size_t)w.bh * N + pos_u;
-    a.delta[at] = -dlt;
-    a.delta[plane + at] = nls;
-    a.delta[2 * plane + at] = row_glob ? -__builtin_inff() : nls;
+    a.terms[at] = -dlt;
+    a.terms[plane + at] = nls;
+    a.terms[2 * plane + at] = row_glob ? -__builtin_inff() : nls;
   }
   // With separate projections a band row has no Qg gradient.
   if (a.proj && !gi) {
@@ -640,14 +640,14 @@ void bwd_keys_kernel(BwdArgs a) {
       const unsigned lds = ml + (unsigned)(j & 1) * (2 * 32 * 4);
       if (fast_tile(t0s + KS - 1) && t0s + KS - 1 < te) {
         const int pl = wave == 1 ? 0 : 2;
-        dma4_s(a.delta + ((size_t)pl * mplane + (size_t)w.bh * N + r + d * (q_lo + 32 * t0s)),
+        dma4_s(a.terms + ((size_t)pl * mplane + (size_t)w.bh * N + r + d * (q_lo + 32 * t0s)),
                moff, lds);
       } else {
         const int t = min(t0s + (KS == 2 ? lane >> 5 : 0), te - 1);
         bool part;
         const int p = row_pos(t, lane & 31, part);
         const int pl = wave == 1 ? 0 : ((!gk && t < n_band) || (gk && PROJ) ? 2 : 1);
-        dma4(a.delta + ((size_t)pl * mplane + (size_t)w.bh * N + p), lds);
+        dma4(a.terms + ((size_t)pl * mplane + (size_t)w.bh * N + p), lds);
       }
     }
   };

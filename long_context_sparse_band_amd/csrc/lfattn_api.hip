@@ -117,7 +117,7 @@ struct lfattn_ctx {
   // Backward pass (bf16, D = 64): its work table and the per-row Delta.
   BandWork* d_bwork = nullptr;  // backward tables: row side, then key side
   int n_bwork[2] = {0, 0};
-  float* d_delta = nullptr;
+  float* d_terms = nullptr;  // backward: the key side's per-row terms (three planes)
   float* d_gpart = nullptr;  // backward: global items' partial gradients
   int n_gch = 0;             // backward: key (row) chunks of a global item
   int n_band_wg = 0;
@@ -188,7 +188,7 @@ bool capturing(hipStream_t stream) {
 void free_ctx(lfattn_ctx* c) {
   if (!c) return;
   void* ptrs[] = {c->d_work, c->d_glob, c->d_gsel, c->d_isglob, c->d_part, c->d_bwork,
-                  c->d_delta, c->d_gpart, c->d_gcount};
+                  c->d_terms, c->d_gpart, c->d_gcount};
   if (c->async_mem) {
     if (c->used && !capturing(c->last)) {
       if (hipEventRecord(c->done, c->last) != hipSuccess ||
@@ -625,7 +625,7 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
     return st;
   }
   if (has_bwd && ((st = dev_alloc(c, &c->d_bwork, btable.size())) != LFATTN_OK ||
-                   (st = dev_alloc(c, &c->d_delta, (size_t)3 * B * H * N)) != LFATTN_OK ||
+                   (st = dev_alloc(c, &c->d_terms, (size_t)3 * B * H * N)) != LFATTN_OK ||
                    (n_g > 0 &&
                     (st = dev_alloc(c, &c->d_gpart, (size_t)3 * B * H * c->n_gch * n_g * D)) !=
                         LFATTN_OK))) {
@@ -923,7 +923,7 @@ lfattn_status backward_impl(lfattn_t c, const void* Q, const void* K, const void
   if (hipGetDevice(&cur) != hipSuccess || cur != c->device) return LFATTN_EINVAL;
 
   lfattn::BwdArgs a;
-  a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.lse = LSE; a.delta = c->d_delta;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.lse = LSE; a.terms = c->d_terms;
   a.dQ = dQ; a.dK = dK; a.dV = dV;
   a.Qg = Qg; a.Kg = Kg; a.Vg = Vg;
   a.dQg = proj ? dQg : nullptr; a.dKg = proj ? dKg : nullptr; a.dVg = proj ? dVg : nullptr;

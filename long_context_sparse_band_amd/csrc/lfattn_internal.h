@@ -108,7 +108,7 @@ struct BwdArgs {
   // Workspace the row side writes for the key side, three planes of
   // [B, H, N]: -Delta (Delta = dO . O), -lse / scale, and -lse / scale with
   // -inf at global positions.
-  float* delta;
+  float* terms;
   float* dQ;                   // [B, H, N, D] fp32 outputs
   float* dK;
   float* dV;
