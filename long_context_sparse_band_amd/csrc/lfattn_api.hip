@@ -48,7 +48,8 @@ constexpr int kWideRounds = 2;
 constexpr int kSpreadRounds = 4;
 // Backward work items: rows or keys per item, and the key or row chunk of a
 // global item.
-constexpr int kBwdChunk = 512;
+constexpr int kBwdChunk = 512, kBwdChunkShort = 256;
+constexpr int kBwdShortRounds = 2;
 // At most this many chunks per global set (longer chunks past 32768 keys),
 // bounding the partial-gradient workspace.
 constexpr int kBwdMaxChunks = 64;
@@ -558,7 +559,25 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
   std::vector<BandWork> btable;
   const bool has_bwd = dtype == LFATTN_BF16;
   if (has_bwd) {
-    c->bwd_chunk = std::max(kBwdChunk, (N + kBwdMaxChunks * 32 - 1) / (kBwdMaxChunks * 32) * 32);
+    // Chunks of kBwdChunkShort keys (rows) when a side's band items and global
+    // items come to less than kBwdShortRounds rounds of workgroup slots: the
+    // global items, dispatched last, then form a short tail; kBwdChunk
+    // otherwise (fewer partials to merge).
+    int chunk = kBwdChunk;
+    if (n_g > 0) {
+      long long n_band_items = 0;
+      for (int bh = 0; bh < B * H; ++bh) {
+        const int d = c->dil[bh % H];
+        for (int r = 0; r < d && r < N; ++r)
+          n_band_items += ((N - r + d - 1) / d + c->bwd_rows[0] - 1) / c->bwd_rows[0];
+      }
+      long long sets = 0;
+      for (int b = 0; b < B; ++b) sets += (long long)H * ((gsel[b].y + c->bwd_rows[0] - 1) / c->bwd_rows[0]);
+      const long long bwd_slots = (long long)(D == 64 ? 3 : 2) * cus;
+      if (n_band_items + sets * ((N + kBwdChunk - 1) / kBwdChunk) < kBwdShortRounds * bwd_slots)
+        chunk = kBwdChunkShort;
+    }
+    c->bwd_chunk = std::max(chunk, (N + kBwdMaxChunks * 32 - 1) / (kBwdMaxChunks * 32) * 32);
     c->n_gch = (N + c->bwd_chunk - 1) / c->bwd_chunk;
     for (int side = 0; side < 2; ++side) {
       const int rows = c->bwd_rows[side];
