@@ -55,6 +55,9 @@ CASES = [
     ("band", dict(B=1, H=1, N=1, window=8, dil=[1], glob=[])),
     ("band", dict(B=1, H=1, N=65, window=16, dil=[3], glob=[64])),
     ("causal", dict(B=2, H=1, N=1, window=4, dil=[1])),
+    # 512 global positions (the most a bf16 handle takes); every position global.
+    ("band", dict(B=1, H=1, N=600, window=32, dil=[1], glob=[i * 599 // 511 for i in range(512)])),
+    ("band", dict(B=1, H=2, N=96, window=16, dil=[1, 2], glob=list(range(96)))),
 ]
 
 

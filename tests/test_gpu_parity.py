@@ -44,6 +44,13 @@ SMALL = [
     (1, 2, 129, 128, "f32", 2, [1, 64], [64, 128], 14),
     (1, 1, 2050, 64, "bf16", 512, None, list(range(32)), 15),
     (1, 2, 4099, 64, "bf16", 300, [3, 1], [4098, 1, 2048], 16),
+    # The most global positions a bf16 handle takes (512), spread and
+    # contiguous; every position global (no band row left: all output comes
+    # from the global rows' merge).
+    (1, 2, 600, 64, "bf16", 64, None, [i * 599 // 511 for i in range(512)], 17),
+    (1, 2, 600, 128, "bf16", 64, [1, 3], list(range(44, 556)), 18),
+    (1, 1, 96, 64, "bf16", 16, None, list(range(96)), 19),
+    (1, 2, 96, 128, "f32", 16, [1, 2], list(range(96)), 20),
 ]
 
 
@@ -252,6 +259,8 @@ READOUT_ROWS = [
     (1, 3, 333, 128, 100, [1, 2, 5], [0, 17, 300]),
     (1, 2, 1201, 128, 300, [2, 1], [1200, 600, 3]),
     (1, 1, 4099, 64, 300, [3], [4098, 1, 2048]),
+    (1, 2, 600, 64, 64, [1, 3], [i * 599 // 511 for i in range(512)]),
+    (1, 1, 96, 128, 16, [2], list(range(96))),
 ]
 
 
