@@ -1,9 +1,8 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle.
 
 Small shapes are compared on every output element, and so are the full-size
-workloads up to 16448 tokens, in the launch configuration the benchmark times;
-the 65536-token workload on every row of four heads and every global row of
-every head.  The allowed key sets are recovered bit-exactly from the
+workloads, in the launch configuration the benchmark times (the 65536-token
+workload one head at a time).  The allowed key sets are recovered bit-exactly from the
 production kernels (mask readout), every head of the full-size workloads.
 """
 
@@ -13,7 +12,7 @@ import pytest
 import oracle
 from long_context_sparse_band_amd import lfattn as L
 from long_context_sparse_band_amd import workloads as W
-from gpu_util import KeyMajorSets, compare, readout_compare, run, say, to_device
+from gpu_util import TOL, KeyMajorSets, compare, readout_compare, run, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -131,8 +130,7 @@ def test_duplicate_unsorted_globals_are_one_set():
 
 # --------------------------------------------------------------------------
 # Full-size workloads in the benchmark's launch configuration, every output
-# element (the 65536-token workload: every row of four heads and every global
-# row of every head, each head compared on its own).
+# element (the 65536-token workload: each head compared on its own).
 # --------------------------------------------------------------------------
 
 _INPUTS = {}
@@ -186,19 +184,19 @@ def test_workload_full_size(wl):
         return
     got = flat.float().cpu().numpy()
     del o, flat
-    heads = sorted({0, wl.H // 3, (2 * wl.H) // 3, wl.H - 1})
-    for h in heads:
-        rows = np.arange(h * wl.N, (h + 1) * wl.N, dtype=np.int64)
-        say(f"workload {wl.name}: oracle on every row of head {h}")
+    # Longer sequences: every row of every head, one head at a time (the
+    # oracle's output for all of them at once would take gigabytes).
+    means = []
+    for bh in range(wl.B * wl.H):
+        rows = np.arange(bh * wl.N, (bh + 1) * wl.N, dtype=np.int64)
+        say(f"workload {wl.name}: oracle on every row of head {bh}")
         want = oracle.attention(inp.q, inp.k, inp.v, wl.window, dil, glob, rows=rows)
-        mx, mean = compare(got[rows].astype(np.float64), want, wl.dtype, f"{wl.name} head {h}")
-        say(f"workload {wl.name}: head {h}: max-abs {mx:.3g}, mean-abs {mean:.3g}")
-    rows = np.array([(b * wl.H + h) * wl.N + g for b in range(wl.B) for h in range(wl.H)
-                     for g in glob], dtype=np.int64)
-    say(f"workload {wl.name}: oracle on the {len(rows)} global rows of every head")
-    want = oracle.attention(inp.q, inp.k, inp.v, wl.window, dil, glob, rows=rows)
-    mx, mean = compare(got[rows].astype(np.float64), want, wl.dtype, f"{wl.name} global rows")
-    say(f"workload {wl.name}: global rows: max-abs {mx:.3g}, mean-abs {mean:.3g}")
+        mx, mean = compare(got[rows].astype(np.float64), want, wl.dtype, f"{wl.name} head {bh}")
+        say(f"workload {wl.name}: head {bh}: max-abs {mx:.3g}, mean-abs {mean:.3g}")
+        means.append(mean)
+    mean = float(np.mean(means))
+    say(f"workload {wl.name}: mean-abs over the whole output {mean:.3g}")
+    assert mean <= TOL[wl.dtype]["mean_abs"]
     # Every head has dilation 1 here, so each head scores the same pairs.
     assert set(dil) == {1}
     say(f"workload {wl.name}: pair count")
