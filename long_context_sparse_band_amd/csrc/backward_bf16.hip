@@ -605,6 +605,15 @@ void bwd_keys_kernel(BwdArgs a) {
   for (int e = 0; e < NL; ++e)
     boff[e] = (unsigned)((d * (ld_row + (256 / CPR) * e)) * kBD + 8 * ld_c) * 2u;
   const unsigned moff = (unsigned)(d * (KS == 2 ? lane : (lane & 31))) * 4u;
+  // D = 128 (256 registers at two wavefronts per SIMD) recomputes these
+  // per-lane offsets where they are used, from a thread index the compiler
+  // cannot carry across the loop, instead of holding them (it would spill an
+  // MFMA operand, whose reload waits for the step's tile loads).
+  auto opaque_tid = [&]() {
+    int x = (int)threadIdx.x;
+    asm volatile("" : "+v"(x));
+    return x;
+  };
   // Tiles tb .. te-1 of this item; step j holds tiles tb + KS j .. + KS - 1.
   int tb = 0, te = n_tiles;
   auto fast_tile = [&](int t) { return !gk && t < n_band && q_lo + 32 * t + 31 <= q_hi; };
@@ -616,18 +625,39 @@ void bwd_keys_kernel(BwdArgs a) {
         const unsigned so = (unsigned)((j & 1) * 2 + q2) * TILE;
         if (fast_tile(t)) {
           const size_t row0 = (size_t)(r + d * (q_lo + 32 * t)) * kBD;
+          if constexpr (D == 128) {
+            const int tx = opaque_tid(), lr = tx / CPR, lc = swz<D>(lr, tx % CPR);
 #pragma unroll
-          for (int e = 0; e < NL; ++e) {
-            dma16_s(Qp + row0, boff[e], xl + so + 4096u * e);
-            dma16_s(dOp + row0, boff[e], yl + so + 4096u * e);
+            for (int e = 0; e < NL; ++e) {
+              const unsigned bo = (unsigned)((d * (lr + (256 / CPR) * e)) * kBD + 8 * lc) * 2u;
+              dma16_s(Qp + row0, bo, xl + so + 4096u * e);
+              dma16_s(dOp + row0, bo, yl + so + 4096u * e);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < NL; ++e) {
+              dma16_s(Qp + row0, boff[e], xl + so + 4096u * e);
+              dma16_s(dOp + row0, boff[e], yl + so + 4096u * e);
+            }
           }
         } else {
+          if constexpr (D == 128) {
+            const int tx = opaque_tid(), lr = tx / CPR, lc = swz<D>(lr, tx % CPR);
 #pragma unroll
-          for (int e = 0; e < NL; ++e) {
-            bool part;
-            const int p = row_pos(t, ld_row + (256 / CPR) * e, part);
-            dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so + 4096u * e);
-            dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so + 4096u * e);
+            for (int e = 0; e < NL; ++e) {
+              bool part;
+              const int p = row_pos(t, lr + (256 / CPR) * e, part);
+              dma16(Qp + (size_t)p * kBD + 8 * lc, xl + so + 4096u * e);
+              dma16(dOp + (size_t)p * kBD + 8 * lc, yl + so + 4096u * e);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < NL; ++e) {
+              bool part;
+              const int p = row_pos(t, ld_row + (256 / CPR) * e, part);
+              dma16(Qp + (size_t)p * kBD + 8 * ld_c, xl + so + 4096u * e);
+              dma16(dOp + (size_t)p * kBD + 8 * ld_c, yl + so + 4096u * e);
+            }
           }
         }
       }
@@ -640,8 +670,14 @@ void bwd_keys_kernel(BwdArgs a) {
       const unsigned lds = ml + (unsigned)(j & 1) * (2 * 32 * 4);
       if (fast_tile(t0s + KS - 1) && t0s + KS - 1 < te) {
         const int pl = wave == 1 ? 0 : 2;
-        dma4_s(a.terms + ((size_t)pl * mplane + (size_t)w.bh * N + r + d * (q_lo + 32 * t0s)),
-               moff, lds);
+        if constexpr (D == 128) {
+          const unsigned mo = (unsigned)(d * (opaque_tid() & (KS == 2 ? 63 : 31))) * 4u;
+          dma4_s(a.terms + ((size_t)pl * mplane + (size_t)w.bh * N + r + d * (q_lo + 32 * t0s)),
+                 mo, lds);
+        } else {
+          dma4_s(a.terms + ((size_t)pl * mplane + (size_t)w.bh * N + r + d * (q_lo + 32 * t0s)),
+                 moff, lds);
+        }
       } else {
         const int t = min(t0s + (KS == 2 ? lane >> 5 : 0), te - 1);
         bool part;
@@ -721,8 +757,15 @@ void bwd_keys_kernel(BwdArgs a) {
         }
         const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
         const unsigned yb = (unsigned)(uintptr_t)(LDS_AS void*)sm.y[st][kq];
-        tr_mfma<D>(yb, ta, pw, accV);   // dV^T += dO^T P
-        tr_mfma<D>(xb, ta, dsw, accK);  // dK^T += Q^T dS
+        if constexpr (D == 128) {
+          TrAddr<D> tq;
+          tq.init(opaque_tid() & 63);
+          tr_mfma<D>(yb, tq, pw, accV);   // dV^T += dO^T P
+          tr_mfma<D>(xb, tq, dsw, accK);  // dK^T += Q^T dS
+        } else {
+          tr_mfma<D>(yb, ta, pw, accV);
+          tr_mfma<D>(xb, ta, dsw, accK);
+        }
       }
       wait_vm0();
       __syncthreads();
