@@ -1,0 +1,100 @@
+"""GPU parity where the online softmax has to move its running maximum.
+
+The band kernels keep a running maximum per row and rescale the sum and the
+accumulator only when a tile's weights would grow past a bound (the
+Unlimiformer page, section 2.3, footnote 3: adding one constant to every
+score leaves the softmax unchanged).  With unit-variance inputs a later tile
+rarely beats the first one by that much, so these cases force it: scores
+that grow along the key axis (every tile outranks the one before), scores
+that shrink along it (the first tile holds the maximum), and large random
+scores.  fp32 takes one rising case at D = 64: with scores near 60 at
+D = 128, or near 90 at random, the float32 rounding of the dot products alone
+moves the output past the fp32 bound of 1e-5 (scores taken as a plain float32
+matrix product, then an exact softmax, are 2.1e-5 to 2.6e-5 off the oracle
+there; 8e-6 on the case kept).  Every output element is compared with the
+oracle, in both band workgroup layouts, at both head dimensions, and for the
+global rows (whose key chunks then carry very different maxima into the
+merge).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_sparse_band_amd import lfattn as L
+from long_context_sparse_band_amd import workloads as W
+from gpu_util import compare, run, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+
+
+def _exact(a, dtype):
+    """The values the GPU will see (bf16: round to nearest even)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype != "bf16":
+        return a
+    return W.bf16_bits_to_f32(W.bf16_round_bits(a)).reshape(a.shape)
+
+
+def _case(kind, B, H, N, D, dtype, window, dil, glob, seed):
+    inp = W.small_case(B, H, N, D, dtype, window, dilation=dil, glob=glob, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    if kind == "large":
+        # Scores with a standard deviation of about 16 (Q and K four times
+        # the unit draw); V stays unit-scale.
+        inp.q = _exact(4.0 * inp.q, dtype)
+        inp.k = _exact(4.0 * inp.k, dtype)
+    else:
+        # Q a positive constant direction plus a little noise, K along the
+        # same direction with a magnitude that rises (or falls) with the key
+        # position: score(i, j) grows (falls) across the sequence up to about
+        # 100 (bf16; fp32: 60), by 4 to 6 per 32 keys, so that a new tile's
+        # weights reach past the bound and the maximum is moved.
+        grow = np.linspace(0.0, 1.0, N, dtype=np.float32)
+        if kind == "falling":
+            grow = grow[::-1].copy()
+        base = np.ones((B, H, N, D), dtype=np.float32)
+        q = base + 0.05 * rng.standard_normal((B, H, N, D)).astype(np.float32)
+        peak = 100.0 if dtype == "bf16" else 60.0
+        mag = (peak * np.sqrt(D) / D) * grow[None, None, :, None]
+        k = mag * (base + 0.05 * rng.standard_normal((B, H, N, D)).astype(np.float32))
+        inp.q = _exact(q, dtype)
+        inp.k = _exact(k, dtype)
+    return inp
+
+
+CASES = [
+    # kind, B, H, N, D, dtype, window, dilation, globals
+    ("rising", 1, 2, 600, 64, "bf16", 512, [1, 2], [0, 300, 599]),
+    ("rising", 1, 2, 600, 128, "bf16", 200, [1, 1], [5]),
+    ("falling", 1, 2, 600, 64, "bf16", 512, [1, 2], [0, 300, 599]),
+    ("falling", 1, 1, 777, 128, "bf16", 300, [3], [100, 700]),
+    ("large", 1, 2, 1000, 64, "bf16", 256, [1, 2], list(range(0, 1000, 50))),
+    ("large", 1, 2, 700, 128, "bf16", 512, [1, 3], [0, 1, 699]),
+    ("rising", 1, 1, 500, 64, "f32", 256, [1], [0, 250]),
+]
+
+
+# bf16 in both band workgroup layouts; fp32 has one.
+RUNS = [(c, r) for c in CASES for r in ((64, 128) if c[5] == "bf16" else (128,))]
+
+
+@pytest.mark.parametrize("case,rows", RUNS,
+                         ids=["%s_N%dD%d_%s-%d" % (c[0], c[3], c[4], c[5], r) for c, r in RUNS])
+def test_running_maximum_moves(case, rows, monkeypatch):
+    kind, B, H, N, D, dt, window, dil, glob = case
+    monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows))
+    inp = _case(kind, B, H, N, D, dt, window, dil, glob, seed=300 + N)
+    say(f"running maximum: {case}, {rows}-row workgroups")
+    got, pairs = run(inp)
+    want = oracle.attention(inp.q, inp.k, inp.v, window, dil, glob)
+    compare(got, want, dt, f"{kind} N{N} D{D} {dt}")
+    assert pairs == oracle.count_pairs(B, H, N, window, dil, glob)
