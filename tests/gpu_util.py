@@ -8,6 +8,7 @@ import sys
 import numpy as np
 
 from long_context_sparse_band_amd import lfattn as L
+from long_context_sparse_band_amd import workloads as W
 
 # Tolerances: fp32 max-abs 1e-5; bf16 (inputs rounded to bf16, oracle on the
 # rounded values) max-abs 2e-2 and mean-abs 2e-3.
@@ -126,3 +127,40 @@ def readout_compare(forward, B, H, N, D, tdt, sets_of, chunks=None, what=""):
         assert np.array_equal(got, want), f"{what}: chunk {c0}: key sets differ"
         total += len(want)
     return total
+
+
+def _bf16_exact(a, dtype):
+    """The values the GPU will see (bf16: round to nearest even)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype != "bf16":
+        return a
+    return W.bf16_bits_to_f32(W.bf16_round_bits(a)).reshape(a.shape)
+
+
+def moving_max_case(kind, B, H, N, D, dtype, window, dil, glob, seed):
+    """Inputs whose scores move the online softmax's running maximum:
+    "rising" / "falling" along the key axis, or "large" random scores."""
+    inp = W.small_case(B, H, N, D, dtype, window, dilation=dil, glob=glob, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    if kind == "large":
+        # Scores with a standard deviation of about 16 (Q and K four times
+        # the unit draw); V stays unit-scale.
+        inp.q = _bf16_exact(4.0 * inp.q, dtype)
+        inp.k = _bf16_exact(4.0 * inp.k, dtype)
+    else:
+        # Q a positive constant direction plus a little noise, K along the
+        # same direction with a magnitude that rises (or falls) with the key
+        # position: score(i, j) grows (falls) across the sequence up to about
+        # 100 (bf16; fp32: 60), by 4 to 6 per 32 keys, so that a new tile's
+        # weights reach past the bound and the maximum is moved.
+        grow = np.linspace(0.0, 1.0, N, dtype=np.float32)
+        if kind == "falling":
+            grow = grow[::-1].copy()
+        base = np.ones((B, H, N, D), dtype=np.float32)
+        q = base + 0.05 * rng.standard_normal((B, H, N, D)).astype(np.float32)
+        peak = 100.0 if dtype == "bf16" else 60.0
+        mag = (peak * np.sqrt(D) / D) * grow[None, None, :, None]
+        k = mag * (base + 0.05 * rng.standard_normal((B, H, N, D)).astype(np.float32))
+        inp.q = _bf16_exact(q, dtype)
+        inp.k = _bf16_exact(k, dtype)
+    return inp

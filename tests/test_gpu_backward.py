@@ -9,7 +9,7 @@ import pytest
 import oracle
 from long_context_sparse_band_amd import lfattn as L
 from long_context_sparse_band_amd import workloads as W
-from gpu_util import say, to_device
+from gpu_util import moving_max_case, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -107,6 +107,90 @@ def test_backward_every_element(case, rows_mode, D, monkeypatch):
     errs = [check(x.cpu().numpy().astype(np.float64), w, f"{kind} {n}")
             for x, w, n in zip((dq, dk, dv), want, ("dq", "dk", "dv"))]
     say(f"  relative max/mean errors dq dk dv: {errs}")
+
+
+# Scores that rise along the keys (up to about 100) or are large at random
+# (standard deviation about 16): softmax weights near one-hot, log-sum-exp
+# far from zero.
+BIG_SCORES = [
+    ("rising", 1, 2, 600, 64, 512, [1, 2], [0, 300, 599]),
+    ("rising", 1, 1, 500, 128, 200, [1], [5]),
+    ("large", 1, 2, 700, 64, 256, [1, 3], [0, 1, 699]),
+    ("large", 1, 2, 400, 128, 128, [1, 2], [7]),
+]
+
+
+@pytest.mark.parametrize("rows_mode", [64, 128])
+@pytest.mark.parametrize("case", BIG_SCORES, ids=lambda c: "%s_N%dD%d" % (c[0], c[3], c[4]))
+def test_backward_large_scores(case, rows_mode, monkeypatch):
+    import torch
+    monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows_mode))
+    monkeypatch.setenv("LFATTN_BWD_ROWS", str(rows_mode))
+    kind, B, H, N, D, window, dil, glob = case
+    a = moving_max_case(kind, B, H, N, D, "bf16", window, dil, glob, seed=500 + N)
+    rng = np.random.default_rng(501 + N)
+    do = _bf16(rng.standard_normal((B, H, N, D)).astype(np.float32))
+    h = L.lfattn_create(B, H, N, D, L.LFATTN_BF16, window, dil, glob)
+    try:
+        q, k, v = to_device(a)
+        g = torch.from_numpy(do).to("cuda:0").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        dq, dk, dv = (torch.full((B, H, N, D), float("nan"), dtype=torch.float32,
+                                 device=q.device) for _ in range(3))
+        say(f"backward, large scores: {case}, rows {rows_mode}")
+        L.lfattn_forward_lse(h, q, k, v, o, lse)
+        L.lfattn_backward(h, q, k, v, o, g, lse, dq, dk, dv)
+        torch.cuda.synchronize()
+    finally:
+        L.lfattn_destroy(h)
+    kw = dict(window=window, dilation=dil, glob=glob)
+    want = oracle.attention_grad(a.q, a.k, a.v, do, **kw)
+    want_lse = oracle.row_lse(a.q, a.k, **kw)
+    err = np.abs(lse.cpu().numpy().astype(np.float64) - want_lse)
+    assert err.max() <= 1e-2, f"{kind}: LSE max-abs {err.max():.3g}"
+    # The backward takes Delta = dO . O from the O it is given (the forward's
+    # bf16 output), so it computes the gradient with dS' = P (dP - Delta -
+    # dDelta) = dS - P dDelta: dQ' = dQ - scale dDelta (P K) and dK' = dK -
+    # scale P^T (dDelta Q).  Both terms come from the oracle (attention with
+    # K as the values; the value gradient for the upstream gradient dDelta Q).
+    o_got = o.float().cpu().numpy().astype(np.float64)
+    ddelta = np.sum(do.astype(np.float64) * (o_got - oracle.attention(a.q, a.k, a.v, **kw)),
+                    axis=-1)
+    scale = 1.0 / np.sqrt(D)
+    pk = oracle.attention(a.q, a.k, a.k, **kw)
+    ptq = oracle.attention_grad(a.q, a.k, a.v, ddelta[..., None] * a.q, **kw)[2]
+    want = (want[0] - scale * ddelta[..., None] * pk, want[1] - scale * ptq, want[2])
+    # dS enters the dS K and dS^T Q products rounded to bf16 (relative error
+    # at most 2^-9), so dQ_i can be off by up to scale 2^-9 sum_j |dS_ij| |K_j|
+    # (and dK_j by scale 2^-9 sum_i |dS_ij| |Q_i|): terms that the exact
+    # gradient cancels (it does not change when every key moves by one
+    # vector) but this rounding does not.  Here the keys share a large common
+    # direction, and that bound (doubled), not the plain relative one, is
+    # the measure.  |dS| from the dense masked softmax of each head.
+    extra = [np.zeros_like(want[0]), np.zeros_like(want[1])]
+    for b in range(B):
+        for hh in range(H):
+            qh, kh_, vh = (x[b, hh].astype(np.float64) for x in (a.q, a.k, a.v))
+            allowed = np.zeros((N, N), dtype=bool)
+            for i in range(N):
+                allowed[i, oracle.allowed_set(N, window, dil[hh], glob, i)] = True
+            sc = np.where(allowed, scale * (qh @ kh_.T), -np.inf)
+            pm = np.exp(sc - sc.max(axis=1, keepdims=True))
+            pm /= pm.sum(axis=1, keepdims=True)
+            dp = do[b, hh].astype(np.float64) @ vh.T
+            dsm = np.abs(pm * (dp - np.sum(do[b, hh] * o_got[b, hh], axis=1)[:, None]))
+            extra[0][b, hh] = 2 * scale * 2.0 ** -9 * (dsm @ np.abs(kh_))
+            extra[1][b, hh] = 2 * scale * 2.0 ** -9 * (dsm.T @ np.abs(qh))
+    for i, (x, w, n) in enumerate(zip((dq, dk, dv), want, ("dq", "dk", "dv"))):
+        got = x.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), f"{kind} {n}: non-finite"
+        ref = max(1e-3, float(np.abs(w).max()))
+        allow = REL_MAX * ref + (extra[i] if i < 2 else 0.0)
+        over = np.abs(got - w) - allow
+        say(f"  {n}: max-abs {np.abs(got - w).max():.3g}, worst margin {over.max():.3g}")
+        assert over.max() <= 0, f"{kind} {n}: max-abs {np.abs(got - w).max():.3g} over the bound"
+        assert np.abs(got - w).mean() <= REL_MEAN * ref + (extra[i].mean() if i < 2 else 0.0)
 
 
 FULL = ["longformer_base_n4096", "dilated_charlm_n8192", "gmat_memory_m64_l16384",

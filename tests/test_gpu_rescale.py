@@ -22,8 +22,7 @@ import pytest
 
 import oracle
 from long_context_sparse_band_amd import lfattn as L
-from long_context_sparse_band_amd import workloads as W
-from gpu_util import compare, run, say
+from gpu_util import compare, moving_max_case, run, say
 
 pytestmark = pytest.mark.gpu
 
@@ -34,41 +33,6 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     L.load()
-
-
-def _exact(a, dtype):
-    """The values the GPU will see (bf16: round to nearest even)."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    if dtype != "bf16":
-        return a
-    return W.bf16_bits_to_f32(W.bf16_round_bits(a)).reshape(a.shape)
-
-
-def _case(kind, B, H, N, D, dtype, window, dil, glob, seed):
-    inp = W.small_case(B, H, N, D, dtype, window, dilation=dil, glob=glob, seed=seed)
-    rng = np.random.default_rng(seed + 1)
-    if kind == "large":
-        # Scores with a standard deviation of about 16 (Q and K four times
-        # the unit draw); V stays unit-scale.
-        inp.q = _exact(4.0 * inp.q, dtype)
-        inp.k = _exact(4.0 * inp.k, dtype)
-    else:
-        # Q a positive constant direction plus a little noise, K along the
-        # same direction with a magnitude that rises (or falls) with the key
-        # position: score(i, j) grows (falls) across the sequence up to about
-        # 100 (bf16; fp32: 60), by 4 to 6 per 32 keys, so that a new tile's
-        # weights reach past the bound and the maximum is moved.
-        grow = np.linspace(0.0, 1.0, N, dtype=np.float32)
-        if kind == "falling":
-            grow = grow[::-1].copy()
-        base = np.ones((B, H, N, D), dtype=np.float32)
-        q = base + 0.05 * rng.standard_normal((B, H, N, D)).astype(np.float32)
-        peak = 100.0 if dtype == "bf16" else 60.0
-        mag = (peak * np.sqrt(D) / D) * grow[None, None, :, None]
-        k = mag * (base + 0.05 * rng.standard_normal((B, H, N, D)).astype(np.float32))
-        inp.q = _exact(q, dtype)
-        inp.k = _exact(k, dtype)
-    return inp
 
 
 CASES = [
@@ -92,7 +56,7 @@ RUNS = [(c, r) for c in CASES for r in ((64, 128) if c[5] == "bf16" else (128,))
 def test_running_maximum_moves(case, rows, monkeypatch):
     kind, B, H, N, D, dt, window, dil, glob = case
     monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows))
-    inp = _case(kind, B, H, N, D, dt, window, dil, glob, seed=300 + N)
+    inp = moving_max_case(kind, B, H, N, D, dt, window, dil, glob, seed=300 + N)
     say(f"running maximum: {case}, {rows}-row workgroups")
     got, pairs = run(inp)
     want = oracle.attention(inp.q, inp.k, inp.v, window, dil, glob)
