@@ -314,28 +314,6 @@ void bwd_rows_kernel(BwdArgs a) {
   const int n_band = gi ? (c1 - c0 + 31) / 32 : (s_hi - s_lo) / 32 + 1;
   const int n_tiles = n_band + (gi ? 0 : (ng + 31) / 32);
 
-  // Operands of the rows: Q and dO rows (B of S^T = K Q^T and dP^T = V dO^T),
-  // the log-sum-exp (base 2 of scores times scale * log2(e)) and Delta.
-  bf16x8 q[kBD / 16], g[kBD / 16];
-#pragma unroll
-  for (int ks = 0; ks < kBD / 16; ++ks) {
-    q[ks] = *(const bf16x8*)(Qp + (size_t)pos_u * kBD + 16 * ks + 8 * hi);
-    g[ks] = *(const bf16x8*)(dOp + (size_t)pos_u * kBD + 16 * ks + 8 * hi);
-  }
-  const float lse2 = a.lse[(size_t)w.bh * N + pos_u] * kLog2e;
-  // Delta = dO . O of the row (each lane half holds 32 of its columns); the
-  // band items write it, with the row's -lse / scale, for the key side,
-  // which runs after this kernel.
-  float dlt = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < kBD / 16; ++ks) {
-    const bf16x8 o8 = *(const bf16x8*)(Op + (size_t)pos_u * kBD + 16 * ks + 8 * hi);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dlt = fmaf((float)g[ks][e], (float)o8[e], dlt);
-  }
-  dlt += __shfl_xor(dlt, 32);
-  const float nls = -a.lse[(size_t)w.bh * N + pos_u] / a.scale;
-
   // Key position of row rr of tile t; a row past the end of the tile's keys
   // takes the last one (its weights are masked).
   auto key_pos = [&](int t, int rr) -> int {
@@ -370,13 +348,38 @@ void bwd_rows_kernel(BwdArgs a) {
     }
   };
 
+  // The first tile's loads go out before the rows' operands, so that their
+  // latency overlaps the operand loads and Delta instead of following them.
+  if (n_steps > 0) load(0);
+
+  // Operands of the rows: Q and dO rows (B of S^T = K Q^T and dP^T = V dO^T),
+  // the log-sum-exp (base 2 of scores times scale * log2(e)) and Delta.
+  bf16x8 q[kBD / 16], g[kBD / 16];
+#pragma unroll
+  for (int ks = 0; ks < kBD / 16; ++ks) {
+    q[ks] = *(const bf16x8*)(Qp + (size_t)pos_u * kBD + 16 * ks + 8 * hi);
+    g[ks] = *(const bf16x8*)(dOp + (size_t)pos_u * kBD + 16 * ks + 8 * hi);
+  }
+  const float lse2 = a.lse[(size_t)w.bh * N + pos_u] * kLog2e;
+  // Delta = dO . O of the row (each lane half holds 32 of its columns); the
+  // band items write it, with the row's -lse / scale, for the key side,
+  // which runs after this kernel.
+  float dlt = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < kBD / 16; ++ks) {
+    const bf16x8 o8 = *(const bf16x8*)(Op + (size_t)pos_u * kBD + 16 * ks + 8 * hi);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dlt = fmaf((float)g[ks][e], (float)o8[e], dlt);
+  }
+  dlt += __shfl_xor(dlt, 32);
+  const float nls = -a.lse[(size_t)w.bh * N + pos_u] / a.scale;
+
   TrAddr<D> ta;
   ta.init(lane);
   f32x16 acc[D / 32];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b) acc[b] = f32x16{};
 
-  if (n_steps > 0) load(0);
   wait_vm0();
   __syncthreads();
   for (int j = 0; j < n_steps; ++j) {
