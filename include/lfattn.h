@@ -75,7 +75,10 @@
  * are the same either way up to floating-point summation order.  The
  * backward (bf16) takes 64-row items with split key tiles on its query side
  * and 64-key items with split row tiles on its key side; LFATTN_BWD_ROWS, 64
- * or 128 when lfattn_create runs, sets both sides to that size.  With
+ * or 128 when lfattn_create runs, sets both sides to that size.  At D = 64
+ * its query side runs three or four wavefronts per SIMD (four when its items
+ * come to two or more rounds of the three-per-CU slots);
+ * LFATTN_BWD_ROWS_WPE, 3 or 4, overrides that choice (the same results).  With
  * LFATTN_FUSE_MERGE=1 at lfattn_create, bf16 handles merge the global rows'
  * partial results inside the band launch instead of a separate launch (the
  * same results; slower on the workloads measured, hence not the default).

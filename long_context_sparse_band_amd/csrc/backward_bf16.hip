@@ -266,9 +266,14 @@ __device__ __forceinline__ void stage_globals(SM& sm, const int* gl, int ng, int
 template <int D>
 constexpr int bwd_wpe() { return D == 64 ? 3 : 2; }
 
-template <int D, int KS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_wpe<D>(), bwd_wpe<D>())))
+// The query side takes WPE wavefronts per SIMD: bwd_wpe, or 4 at D = 64 (128
+// registers), where it recomputes its per-lane load and transposed-read
+// offsets each step from a thread index the compiler cannot carry across the
+// loop, instead of holding them (which would spill inside the loop).
+template <int D, int KS, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void bwd_rows_kernel(BwdArgs a) {
+  constexpr bool kLean = WPE > bwd_wpe<D>();
   constexpr int RB = 4 / KS, IR = 32 * RB;  // row blocks, rows per item
   constexpr int kBD = D, TILE = BwdDim<D>::TILE, CPR = BwdDim<D>::CPR;
   __shared__ __attribute__((aligned(16))) BwdSmem<D> sm;
@@ -340,9 +345,16 @@ void bwd_rows_kernel(BwdArgs a) {
         const unsigned so = (unsigned)((j & 1) * 2 + q2) * TILE;
 #pragma unroll
         for (int e = 0; e < NL; ++e) {
-          const size_t p = (size_t)key_pos(t, ld_row + (256 / CPR) * e);
-          dma16(Kp + p * kBD + 8 * ld_c, xl + so + 4096u * e);
-          dma16(Vp + p * kBD + 8 * ld_c, yl + so + 4096u * e);
+          int lr = ld_row, lc = ld_c;
+          if constexpr (kLean) {
+            int tx = (int)threadIdx.x;
+            asm volatile("" : "+v"(tx));
+            lr = tx / CPR;
+            lc = swz<D>(lr, tx % CPR);
+          }
+          const size_t p = (size_t)key_pos(t, lr + (256 / CPR) * e);
+          dma16(Kp + p * kBD + 8 * lc, xl + so + 4096u * e);
+          dma16(Vp + p * kBD + 8 * lc, yl + so + 4096u * e);
         }
       }
     }
@@ -435,7 +447,15 @@ void bwd_rows_kernel(BwdArgs a) {
         }
       }
       const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
-      tr_mfma<D>(xb, ta, dsw, acc);
+      if constexpr (kLean) {
+        TrAddr<D> tq;
+        int ll = (int)threadIdx.x & 63;
+        asm volatile("" : "+v"(ll));
+        tq.init(ll);
+        tr_mfma<D>(xb, tq, dsw, acc);
+      } else {
+        tr_mfma<D>(xb, ta, dsw, acc);
+      }
     }
     wait_vm0();
     __syncthreads();
@@ -868,8 +888,11 @@ __global__ __launch_bounds__(3 * D) void bwd_merge_kernel(BwdArgs a) {
 template <int D>
 static hipError_t launch_backward_d(const BwdArgs& rows, const BwdArgs& keys, int n_rows_wg,
                                    int n_keys_wg, hipStream_t s, const Timing* t) {
-  hipError_t e = launch_kernel(rows.ks == 2 ? bwd_rows_kernel<D, 2> : bwd_rows_kernel<D, 1>,
-                               dim3(n_rows_wg), dim3(256), s, rows, t[0]);
+  constexpr int W = bwd_wpe<D>();
+  auto rk = rows.ks == 2 ? bwd_rows_kernel<D, 2, W> : bwd_rows_kernel<D, 1, W>;
+  if constexpr (D == 64)
+    if (rows.rows_wpe == 4) rk = rows.ks == 2 ? bwd_rows_kernel<D, 2, 4> : bwd_rows_kernel<D, 1, 4>;
+  hipError_t e = launch_kernel(rk, dim3(n_rows_wg), dim3(256), s, rows, t[0]);
   if (e != hipSuccess) return e;
   auto kk = keys.proj ? (keys.ks == 2 ? bwd_keys_kernel<D, 2, true> : bwd_keys_kernel<D, 1, true>)
                       : (keys.ks == 2 ? bwd_keys_kernel<D, 2, false> : bwd_keys_kernel<D, 1, false>);

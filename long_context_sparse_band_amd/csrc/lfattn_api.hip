@@ -132,6 +132,7 @@ struct lfattn_ctx {
   size_t n_gcount = 0;
   int band_rows = 0;  // rows per band workgroup
   int bwd_rows[2] = {0, 0};  // rows (keys) per backward item, row / key side: 64 or 128
+  int bwd_rows_wpe = 0;      // query side, D = 64: its kernel's wavefronts per SIMD (3 or 4)
   int bwd_chunk = 0;  // keys (rows) per chunk of a backward global item
   int g_waves = 0, g_rows = 0, n_sets = 0, n_chunks = 0, chunk_keys = 0, n_glob_wg = 0;
   bool glob_items = false;  // global-row partials run as items of the band launch
@@ -619,6 +620,18 @@ lfattn_status create_impl(lfattn_t* out, int B, int H, int N, int D, lfattn_dtyp
         }
       }
     }
+    // The query side at D = 64 runs at four wavefronts per SIMD (a third more
+    // workgroups per round, with a leaner register budget) when its items
+    // come to two or more rounds of three-per-CU slots: 8K -6%, 16K -7%; at
+    // Longformer-base (1.25 rounds) three are faster.  LFATTN_BWD_ROWS_WPE=3
+    // or 4 overrides the choice (both give the same results).
+    c->bwd_rows_wpe = 3;
+    if (D == 64 && (long long)c->n_bwork[0] >= 2LL * 3 * cus) c->bwd_rows_wpe = 4;
+    if (D == 64)
+      if (const char* e = std::getenv("LFATTN_BWD_ROWS_WPE")) {
+        if (std::strcmp(e, "3") == 0) c->bwd_rows_wpe = 3;
+        if (std::strcmp(e, "4") == 0) c->bwd_rows_wpe = 4;
+      }
   }
 
   // ---- device state ----
@@ -958,6 +971,7 @@ lfattn_status backward_impl(lfattn_t c, const void* Q, const void* K, const void
   lfattn::BwdArgs ak = a;
   a.work = c->d_bwork;
   a.ks = c->bwd_rows[0] == 64 ? 2 : 1;
+  a.rows_wpe = c->bwd_rows_wpe;
   ak.work = c->d_bwork + c->n_bwork[0];
   ak.ks = c->bwd_rows[1] == 64 ? 2 : 1;
   lfattn::Timing t[3];

@@ -128,6 +128,9 @@ struct BwdArgs {
   long long isg_stride;
   int H, N, D, n_bh, hw, hr, chunk, cbase, chunk_keys, n_glob;
   int ks;                      // 1: 128 rows (keys) per item; 2: 64, tiles split in two
+  // Query side, D = 64: wavefronts per SIMD of its kernel, 3 (168 registers)
+  // or 4 (128; more workgroups per round for launches of several rounds).
+  int rows_wpe;
   float sl2, scale;
   // Global items' partial gradients, three planes (dQ, dK, dV) of
   // [B*H][n_gch chunks][n_glob][D] fp32, summed by the merge kernel; gsel:

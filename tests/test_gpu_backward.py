@@ -61,15 +61,22 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("D", [64, 128])
+# D, query-side wavefronts per SIMD (D = 64: the 3- and 4-wavefront kernels).
+KERNELS = [(64, 3), (64, 4), (128, 2)]
+
+
+@pytest.mark.parametrize("D,wpe", KERNELS, ids=["D%d-w%d" % k for k in KERNELS])
 @pytest.mark.parametrize("rows_mode", [64, 128])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0] + "_N%d" % c[1]["N"])
-def test_backward_every_element(case, rows_mode, D, monkeypatch):
+def test_backward_every_element(case, rows_mode, D, wpe, monkeypatch):
     import torch
-    # Both forward band kernels (the log-sum-exp) and both backward item
-    # sizes (64 rows with split tiles, 128 rows with one tile stream).
+    # Both forward band kernels (the log-sum-exp), both backward item sizes
+    # (64 rows with split tiles, 128 rows with one tile stream) and both
+    # query-side kernels at D = 64.
     monkeypatch.setenv("LFATTN_BAND_ROWS", str(rows_mode))
     monkeypatch.setenv("LFATTN_BWD_ROWS", str(rows_mode))
+    if D == 64:
+        monkeypatch.setenv("LFATTN_BWD_ROWS_WPE", str(wpe))
     kind, p = case
     B, H, N = p["B"], p["H"], p["N"]
     a = W.small_case(B, H, N, D, "bf16", p.get("window", 0), dilation=p.get("dil"), seed=88)
