@@ -967,11 +967,11 @@ lfattn_status backward_impl(lfattn_t c, const void* Q, const void* K, const void
   a.chunk_keys = c->bwd_chunk; a.n_glob = c->n_gmax;
   a.gpart = c->d_gpart; a.n_gch = c->n_gch; a.gsel = c->d_gsel;
   a.scale = c->scale; a.sl2 = c->scale * 1.4426950408889634f;
+  a.rows_wpe = c->bwd_rows_wpe;
   // The key side: the same arguments with its own table and item size.
   lfattn::BwdArgs ak = a;
   a.work = c->d_bwork;
   a.ks = c->bwd_rows[0] == 64 ? 2 : 1;
-  a.rows_wpe = c->bwd_rows_wpe;
   ak.work = c->d_bwork + c->n_bwork[0];
   ak.ks = c->bwd_rows[1] == 64 ? 2 : 1;
   lfattn::Timing t[3];
