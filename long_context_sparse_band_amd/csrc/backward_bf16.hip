@@ -762,21 +762,28 @@ void bwd_keys_kernel(BwdArgs a) {
         unsigned pw[8], dsw[8];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          float p2[2], ds2[2];
+          const float p0 = __builtin_amdgcn_exp2f(s[i] * a.sl2);
+          const float p1 = __builtin_amdgcn_exp2f(s[i + 1] * a.sl2);
+          pw[i / 2] = pack2(p0, p1);
+          dsw[i / 2] = pack2(p0 * dp[i], p1 * dp[i + 1]);
+        }
+        if (!full) {
+          // Pairs outside the key's rows (or padding rows) keep no weight:
+          // their bf16 halves are cleared bitwise (whatever the weight was,
+          // an infinity or a NaN included).  The lane's row offset is opaque
+          // so that the sixteen per-register offsets are formed here, not
+          // kept live through the loop.
+          int mb = band_tile ? q_lo + 32 * t - rlo_k : 0;
+          asm volatile("" : "+v"(mb));
+          const unsigned ms = band_tile ? rspan_k : (unsigned)(glim - 1);
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            float p = __builtin_amdgcn_exp2f(s[i + e] * a.sl2);
-            if (!full) {
-              const int qq = brow(i + e, hi);
-              const bool keep = band_tile ? (unsigned)(q_lo + 32 * t + qq - rlo_k) <= rspan_k
-                                          : qq < glim;
-              p = keep ? p : 0.0f;
-            }
-            p2[e] = p;
-            ds2[e] = p * dp[i + e];
+          for (int i = 0; i < 16; i += 2) {
+            const bool k0 = (unsigned)(mb + brow(i, hi)) <= ms;
+            const bool k1 = (unsigned)(mb + brow(i + 1, hi)) <= ms;
+            const unsigned m = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
+            pw[i / 2] &= m;
+            dsw[i / 2] &= m;
           }
-          pw[i / 2] = pack2(p2[0], p2[1]);
-          dsw[i / 2] = pack2(ds2[0], ds2[1]);
         }
         const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
         const unsigned yb = (unsigned)(uintptr_t)(LDS_AS void*)sm.y[st][kq];
