@@ -434,35 +434,47 @@ void bwd_rows_kernel(BwdArgs a) {
       const f32x16 s = rows_mfma<D>(sm.x[st][kq], l32, hi, q);
       const f32x16 dp = rows_mfma<D>(sm.y[st][kq], l32, hi, g);
       unsigned dsw[8];
-      if (full) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i], a.sl2, -lse2));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], a.sl2, -lse2));
-          dsw[i / 2] = pack2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
-        }
-      } else {
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i], a.sl2, -lse2));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], a.sl2, -lse2));
+        dsw[i / 2] = pack2(p0 * (dp[i] - dlt), p1 * (dp[i + 1] - dlt));
+      }
+      if (!full) {
+        // Keys the row does not score keep no weight: their bf16 halves are
+        // cleared bitwise (whatever the value was, an infinity or a NaN
+        // included), under one branch rather than a test per register.
+        unsigned mk[8];
+        if (gi || t < n_band) {
+          // Key kk of the tile is allowed when mb + kk lies in [0, lim]: a
+          // chunk's keys before c1, or band keys within the row's interval
+          // and the item's key range.
+          int mb = gi ? 32 * t : s_lo + 32 * t - lo_u;
+          int lim = gi ? c1 - c0 - 1 : min((int)span_u, s_hi - lo_u);
+          if (!row_ok || lim < 0) mb = -64, lim = 0;
+          asm volatile("" : "+v"(mb));
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          float ds2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int kk = brow(i + e, hi);
-            bool ok = row_ok;
-            if (gi) {
-              ok &= c0 + 32 * t + kk < c1;
-            } else if (t < n_band) {
-              const int k = s_lo + 32 * t + kk;
-              ok &= (k <= s_hi) & ((unsigned)(k - lo_u) <= span_u);
-            } else {
-              const int slot = 32 * (t - n_band) + kk;
-              ok &= (slot < ng) && ((unsigned)(sm.gsp[min(slot, kGCap - 1)] - lo_u) > span_u);
-            }
-            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[i + e], a.sl2, -lse2)) : 0.0f;
-            ds2[e] = p * (dp[i + e] - dlt);
+          for (int i = 0; i < 16; i += 2) {
+            const bool k0 = (unsigned)(mb + brow(i, hi)) <= (unsigned)lim;
+            const bool k1 = (unsigned)(mb + brow(i + 1, hi)) <= (unsigned)lim;
+            mk[i / 2] = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
           }
-          dsw[i / 2] = pack2(ds2[0], ds2[1]);
+        } else {
+          // A global key is scored here unless the row's band already holds it.
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            bool ok[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int slot = 32 * (t - n_band) + brow(i + e, hi);
+              ok[e] = row_ok & (slot < ng) &
+                      ((unsigned)(sm.gsp[min(slot, kGCap - 1)] - lo_u) > span_u);
+            }
+            mk[i / 2] = (ok[0] ? 0x0000ffffu : 0u) | (ok[1] ? 0xffff0000u : 0u);
+          }
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dsw[i] &= mk[i];
       }
       const unsigned xb = (unsigned)(uintptr_t)(LDS_AS void*)sm.x[st][kq];
       if constexpr (kLean) {
