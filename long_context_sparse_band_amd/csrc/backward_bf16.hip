@@ -290,7 +290,7 @@ constexpr int bwd_wpe() { return D == 64 ? 3 : 2; }
 // loop, instead of holding them (which would spill inside the loop).
 template <int D, int KS, int WPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void bwd_rows_kernel(BwdArgs a) {
+void bwd_rows_kernel(const BandWork* __restrict__ work, BwdArgs a) {
   constexpr bool kLean = WPE > bwd_wpe<D>();
   constexpr int RB = 4 / KS, IR = 32 * RB;  // row blocks, rows per item
   constexpr int kBD = D, TILE = BwdDim<D>::TILE, CPR = BwdDim<D>::CPR;
@@ -299,7 +299,7 @@ void bwd_rows_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rb = wave % RB, kq = wave / RB;
   const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
-  const BandWork w = a.work[blockIdx.x];
+  const BandWork w = work[blockIdx.x];
   const bool gi = w.dil == 0;
   const int d = gi ? 1 : w.dil, r = gi ? 0 : w.r, N = a.N;
   const int Lr = d == 1 ? N - r : (N - r + d - 1) / d;
@@ -548,7 +548,7 @@ void bwd_rows_kernel(BwdArgs a) {
 // instantiation: a second pass over the gathered global rows).
 template <int D, int KS, bool PROJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_wpe<D>(), bwd_wpe<D>())))
-void bwd_keys_kernel(BwdArgs a) {
+void bwd_keys_kernel(const BandWork* __restrict__ work, BwdArgs a) {
   constexpr int RB = 4 / KS, IK = 32 * RB;  // key blocks, keys per item
   constexpr int kBD = D, TILE = BwdDim<D>::TILE, CPR = BwdDim<D>::CPR;
   __shared__ __attribute__((aligned(16))) BwdSmem<D> sm;
@@ -556,7 +556,7 @@ void bwd_keys_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rb = wave % RB, kq = wave / RB;
   const int lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
-  const BandWork w = a.work[blockIdx.x];
+  const BandWork w = work[blockIdx.x];
   const bool gk = w.dil == 0;
   const int d = gk ? 1 : w.dil, r = gk ? 0 : w.r, N = a.N;
   const int Lr = d == 1 ? N - r : (N - r + d - 1) / d;

@@ -908,9 +908,9 @@ __device__ __forceinline__ void band_item(const BandArgs& a, const BandWork& w, 
 template <int D, int KS, bool CHUNK>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(B32<D, KS>::WPE, B32<D, KS>::WPE)))
-void band32_kernel(BandArgs a) {
+void band32_kernel(const BandWork* __restrict__ work, BandArgs a) {
   __shared__ __attribute__((aligned(16))) BandSmem<D, KS> sm;
-  const BandWork w = a.work[blockIdx.x];
+  const BandWork w = work[blockIdx.x];
   if constexpr (global_ks<D, KS>() != KS) {
     if (w.dil == 0) {
       band_item<D, global_ks<D, KS>(), CHUNK>(a, w, sm);

@@ -156,6 +156,19 @@ inline hipError_t launch_kernel(void (*k)(A), dim3 grid, dim3 block, hipStream_t
                             t.stop, 0);
 }
 
+// Kernels that take the work table as a separate first argument: the build
+// preloads the first kernel-argument dwords into scalar registers, so each
+// wavefront's load of its work item goes out at once instead of after the
+// load of the argument block.
+template <typename A>
+inline hipError_t launch_kernel(void (*k)(const BandWork*, A), dim3 grid, dim3 block,
+                                hipStream_t s, const A& a, const Timing& t) {
+  const BandWork* work = a.work;
+  void* args[] = {const_cast<BandWork**>(&work), const_cast<A*>(&a)};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, 0, s, t.start,
+                            t.stop, 0);
+}
+
 // Launchers (defined next to the kernels).  dtype: 0 fp32, 1 bf16.
 hipError_t launch_band(int dtype, int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t);
 hipError_t launch_band_bf16(int D, const BandArgs& a, int n_wg, hipStream_t s, const Timing& t);
