@@ -24,9 +24,10 @@ def command(out: str):
     return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
             # Packed fp32 VALU forms are kept out of the generated code.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # The first two kernel-argument dwords (the work-table pointer of
-            # the band and backward kernels) arrive preloaded in SGPRs.
-            "-mllvm", "-amdgpu-kernarg-preload-count=2",
+            # The leading scalar kernel arguments (the work-table pointer of
+            # the band and backward kernels, the record base and geometry of
+            # the global-row merge) arrive preloaded in SGPRs.
+            "-mllvm", "-amdgpu-kernarg-preload-count=6",
             "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
             *sources(), "-o", out]
 

@@ -468,9 +468,15 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
 // row); thread (g, q) combines chunks g, g + 16, ... for columns 4q .. 4q+3
 // (D = 64: 16 column quads; D = 128: each thread takes two quads), then the
 // 16 chunk groups are combined through LDS.  Every chunk record is loaded
-// once, in one round of independent loads per thread.
+// once, two chunks' loads in flight per thread.  The records' base and
+// geometry come ahead of the argument block as scalars the build preloads
+// into SGPRs, so that the record loads go out before any argument load
+// returns; the batch element's list extent is read alongside them (a slot
+// past its end reads records that exist but hold nothing, and stores none).
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
+__global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict__ part,
+                                                         int n_glob, int rows, int n_sets,
+                                                         int n_chunks, GlobArgs a) {
   typedef typename ElemT<BF16>::type E;
   constexpr int REC = D + 4;
   constexpr int NQ = D / 4;          // column quads
@@ -478,26 +484,17 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
   constexpr int NG = 16;             // chunk groups
   __shared__ float sm_m[NG][16], sm_l[NG][16];
   __shared__ float4 sm_a[NG][NQ];
-  const int slot = blockIdx.x % a.n_glob;
-  const int bh = blockIdx.x / a.n_glob;
-  // Slots past the end of this batch element's global list have no row.
-  const int2 gs = a.gsel[bh / a.H];
-  if (slot >= gs.y) return;
+  const int slot = blockIdx.x % n_glob;
+  const int bh = blockIdx.x / n_glob;
   const int q0 = threadIdx.x & 15, g = threadIdx.x >> 4;
-  const int rows = a.rows_per_set;
   const int set = slot / rows, rr = slot % rows;
-  const float* part0 = a.part + ((size_t)(bh * a.n_sets + set) * a.n_chunks * rows + rr) * REC;
+  const float* part0 = part + ((size_t)(bh * n_sets + set) * n_chunks * rows + rr) * REC;
   const size_t cs = (size_t)rows * REC;
   float m = kNegInit, l = 0.0f;
   float4 acc[QPT];
 #pragma unroll
   for (int t = 0; t < QPT; ++t) acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = g; c < a.n_chunks; c += NG) {
-    const float* rec = part0 + (size_t)c * cs;
-    const float2 ml = *(const float2*)rec;
-    float4 v[QPT];
-#pragma unroll
-    for (int t = 0; t < QPT; ++t) v[t] = *(const float4*)(rec + 4 + 4 * (q0 + 16 * t));
+  auto combine = [&](const float2 ml, const float4* v) {
     const float mn = fmaxf(m, ml.x);
     const float a0 = fast_exp2(m - mn), a1 = fast_exp2(ml.x - mn);
     l = l * a0 + ml.y * a1;
@@ -509,7 +506,30 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
       acc[t].w = acc[t].w * a0 + v[t].w * a1;
     }
     m = mn;
+  };
+  for (int c = g; c < n_chunks; c += 2 * NG) {
+    // Chunks c and c + NG (the second when there is one), both loaded
+    // before either is combined.
+    const bool two = c + NG < n_chunks;
+    const float* r0 = part0 + (size_t)c * cs;
+    const float2 ml0 = *(const float2*)r0;
+    float4 v0[QPT], v1[QPT];
+    float2 ml1 = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int t = 0; t < QPT; ++t) v0[t] = *(const float4*)(r0 + 4 + 4 * (q0 + 16 * t));
+    if (two) {
+      const float* r1 = r0 + (size_t)NG * cs;
+      ml1 = *(const float2*)r1;
+#pragma unroll
+      for (int t = 0; t < QPT; ++t) v1[t] = *(const float4*)(r1 + 4 + 4 * (q0 + 16 * t));
+    }
+    combine(ml0, v0);
+    if (two) combine(ml1, v1);
   }
+  // Slots past the end of this batch element's global list have no row.
+  const int2 gs = a.gsel[bh / a.H];
+  if (slot >= gs.y) return;
+  const int orow = a.glob[gs.x + slot];
   sm_m[g][q0] = m;
   sm_l[g][q0] = l;
 #pragma unroll
@@ -537,7 +557,6 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(GlobArgs a) {
     }
   }
   const float inv = 1.0f / lt;
-  const int orow = a.glob[gs.x + slot];
   if (a.lse && q0 == 0)
     a.lse[(size_t)bh * a.N + orow] = (mt + __log2f(lt)) * 0.6931471805599453f;
   E* Orow = (E*)a.O + (size_t)bh * a.N * D + (size_t)orow * D;
@@ -589,11 +608,19 @@ hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s,
   if (n_wg <= 0) return hipSuccess;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n_wg), block(256);
-  if (dtype == 1 && D == 64) return launch_kernel(glob_merge_kernel<true, 64>, grid, block, s, a, t);
-  if (dtype == 1 && D == 128) return launch_kernel(glob_merge_kernel<true, 128>, grid, block, s, a, t);
-  if (dtype == 0 && D == 64) return launch_kernel(glob_merge_kernel<false, 64>, grid, block, s, a, t);
-  if (dtype == 0 && D == 128) return launch_kernel(glob_merge_kernel<false, 128>, grid, block, s, a, t);
-  return hipErrorInvalidValue;
+  void (*k)(const float*, int, int, int, int, GlobArgs) = nullptr;
+  if (dtype == 1 && D == 64) k = glob_merge_kernel<true, 64>;
+  if (dtype == 1 && D == 128) k = glob_merge_kernel<true, 128>;
+  if (dtype == 0 && D == 64) k = glob_merge_kernel<false, 64>;
+  if (dtype == 0 && D == 128) k = glob_merge_kernel<false, 128>;
+  if (!k || a.n_glob <= 0 || a.rows_per_set <= 0 || a.n_sets <= 0 || a.n_chunks <= 0)
+    return hipErrorInvalidValue;
+  const float* part = a.part;
+  int n_glob = a.n_glob, rows = a.rows_per_set, n_sets = a.n_sets, n_chunks = a.n_chunks;
+  void* args[] = {const_cast<float**>(&part), &n_glob, &rows, &n_sets, &n_chunks,
+                  const_cast<GlobArgs*>(&a)};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, 0, s, t.start,
+                            t.stop, 0);
 }
 
 }  // namespace lfattn
