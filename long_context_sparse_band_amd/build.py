@@ -25,9 +25,9 @@ def command(out: str):
             # Packed fp32 VALU forms are kept out of the generated code.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # The leading scalar kernel arguments (the work-table pointer of
-            # the band and backward kernels, the record base and geometry of
-            # the global-row merge) arrive preloaded in SGPRs.
-            "-mllvm", "-amdgpu-kernarg-preload-count=6",
+            # the band and backward kernels, the record base, list extents and
+            # geometry of the merge kernels) arrive preloaded in SGPRs.
+            "-mllvm", "-amdgpu-kernarg-preload-count=9",
             "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
             *sources(), "-o", out]
 

@@ -908,19 +908,42 @@ void bwd_keys_kernel(const BandWork* __restrict__ work, BwdArgs a) {
 // Global rows and keys: the sums of the chunks' partial gradients.
 // ---------------------------------------------------------------------------
 // One workgroup per (b*h, global slot), 3 D threads: plane (dQ, dK, dV) and
-// column; each adds the slot's partials over the chunks and writes the row.
+// column; each adds the slot's partials over the chunks (in chunk order) and
+// writes the row.  The partials' base and geometry and the per-batch list
+// extents come ahead of the argument block as scalars the build preloads into
+// SGPRs, so that the partial loads and the list-extent load go out before any
+// argument load returns (a slot past the end of its batch element's list
+// reads partials that exist but hold nothing, and stores none).
 template <int D>
-__global__ __launch_bounds__(3 * D) void bwd_merge_kernel(BwdArgs a) {
+__global__ __launch_bounds__(3 * D) void bwd_merge_kernel(const float* __restrict__ gpart,
+                                                         const int2* __restrict__ gsel,
+                                                         int n_glob, int n_gch, int n_bh, int H,
+                                                         BwdArgs a) {
   constexpr int kBD = D;
-  const int bh = blockIdx.x / a.n_glob, g = blockIdx.x % a.n_glob;
-  const int2 gs = a.gsel[bh / a.H];
-  if (g >= gs.y) return;
+  constexpr int kFirst = 16;  // chunks loaded before the list extent is read
+  const int bh = blockIdx.x / n_glob, g = blockIdx.x % n_glob;
   const int pl = threadIdx.x / D, col = threadIdx.x % D;
-  const size_t plane = (size_t)a.n_bh * a.n_gch * a.n_glob * kBD;
-  const float* src = a.gpart + pl * plane + ((size_t)bh * a.n_gch * a.n_glob + g) * kBD + col;
+  const size_t plane = (size_t)n_bh * n_gch * n_glob * kBD;
+  const size_t step = (size_t)n_glob * kBD;
+  const float* src = gpart + pl * plane + ((size_t)bh * n_gch * n_glob + g) * kBD + col;
+  // (Addresses clamped to the last chunk, the values past it dropped in the
+  // sum: no branches between the loads.)
+  float v[kFirst];
+#pragma unroll
+  for (int ch = 0; ch < kFirst; ++ch) v[ch] = src[(size_t)min(ch, n_gch - 1) * step];
+  const int2 gs = gsel[bh / H];
+  // The sum starts from a value this statement defines, after the list
+  // extent has arrived: the extent's load is then in flight with the
+  // partials' loads instead of being sunk to the end.
   float sum = 0.0f;
+  asm volatile("" : "+v"(sum) : "s"(gs.x), "s"(gs.y) : "memory");
+  // In chunk order (the trailing zeros of a shorter list add nothing: the
+  // sum is never -0).
+#pragma unroll
+  for (int ch = 0; ch < kFirst; ++ch) sum += ch < n_gch ? v[ch] : 0.0f;
 #pragma unroll 8
-  for (int ch = 0; ch < a.n_gch; ++ch) sum += src[(size_t)ch * a.n_glob * kBD];
+  for (int ch = kFirst; ch < n_gch; ++ch) sum += src[ch * step];
+  if (g >= gs.y) return;
   // The global rows' dQ partials: their Qg gradient with separate
   // projections (and no Q gradient).
   float* dst = pl == 0 ? (a.proj ? a.dQg : a.dQ) : (pl == 1 ? a.dK : a.dV);
@@ -942,8 +965,15 @@ static hipError_t launch_backward_d(const BwdArgs& rows, const BwdArgs& keys, in
                       : (keys.ks == 2 ? bwd_keys_kernel<D, 2, false> : bwd_keys_kernel<D, 1, false>);
   e = launch_kernel(kk, dim3(n_keys_wg), dim3(256), s, keys, t[1]);
   if (e != hipSuccess || keys.n_glob <= 0) return e;
-  return launch_kernel(bwd_merge_kernel<D>, dim3((unsigned)(keys.n_bh * keys.n_glob)),
-                       dim3(3 * D), s, keys, t[2]);
+  const float* gpart = keys.gpart;
+  int n_glob = keys.n_glob, n_gch = keys.n_gch, n_bh = keys.n_bh, H = keys.H;
+  if (n_gch <= 0 || H <= 0) return hipErrorInvalidValue;
+  const int2* gsel = keys.gsel;
+  void* args[] = {const_cast<float**>(&gpart), const_cast<int2**>(&gsel), &n_glob, &n_gch,
+                  &n_bh, &H, const_cast<BwdArgs*>(&keys)};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(bwd_merge_kernel<D>),
+                            dim3((unsigned)(n_bh * n_glob)), dim3(3 * D), args, 0, s,
+                            t[2].start, t[2].stop, 0);
 }
 
 hipError_t launch_backward_bf16(const BwdArgs& rows, const BwdArgs& keys, int n_rows_wg,

@@ -469,14 +469,16 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
 // (D = 64: 16 column quads; D = 128: each thread takes two quads), then the
 // 16 chunk groups are combined through LDS.  Every chunk record is loaded
 // once, two chunks' loads in flight per thread.  The records' base and
-// geometry come ahead of the argument block as scalars the build preloads
-// into SGPRs, so that the record loads go out before any argument load
-// returns; the batch element's list extent is read alongside them (a slot
-// past its end reads records that exist but hold nothing, and stores none).
+// geometry and the per-batch list extents come ahead of the argument block as
+// scalars the build preloads into SGPRs (per_b: workgroups per batch element),
+// so that the record loads and the list-extent load go out before any
+// argument load returns (a slot past the end of its batch element's list
+// reads records that exist but hold nothing, and stores none).
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict__ part,
+                                                         const int2* __restrict__ gsel,
                                                          int n_glob, int rows, int n_sets,
-                                                         int n_chunks, GlobArgs a) {
+                                                         int n_chunks, int per_b, GlobArgs a) {
   typedef typename ElemT<BF16>::type E;
   constexpr int REC = D + 4;
   constexpr int NQ = D / 4;          // column quads
@@ -507,7 +509,27 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
     }
     m = mn;
   };
-  for (int c = g; c < n_chunks; c += 2 * NG) {
+  // The first chunk of this thread's group (clamped: a group past the last
+  // chunk loads the last record and combines an empty state instead), then
+  // the batch element's list extent, taken before anything is combined so
+  // that its load is in flight with the records'.
+  {
+    const bool have = g < n_chunks;
+    const float* r0 = part0 + (size_t)min(g, n_chunks - 1) * cs;
+    float2 ml0 = *(const float2*)r0;
+    float4 v0[QPT];
+#pragma unroll
+    for (int t = 0; t < QPT; ++t) v0[t] = *(const float4*)(r0 + 4 + 4 * (q0 + 16 * t));
+    const int2 gs0 = gsel[blockIdx.x / per_b];
+    asm volatile("" ::"s"(gs0.x), "s"(gs0.y) : "memory");
+    // (An empty state, maximum kNegInit and no weight, leaves (m, l, acc)
+    // as they are.)
+    ml0 = have ? ml0 : make_float2(kNegInit, 0.0f);
+#pragma unroll
+    for (int t = 0; t < QPT; ++t) v0[t] = have ? v0[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+    combine(ml0, v0);
+  }
+  for (int c = g + NG; c < n_chunks; c += 2 * NG) {
     // Chunks c and c + NG (the second when there is one), both loaded
     // before either is combined.
     const bool two = c + NG < n_chunks;
@@ -526,8 +548,8 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
     combine(ml0, v0);
     if (two) combine(ml1, v1);
   }
+  const int2 gs = gsel[blockIdx.x / per_b];
   // Slots past the end of this batch element's global list have no row.
-  const int2 gs = a.gsel[bh / a.H];
   if (slot >= gs.y) return;
   const int orow = a.glob[gs.x + slot];
   sm_m[g][q0] = m;
@@ -608,17 +630,20 @@ hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s,
   if (n_wg <= 0) return hipSuccess;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n_wg), block(256);
-  void (*k)(const float*, int, int, int, int, GlobArgs) = nullptr;
+  void (*k)(const float*, const int2*, int, int, int, int, int, GlobArgs) = nullptr;
   if (dtype == 1 && D == 64) k = glob_merge_kernel<true, 64>;
   if (dtype == 1 && D == 128) k = glob_merge_kernel<true, 128>;
   if (dtype == 0 && D == 64) k = glob_merge_kernel<false, 64>;
   if (dtype == 0 && D == 128) k = glob_merge_kernel<false, 128>;
   if (!k || a.n_glob <= 0 || a.rows_per_set <= 0 || a.n_sets <= 0 || a.n_chunks <= 0)
     return hipErrorInvalidValue;
+  if ((long long)a.n_glob * a.H > 0x7fffffffLL) return hipErrorInvalidValue;
   const float* part = a.part;
+  const int2* gsel = a.gsel;
   int n_glob = a.n_glob, rows = a.rows_per_set, n_sets = a.n_sets, n_chunks = a.n_chunks;
-  void* args[] = {const_cast<float**>(&part), &n_glob, &rows, &n_sets, &n_chunks,
-                  const_cast<GlobArgs*>(&a)};
+  int per_b = a.n_glob * a.H;
+  void* args[] = {const_cast<float**>(&part), const_cast<int2**>(&gsel), &n_glob, &rows,
+                  &n_sets, &n_chunks, &per_b, const_cast<GlobArgs*>(&a)};
   return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, 0, s, t.start,
                             t.stop, 0);
 }
