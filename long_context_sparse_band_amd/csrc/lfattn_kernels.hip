@@ -513,6 +513,7 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
   // chunk loads the last record and combines an empty state instead), then
   // the batch element's list extent, taken before anything is combined so
   // that its load is in flight with the records'.
+  int2 gs;
   {
     const bool have = g < n_chunks;
     const float* r0 = part0 + (size_t)min(g, n_chunks - 1) * cs;
@@ -520,8 +521,8 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
     float4 v0[QPT];
 #pragma unroll
     for (int t = 0; t < QPT; ++t) v0[t] = *(const float4*)(r0 + 4 + 4 * (q0 + 16 * t));
-    const int2 gs0 = gsel[blockIdx.x / per_b];
-    asm volatile("" ::"s"(gs0.x), "s"(gs0.y) : "memory");
+    gs = gsel[blockIdx.x / per_b];
+    asm volatile("" ::"s"(gs.x), "s"(gs.y) : "memory");
     // (An empty state, maximum kNegInit and no weight, leaves (m, l, acc)
     // as they are.)
     ml0 = have ? ml0 : make_float2(kNegInit, 0.0f);
@@ -548,7 +549,6 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
     combine(ml0, v0);
     if (two) combine(ml1, v1);
   }
-  const int2 gs = gsel[blockIdx.x / per_b];
   // Slots past the end of this batch element's global list have no row.
   if (slot >= gs.y) return;
   const int orow = a.glob[gs.x + slot];
