@@ -27,7 +27,7 @@ def command(out: str):
             # The leading scalar kernel arguments (the work-table pointer of
             # the band and backward kernels, the record base, list extents and
             # geometry of the merge kernels) arrive preloaded in SGPRs.
-            "-mllvm", "-amdgpu-kernarg-preload-count=9",
+            "-mllvm", "-amdgpu-kernarg-preload-count=11",
             "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC,
             *sources(), "-o", out]
 

@@ -469,16 +469,18 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
 // (D = 64: 16 column quads; D = 128: each thread takes two quads), then the
 // 16 chunk groups are combined through LDS.  Every chunk record is loaded
 // once, two chunks' loads in flight per thread.  The records' base and
-// geometry and the per-batch list extents come ahead of the argument block as
-// scalars the build preloads into SGPRs (per_b: workgroups per batch element),
-// so that the record loads and the list-extent load go out before any
-// argument load returns (a slot past the end of its batch element's list
-// reads records that exist but hold nothing, and stores none).
+// geometry, the per-batch list extents and the lists come ahead of the
+// argument block as scalars the build preloads into SGPRs (per_b: workgroups
+// per batch element), so that the record loads, the list-extent load and the
+// row-position load go out before any argument load returns (a slot past the
+// end of its batch element's list reads records that exist but hold nothing,
+// and stores none).
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict__ part,
                                                          const int2* __restrict__ gsel,
-                                                         int n_glob, int rows, int n_sets,
-                                                         int n_chunks, int per_b, GlobArgs a) {
+                                                         const int* glob, int n_glob, int rows,
+                                                         int n_sets, int n_chunks, int per_b,
+                                                         GlobArgs a) {
   typedef typename ElemT<BF16>::type E;
   constexpr int REC = D + 4;
   constexpr int NQ = D / 4;          // column quads
@@ -514,6 +516,7 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
   // the batch element's list extent, taken before anything is combined so
   // that its load is in flight with the records'.
   int2 gs;
+  int orow;
   {
     const bool have = g < n_chunks;
     const float* r0 = part0 + (size_t)min(g, n_chunks - 1) * cs;
@@ -522,7 +525,13 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
 #pragma unroll
     for (int t = 0; t < QPT; ++t) v0[t] = *(const float4*)(r0 + 4 + 4 * (q0 + 16 * t));
     gs = gsel[blockIdx.x / per_b];
-    asm volatile("" ::"s"(gs.x), "s"(gs.y) : "memory");
+    // (The output arguments are taken here too, so that their loads go out
+    // with this one instead of after the combine.)
+    asm volatile("" ::"s"(gs.x), "s"(gs.y), "s"(a.O), "s"(a.lse), "s"(a.N) : "memory");
+    // The row's position, its load issued now (an index clamped into the
+    // list for a slot past its end, whose value is not used).
+    orow = glob[gs.y > 0 ? gs.x + min(slot, gs.y - 1) : 0];
+    asm volatile("" ::: "memory");
     // (An empty state, maximum kNegInit and no weight, leaves (m, l, acc)
     // as they are.)
     ml0 = have ? ml0 : make_float2(kNegInit, 0.0f);
@@ -551,7 +560,6 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
   }
   // Slots past the end of this batch element's global list have no row.
   if (slot >= gs.y) return;
-  const int orow = a.glob[gs.x + slot];
   sm_m[g][q0] = m;
   sm_l[g][q0] = l;
 #pragma unroll
@@ -630,7 +638,7 @@ hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s,
   if (n_wg <= 0) return hipSuccess;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n_wg), block(256);
-  void (*k)(const float*, const int2*, int, int, int, int, int, GlobArgs) = nullptr;
+  void (*k)(const float*, const int2*, const int*, int, int, int, int, int, GlobArgs) = nullptr;
   if (dtype == 1 && D == 64) k = glob_merge_kernel<true, 64>;
   if (dtype == 1 && D == 128) k = glob_merge_kernel<true, 128>;
   if (dtype == 0 && D == 64) k = glob_merge_kernel<false, 64>;
@@ -640,10 +648,12 @@ hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s,
   if ((long long)a.n_glob * a.H > 0x7fffffffLL) return hipErrorInvalidValue;
   const float* part = a.part;
   const int2* gsel = a.gsel;
+  const int* glob = a.glob;
   int n_glob = a.n_glob, rows = a.rows_per_set, n_sets = a.n_sets, n_chunks = a.n_chunks;
   int per_b = a.n_glob * a.H;
-  void* args[] = {const_cast<float**>(&part), const_cast<int2**>(&gsel), &n_glob, &rows,
-                  &n_sets, &n_chunks, &per_b, const_cast<GlobArgs*>(&a)};
+  void* args[] = {const_cast<float**>(&part), const_cast<int2**>(&gsel),
+                  const_cast<int**>(&glob), &n_glob, &rows, &n_sets, &n_chunks, &per_b,
+                  const_cast<GlobArgs*>(&a)};
   return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, 0, s, t.start,
                             t.stop, 0);
 }
