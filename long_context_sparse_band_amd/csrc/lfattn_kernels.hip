@@ -465,18 +465,19 @@ __global__ __launch_bounds__(WAVES * 64) void glob_kernel(GlobArgs a) {
 }
 
 // Merge of the global-row partials: one workgroup per (batch-head, global
-// row); thread (g, q) combines chunks g, g + 16, ... for columns 4q .. 4q+3
-// (D = 64: 16 column quads; D = 128: each thread takes two quads), then the
-// 16 chunk groups are combined through LDS.  Every chunk record is loaded
-// once, two chunks' loads in flight per thread.  The records' base and
+// row) of NG groups of 16 threads; thread (g, q) combines chunks g, g + NG,
+// ... for columns 4q .. 4q+3 (D = 64: 16 column quads; D = 128: each thread
+// takes two quads), then the NG chunk groups are combined through LDS.  Every
+// chunk record is loaded once: the first 16 chunks in one round (16 / NG per
+// thread), later ones two per thread at a time.  The records' base and
 // geometry, the per-batch list extents and the lists come ahead of the
 // argument block as scalars the build preloads into SGPRs (per_b: workgroups
 // per batch element), so that the record loads, the list-extent load and the
 // row-position load go out before any argument load returns (a slot past the
 // end of its batch element's list reads records that exist but hold nothing,
 // and stores none).
-template <bool BF16, int D>
-__global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict__ part,
+template <bool BF16, int D, int NG>
+__global__ __launch_bounds__(NG * 16) void glob_merge_kernel(const float* __restrict__ part,
                                                          const int2* __restrict__ gsel,
                                                          const int* glob, int n_glob, int rows,
                                                          int n_sets, int n_chunks, int per_b,
@@ -485,7 +486,10 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
   constexpr int REC = D + 4;
   constexpr int NQ = D / 4;          // column quads
   constexpr int QPT = NQ / 16;       // quads per thread
-  constexpr int NG = 16;             // chunk groups
+  // NG chunk groups of 16 threads; the first round loads FIRST chunks per
+  // thread (16 chunks over the groups).
+  constexpr int FIRST = 16 / NG;
+  static_assert(NG * FIRST == 16, "chunk groups");
   __shared__ float sm_m[NG][16], sm_l[NG][16];
   __shared__ float4 sm_a[NG][NQ];
   const int slot = blockIdx.x % n_glob;
@@ -511,19 +515,22 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
     }
     m = mn;
   };
-  // The first chunk of this thread's group (clamped: a group past the last
-  // chunk loads the last record and combines an empty state instead), then
-  // the batch element's list extent, taken before anything is combined so
-  // that its load is in flight with the records'.
+  // The first chunks of this thread's group, g + NG f for f < FIRST (clamped:
+  // a chunk past the last loads the last record and combines an empty state
+  // instead), then the batch element's list extent, taken before anything is
+  // combined so that its load is in flight with the records'.
   int2 gs;
   int orow;
   {
-    const bool have = g < n_chunks;
-    const float* r0 = part0 + (size_t)min(g, n_chunks - 1) * cs;
-    float2 ml0 = *(const float2*)r0;
-    float4 v0[QPT];
+    float2 ml0[FIRST];
+    float4 v0[FIRST][QPT];
 #pragma unroll
-    for (int t = 0; t < QPT; ++t) v0[t] = *(const float4*)(r0 + 4 + 4 * (q0 + 16 * t));
+    for (int f = 0; f < FIRST; ++f) {
+      const float* r0 = part0 + (size_t)min(g + NG * f, n_chunks - 1) * cs;
+      ml0[f] = *(const float2*)r0;
+#pragma unroll
+      for (int t = 0; t < QPT; ++t) v0[f][t] = *(const float4*)(r0 + 4 + 4 * (q0 + 16 * t));
+    }
     gs = gsel[blockIdx.x / per_b];
     // (The output arguments are taken here too, so that their loads go out
     // with this one instead of after the combine.)
@@ -532,14 +539,19 @@ __global__ __launch_bounds__(256) void glob_merge_kernel(const float* __restrict
     // list for a slot past its end, whose value is not used).
     orow = glob[gs.y > 0 ? gs.x + min(slot, gs.y - 1) : 0];
     asm volatile("" ::: "memory");
-    // (An empty state, maximum kNegInit and no weight, leaves (m, l, acc)
-    // as they are.)
-    ml0 = have ? ml0 : make_float2(kNegInit, 0.0f);
 #pragma unroll
-    for (int t = 0; t < QPT; ++t) v0[t] = have ? v0[t] : make_float4(0.f, 0.f, 0.f, 0.f);
-    combine(ml0, v0);
+    for (int f = 0; f < FIRST; ++f) {
+      // (An empty state, maximum kNegInit and no weight, leaves (m, l, acc)
+      // as they are.)
+      const bool have = g + NG * f < n_chunks;
+      ml0[f] = have ? ml0[f] : make_float2(kNegInit, 0.0f);
+#pragma unroll
+      for (int t = 0; t < QPT; ++t)
+        v0[f][t] = have ? v0[f][t] : make_float4(0.f, 0.f, 0.f, 0.f);
+      combine(ml0[f], v0[f]);
+    }
   }
-  for (int c = g + NG; c < n_chunks; c += 2 * NG) {
+  for (int c = g + 16; c < n_chunks; c += 2 * NG) {
     // Chunks c and c + NG (the second when there is one), both loaded
     // before either is combined.
     const bool two = c + NG < n_chunks;
@@ -637,12 +649,16 @@ hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s,
   const long long n_wg = (long long)a.n_bh * a.n_glob;
   if (n_wg <= 0) return hipSuccess;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)n_wg), block(256);
+  const dim3 grid((unsigned)n_wg);
+  // Sets of at most 16 chunks: one wavefront per row (4 chunk groups, each
+  // loading its 4 chunks at once); more: 16 groups.
+  const bool small = a.n_chunks <= 16;
+  const dim3 blk(small ? 64 : 256);
   void (*k)(const float*, const int2*, const int*, int, int, int, int, int, GlobArgs) = nullptr;
-  if (dtype == 1 && D == 64) k = glob_merge_kernel<true, 64>;
-  if (dtype == 1 && D == 128) k = glob_merge_kernel<true, 128>;
-  if (dtype == 0 && D == 64) k = glob_merge_kernel<false, 64>;
-  if (dtype == 0 && D == 128) k = glob_merge_kernel<false, 128>;
+  if (dtype == 1 && D == 64) k = small ? glob_merge_kernel<true, 64, 4> : glob_merge_kernel<true, 64, 16>;
+  if (dtype == 1 && D == 128) k = small ? glob_merge_kernel<true, 128, 4> : glob_merge_kernel<true, 128, 16>;
+  if (dtype == 0 && D == 64) k = small ? glob_merge_kernel<false, 64, 4> : glob_merge_kernel<false, 64, 16>;
+  if (dtype == 0 && D == 128) k = small ? glob_merge_kernel<false, 128, 4> : glob_merge_kernel<false, 128, 16>;
   if (!k || a.n_glob <= 0 || a.rows_per_set <= 0 || a.n_sets <= 0 || a.n_chunks <= 0)
     return hipErrorInvalidValue;
   if ((long long)a.n_glob * a.H > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -654,7 +670,7 @@ hipError_t launch_glob_merge(int dtype, int D, const GlobArgs& a, hipStream_t s,
   void* args[] = {const_cast<float**>(&part), const_cast<int2**>(&gsel),
                   const_cast<int**>(&glob), &n_glob, &rows, &n_sets, &n_chunks, &per_b,
                   const_cast<GlobArgs*>(&a)};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, 0, s, t.start,
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, blk, args, 0, s, t.start,
                             t.stop, 0);
 }
 
